@@ -1,0 +1,198 @@
+"""Python binding of the gfx950 routed mixture-of-experts library (libmoe.so).
+
+Argument marshalling only: every step of the block runs in the HIP kernels
+behind the C ABI of include/moe.h.  PyTorch supplies device memory and the
+current stream; nothing here computes.  If the library is not built the
+import of this module fails loudly: there is no fallback path.
+"""
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+F32, BF16, Q2K, Q8_0, CB2 = 0, 1, 2, 3, 4
+ACCUMULATE = 1
+STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EALIGN", -3: "MOE_EWORKSPACE", -4: "MOE_EUNSUPPORTED",
+          -5: "MOE_EDEVICE"}
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libmoe.so is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
+                      "(or python quantized_routed_moe_router_amd/build.py) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+
+class LayerDesc(ctypes.Structure):
+    """moe_layer_desc (host struct of device pointers)."""
+    _fields_ = [
+        ("n_embd", ctypes.c_int32), ("n_expert", ctypes.c_int32), ("n_expert_used", ctypes.c_int32),
+        ("n_ff_exp", ctypes.c_int32), ("n_ff_shared", ctypes.c_int32),
+        ("gate_type", ctypes.c_int32), ("up_type", ctypes.c_int32), ("down_type", ctypes.c_int32),
+        ("shared_type", ctypes.c_int32),
+        ("router_w", ctypes.c_void_p), ("router_bias", ctypes.c_void_p), ("route_scale", ctypes.c_float),
+        ("gate", ctypes.c_void_p), ("up", ctypes.c_void_p), ("down", ctypes.c_void_p),
+        ("sh_gate", ctypes.c_void_p), ("sh_up", ctypes.c_void_p), ("sh_down", ctypes.c_void_p),
+        ("codebook", ctypes.c_void_p),
+    ]
+
+
+class RoutingStruct(ctypes.Structure):
+    """moe_routing (host struct of device pointers)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("topk_idx", "topk_w", "count", "offset", "perm", "pos", "active", "n_active")]
+
+
+_P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_lib.moe_workspace_size.restype = _SZ
+_lib.moe_workspace_size.argtypes = [ctypes.POINTER(LayerDesc), _I32, _I32]
+_lib.moe_route.argtypes = [ctypes.POINTER(LayerDesc), _P, _I32, _I32, ctypes.POINTER(RoutingStruct), _P, _SZ, _P,
+                           ctypes.c_char_p, _SZ]
+_lib.moe_expert_ffn.argtypes = [ctypes.POINTER(LayerDesc), _P, _I32, _I32, ctypes.POINTER(RoutingStruct), _P,
+                                ctypes.c_uint32, _P, _SZ, _P, ctypes.c_char_p, _SZ]
+_lib.moe_layer_forward.argtypes = [ctypes.POINTER(LayerDesc), _P, _I32, _I32, _P, ctypes.c_uint32,
+                                   ctypes.POINTER(RoutingStruct), _P, _SZ, _P, ctypes.c_char_p, _SZ]
+_lib.moe_rmsnorm.argtypes = [_P, _P, ctypes.c_float, _I32, _I32, _P, _P, ctypes.c_char_p, _SZ]
+_lib.moe_dequant.argtypes = [_I32, _P, _I64, _P, _I32, _P, _P, ctypes.c_char_p, _SZ]
+_lib.moe_version.restype = ctypes.c_char_p
+for _f in ("moe_route", "moe_expert_ffn", "moe_layer_forward", "moe_rmsnorm", "moe_dequant"):
+    getattr(_lib, _f).restype = ctypes.c_int
+
+
+class MoEError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__("%s (%d): %s" % (STATUS.get(code, "?"), code, msg))
+        self.code = code
+
+
+def _check(rc, buf):
+    if rc != 0:
+        raise MoEError(rc, buf.value.decode(errors="replace"))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def version():
+    return _lib.moe_version().decode()
+
+
+@dataclass
+class LayerWeights:
+    """One layer's device tensors (uint8 for block formats) and its shape."""
+    n_embd: int
+    n_expert: int
+    n_expert_used: int
+    n_ff_exp: int
+    n_ff_shared: int
+    gate_type: int
+    up_type: int
+    down_type: int
+    shared_type: int
+    router_w: torch.Tensor
+    gate: torch.Tensor
+    up: torch.Tensor
+    down: torch.Tensor
+    sh_gate: Optional[torch.Tensor] = None
+    sh_up: Optional[torch.Tensor] = None
+    sh_down: Optional[torch.Tensor] = None
+    router_bias: Optional[torch.Tensor] = None
+    route_scale: float = 1.0
+    codebook: Optional[torch.Tensor] = None
+    gamma: Optional[torch.Tensor] = None
+
+    def desc(self):
+        return LayerDesc(self.n_embd, self.n_expert, self.n_expert_used, self.n_ff_exp, self.n_ff_shared,
+                         self.gate_type, self.up_type, self.down_type, self.shared_type,
+                         self.router_w.data_ptr(), _ptr(self.router_bias), float(self.route_scale),
+                         self.gate.data_ptr(), self.up.data_ptr(), self.down.data_ptr(),
+                         _ptr(self.sh_gate), _ptr(self.sh_up), _ptr(self.sh_down), _ptr(self.codebook))
+
+
+class Routing:
+    """Caller-owned routing arrays for T rows (device int32 / fp32 tensors)."""
+
+    def __init__(self, T, k, E, device="cuda"):
+        i32 = dict(dtype=torch.int32, device=device)
+        self.topk_idx = torch.empty((T, k), **i32)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=device)
+        self.count = torch.empty(E, **i32)
+        self.offset = torch.empty(E + 1, **i32)
+        self.perm = torch.empty(T * k, **i32)
+        self.pos = torch.empty(T * k, **i32)
+        self.active = torch.empty(E, **i32)
+        self.n_active = torch.empty(1, **i32)
+
+    def struct(self):
+        return RoutingStruct(*[t.data_ptr() for t in (self.topk_idx, self.topk_w, self.count, self.offset,
+                                                      self.perm, self.pos, self.active, self.n_active)])
+
+
+def _xtype(x):
+    if x.dtype == torch.float32:
+        return F32
+    if x.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError("x must be float32 or bfloat16, got %s" % x.dtype)
+
+
+def workspace_size(layer, max_rows, x_type=F32):
+    d = layer.desc()
+    return int(_lib.moe_workspace_size(ctypes.byref(d), max_rows, x_type))
+
+
+def alloc_workspace(layer, max_rows, x_type=F32, device="cuda"):
+    n = workspace_size(layer, max_rows, x_type)
+    if n == 0:
+        raise MoEError(-1, "invalid layer descriptor")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _rows(x):
+    if x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [T][D] tensor")
+    return x.shape[0]
+
+
+def route(layer, x, routing, ws, stream=None):
+    d, r, err = layer.desc(), routing.struct(), ctypes.create_string_buffer(512)
+    _check(_lib.moe_route(ctypes.byref(d), _ptr(x), _rows(x), _xtype(x), ctypes.byref(r), _ptr(ws), ws.numel(),
+                          _stream(stream), err, 512), err)
+
+
+def expert_ffn(layer, x, routing, y, ws, accumulate=False, stream=None):
+    d, r, err = layer.desc(), routing.struct(), ctypes.create_string_buffer(512)
+    _check(_lib.moe_expert_ffn(ctypes.byref(d), _ptr(x), _rows(x), _xtype(x), ctypes.byref(r), _ptr(y),
+                               ACCUMULATE if accumulate else 0, _ptr(ws), ws.numel(), _stream(stream), err, 512),
+           err)
+
+
+def layer_forward(layer, x, y, ws, routing=None, accumulate=False, stream=None):
+    d, err = layer.desc(), ctypes.create_string_buffer(512)
+    r = routing.struct() if routing is not None else None
+    _check(_lib.moe_layer_forward(ctypes.byref(d), _ptr(x), _rows(x), _xtype(x), _ptr(y),
+                                  ACCUMULATE if accumulate else 0, ctypes.byref(r) if r is not None else None,
+                                  _ptr(ws), ws.numel(), _stream(stream), err, 512), err)
+
+
+def rmsnorm(x, gamma, out, eps=1e-6, stream=None):
+    err = ctypes.create_string_buffer(512)
+    _check(_lib.moe_rmsnorm(_ptr(x), _ptr(gamma), eps, x.shape[0], x.shape[1], _ptr(out), _stream(stream), err,
+                            512), err)
+
+
+def dequant(fmt, src, n_weights, out, codebook=None, stream=None):
+    err = ctypes.create_string_buffer(512)
+    ot = BF16 if out.dtype == torch.bfloat16 else F32
+    _check(_lib.moe_dequant(fmt, _ptr(src), n_weights, _ptr(codebook), ot, _ptr(out), _stream(stream), err, 512),
+           err)

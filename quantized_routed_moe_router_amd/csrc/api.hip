@@ -1,0 +1,182 @@
+// api.hip - the C ABI declared in include/moe.h: argument validation (all of
+// it before anything is enqueued), workspace sizing, and the launches.
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+int fail(char *err, size_t errlen, int code, const char *fmt, ...) {
+    if (err && errlen) {
+        va_list ap;
+        va_start(ap, fmt);
+        vsnprintf(err, errlen, fmt, ap);
+        va_end(ap);
+    }
+    return code;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
+bool block_fmt(int f) { return f == MOE_Q2K || f == MOE_Q8_0 || f == MOE_CB2; }
+
+// Rows are split into 64-weight chunks, one per lane, up to 64 lanes per row.
+bool row_ok(int n_in) { return n_in > 0 && n_in % 64 == 0 && pow2(n_in / 64) && n_in / 64 <= 64; }
+
+int check_desc(const moe_layer_desc *d, char *err, size_t errlen) {
+    if (!d) return fail(err, errlen, MOE_EINVAL, "desc is NULL");
+    int D = d->n_embd, E = d->n_expert, k = d->n_expert_used, F = d->n_ff_exp, Fs = d->n_ff_shared;
+    if (D <= 0 || E <= 0 || k <= 0 || F <= 0 || Fs < 0)
+        return fail(err, errlen, MOE_EINVAL, "sizes must be positive (D=%d E=%d k=%d F=%d Fs=%d)", D, E, k, F, Fs);
+    if (E > kMaxExperts || k > kMaxUsed || k > E)
+        return fail(err, errlen, MOE_EUNSUPPORTED, "need 1 <= k <= min(16, E) and E <= 1024 (E=%d k=%d)", E, k);
+    if (D % 256 || !row_ok(D) || !row_ok(F) || (Fs && !row_ok(Fs)))
+        return fail(err, errlen, MOE_EUNSUPPORTED,
+                    "D must be a multiple of 256 and D, F, Fs of the form 64*2^j <= 4096 (D=%d F=%d Fs=%d)", D, F,
+                    Fs);
+    if (!block_fmt(d->gate_type) || d->up_type != d->gate_type || !block_fmt(d->down_type) ||
+        (Fs && !block_fmt(d->shared_type)))
+        return fail(err, errlen, MOE_EUNSUPPORTED,
+                    "formats: gate = up in {Q2K, Q8_0, CB2}, down and shared in {Q2K, Q8_0, CB2}");
+    if (!d->router_w || !d->gate || !d->up || !d->down)
+        return fail(err, errlen, MOE_EINVAL, "router_w, gate, up and down must be set");
+    if (Fs && (!d->sh_gate || !d->sh_up || !d->sh_down))
+        return fail(err, errlen, MOE_EINVAL, "n_ff_shared > 0 needs sh_gate, sh_up and sh_down");
+    bool cb = d->gate_type == MOE_CB2 || d->down_type == MOE_CB2 || (Fs && d->shared_type == MOE_CB2);
+    if (cb && !d->codebook) return fail(err, errlen, MOE_EINVAL, "a CB2 format needs the codebook");
+    const void *ptrs[] = {d->router_w, d->router_bias, d->gate, d->up, d->down, d->sh_gate, d->sh_up, d->sh_down,
+                          d->codebook};
+    for (const void *p : ptrs)
+        if (p && !aligned16(p)) return fail(err, errlen, MOE_EALIGN, "weight pointers must be 16-byte aligned");
+    return MOE_OK;
+}
+
+size_t ws_bytes_for(const moe_layer_desc *d, int32_t T) {
+    return workspace_layout(d, T, nullptr).bytes;
+}
+
+int check_call(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, void *ws, size_t ws_bytes,
+               char *err, size_t errlen) {
+    int rc = check_desc(d, err, errlen);
+    if (rc) return rc;
+    if (T < 0) return fail(err, errlen, MOE_EINVAL, "T must be >= 0 (T=%d)", T);
+    if (x_type != MOE_F32 && x_type != MOE_BF16)
+        return fail(err, errlen, MOE_EUNSUPPORTED, "x_type must be MOE_F32 or MOE_BF16");
+    if (T == 0) return MOE_OK;
+    if ((int64_t)T * d->n_expert_used > INT32_MAX / 2) return fail(err, errlen, MOE_EUNSUPPORTED, "T too large");
+    if (!x) return fail(err, errlen, MOE_EINVAL, "x is NULL");
+    if (!aligned16(x)) return fail(err, errlen, MOE_EALIGN, "x must be 16-byte aligned");
+    size_t need = ws_bytes_for(d, T);
+    if (!ws || ws_bytes < need)
+        return fail(err, errlen, MOE_EWORKSPACE, "workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : 0);
+    if (!aligned16(ws)) return fail(err, errlen, MOE_EALIGN, "workspace must be 16-byte aligned");
+    return MOE_OK;
+}
+
+int check_routing(const moe_routing *r, char *err, size_t errlen) {
+    if (!r) return fail(err, errlen, MOE_EINVAL, "routing is NULL");
+    if (!r->topk_idx || !r->topk_w || !r->count || !r->offset || !r->perm || !r->pos || !r->active || !r->n_active)
+        return fail(err, errlen, MOE_EINVAL, "every routing array must be set");
+    return MOE_OK;
+}
+
+RoutingPtrs from_routing(const moe_routing *r) {
+    return RoutingPtrs{r->topk_idx, r->topk_w, r->count, r->offset, r->perm, r->pos, r->active, r->n_active};
+}
+
+RoutingPtrs from_ws(const Workspace &w) {
+    return RoutingPtrs{w.topk_idx, w.topk_w, w.count, w.offset, w.perm, w.pos, w.active, w.n_active};
+}
+
+int device_status(hipError_t e, char *err, size_t errlen) {
+    if (e == hipSuccess) return MOE_OK;
+    return fail(err, errlen, MOE_EDEVICE, "HIP: %s", hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_layer_desc *d, int32_t max_rows, int32_t x_type) {
+    if (check_desc(d, nullptr, 0) || max_rows < 0 || (x_type != MOE_F32 && x_type != MOE_BF16)) return 0;
+    if (max_rows == 0) return 256;
+    // the router's chunking changes with T, so cover every plan up to max_rows
+    size_t b = ws_bytes_for(d, max_rows);
+    b = std::max(b, ws_bytes_for(d, std::min<int32_t>(max_rows, 4)));
+    b = std::max(b, ws_bytes_for(d, std::min<int32_t>(max_rows, 64)));
+    return b;
+}
+
+int moe_route(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const moe_routing *out, void *ws,
+              size_t ws_bytes, void *stream, char *err, size_t errlen) {
+    int rc = check_call(d, x, T, x_type, ws, ws_bytes, err, errlen);
+    if (rc) return rc;
+    if ((rc = check_routing(out, err, errlen))) return rc;
+    if (T == 0) return MOE_OK;
+    Workspace w = workspace_layout(d, T, ws);
+    return device_status(launch_route(d, x, T, x_type, from_routing(out), w, (hipStream_t)stream), err, errlen);
+}
+
+int moe_expert_ffn(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const moe_routing *r,
+                   float *y, uint32_t flags, void *ws, size_t ws_bytes, void *stream, char *err, size_t errlen) {
+    int rc = check_call(d, x, T, x_type, ws, ws_bytes, err, errlen);
+    if (rc) return rc;
+    if ((rc = check_routing(r, err, errlen))) return rc;
+    if (flags & ~(uint32_t)MOE_ACCUMULATE) return fail(err, errlen, MOE_EINVAL, "unknown flags 0x%x", flags);
+    if (T == 0) return MOE_OK;
+    if (!y) return fail(err, errlen, MOE_EINVAL, "y is NULL");
+    if (!aligned16(y)) return fail(err, errlen, MOE_EALIGN, "y must be 16-byte aligned");
+    Workspace w = workspace_layout(d, T, ws);
+    return device_status(launch_ffn_decode(d, x, T, x_type, from_routing(r), y, flags, w, (hipStream_t)stream),
+                         err, errlen);
+}
+
+int moe_layer_forward(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, float *y, uint32_t flags,
+                      const moe_routing *routing, void *ws, size_t ws_bytes, void *stream, char *err,
+                      size_t errlen) {
+    int rc = check_call(d, x, T, x_type, ws, ws_bytes, err, errlen);
+    if (rc) return rc;
+    if (routing && (rc = check_routing(routing, err, errlen))) return rc;
+    if (flags & ~(uint32_t)MOE_ACCUMULATE) return fail(err, errlen, MOE_EINVAL, "unknown flags 0x%x", flags);
+    if (T == 0) return MOE_OK;
+    if (!y) return fail(err, errlen, MOE_EINVAL, "y is NULL");
+    if (!aligned16(y)) return fail(err, errlen, MOE_EALIGN, "y must be 16-byte aligned");
+    Workspace w = workspace_layout(d, T, ws);
+    RoutingPtrs r = routing ? from_routing(routing) : from_ws(w);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = launch_route(d, x, T, x_type, r, w, s);
+    if (e == hipSuccess) e = launch_ffn_decode(d, x, T, x_type, r, y, flags, w, s);
+    return device_status(e, err, errlen);
+}
+
+int moe_rmsnorm(const float *x, const float *gamma, float eps, int32_t T, int32_t D, float *out, void *stream,
+                char *err, size_t errlen) {
+    if (T < 0 || D <= 0) return fail(err, errlen, MOE_EINVAL, "need T >= 0 and D > 0 (T=%d D=%d)", T, D);
+    if (!(eps >= 0.f)) return fail(err, errlen, MOE_EINVAL, "eps must be >= 0");
+    if (T == 0) return MOE_OK;
+    if (!x || !gamma || !out) return fail(err, errlen, MOE_EINVAL, "x, gamma and out must be set");
+    return device_status(launch_rmsnorm(x, gamma, eps, T, D, out, (hipStream_t)stream), err, errlen);
+}
+
+int moe_dequant(int32_t type, const void *src, int64_t n, const int8_t *codebook, int32_t out_type, void *dst,
+                void *stream, char *err, size_t errlen) {
+    if (!block_fmt(type)) return fail(err, errlen, MOE_EUNSUPPORTED, "type must be Q2K, Q8_0 or CB2");
+    if (out_type != MOE_F32 && out_type != MOE_BF16)
+        return fail(err, errlen, MOE_EUNSUPPORTED, "out_type must be MOE_F32 or MOE_BF16");
+    int64_t unit = type == MOE_Q8_0 ? 32 : 256;
+    if (n < 0 || n % unit) return fail(err, errlen, MOE_EINVAL, "n_weights must be a multiple of %lld", (long long)unit);
+    if (n == 0) return MOE_OK;
+    if (!src || !dst) return fail(err, errlen, MOE_EINVAL, "src and dst must be set");
+    if (type == MOE_CB2 && !codebook) return fail(err, errlen, MOE_EINVAL, "CB2 needs the codebook");
+    if (((uintptr_t)src & 3u) || ((uintptr_t)dst & 3u) || (codebook && ((uintptr_t)codebook & 3u)))
+        return fail(err, errlen, MOE_EALIGN, "src, dst and codebook must be 4-byte aligned");
+    return device_status(launch_dequant(type, src, n, codebook, out_type, dst, (hipStream_t)stream), err, errlen);
+}
+
+const char *moe_version(void) { return "moe-gfx950 0.1"; }
+
+}  // extern "C"

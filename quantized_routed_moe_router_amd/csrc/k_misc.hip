@@ -1,0 +1,73 @@
+// k_misc.hip - RMSNorm before each block ("Understanding Dwarf Star", 5.2.1
+// norm + residual, 5.6.2 step 1) and the dequantization test hook
+// ("Understanding Dwarf Star", 2.8.2 steps 1-3).
+#include "common.h"
+
+namespace moe {
+
+// One block per row: sum of squares in fp32 (fixed reduction tree), then
+// out = gamma * x / sqrt(mean + eps).
+__global__ void __launch_bounds__(256) rmsnorm_kernel(const float *__restrict__ x, const float *__restrict__ gamma,
+                                                      float eps, int D, float *__restrict__ out) {
+    __shared__ float red[4];
+    int t = blockIdx.x;
+    const float *xr = x + (int64_t)t * D;
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < D; i += 256) ss = __builtin_fmaf(xr[i], xr[i], ss);
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, kWave);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float tot = (red[0] + red[1]) + (red[2] + red[3]);
+    float inv = 1.0f / sqrtf(tot / (float)D + eps);
+    __syncthreads();  // all reads of x done before an in-place write
+    for (int i = threadIdx.x; i < D; i += 256) out[(int64_t)t * D + i] = gamma[i] * (xr[i] * inv);
+}
+
+hipError_t launch_rmsnorm(const float *x, const float *gamma, float eps, int32_t T, int32_t D, float *out,
+                          hipStream_t s) {
+    rmsnorm_kernel<<<T, 256, 0, s>>>(x, gamma, eps, D, out);
+    return hipGetLastError();
+}
+
+MOE_DEV void store_vals(void *dst, int out_bf16, int64_t at, const float *w, int n) {
+    if (out_bf16) {
+        uint16_t *o = (uint16_t *)dst + at;
+        for (int i = 0; i < n; ++i) o[i] = (uint16_t)float_to_bf16_bits(w[i]);
+    } else {
+        float *o = (float *)dst + at;
+        for (int i = 0; i < n; ++i) o[i] = w[i];
+    }
+}
+
+// One thread per 64-weight chunk (Q2K, CB2) or per 32-weight block (Q8_0).
+__global__ void __launch_bounds__(256) dequant_kernel(int type, const uint8_t *__restrict__ src, int64_t nunits,
+                                                      const int8_t *__restrict__ cb, int out_bf16, void *dst) {
+    __shared__ uint32_t cb_lds[512];
+    if (type == MOE_CB2) {
+        for (int i = threadIdx.x; i < 512; i += blockDim.x) cb_lds[i] = ((const uint32_t *)cb)[i];
+    }
+    __syncthreads();
+    int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (u >= nunits) return;
+    float w[64];
+    if (type == MOE_Q2K) {
+        q2k_values(q2k_load(src, 64 * u), w);
+        store_vals(dst, out_bf16, 64 * u, w, 64);
+    } else if (type == MOE_CB2) {
+        cb2_values(cb2_load(src, 64 * u), cb_lds, w);
+        store_vals(dst, out_bf16, 64 * u, w, 64);
+    } else {
+        q8_block_values(src + u * kQ8Bytes, w);
+        store_vals(dst, out_bf16, 32 * u, w, 32);
+    }
+}
+
+hipError_t launch_dequant(int32_t type, const void *src, int64_t n, const int8_t *cb, int32_t out_type, void *dst,
+                          hipStream_t s) {
+    int64_t units = type == MOE_Q8_0 ? n / 32 : n / 64;
+    dequant_kernel<<<(unsigned)((units + 255) / 256), 256, 0, s>>>(type, (const uint8_t *)src, units, cb,
+                                                                 out_type == MOE_BF16, dst);
+    return hipGetLastError();
+}
+
+}  // namespace moe

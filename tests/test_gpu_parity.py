@@ -1,0 +1,162 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs.  Integer results (indices, bucketing, decoded weights)
+must match bit for bit; fp32 outputs within |gpu-ref| <= 2e-3 (1+|ref|)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_bits_of(f32):
+    u = np.asarray(f32, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("fmt", [synth.Q2K, synth.Q8_0, synth.CB2])
+def test_dequant_bit_exact(fmt):
+    import quantized_routed_moe_router_amd as moe
+    cb = synth.codebook(4)
+    n = 256 * 96
+    b = synth.expert_tensor(fmt, 7, 0, 3, 1, n // 256, 256, codebook=cb)
+    ref = oracle.dequant(fmt, b, n, codebook=cb)
+    src = gu.dev(b)
+    cbd = gu.dev(cb) if fmt == synth.CB2 else None
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    moe.dequant(fmt, src, n, out, codebook=cbd)
+    outb = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    moe.dequant(fmt, src, n, outb, codebook=cbd)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    assert np.array_equal(outb.cpu().view(torch.int16).numpy().view(np.uint16), _bf16_bits_of(ref))
+    # code-sampled blocks (all fields uniform) decode the same way
+    b2 = synth.sampled_tensor(fmt, 8, 0, 3, 1, n // 256, 256, codebook=cb)
+    moe.dequant(fmt, gu.dev(b2), n, out, codebook=cbd)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), oracle.dequant(fmt, b2, n, codebook=cb).view(np.uint32))
+
+
+def _check_layer(L, T, seed, bf16=False, rows=None):
+    x = synth.activations(seed, T, L.n_embd)
+    kw = dict(x_bf16=synth.to_bf16_bits(x)) if bf16 else dict(x=x)
+    y_ref, idx_ref, w_ref = oracle.moe_forward(L, rows=rows, **kw)
+    W = gu.upload(L)
+    y, r = gu.run_forward(W, gu.x_to_device(**kw))
+    gu.check_routing(r, idx_ref, w_ref, L.n_expert)
+    yg = y.cpu().numpy()
+    sel = slice(None) if rows is None else rows
+    return gu.assert_close(yg[sel], y_ref[sel]), W, y
+
+
+def test_tiny_workload():
+    wl = synth.tiny()
+    _check_layer(wl.layers[0], wl.T, 0)
+
+
+@pytest.mark.parametrize("T", [1, 5, 37])
+@pytest.mark.parametrize("shared", [True, False])
+def test_mini_layers_several_tiles(T, shared):
+    L = synth.make_layer(50 + T, 0, D=512, E=32, k=4, F=256, Fs=128 if shared else 0)
+    _check_layer(L, T, 60 + T)
+
+
+@pytest.mark.parametrize("T", [3, 33])
+def test_bf16_small(T):
+    L = synth.make_layer(70, 0, D=512, E=32, k=4, F=256, Fs=128)
+    _check_layer(L, T, 71, bf16=True)
+
+
+def test_cb2_gate_up_layer():
+    cb = synth.codebook(4)
+    L = synth.make_layer(72, 0, D=1024, E=16, k=6, F=512, Fs=256, gate_fmt=synth.CB2, cb=cb)
+    _check_layer(L, 9, 73)
+
+
+@pytest.mark.parametrize("E,k", [(1, 1), (6, 6), (16, 1)])
+def test_degenerate_routings(E, k):
+    L = synth.make_layer(80 + E, 0, D=256, E=E, k=k, F=128, Fs=64)
+    _check_layer(L, 7, 81)
+
+
+def test_exact_ties_go_to_lower_index():
+    L = synth.make_layer(90, 0, D=256, E=16, k=3, F=128, Fs=0)
+    W = L.router_w.copy()
+    W[:, 12] = W[:, 3]
+    W[:, 9] = W[:, 3]
+    L.router_w = W
+    bias = np.zeros(16, np.float32)
+    bias[[3, 9, 12]] = 40.0
+    L.router_bias = bias
+    _check_layer(L, 6, 91)
+    _, idx, _ = oracle.moe_forward(L, x=synth.activations(91, 6, 256))
+    assert np.all(idx == [3, 9, 12])
+
+
+def test_route_scale_and_accumulate():
+    L = synth.make_layer(92, 0, D=512, E=32, k=4, F=256, Fs=128)
+    L.route_scale = 1.5
+    x = synth.activations(93, 4, 512)
+    y_ref, _, _ = oracle.moe_forward(L, x=x)
+    W = gu.upload(L)
+    y0 = torch.full((4, 512), 0.25, dtype=torch.float32, device="cuda")
+    y, _ = gu.run_forward(W, gu.x_to_device(x=x), accumulate=True, y0=y0)
+    gu.assert_close(y.cpu().numpy(), y_ref + np.float32(0.25))
+
+
+def test_zero_rows_is_a_no_op():
+    import quantized_routed_moe_router_amd as moe
+    L = synth.make_layer(94, 0, D=256, E=16, k=2, F=128, Fs=0)
+    W = gu.upload(L)
+    x = torch.empty((0, 256), dtype=torch.float32, device="cuda")
+    y = torch.empty((0, 256), dtype=torch.float32, device="cuda")
+    ws = torch.empty(256, dtype=torch.uint8, device="cuda")
+    moe.layer_forward(W, x, y, ws)
+    torch.cuda.synchronize()
+
+
+def test_run_twice_is_bitwise_identical_and_batch_invariant():
+    L = synth.make_layer(95, 0, D=512, E=32, k=4, F=256, Fs=128)
+    x = synth.activations(96, 32, 512)
+    W = gu.upload(L)
+    y1, r1 = gu.run_forward(W, gu.x_to_device(x=x))
+    y2, r2 = gu.run_forward(W, gu.x_to_device(x=x))
+    assert torch.equal(y1, y2) and torch.equal(r1.perm, r2.perm) and torch.equal(r1.topk_w, r2.topk_w)
+    # each row of the batch equals the same row evaluated alone
+    for t in (0, 7, 31):
+        yt, rt = gu.run_forward(W, gu.x_to_device(x=x[t:t + 1]))
+        assert torch.equal(rt.topk_idx[0], r1.topk_idx[t])
+        gu.assert_close(yt.cpu().numpy()[0], y1.cpu().numpy()[t], tol=1e-5)
+
+
+def test_route_then_expert_ffn_matches_layer_forward():
+    import quantized_routed_moe_router_amd as moe
+    L = synth.make_layer(97, 0, D=512, E=32, k=4, F=256, Fs=128)
+    x = gu.x_to_device(x=synth.activations(98, 11, 512))
+    W = gu.upload(L)
+    ws = moe.alloc_workspace(W, 11)
+    r = moe.Routing(11, 4, 32)
+    moe.route(W, x, r, ws)
+    y = torch.zeros((11, 512), dtype=torch.float32, device="cuda")
+    moe.expert_ffn(W, x, r, y, ws)
+    y2, _ = gu.run_forward(W, x)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2)
+
+
+def test_rmsnorm():
+    import quantized_routed_moe_router_amd as moe
+    x = synth.activations(99, 8, 4096)
+    g = (0.9 + 0.2 * synth.uniform(99, 0, synth.TAG_GAMMA, 0, 4096)).astype(np.float32)
+    ref = oracle.rmsnorm(x, g, 1e-6)
+    xd, gd = gu.dev(x), gu.dev(g)
+    out = torch.empty_like(xd)
+    moe.rmsnorm(xd, gd, out, 1e-6)
+    moe.rmsnorm(xd, gd, xd, 1e-6)  # in place
+    torch.cuda.synchronize()
+    gu.assert_close(out.cpu().numpy(), ref, tol=1e-5)
+    assert torch.equal(out, xd)

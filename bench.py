@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Throughput of the routed mixture-of-experts block on one MI355X.
+
+One step = one pass of the whole block (router logits, top-k, bucketing,
+gate/up dequant-GEMV with SwiGLU, down, shared expert, combine) over one
+batch of synthetic tokens with every input already resident in HBM.
+
+Default workload (the headline): decode of one token through a
+DeepSeek-V4-Flash-shaped layer (n_embd 4096, 256 routed experts, top-6, FFN
+width 2048, Q2K routed experts, Q8_0 shared expert, fp32 router), weights
+drawn from N(0, 0.02) and encoded, activations N(0, 1).
+
+Cold-cache timing: step i runs on device replica i % R of the layer (R x
+2.14 GB, far above the 256 MB last-level cache) with token i % 64, so no
+step finds the previous steps' weights in cache and the routing varies.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s; decode HBM GB/s and prefill MFMA % of MI355X peak"
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2048)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="decode_b1", choices=["decode_b1", "decode_b32", "prefill_2048"])
+    ap.add_argument("--replicas", type=int, default=16)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d, WORLD_SIZE %d). "
+              "Run it with --gpus 1." % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import quantized_routed_moe_router_amd as moe
+    import synth
+
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    L = synth.flash_layer()
+    log("layer generated in %.1f s" % (time.time() - t0))
+    if args.workload == "decode_b1":
+        T, n_x = 1, 64
+        x_all = synth.activations(1, n_x, L.n_embd)
+        mode = moe.F32
+    elif args.workload == "decode_b32":
+        T, n_x = 32, 8
+        x_all = synth.activations(2, 32 * n_x, L.n_embd)
+        L.router_bias = synth.zipf_bias(2, L.n_expert)
+        mode = moe.F32
+    else:
+        T, n_x = 2048, 1
+        x_all = synth.activations(3, 2048, L.n_embd)
+        mode = moe.BF16
+
+    dev = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    base = moe.LayerWeights(L.n_embd, L.n_expert, L.n_expert_used, L.n_ff_exp, L.n_ff_shared, L.gate_fmt,
+                            L.up_fmt, L.down_fmt, L.shared_fmt, dev(L.router_w), dev(L.gate), dev(L.up),
+                            dev(L.down), dev(L.sh_gate), dev(L.sh_up), dev(L.sh_down), dev(L.router_bias),
+                            L.route_scale)
+    R = max(1, args.replicas)
+    reps = [base]
+    for _ in range(R - 1):
+        reps.append(moe.LayerWeights(**{f: (getattr(base, f).clone() if isinstance(getattr(base, f), torch.Tensor)
+                                            else getattr(base, f)) for f in base.__dataclass_fields__}))
+    if mode == moe.BF16:
+        xs = torch.from_numpy(synth.to_bf16_bits(x_all).view(np.int16)).cuda().view(torch.bfloat16)
+    else:
+        xs = dev(x_all)
+    xin = [xs[(i % n_x) * T:(i % n_x) * T + T] for i in range(n_x)]
+    ws = moe.alloc_workspace(base, T, mode)
+    r = moe.Routing(T, L.n_expert_used, L.n_expert)
+    y = torch.zeros((T, L.n_embd), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    log("%d replicas resident (%.1f GB)" % (R, R * (base.gate.numel() * 3 + base.sh_gate.numel() * 3) / 1e9))
+
+    # The four stages of one forward; events bracket stage 3 (gate/up), the
+    # kernel that moves the most bytes.
+    def step(i, ev=None):
+        W = reps[i % R]
+        x = xin[i % n_x]
+        moe.layer_forward_stage(W, x, y, ws, moe.STAGE_ROUTER, routing=r)
+        moe.layer_forward_stage(W, x, y, ws, moe.STAGE_ROUTE, routing=r)
+        if ev is not None:
+            ev[0].record()
+        moe.layer_forward_stage(W, x, y, ws, moe.STAGE_GATE_UP, routing=r)
+        if ev is not None:
+            ev[1].record()
+        moe.layer_forward_stage(W, x, y, ws, moe.STAGE_DOWN_COMBINE, routing=r)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # One graph holds R consecutive steps (one per replica).  Replaying it is
+    # how a decode loop issues the block without per-kernel host overhead; the
+    # event nodes around each gate/up launch time the dominant kernel.
+    K = args.steps
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(R)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graphs = []
+    with torch.cuda.stream(side):
+        for n in sorted({R, K % R} - {0}, reverse=True):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                for i in range(n):
+                    step(i, events[i] if n == R else None)
+            graphs.append((n, g))
+    torch.cuda.current_stream().wait_stream(side)
+    full = [g for n, g in graphs if n == R]
+    rest = [g for n, g in graphs if n != R]
+    plan = full * (K // R) + rest
+    for g in (full or rest)[:1] * 2:
+        g.replay()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for g in plan:
+        g.replay()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_step = 1000.0 * wall / K
+    ev_src = "graph event nodes"
+    try:
+        gateup_ms = float(np.mean([a.elapsed_time(b) for a, b in events])) if full else float("nan")
+    except RuntimeError:
+        gateup_ms = float("nan")
+    if not (gateup_ms > 0):
+        # eager pass with events on the launch stream
+        ev_src = "eager events"
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4 * R)]
+        for i, e in enumerate(evs):
+            step(i, e)
+        torch.cuda.synchronize()
+        gateup_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    log("timed %d steps in %.3f s (%d graph replays); gate/up avg %.2f us (%s)" % (
+        K, wall, len(plan), gateup_ms * 1e3, ev_src))
+
+    # routing of every distinct input, outside the timed region, for the byte counts
+    n_unique = []
+    for i in range(n_x):
+        moe.route(base, xin[i], r, ws)
+        torch.cuda.synchronize()
+        n_unique.append(int(r.n_active.item()))
+    nu = float(np.mean(n_unique))
+    D, F, Fs, k = L.n_embd, L.n_ff_exp, L.n_ff_shared, L.n_expert_used
+    xb = 2 if mode == moe.BF16 else 4
+    gu_expert = 2 * synth.tensor_bytes(L.gate_fmt, F * D)
+    dn_expert = synth.tensor_bytes(L.down_fmt, D * F)
+    sh_gu = 2 * synth.tensor_bytes(L.shared_fmt, Fs * D)
+    sh_dn = synth.tensor_bytes(L.shared_fmt, D * Fs)
+    router_b = D * L.n_expert * 4 + (L.n_expert * 4 if L.router_bias is not None else 0)
+    step_bytes = router_b + nu * (gu_expert + dn_expert) + sh_gu + sh_dn + T * D * xb + T * D * 4
+    # stage 3 of the decode schedule (T <= 16) holds the routed experts only;
+    # the batched schedule's stage 3 also runs the shared expert
+    small = T <= 16
+    gateup_bytes = nu * gu_expert + T * D * xb + T * k * F * 4
+    if not small:
+        gateup_bytes += sh_gu + T * Fs * 4
+    achieved = gateup_bytes / (gateup_ms * 1e-3) / 1e9
+    tokens_s = T / (ms_step * 1e-3)
+    flops = 2.0 * T * (k * 3 * D * F + 3 * D * Fs)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(L, x_all, T, mode, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if mode == moe.BF16 else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "tokens_per_step": T,
+            "n_embd": D, "n_expert": L.n_expert, "n_expert_used": k, "n_ff_exp": F, "n_ff_shared": Fs,
+            "formats": "Q2K gate/up/down, Q8_0 shared, fp32 router",
+            "cache": "cold: %d device replicas rotated, %d distinct inputs" % (R, n_x),
+            "launch": "hipGraph of %d steps, replayed" % R,
+        },
+        "hbm_gbps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "algorithmic_bytes_per_step": int(step_bytes),
+        "tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unique_experts_per_step": nu,
+        "roofline": {
+            "kernel": ("dec_k3_kernel (routed gate/up dequant-GEMV + SwiGLU)" if small else
+                       "large_gateup_kernel (gate/up dequant-GEMV + SwiGLU, routed and shared)"),
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": int(gateup_bytes),
+            "avg_launch_us": round(gateup_ms * 1e3, 3),
+            "timing": ev_src,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(L, x_all, T, mode, budget_s):
+    """The plain C oracle, single-threaded, on a bounded sample of the same workload."""
+    import numpy as np
+
+    import oracle
+    import synth
+    done, t_start = 0, time.perf_counter()
+    nrow = x_all.shape[0]
+    while True:
+        x = x_all[(done * T) % nrow:(done * T) % nrow + T]
+        if mode == 1:
+            oracle.moe_forward(L, x_bf16=synth.to_bf16_bits(x))
+        else:
+            oracle.moe_forward(L, x=x)
+        done += 1
+        el = time.perf_counter() - t_start
+        if el >= budget_s or (T > 1 and done >= 1):
+            break
+    cpu = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(done * T / el, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%d step(s) of %d token(s) through the full layer in %.1f s (%s, nproc %d)" % (
+                done, T, el, cpu, os.cpu_count() or 0)}
+
+
+if __name__ == "__main__":
+    main()

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 F32, BF16, Q2K, Q8_0, CB2 = 0, 1, 2, 3, 4
 ACCUMULATE = 1
+STAGE_ROUTER, STAGE_ROUTE, STAGE_GATE_UP, STAGE_DOWN_COMBINE = 1, 2, 3, 4
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EALIGN", -3: "MOE_EWORKSPACE", -4: "MOE_EUNSUPPORTED",
           -5: "MOE_EDEVICE"}
 
@@ -56,10 +57,12 @@ _lib.moe_expert_ffn.argtypes = [ctypes.POINTER(LayerDesc), _P, _I32, _I32, ctype
                                 ctypes.c_uint32, _P, _SZ, _P, ctypes.c_char_p, _SZ]
 _lib.moe_layer_forward.argtypes = [ctypes.POINTER(LayerDesc), _P, _I32, _I32, _P, ctypes.c_uint32,
                                    ctypes.POINTER(RoutingStruct), _P, _SZ, _P, ctypes.c_char_p, _SZ]
+_lib.moe_layer_forward_stage.argtypes = [ctypes.POINTER(LayerDesc), _P, _I32, _I32, _P, ctypes.c_uint32,
+                                         ctypes.POINTER(RoutingStruct), _I32, _P, _SZ, _P, ctypes.c_char_p, _SZ]
 _lib.moe_rmsnorm.argtypes = [_P, _P, ctypes.c_float, _I32, _I32, _P, _P, ctypes.c_char_p, _SZ]
 _lib.moe_dequant.argtypes = [_I32, _P, _I64, _P, _I32, _P, _P, ctypes.c_char_p, _SZ]
 _lib.moe_version.restype = ctypes.c_char_p
-for _f in ("moe_route", "moe_expert_ffn", "moe_layer_forward", "moe_rmsnorm", "moe_dequant"):
+for _f in ("moe_route", "moe_expert_ffn", "moe_layer_forward_stage", "moe_layer_forward", "moe_rmsnorm", "moe_dequant"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -175,6 +178,15 @@ def expert_ffn(layer, x, routing, y, ws, accumulate=False, stream=None):
     _check(_lib.moe_expert_ffn(ctypes.byref(d), _ptr(x), _rows(x), _xtype(x), ctypes.byref(r), _ptr(y),
                                ACCUMULATE if accumulate else 0, _ptr(ws), ws.numel(), _stream(stream), err, 512),
            err)
+
+
+def layer_forward_stage(layer, x, y, ws, stage, routing=None, accumulate=False, stream=None):
+    d, err = layer.desc(), ctypes.create_string_buffer(512)
+    r = routing.struct() if routing is not None else None
+    _check(_lib.moe_layer_forward_stage(ctypes.byref(d), _ptr(x), _rows(x), _xtype(x), _ptr(y),
+                                        ACCUMULATE if accumulate else 0,
+                                        ctypes.byref(r) if r is not None else None, stage, _ptr(ws), ws.numel(),
+                                        _stream(stream), err, 512), err)
 
 
 def layer_forward(layer, x, y, ws, routing=None, accumulate=False, stream=None):

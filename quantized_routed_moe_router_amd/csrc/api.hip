@@ -92,6 +92,18 @@ RoutingPtrs from_ws(const Workspace &w) {
     return RoutingPtrs{w.topk_idx, w.topk_w, w.count, w.offset, w.perm, w.pos, w.active, w.n_active};
 }
 
+// The whole block (stage 0) or one of its four stages.  Few rows: the decode
+// schedule; otherwise router partials, top-k + bucketing, gate/up, down.
+hipError_t forward(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r, float *y,
+                   uint32_t flags, const Workspace &w, hipStream_t s, int stage) {
+    if (small_path_ok(d, T) && small_route_ok(d, T)) return launch_small(d, x, T, x_type, r, y, flags, w, s, stage, true);
+    hipError_t e = hipSuccess;
+    if (stage == 0 || stage == 1) e = launch_router_partial(d, x, T, x_type, w, s);
+    if (e == hipSuccess && (stage == 0 || stage == 2)) e = launch_route_finish(d, T, r, w, s);
+    if (e == hipSuccess && (stage == 0 || stage >= 3)) e = launch_ffn_large(d, x, T, x_type, r, y, flags, w, s, stage);
+    return e;
+}
+
 int device_status(hipError_t e, char *err, size_t errlen) {
     if (e == hipSuccess) return MOE_OK;
     return fail(err, errlen, MOE_EDEVICE, "HIP: %s", hipGetErrorString(e));
@@ -131,8 +143,10 @@ int moe_expert_ffn(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_
     if (!y) return fail(err, errlen, MOE_EINVAL, "y is NULL");
     if (!aligned16(y)) return fail(err, errlen, MOE_EALIGN, "y must be 16-byte aligned");
     Workspace w = workspace_layout(d, T, ws);
-    return device_status(launch_ffn_decode(d, x, T, x_type, from_routing(r), y, flags, w, (hipStream_t)stream),
-                         err, errlen);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = small_path_ok(d, T) ? launch_small(d, x, T, x_type, from_routing(r), y, flags, w, s, 0, false)
+                                       : launch_ffn_large(d, x, T, x_type, from_routing(r), y, flags, w, s, 0);
+    return device_status(e, err, errlen);
 }
 
 int moe_layer_forward(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, float *y, uint32_t flags,
@@ -147,10 +161,23 @@ int moe_layer_forward(const moe_layer_desc *d, const void *x, int32_t T, int32_t
     if (!aligned16(y)) return fail(err, errlen, MOE_EALIGN, "y must be 16-byte aligned");
     Workspace w = workspace_layout(d, T, ws);
     RoutingPtrs r = routing ? from_routing(routing) : from_ws(w);
-    hipStream_t s = (hipStream_t)stream;
-    hipError_t e = launch_route(d, x, T, x_type, r, w, s);
-    if (e == hipSuccess) e = launch_ffn_decode(d, x, T, x_type, r, y, flags, w, s);
-    return device_status(e, err, errlen);
+    return device_status(forward(d, x, T, x_type, r, y, flags, w, (hipStream_t)stream, 0), err, errlen);
+}
+
+int moe_layer_forward_stage(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, float *y,
+                            uint32_t flags, const moe_routing *routing, int32_t stage, void *ws, size_t ws_bytes,
+                            void *stream, char *err, size_t errlen) {
+    if (stage < 1 || stage > 4) return fail(err, errlen, MOE_EINVAL, "stage must be 1, 2, 3 or 4 (got %d)", stage);
+    int rc = check_call(d, x, T, x_type, ws, ws_bytes, err, errlen);
+    if (rc) return rc;
+    if (routing && (rc = check_routing(routing, err, errlen))) return rc;
+    if (flags & ~(uint32_t)MOE_ACCUMULATE) return fail(err, errlen, MOE_EINVAL, "unknown flags 0x%x", flags);
+    if (T == 0) return MOE_OK;
+    if (!y) return fail(err, errlen, MOE_EINVAL, "y is NULL");
+    if (!aligned16(y)) return fail(err, errlen, MOE_EALIGN, "y must be 16-byte aligned");
+    Workspace w = workspace_layout(d, T, ws);
+    RoutingPtrs r = routing ? from_routing(routing) : from_ws(w);
+    return device_status(forward(d, x, T, x_type, r, y, flags, w, (hipStream_t)stream, stage), err, errlen);
 }
 
 int moe_rmsnorm(const float *x, const float *gamma, float eps, int32_t T, int32_t D, float *out, void *stream,

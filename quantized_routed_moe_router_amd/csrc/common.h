@@ -251,6 +251,185 @@ MOE_DEV void cb2_values(const CB2Chunk &c, const uint32_t *cb, float *w) {
     }
 }
 
+// ---- fp16 dot2 path ------------------------------------------------------
+// v_dot2_f32_f16 multiplies two fp16 pairs exactly and accumulates in fp32.
+// Weight codes enter as exact fp16 values; the activations as a pair of fp16
+// numbers hi + lo (x*S = hi + lo to about 2^-22 relative), scaled per 64-value
+// chunk by a power of two S so that nothing overflows.  Q2K codes are taken
+// straight from their bit field with one AND: code q at bits 2m..2m+1 of a
+// half is the fp16 subnormal q*4^m*2^-24, so the matching activation carries
+// the factor 4^-m and every product is q*x*S*2^-24.
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __fp16 fp16x2_t __attribute__((ext_vector_type(2)));
+
+MOE_DEV half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
+
+MOE_DEV float dot2(uint32_t a, uint32_t b, float c) { return __builtin_amdgcn_fdot2(as_h2(a), as_h2(b), c, false); }
+
+// hi/lo fp16 pair of (a, b), both already scaled: hi rounds toward zero, lo
+// holds the rest (exact in fp32), so hi + lo matches a, b to about 2^-22.
+MOE_DEV void split2(float a, float b, uint32_t &hi, uint32_t &lo) {
+    fp16x2_t h = __builtin_amdgcn_cvt_pkrtz(a, b);
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a - (float)h[0], b - (float)h[1]));
+}
+
+// power-of-two scale for 64 activations: max|x| * S in [2^13, 2^14)
+MOE_DEV float chunk_scale(const float *x, float &inv24) {
+    float m = 0.f;
+#pragma unroll
+    for (int i = 0; i < 64; ++i) m = fmaxf(m, fabsf(x[i]));
+    int e = m > 0.f ? (int)((__float_as_uint(m) >> 23) & 0xFF) - 127 : 0;
+    e = max(-100, min(100, e));
+    inv24 = __uint_as_float((uint32_t)(127 + 11 + e) << 23);  // 2^24 / S
+    return __uint_as_float((uint32_t)(127 + 13 - e) << 23);   // S
+}
+
+// Prepared activations for Q2K rows, one record of 18 dwords per group of 16
+// values v: hi[m], lo[m] (m < 8) = the fp16 pair (v[m], v[m+8]) * S * 4^-m'
+// split into hi + lo, with m' = m for m < 5 and m - 5 after; sx = sum of the
+// 16 values (fp32); inv = 2^24 / S.  S is a power of two per group with
+// max|v| * S in [2^13, 2^14).  A lane's 64 weights use 4 records.
+struct P16 {
+    uint32_t hi[8], lo[8];
+    float sx, inv;
+};
+constexpr int kP16Dwords = 18;
+
+struct XQ2K {
+    P16 g[4];
+};
+
+// scale S and 2^24/S for a group whose largest magnitude is m
+MOE_DEV float group_scale(float m, float &inv24) {
+    int e = m > 0.f ? (int)((__float_as_uint(m) >> 23) & 0xFF) - 127 : 0;
+    e = max(-100, min(100, e));
+    inv24 = __uint_as_float((uint32_t)(127 + 11 + e) << 23);
+    return __uint_as_float((uint32_t)(127 + 13 - e) << 23);
+}
+
+MOE_DEV float p16_factor(int m) { return 1.0f / (float)(1 << (2 * (m < 5 ? m : m - 5))); }
+
+// per-lane preparation of the lane's 64 activations
+MOE_DEV void prep_q2k(const float *x, XQ2K &p) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        float s = 0.f, m = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            s += x[16 * g + i];
+            m = fmaxf(m, fabsf(x[16 * g + i]));
+        }
+        p.g[g].sx = s;
+        const float S = group_scale(m, p.g[g].inv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const float f = S * p16_factor(j);
+            split2(x[16 * g + j] * f, x[16 * g + j + 8] * f, p.g[g].hi[j], p.g[g].lo[j]);
+        }
+    }
+}
+
+// wave-cooperative preparation: lane l holds value v of position l % 16 in
+// group l / 16; records of groups < ngroups go to out[(l / 16) * 18 ...].
+// All lanes of the wave must call it.
+MOE_DEV void prep16_wave(float v, uint32_t *out, int ngroups = 4) {
+    const int lane = threadIdx.x & 63, gl = lane & 15;
+    float m = fabsf(v), s = v;
+    for (int o = 1; o < 16; o <<= 1) {  // within the 16-lane group, fixed order
+        m = fmaxf(m, __shfl_xor(m, o, kWave));
+        s += __shfl_xor(s, o, kWave);
+    }
+    float inv;
+    const float S = group_scale(m, inv);
+    const float partner = __shfl_down(v, 8, kWave);
+    uint32_t *rec = out + (lane >> 4) * kP16Dwords;
+    if ((lane >> 4) >= ngroups) return;
+    if (gl < 8) {
+        const float f = S * p16_factor(gl);
+        uint32_t hi, lo;
+        split2(v * f, partner * f, hi, lo);
+        rec[gl] = hi;
+        rec[8 + gl] = lo;
+    } else if (gl == 8) {
+        rec[16] = __float_as_uint(s);
+        rec[17] = __float_as_uint(inv);
+    }
+}
+
+MOE_DEV void load_q2k_prep(const uint32_t *rec4, XQ2K &p) {
+    u32x4 *dst = (u32x4 *)&p;
+#pragma unroll
+    for (int i = 0; i < 18; ++i) dst[i] = *(const u32x4 *)(rec4 + 4 * i);
+}
+
+MOE_DEV float q2k_dot2(const Q2KChunk &c, const XQ2K &p) {
+    const float d = half_bits_to_float(c.dd), dmin = half_bits_to_float(c.dd >> 16);
+    float acc_q = 0.f, acc_m = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const uint32_t q = c.qs[g], q5 = q >> 10;
+        float a = 0.f;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const uint32_t t = m < 5 ? (q & (0x00030003u << (2 * m))) : (q5 & (0x00030003u << (2 * (m - 5))));
+            a = dot2(t, p.g[g].hi[m], a);
+            a = dot2(t, p.g[g].lo[m], a);
+        }
+        const uint32_t smb = (c.sm >> (8 * g)) & 0xFFu;
+        acc_q = __builtin_fmaf((float)(smb & 15u), a * p.g[g].inv, acc_q);
+        acc_m = __builtin_fmaf((float)(smb >> 4), p.g[g].sx, acc_m);
+    }
+    return d * acc_q - dmin * acc_m;
+}
+
+// Activations of one lane chunk for Q8_0 codes: pair i holds
+// (x[2i], x[2i+1]) * S; int8 codes enter as the fp16 subnormal (q+128)*2^-24.
+struct XQ8 {
+    uint32_t hi[32], lo[32];
+    float sx[2];  // sum of each 32-block of activations
+    float inv;
+};
+
+MOE_DEV void prep_q8(const float *x, XQ8 &p) {
+    const float S = chunk_scale(x, p.inv);
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        float s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) s += x[32 * b + i];
+        p.sx[b] = s;
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) split2(x[2 * i] * S, x[2 * i + 1] * S, p.hi[i], p.lo[i]);
+}
+
+MOE_DEV float q8_dot2(const Q8Chunk &c, const XQ8 &p) {
+    const float d0 = half_bits_to_float(c.w[0]), d1 = half_bits_to_float(c.w[8] >> 16);
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t v = __builtin_amdgcn_alignbyte(c.w[i + 1], c.w[i], 2) ^ 0x80808080u;  // bytes 2..33
+        const uint32_t lo = __builtin_amdgcn_perm(0u, v, 0x0C010C00u), hi = __builtin_amdgcn_perm(0u, v, 0x0C030C02u);
+        a0 = dot2(lo, p.hi[2 * i], a0);
+        a0 = dot2(lo, p.lo[2 * i], a0);
+        a0 = dot2(hi, p.hi[2 * i + 1], a0);
+        a0 = dot2(hi, p.lo[2 * i + 1], a0);
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t v = c.w[9 + i] ^ 0x80808080u;  // bytes 36..67
+        const uint32_t lo = __builtin_amdgcn_perm(0u, v, 0x0C010C00u), hi = __builtin_amdgcn_perm(0u, v, 0x0C030C02u);
+        a1 = dot2(lo, p.hi[16 + 2 * i], a1);
+        a1 = dot2(lo, p.lo[16 + 2 * i], a1);
+        a1 = dot2(hi, p.hi[17 + 2 * i], a1);
+        a1 = dot2(hi, p.lo[17 + 2 * i], a1);
+    }
+    // sum (q+128) x = sum q x + 128 sum x
+    return d0 * __builtin_fmaf(p.inv, a0, -128.0f * p.sx[0]) + d1 * __builtin_fmaf(p.inv, a1, -128.0f * p.sx[1]);
+}
+
 template <int FMT>
 MOE_DEV float chunk_dot(const uint8_t *base, int64_t i0, const float *x, const uint32_t *cb_lds) {
     if constexpr (FMT == MOE_Q2K) {
@@ -272,9 +451,9 @@ struct RouterPlan {
 
 __host__ inline RouterPlan router_plan(int T, int D) {
     RouterPlan p;
-    if (T <= 4) { p.kc = 16; p.tt = T < 1 ? 1 : T; }
-    else if (T <= 64) { p.kc = 64; p.tt = 8; }
-    else { p.kc = 1024; p.tt = 32; }
+    if (T <= 4) { p.kc = 64; p.tt = T < 1 ? 1 : T; }
+    else if (T <= 64) { p.kc = 128; p.tt = 8; }
+    else { p.kc = 512; p.tt = 32; }
     while (p.kc > D) p.kc >>= 1;
     p.nchunk = D / p.kc;
     return p;
@@ -285,10 +464,12 @@ struct Workspace {
     int32_t *topk_idx;    // routing kept in the workspace when the caller gives none
     float *topk_w;
     int32_t *count, *offset, *perm, *pos, *active, *n_active;
-    float *h;             // [T*k][F] fp32 (F32 mode) or bf16 pairs (BF16 mode)
+    float *h;             // [T*k][F] fp32
     float *hs;            // [T][Fs]
     float *ypart;         // [T*k][D]
     float *ys;            // [T][D]
+    uint32_t *xp16;       // [T][D/16][18] x prepared for Q2K rows
+    uint32_t *hp16;       // [T*k][F/16][18] h prepared for Q2K rows
     size_t bytes;
 };
 
@@ -319,6 +500,8 @@ __host__ inline Workspace workspace_layout(const moe_layer_desc *d, int32_t T, v
     w.hs = (float *)take(sizeof(float) * (size_t)T * (size_t)(Fs > 0 ? Fs : 1));
     w.ypart = (float *)take(sizeof(float) * (size_t)P * (size_t)D);
     w.ys = (float *)take(sizeof(float) * (size_t)T * (size_t)D);
+    w.xp16 = (uint32_t *)take(sizeof(uint32_t) * kP16Dwords * (size_t)T * (size_t)(D / 16));
+    w.hp16 = (uint32_t *)take(sizeof(uint32_t) * kP16Dwords * (size_t)P * (size_t)(F / 16));
     w.bytes = off;
     return w;
 }
@@ -331,10 +514,20 @@ struct RoutingPtrs {
     int32_t *count, *offset, *perm, *pos, *active, *n_active;
 };
 
+hipError_t launch_router_partial(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type,
+                                 const Workspace &ws, hipStream_t s);
+hipError_t launch_route_finish(const moe_layer_desc *d, int32_t T, const RoutingPtrs &r, const Workspace &ws,
+                               hipStream_t s);
 hipError_t launch_route(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
                         const Workspace &ws, hipStream_t s);
-hipError_t launch_ffn_decode(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type,
-                             const RoutingPtrs &r, float *y, uint32_t flags, const Workspace &ws, hipStream_t s);
+// decode schedule (few rows): stage 0 = all, 1..4 = its four kernels
+bool small_path_ok(const moe_layer_desc *d, int32_t T);
+bool small_route_ok(const moe_layer_desc *d, int32_t T);
+hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
+                        float *y, uint32_t flags, const Workspace &ws, hipStream_t s, int stage, bool route);
+// any number of rows: stage 3 = gate/up, 4 = down + combine, 0 = both
+hipError_t launch_ffn_large(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
+                            float *y, uint32_t flags, const Workspace &ws, hipStream_t s, int stage);
 hipError_t launch_rmsnorm(const float *x, const float *gamma, float eps, int32_t T, int32_t D, float *out,
                           hipStream_t s);
 hipError_t launch_dequant(int32_t type, const void *src, int64_t n, const int8_t *cb, int32_t out_type, void *dst,

@@ -1,0 +1,86 @@
+// k_ffn_large.hip - the expert FFNs for batches beyond the decode schedule
+// (any T): blockIdx.y is a slot (0 = shared expert when present, then the
+// active experts in ascending id), blockIdx.x a block of 16 output rows; the
+// down pass writes one row per (token, slot) pair and a gather pass combines
+// them in slot order ("Understanding Dwarf Star", 5.3.7 steps 2-5).
+#include <algorithm>
+#include <type_traits>
+
+#include "ffn_dev.h"
+
+namespace moe {
+
+constexpr int kLargeRows = 16;  // rows per block: 4 waves x 4 rows
+
+template <int GFMT, int SFMT>
+__global__ void __launch_bounds__(256) large_gateup_kernel(FfnArgs a) {
+    __shared__ uint32_t cb_lds[512];
+    const bool has_shared = a.Fs > 0;
+    const int slot = blockIdx.y;
+    const bool shared = has_shared && slot == 0;
+    const int s = slot - (has_shared ? 1 : 0);
+    if (!shared && s >= a.n_active[0]) return;
+    const int rows = shared ? a.Fs : a.F;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int row0 = blockIdx.x * kLargeRows + wave * 4;
+    if (blockIdx.x * kLargeRows >= rows) return;
+    load_codebook(a.codebook, cb_lds);
+    if (row0 >= rows) return;
+    if (shared) shared_gateup<SFMT>(a, row0, min(4, rows - row0), cb_lds, lane);
+    else routed_gateup<GFMT>(a, a.active[s], row0, min(4, rows - row0), cb_lds, lane);
+}
+
+template <int DFMT, int SFMT>
+__global__ void __launch_bounds__(256) large_down_kernel(FfnArgs a) {
+    __shared__ uint32_t cb_lds[512];
+    const bool has_shared = a.Fs > 0;
+    const int slot = blockIdx.y;
+    const bool shared = has_shared && slot == 0;
+    const int s = slot - (has_shared ? 1 : 0);
+    if (!shared && s >= a.n_active[0]) return;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int row0 = blockIdx.x * kLargeRows + wave * 4;
+    load_codebook(a.codebook, cb_lds);
+    if (row0 >= a.D) return;
+    if (shared) shared_down<SFMT>(a, row0, min(4, a.D - row0), cb_lds, lane);
+    else routed_down<DFMT>(a, a.active[s], row0, min(4, a.D - row0), cb_lds, lane, a.ypart + row0, a.D);
+}
+
+// y[t][d] = (y if accumulating) + ys[t][d] + sum_s w[t][s] * ypart[pos[t*k+s]][d]
+__global__ void __launch_bounds__(256) combine_kernel(FfnArgs a) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)a.T * a.D) return;
+    const int t = (int)(i / a.D), d = (int)(i % a.D);
+    float acc = a.Fs > 0 ? a.ys[i] : 0.f;
+    for (int s = 0; s < a.k; ++s) {
+        const int p = t * a.k + s;
+        acc = __builtin_fmaf(a.topk_w[p], a.ypart[(int64_t)a.pos[p] * a.D + d], acc);
+    }
+    if (a.flags & MOE_ACCUMULATE) acc += a.y[i];
+    a.y[i] = acc;
+}
+
+// stage 3 = gate/up, 4 = down + combine, 0 = both
+hipError_t launch_ffn_large(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
+                            float *y, uint32_t flags, const Workspace &ws, hipStream_t s, int stage) {
+    FfnArgs a = make_ffn_args(d, x, T, x_type, r, y, flags, ws);
+    const int max_active = (int)std::min<int64_t>((int64_t)T * a.k, d->n_expert);
+    const int slots = max_active + (a.Fs > 0 ? 1 : 0);
+    const int sf = a.Fs > 0 ? d->shared_type : MOE_Q8_0;
+    dim3 g1((std::max(a.F, a.Fs) + kLargeRows - 1) / kLargeRows, slots);
+    dim3 g2((a.D + kLargeRows - 1) / kLargeRows, slots);
+    if (stage == 0 || stage == 3)
+        with_fmt(d->gate_type, [&](auto G) {
+            with_fmt(sf, [&](auto S) { large_gateup_kernel<decltype(G)::value, decltype(S)::value><<<g1, 256, 0, s>>>(a); });
+        });
+    if (stage == 0 || stage == 4) {
+        with_fmt(d->down_type, [&](auto DN) {
+            with_fmt(sf, [&](auto S) { large_down_kernel<decltype(DN)::value, decltype(S)::value><<<g2, 256, 0, s>>>(a); });
+        });
+        const int64_t n = (int64_t)T * a.D;
+        combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

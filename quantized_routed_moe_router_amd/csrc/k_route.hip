@@ -1,127 +1,47 @@
-// k_route.hip - router logits, top-k with renormalized softmax, and the
-// stable token-to-expert bucketing ("Understanding Dwarf Star", 5.3.2 router
-// and top-k formula; 5.3.7 step 1 and the sparse indexing of step 2).
-#include "common.h"
+// k_route.hip - routing kernels for moe_route and for batches too large for
+// the one-block finisher ("Understanding Dwarf Star", 5.3.2 router and top-k;
+// 5.3.7 step 1 and the sparse indexing of step 2).
+#include "route_dev.h"
 
 namespace moe {
-
-// Partial router logits in fp64.  Block (chunk c, token tile, expert group):
-// rows k in [c*kc, (c+1)*kc) of W_r [D][E] against up to 32 tokens; thread
-// e of the group holds one expert's partial sums.  Products of two fp32 (or
-// bf16 and fp32) values are exact in fp64, so only the additions round, at
-// 2^-53 relative.
-constexpr int kRouterKS = 64;
 
 template <int XT>
 __global__ void __launch_bounds__(256) router_partial_kernel(const float *__restrict__ W, const void *__restrict__ xin,
                                                              int T, int D, int E, int kc, int tt,
                                                              double *__restrict__ partial) {
-    __shared__ double xs[32 * kRouterKS];  // [nt][ks]
-    int c = blockIdx.x, t0 = blockIdx.y * tt;
-    int nt = min(tt, T - t0);
-    int k0 = c * kc;
-    int e = blockIdx.z * 256 + threadIdx.x;
-    double acc[32];
-#pragma unroll
-    for (int j = 0; j < 32; ++j) acc[j] = 0.0;
-    int ks = min(kc, kRouterKS);
-    for (int kb = 0; kb < kc; kb += ks) {
-        __syncthreads();
-        for (int i = threadIdx.x; i < nt * ks; i += blockDim.x) {
-            int tl = i / ks, kk = i % ks;
-            int64_t gi = (int64_t)(t0 + tl) * D + k0 + kb + kk;
-            double v;
-            if constexpr (XT == MOE_BF16) v = (double)bf16_bits_to_float(((const uint16_t *)xin)[gi]);
-            else v = (double)((const float *)xin)[gi];
-            xs[tl * ks + kk] = v;
-        }
-        __syncthreads();
-        if (e < E) {
-            const float *wp = W + (int64_t)(k0 + kb) * E + e;
-            for (int kk = 0; kk < ks; ++kk) {
-                double w = (double)wp[(int64_t)kk * E];
-#pragma unroll
-                for (int j = 0; j < 32; ++j)
-                    if (j < nt) acc[j] = __builtin_fma(xs[j * ks + kk], w, acc[j]);
-            }
-        }
-    }
-    if (e < E)
-        for (int j = 0; j < nt; ++j) partial[((int64_t)c * T + t0 + j) * E + e] = acc[j];
+    router_partial_block<XT>(W, xin, T, D, E, kc, tt, partial, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
-// a ranks before b: larger logit, then lower expert index
-MOE_DEV bool before(double va, int ea, double vb, int eb) { return va > vb || (va == vb && ea < eb); }
+__global__ void __launch_bounds__(1024) route_finish_small_kernel(
+    const double *__restrict__ partial, const float *__restrict__ bias, int T, int E, int nchunk, int k,
+    float route_scale, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, int32_t *__restrict__ count,
+    int32_t *__restrict__ offset, int32_t *__restrict__ perm, int32_t *__restrict__ pos,
+    int32_t *__restrict__ active, int32_t *__restrict__ n_active) {
+    route_finish_small(partial, bias, T, E, nchunk, k, route_scale, topk_idx, topk_w, count, offset, perm, pos, active,
+                       n_active);
+}
 
-// One wave per token: sum the chunk partials in fixed order (+ bias), select
-// the top k by (logit desc, index asc) with k wave-wide arg-max rounds, then
-// weights = route_scale * exp(l_s - l_0) / sum_j exp(l_j - l_0) in fp64.
+// One block per token: logits from the chunk partials, then wave 0 selects.
 __global__ void __launch_bounds__(256) router_topk_kernel(const double *__restrict__ partial,
                                                           const float *__restrict__ bias, int T, int E, int nchunk,
                                                           int k, float route_scale, int32_t *__restrict__ topk_idx,
                                                           float *__restrict__ topk_w) {
-    int lane = threadIdx.x & 63;
-    int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
-    constexpr int PER = kMaxExperts / kWave;  // 16 experts per lane at most
-    double v[PER];
-    uint32_t taken = 0;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        int e = lane + 64 * i;
-        double s = 0.0;
-        if (e < E) {
-            for (int c = 0; c < nchunk; ++c) s += partial[((int64_t)c * T + t) * E + e];
-            if (bias) s += (double)bias[e];
-        } else {
-            taken |= 1u << i;
-        }
-        v[i] = s;
-    }
-    double sel_v[kMaxUsed];
-    int sel_e[kMaxUsed];
-    for (int s = 0; s < k; ++s) {
-        // lane-local best among not-yet-taken experts
-        double bv = 0.0;
-        int be = 0x7FFFFFFF, bi = -1;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            int e = lane + 64 * i;
-            if (!((taken >> i) & 1u) && (bi < 0 || before(v[i], e, bv, be))) {
-                bv = v[i];
-                be = e;
-                bi = i;
-            }
-        }
-        // wave arg-max (lanes without a candidate carry e = INT_MAX, never chosen over a real one)
-        double wv = bv;
-        int we = be;
-        bool have = bi >= 0;
-        for (int o = 32; o > 0; o >>= 1) {
-            double ov = __shfl_xor(wv, o, kWave);
-            int oe = __shfl_xor(we, o, kWave);
-            int oh = __shfl_xor((int)have, o, kWave);
-            if (oh && (!have || before(ov, oe, wv, we))) {
-                wv = ov;
-                we = oe;
-                have = true;
-            }
-        }
-        sel_v[s] = wv;
-        sel_e[s] = we;
-        if (have && we == be && bi >= 0) taken |= 1u << bi;
-    }
-    if (lane == 0) {
-        double mx = sel_v[0], den = 0.0, ex[kMaxUsed];
-        for (int s = 0; s < k; ++s) {
-            ex[s] = exp(sel_v[s] - mx);
-            den += ex[s];
-        }
-        for (int s = 0; s < k; ++s) {
-            topk_idx[(int64_t)t * k + s] = sel_e[s];
-            topk_w[(int64_t)t * k + s] = (float)((double)route_scale * ex[s] / den);
-        }
-    }
+    __shared__ double lg[kMaxExperts];
+    const int t = blockIdx.x;
+    reduce_logits(partial, bias, T, E, nchunk, t, 1, lg);
+    if (threadIdx.x >= 64) return;
+    select_topk(lg, E, k, route_scale, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k, nullptr, nullptr);
+}
+
+__global__ void __launch_bounds__(1024) bucket_small_kernel(const int32_t *__restrict__ topk_idx, int P, int E,
+                                                            int32_t *__restrict__ count, int32_t *__restrict__ offset,
+                                                            int32_t *__restrict__ perm, int32_t *__restrict__ pos,
+                                                            int32_t *__restrict__ active,
+                                                            int32_t *__restrict__ n_active) {
+    __shared__ int32_t sidx[1024];
+    for (int p = threadIdx.x; p < P; p += blockDim.x) sidx[p] = topk_idx[p];
+    __syncthreads();
+    bucket_small(sidx, P, E, count, offset, perm, pos, active, n_active);
 }
 
 // Stable counting sort of the P = T*k pairs by expert, one block of 8 waves.
@@ -138,15 +58,14 @@ __global__ void __launch_bounds__(512) bucket_kernel(const int32_t *__restrict__
     __shared__ int32_t wc[kBucketWaves][kMaxExperts];
     __shared__ int32_t tot[kMaxExperts];
     __shared__ int32_t scan_tmp[kMaxExperts];
-    int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     for (int i = tid; i < kBucketWaves * kMaxExperts; i += blockDim.x) (&wc[0][0])[i] = 0;
     __syncthreads();
-    int seg = ((P + kBucketWaves - 1) / kBucketWaves + 63) / 64 * 64;
-    int s0 = w * seg, s1 = min(P, s0 + seg);
+    const int seg = ((P + kBucketWaves - 1) / kBucketWaves + 63) / 64 * 64;
+    const int s0 = w * seg, s1 = min(P, s0 + seg);
     for (int p = s0 + lane; p < s1; p += 64) atomicAdd(&wc[w][topk_idx[p]], 1);
     __syncthreads();
-    // per expert: exclusive prefix over waves, total
-    for (int e = tid; e < E; e += blockDim.x) {
+    for (int e = tid; e < E; e += blockDim.x) {  // exclusive prefix over waves
         int run = 0;
         for (int ww = 0; ww < kBucketWaves; ++ww) {
             int c = wc[ww][e];
@@ -156,10 +75,9 @@ __global__ void __launch_bounds__(512) bucket_kernel(const int32_t *__restrict__
         tot[e] = run;
     }
     __syncthreads();
-    // exclusive scan of tot over experts (Hillis-Steele on up to 1024 entries, 2 per thread)
     for (int e = tid; e < kMaxExperts; e += blockDim.x) scan_tmp[e] = e < E ? tot[e] : 0;
     __syncthreads();
-    for (int o = 1; o < kMaxExperts; o <<= 1) {
+    for (int o = 1; o < kMaxExperts; o <<= 1) {  // inclusive scan over experts
         int a0 = tid, a1 = tid + 512;
         int v0 = scan_tmp[a0] + (a0 >= o ? scan_tmp[a0 - o] : 0);
         int v1 = scan_tmp[a1] + (a1 >= o ? scan_tmp[a1 - o] : 0);
@@ -168,7 +86,6 @@ __global__ void __launch_bounds__(512) bucket_kernel(const int32_t *__restrict__
         scan_tmp[a1] = v1;
         __syncthreads();
     }
-    // scan_tmp now inclusive
     for (int e = tid; e < E; e += blockDim.x) {
         int excl = scan_tmp[e] - tot[e];
         count[e] = tot[e];
@@ -177,9 +94,8 @@ __global__ void __launch_bounds__(512) bucket_kernel(const int32_t *__restrict__
     }
     if (tid == 0) offset[E] = scan_tmp[E - 1];
     __syncthreads();
-    // pass 2: stable scatter
-    int nbits = 32 - __clz(max(E - 1, 1));
-    for (int base = s0; base < s1; base += 64) {
+    const int nbits = 32 - __clz(max(E - 1, 1));
+    for (int base = s0; base < s1; base += 64) {  // stable scatter
         int p = base + lane;
         bool valid = p < s1;
         int key = valid ? topk_idx[p] : 0;
@@ -188,8 +104,7 @@ __global__ void __launch_bounds__(512) bucket_kernel(const int32_t *__restrict__
             uint64_t bal = __ballot(valid && ((key >> b) & 1));
             same &= ((key >> b) & 1) ? bal : ~bal;
         }
-        uint64_t below = same & ((1ull << lane) - 1ull);
-        int rank = __popcll(below);
+        int rank = __popcll(same & ((1ull << lane) - 1ull));
         int slot = valid ? wc[w][key] + rank : 0;
         __builtin_amdgcn_wave_barrier();
         if (valid) {
@@ -200,7 +115,6 @@ __global__ void __launch_bounds__(512) bucket_kernel(const int32_t *__restrict__
         __builtin_amdgcn_wave_barrier();
     }
     __syncthreads();
-    // active experts, ascending: scan of (count > 0)
     for (int e = tid; e < kMaxExperts; e += blockDim.x) scan_tmp[e] = (e < E && tot[e] > 0) ? 1 : 0;
     __syncthreads();
     for (int o = 1; o < kMaxExperts; o <<= 1) {
@@ -212,29 +126,51 @@ __global__ void __launch_bounds__(512) bucket_kernel(const int32_t *__restrict__
         scan_tmp[a1] = v1;
         __syncthreads();
     }
-    int na = scan_tmp[kMaxExperts - 1];
-    for (int e = tid; e < E; e += blockDim.x) {
-        active[e] = -1;
-    }
+    const int na = scan_tmp[kMaxExperts - 1];
+    for (int e = tid; e < E; e += blockDim.x) active[e] = -1;
     __syncthreads();
     for (int e = tid; e < E; e += blockDim.x)
         if (tot[e] > 0) active[scan_tmp[e] - 1] = e;
     if (tid == 0) n_active[0] = na;
 }
 
+hipError_t launch_router_partial(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type,
+                                 const Workspace &ws, hipStream_t s) {
+    const int D = d->n_embd, E = d->n_expert;
+    RouterPlan rp = router_plan(T, D);
+    dim3 g(rp.nchunk, (T + rp.tt - 1) / rp.tt, (E + 63) / 64);
+    if (x_type == MOE_BF16)
+        router_partial_kernel<MOE_BF16><<<g, 256, 0, s>>>(d->router_w, x, T, D, E, rp.kc, rp.tt, ws.partial);
+    else
+        router_partial_kernel<MOE_F32><<<g, 256, 0, s>>>(d->router_w, x, T, D, E, rp.kc, rp.tt, ws.partial);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_finish(const moe_layer_desc *d, int32_t T, const RoutingPtrs &r, const Workspace &ws,
+                               hipStream_t s) {
+    const int D = d->n_embd, E = d->n_expert, k = d->n_expert_used, P = T * k;
+    RouterPlan rp = router_plan(T, D);
+    if (route_small_ok(T, E, k)) {
+        route_finish_small_kernel<<<1, 1024, 0, s>>>(ws.partial, d->router_bias, T, E, rp.nchunk, k, d->route_scale,
+                                                     r.topk_idx, r.topk_w, r.count, r.offset, r.perm, r.pos,
+                                                     r.active, r.n_active);
+        return hipGetLastError();
+    }
+    router_topk_kernel<<<T, 256, 0, s>>>(ws.partial, d->router_bias, T, E, rp.nchunk, k, d->route_scale,
+                                         r.topk_idx, r.topk_w);
+    if (P <= 1024)
+        bucket_small_kernel<<<1, 1024, 0, s>>>(r.topk_idx, P, E, r.count, r.offset, r.perm, r.pos, r.active,
+                                               r.n_active);
+    else
+        bucket_kernel<<<1, 512, 0, s>>>(r.topk_idx, P, E, r.count, r.offset, r.perm, r.pos, r.active, r.n_active);
+    return hipGetLastError();
+}
+
 hipError_t launch_route(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
                         const Workspace &ws, hipStream_t s) {
-    int D = d->n_embd, E = d->n_expert, k = d->n_expert_used;
-    RouterPlan rp = router_plan(T, D);
-    dim3 g1(rp.nchunk, (T + rp.tt - 1) / rp.tt, (E + 255) / 256);
-    if (x_type == MOE_BF16)
-        router_partial_kernel<MOE_BF16><<<g1, 256, 0, s>>>(d->router_w, x, T, D, E, rp.kc, rp.tt, ws.partial);
-    else
-        router_partial_kernel<MOE_F32><<<g1, 256, 0, s>>>(d->router_w, x, T, D, E, rp.kc, rp.tt, ws.partial);
-    router_topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(ws.partial, d->router_bias, T, E, rp.nchunk, k,
-                                                   d->route_scale, r.topk_idx, r.topk_w);
-    bucket_kernel<<<1, 512, 0, s>>>(r.topk_idx, T * k, E, r.count, r.offset, r.perm, r.pos, r.active, r.n_active);
-    return hipGetLastError();
+    hipError_t e = launch_router_partial(d, x, T, x_type, ws, s);
+    if (e != hipSuccess) return e;
+    return launch_route_finish(d, T, r, ws, s);
 }
 
 }  // namespace moe

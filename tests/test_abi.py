@@ -22,8 +22,8 @@ def _declared():
 def test_exports_every_declared_symbol():
     import quantized_routed_moe_router_amd as moe
     names = _declared()
-    assert {"moe_route", "moe_expert_ffn", "moe_layer_forward", "moe_workspace_size", "moe_rmsnorm",
-            "moe_dequant", "moe_version"} <= names
+    assert {"moe_route", "moe_expert_ffn", "moe_layer_forward", "moe_layer_forward_stage", "moe_workspace_size",
+            "moe_rmsnorm", "moe_dequant", "moe_version"} <= names
     for n in names:
         assert hasattr(moe._lib, n), n
     assert moe.version().startswith("moe-gfx950")
@@ -105,3 +105,6 @@ def test_other_entry_points_validate():
                                    None, err, 256) == -1
     assert moe._lib.moe_layer_forward(ctypes.byref(d), 0x80000, 1, 0, None, 0, None, 0x90000, 1 << 30, None,
                                       err, 256) == -1
+    for stage in (0, 5):
+        assert moe._lib.moe_layer_forward_stage(ctypes.byref(d), 0x80000, 1, 0, 0x100000, 0, None, stage, 0x90000,
+                                                1 << 30, None, err, 256) == -1

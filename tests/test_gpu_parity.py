@@ -148,6 +148,22 @@ def test_route_then_expert_ffn_matches_layer_forward():
     assert torch.equal(y, y2)
 
 
+@pytest.mark.parametrize("T", [1, 3, 40])
+def test_stages_equal_layer_forward(T):
+    import quantized_routed_moe_router_amd as moe
+    L = synth.make_layer(103, 0, D=512, E=32, k=4, F=256, Fs=128)
+    x = gu.x_to_device(x=synth.activations(104, T, 512))
+    W = gu.upload(L)
+    ws = moe.alloc_workspace(W, T)
+    r = moe.Routing(T, 4, 32)
+    y = torch.zeros((T, 512), dtype=torch.float32, device="cuda")
+    for st in (1, 2, 3, 4):
+        moe.layer_forward_stage(W, x, y, ws, st, routing=r)
+    y2, r2 = gu.run_forward(W, x)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(r.perm, r2.perm)
+
+
 def test_rmsnorm():
     import quantized_routed_moe_router_amd as moe
     x = synth.activations(99, 8, 4096)
@@ -160,3 +176,35 @@ def test_rmsnorm():
     torch.cuda.synchronize()
     gu.assert_close(out.cpu().numpy(), ref, tol=1e-5)
     assert torch.equal(out, xd)
+
+
+def test_graph_replays_match_eager():
+    # the block captured into a HIP graph, replayed several times with eager
+    # work and synchronizations between replays; every replay must equal the
+    # eager result bit for bit
+    import quantized_routed_moe_router_amd as moe
+    L = synth.make_layer(100, 0, D=512, E=32, k=4, F=256, Fs=128)
+    W = gu.upload(L)
+    xa = gu.x_to_device(x=synth.activations(101, 3, 512))
+    xb = gu.x_to_device(x=synth.activations(102, 3, 512))
+    ws = moe.alloc_workspace(W, 3)
+    r = moe.Routing(3, 4, 32)
+    y = torch.zeros((3, 512), dtype=torch.float32, device="cuda")
+    moe.layer_forward(W, xa, y, ws, routing=r)
+    torch.cuda.synchronize()
+    eager = y.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            moe.layer_forward(W, xa, y, ws, routing=r)
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(4):
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager), "replay %d" % rep
+        yb = torch.zeros_like(y)
+        moe.layer_forward(W, xb, yb, ws)  # other eager work on the same workspace
+        torch.cuda.synchronize()

@@ -6,7 +6,7 @@
  * sparsity that pays for everything else in DwarfStar", "Where the parameters
  * actually are"):
  *
- *   logits  l[t][e] = sum_k x[t][k] * W_r[k][e] (+ bias[e])        fp64 accumulation
+ *   logits  l[t][e] = sum_k x[t][k] * W_r[e][k] (+ bias[e])        fp64 accumulation
  *   top-k   the k experts of largest logit, ties to the lower index, slot 0 best
  *   weights w[t][s] = route_scale * softmax over the k chosen logits
  *   FFN_e   y = W_down[e] (silu(W_gate[e] x) * (W_up[e] x))           SwiGLU
@@ -30,7 +30,8 @@
  * A matrix [n_out][n_in] is flattened row-major and cut into consecutive
  * blocks, so blocks run along the reduction dimension.  Expert tensors are
  * expert-major: gate/up [E][F][D], down [E][D][F]; shared [Fs][D], [Fs][D],
- * [D][Fs]; router [D][E] fp32.
+ * [D][Fs]; router [E][D] fp32 (the D x E router matrix stored with each
+ * expert's D weights contiguous).
  *
  * Conventions ("Understanding Dwarf Star", 3.3.3 opaque types, 3.7.1-3.7.2
  * return codes and the caller's error buffer, 3.2.2-3.2.3 scratch buffers
@@ -83,7 +84,7 @@ typedef struct {
     int32_t n_ff_exp;      /* F: routed expert FFN width */
     int32_t n_ff_shared;   /* Fs: shared expert FFN width, 0 = no shared expert */
     int32_t gate_type, up_type, down_type, shared_type; /* moe_dtype block formats */
-    const float *router_w;    /* [D][E] fp32 */
+    const float *router_w;    /* [E][D] fp32, expert-major: row e = the D weights of expert e */
     const float *router_bias; /* [E] fp32 added to the logits before top-k, or NULL */
     float route_scale;        /* multiplies the renormalized weights (1.0 = plain) */
     const void *gate, *up;    /* [E][F][D] in gate_type / up_type blocks */

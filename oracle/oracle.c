@@ -128,13 +128,14 @@ int orc_dequant(int fmt, const uint8_t *src, int64_t n, const int8_t *cb, float 
 
 /* ---- routing ([UDS] 5.3.2, 5.3.5, 5.3.7 step 1) ------------------------- */
 
-/* router(x) starts from the logits x * W_router ([UDS] 5.3.2), W_router [D][E]. */
+/* router(x) starts from the logits x * W_router ([UDS] 5.3.2); W_router is
+ * stored expert-major, row e = the D weights of expert e. */
 int orc_logits(const orc_layer *L, const double *x, int32_t T, double *logits) {
     int32_t D = L->n_embd, E = L->n_expert;
     for (int32_t t = 0; t < T; ++t)
         for (int32_t e = 0; e < E; ++e) {
             double s = 0.0;
-            for (int32_t k = 0; k < D; ++k) s += x[(int64_t)t * D + k] * (double)L->router_w[(int64_t)k * E + e];
+            for (int32_t k = 0; k < D; ++k) s += x[(int64_t)t * D + k] * (double)L->router_w[(int64_t)e * D + k];
             if (L->router_bias) s += (double)L->router_bias[e];
             logits[(int64_t)t * E + e] = s;
         }

@@ -35,7 +35,7 @@ typedef struct {
     int32_t n_ff_exp;      /* F */
     int32_t n_ff_shared;   /* Fs, 0 = no shared expert */
     int32_t gate_fmt, up_fmt, down_fmt, shared_fmt;
-    const float *router_w;    /* [D][E] */
+    const float *router_w;    /* [E][D]: row e = expert e's weights */
     const float *router_bias; /* [E] or NULL, added to the logits */
     double route_scale;       /* multiplies the renormalized weights */
     const uint8_t *gate, *up; /* [E][F][D] blocks */
@@ -48,7 +48,7 @@ typedef struct {
 int64_t orc_tensor_bytes(int fmt, int64_t n_weights);
 /* Decode n weights of a flattened block tensor to fp32. 0 on success. */
 int orc_dequant(int fmt, const uint8_t *src, int64_t n_weights, const int8_t *codebook, float *out);
-/* Router logits l[t][e] = sum_k x[t][k] W[k][e] (+ bias[e]) in double, ascending k. */
+/* Router logits l[t][e] = sum_k x[t][k] W[e][k] (+ bias[e]) in double, ascending k. */
 int orc_logits(const orc_layer *L, const double *x, int32_t T, double *logits);
 /* Top-k by (logit desc, index asc); weights = route_scale * softmax over the k chosen logits.
  * gap_out[t] (optional) = l_(k) - l_(k+1), the margin that decided the set. */

@@ -93,12 +93,12 @@ RoutingPtrs from_ws(const Workspace &w) {
 }
 
 // The whole block (stage 0) or one of its four stages.  Few rows: the decode
-// schedule; otherwise router partials, top-k + bucketing, gate/up, down.
+// schedule; otherwise router logits, top-k + bucketing, gate/up, down.
 hipError_t forward(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r, float *y,
                    uint32_t flags, const Workspace &w, hipStream_t s, int stage) {
     if (small_path_ok(d, T) && small_route_ok(d, T)) return launch_small(d, x, T, x_type, r, y, flags, w, s, stage, true);
     hipError_t e = hipSuccess;
-    if (stage == 0 || stage == 1) e = launch_router_partial(d, x, T, x_type, w, s);
+    if (stage == 0 || stage == 1) e = launch_router_logits(d, x, T, x_type, w, s);
     if (e == hipSuccess && (stage == 0 || stage == 2)) e = launch_route_finish(d, T, r, w, s);
     if (e == hipSuccess && (stage == 0 || stage >= 3)) e = launch_ffn_large(d, x, T, x_type, r, y, flags, w, s, stage);
     return e;

@@ -443,24 +443,8 @@ MOE_DEV float chunk_dot(const uint8_t *base, int64_t i0, const float *x, const u
 
 // ---- workspace layout -------------------------------------------------------
 
-struct RouterPlan {
-    int kc;      // router rows (k) per partial-sum chunk
-    int nchunk;  // D / kc
-    int tt;      // tokens per router block
-};
-
-__host__ inline RouterPlan router_plan(int T, int D) {
-    RouterPlan p;
-    if (T <= 4) { p.kc = 64; p.tt = T < 1 ? 1 : T; }
-    else if (T <= 64) { p.kc = 128; p.tt = 8; }
-    else { p.kc = 512; p.tt = 32; }
-    while (p.kc > D) p.kc >>= 1;
-    p.nchunk = D / p.kc;
-    return p;
-}
-
 struct Workspace {
-    double *partial;      // [nchunk][T][E]
+    double *logits;       // [T][E] fp64 router logits
     int32_t *topk_idx;    // routing kept in the workspace when the caller gives none
     float *topk_w;
     int32_t *count, *offset, *perm, *pos, *active, *n_active;
@@ -481,13 +465,12 @@ __host__ inline Workspace workspace_layout(const moe_layer_desc *d, int32_t T, v
     char *b = (char *)base;
     int32_t E = d->n_expert, k = d->n_expert_used, D = d->n_embd, F = d->n_ff_exp, Fs = d->n_ff_shared;
     int64_t P = (int64_t)T * k;
-    RouterPlan rp = router_plan(T, D);
     auto take = [&](size_t n) {
         size_t at = off;
         off = align_up(off + n, 256);
         return b ? (void *)(b + at) : nullptr;
     };
-    w.partial = (double *)take(sizeof(double) * (size_t)rp.nchunk * (size_t)T * (size_t)E);
+    w.logits = (double *)take(sizeof(double) * (size_t)T * (size_t)E);
     w.topk_idx = (int32_t *)take(sizeof(int32_t) * (size_t)P);
     w.topk_w = (float *)take(sizeof(float) * (size_t)P);
     w.count = (int32_t *)take(sizeof(int32_t) * (size_t)E);
@@ -514,7 +497,7 @@ struct RoutingPtrs {
     int32_t *count, *offset, *perm, *pos, *active, *n_active;
 };
 
-hipError_t launch_router_partial(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type,
+hipError_t launch_router_logits(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type,
                                  const Workspace &ws, hipStream_t s);
 hipError_t launch_route_finish(const moe_layer_desc *d, int32_t T, const RoutingPtrs &r, const Workspace &ws,
                                hipStream_t s);

@@ -27,8 +27,8 @@ struct FfnArgs {
     // routing inputs for the kernels that also run the router
     const float *router_w, *router_bias;
     float route_scale;
-    double *partial;
-    int kc, tt, nchunk, n_router_blocks, n_tiles;
+    double *logits;
+    int n_router_blocks, n_slot_blocks;
     int32_t *w_topk_idx, *w_count, *w_offset, *w_perm, *w_pos, *w_active, *w_n_active;
     float *w_topk_w;
     // prepared activations (NULL when the path does not use them)

@@ -6,31 +6,41 @@
 namespace moe {
 
 template <int XT>
-__global__ void __launch_bounds__(256) router_partial_kernel(const float *__restrict__ W, const void *__restrict__ xin,
-                                                             int T, int D, int E, int kc, int tt,
-                                                             double *__restrict__ partial) {
-    router_partial_block<XT>(W, xin, T, D, E, kc, tt, partial, blockIdx.x, blockIdx.y, blockIdx.z);
+__global__ void __launch_bounds__(256) router_rows_kernel(const float *__restrict__ W, const float *__restrict__ bias,
+                                                          const void *__restrict__ xin, int T, int D, int E,
+                                                          double *__restrict__ logits) {
+    router_rows_wave<XT>(W, bias, xin, T, D, E, logits, blockIdx.x * 4 + (threadIdx.x >> 6));
 }
 
-__global__ void __launch_bounds__(1024) route_finish_small_kernel(
-    const double *__restrict__ partial, const float *__restrict__ bias, int T, int E, int nchunk, int k,
-    float route_scale, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w, int32_t *__restrict__ count,
-    int32_t *__restrict__ offset, int32_t *__restrict__ perm, int32_t *__restrict__ pos,
-    int32_t *__restrict__ active, int32_t *__restrict__ n_active) {
-    route_finish_small(partial, bias, T, E, nchunk, k, route_scale, topk_idx, topk_w, count, offset, perm, pos, active,
-                       n_active);
+template <int XT>
+__global__ void __launch_bounds__(256) router_tile_kernel(const float *__restrict__ W, const float *__restrict__ bias,
+                                                          const void *__restrict__ xin, int T, int D, int E,
+                                                          double *__restrict__ logits) {
+    router_tile_block<XT>(W, bias, xin, T, D, E, logits, blockIdx.x, blockIdx.y);
 }
 
-// One block per token: logits from the chunk partials, then wave 0 selects.
-__global__ void __launch_bounds__(256) router_topk_kernel(const double *__restrict__ partial,
-                                                          const float *__restrict__ bias, int T, int E, int nchunk,
-                                                          int k, float route_scale, int32_t *__restrict__ topk_idx,
+__global__ void __launch_bounds__(1024) route_finish_small_kernel(const double *__restrict__ logits, int T, int E,
+                                                                  int k, float route_scale,
+                                                                  int32_t *__restrict__ topk_idx,
+                                                                  float *__restrict__ topk_w,
+                                                                  int32_t *__restrict__ count,
+                                                                  int32_t *__restrict__ offset,
+                                                                  int32_t *__restrict__ perm, int32_t *__restrict__ pos,
+                                                                  int32_t *__restrict__ active,
+                                                                  int32_t *__restrict__ n_active) {
+    route_finish_small(logits, T, E, k, route_scale, topk_idx, topk_w, count, offset, perm, pos, active, n_active);
+}
+
+// One wave per token: top-k of its logit row.
+__global__ void __launch_bounds__(256) router_topk_kernel(const double *__restrict__ logits, int T, int E, int k,
+                                                          float route_scale, int32_t *__restrict__ topk_idx,
                                                           float *__restrict__ topk_w) {
-    __shared__ double lg[kMaxExperts];
-    const int t = blockIdx.x;
-    reduce_logits(partial, bias, T, E, nchunk, t, 1, lg);
-    if (threadIdx.x >= 64) return;
-    select_topk(lg, E, k, route_scale, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k, nullptr, nullptr);
+    __shared__ double lg[4][kMaxExperts];
+    const int wave = threadIdx.x >> 6, t = blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    for (int e = threadIdx.x & 63; e < E; e += 64) lg[wave][e] = logits[(int64_t)t * E + e];
+    __builtin_amdgcn_wave_barrier();
+    select_topk(lg[wave], E, k, route_scale, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k, nullptr, nullptr);
 }
 
 __global__ void __launch_bounds__(1024) bucket_small_kernel(const int32_t *__restrict__ topk_idx, int P, int E,
@@ -134,30 +144,38 @@ __global__ void __launch_bounds__(512) bucket_kernel(const int32_t *__restrict__
     if (tid == 0) n_active[0] = na;
 }
 
-hipError_t launch_router_partial(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type,
-                                 const Workspace &ws, hipStream_t s) {
+// rows kernel for few tokens, tiles for many
+bool router_rows_ok(int T) { return T <= 16; }
+
+hipError_t launch_router_logits(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type,
+                                const Workspace &ws, hipStream_t s) {
     const int D = d->n_embd, E = d->n_expert;
-    RouterPlan rp = router_plan(T, D);
-    dim3 g(rp.nchunk, (T + rp.tt - 1) / rp.tt, (E + 63) / 64);
-    if (x_type == MOE_BF16)
-        router_partial_kernel<MOE_BF16><<<g, 256, 0, s>>>(d->router_w, x, T, D, E, rp.kc, rp.tt, ws.partial);
-    else
-        router_partial_kernel<MOE_F32><<<g, 256, 0, s>>>(d->router_w, x, T, D, E, rp.kc, rp.tt, ws.partial);
+    if (router_rows_ok(T)) {
+        const int per_block = 4 * (4096 / D);
+        const int blocks = (E + per_block - 1) / per_block;
+        if (x_type == MOE_BF16)
+            router_rows_kernel<MOE_BF16><<<blocks, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E, ws.logits);
+        else
+            router_rows_kernel<MOE_F32><<<blocks, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E, ws.logits);
+    } else {
+        dim3 g((T + 15) / 16, (E + 15) / 16);
+        if (x_type == MOE_BF16)
+            router_tile_kernel<MOE_BF16><<<g, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E, ws.logits);
+        else
+            router_tile_kernel<MOE_F32><<<g, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E, ws.logits);
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_route_finish(const moe_layer_desc *d, int32_t T, const RoutingPtrs &r, const Workspace &ws,
                                hipStream_t s) {
-    const int D = d->n_embd, E = d->n_expert, k = d->n_expert_used, P = T * k;
-    RouterPlan rp = router_plan(T, D);
+    const int E = d->n_expert, k = d->n_expert_used, P = T * k;
     if (route_small_ok(T, E, k)) {
-        route_finish_small_kernel<<<1, 1024, 0, s>>>(ws.partial, d->router_bias, T, E, rp.nchunk, k, d->route_scale,
-                                                     r.topk_idx, r.topk_w, r.count, r.offset, r.perm, r.pos,
-                                                     r.active, r.n_active);
+        route_finish_small_kernel<<<1, 1024, 0, s>>>(ws.logits, T, E, k, d->route_scale, r.topk_idx, r.topk_w,
+                                                     r.count, r.offset, r.perm, r.pos, r.active, r.n_active);
         return hipGetLastError();
     }
-    router_topk_kernel<<<T, 256, 0, s>>>(ws.partial, d->router_bias, T, E, rp.nchunk, k, d->route_scale,
-                                         r.topk_idx, r.topk_w);
+    router_topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(ws.logits, T, E, k, d->route_scale, r.topk_idx, r.topk_w);
     if (P <= 1024)
         bucket_small_kernel<<<1, 1024, 0, s>>>(r.topk_idx, P, E, r.count, r.offset, r.perm, r.pos, r.active,
                                                r.n_active);
@@ -168,7 +186,7 @@ hipError_t launch_route_finish(const moe_layer_desc *d, int32_t T, const Routing
 
 hipError_t launch_route(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
                         const Workspace &ws, hipStream_t s) {
-    hipError_t e = launch_router_partial(d, x, T, x_type, ws, s);
+    hipError_t e = launch_router_logits(d, x, T, x_type, ws, s);
     if (e != hipSuccess) return e;
     return launch_route_finish(d, T, r, ws, s);
 }

@@ -138,7 +138,7 @@ class Layer:
     up_fmt: int
     down_fmt: int
     shared_fmt: int
-    router_w: np.ndarray                     # [D][E] fp32
+    router_w: np.ndarray                     # [E][D] fp32, row e = expert e
     gate: np.ndarray                         # [E][F][D] blocks
     up: np.ndarray
     down: np.ndarray                         # [E][D][F] blocks
@@ -169,7 +169,7 @@ def make_layer(seed, layer, D, E, k, F, Fs, gate_fmt=Q2K, down_fmt=Q2K, shared_f
     L = Layer(
         n_embd=D, n_expert=E, n_expert_used=k, n_ff_exp=F, n_ff_shared=Fs,
         gate_fmt=gate_fmt, up_fmt=gate_fmt, down_fmt=down_fmt, shared_fmt=shared_fmt,
-        router_w=normal(seed, layer, TAG_ROUTER, 0, D * E, WEIGHT_SIGMA).reshape(D, E),
+        router_w=normal(seed, layer, TAG_ROUTER, 0, D * E, WEIGHT_SIGMA).reshape(E, D),
         gate=expert_tensor(gate_fmt, seed, layer, TAG_GATE, E, F, D, **kw),
         up=expert_tensor(gate_fmt, seed, layer, TAG_UP, E, F, D, **kw),
         down=expert_tensor(down_fmt, seed, layer, TAG_DOWN, E, D, F, **kw),

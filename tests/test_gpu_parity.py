@@ -86,8 +86,8 @@ def test_degenerate_routings(E, k):
 def test_exact_ties_go_to_lower_index():
     L = synth.make_layer(90, 0, D=256, E=16, k=3, F=128, Fs=0)
     W = L.router_w.copy()
-    W[:, 12] = W[:, 3]
-    W[:, 9] = W[:, 3]
+    W[12] = W[3]
+    W[9] = W[3]
     L.router_w = W
     bias = np.zeros(16, np.float32)
     bias[[3, 9, 12]] = 40.0

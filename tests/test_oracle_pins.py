@@ -228,11 +228,11 @@ def test_router_logits_and_duplicate_columns():
     L = synth.make_layer(21, 0, D=256, E=16, k=2, F=128, Fs=0)
     x = synth.activations(21, 9, 256)
     lg = oracle.logits(L, x=x)
-    ref = x.astype(np.float64) @ L.router_w.astype(np.float64)
+    ref = x.astype(np.float64) @ L.router_w.astype(np.float64).T
     assert np.allclose(lg, ref, rtol=1e-12, atol=1e-12)
-    # duplicated router columns tie exactly; the lower index is taken first
+    # duplicated router rows tie exactly; the lower index is taken first
     W = L.router_w.copy()
-    W[:, 11] = W[:, 4]
+    W[11] = W[4]
     L.router_w = W
     bias = np.zeros(16, np.float32)
     bias[4] = bias[11] = 50.0
@@ -288,7 +288,7 @@ def _dense_numpy(L, xd, bf16=False):
         Fs = L.n_ff_shared
         y += ffn(mat(L.sh_gate, L.shared_fmt, 0, Fs, D), mat(L.sh_up, L.shared_fmt, 0, Fs, D),
                  mat(L.sh_down, L.shared_fmt, 0, D, Fs), xd)
-    lg = xd @ L.router_w.astype(np.float64)
+    lg = xd @ L.router_w.astype(np.float64).T
     if L.router_bias is not None:
         lg = lg + L.router_bias.astype(np.float64)
     for t in range(xd.shape[0]):

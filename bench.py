@@ -44,7 +44,21 @@ def parse():
     ap.add_argument("--replicas", type=int, default=16)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch every step eagerly (for counter profiling)")
+    ap.add_argument("--copy-calib", type=float, default=0.0, metavar="MB",
+                    help="only run 20 plain device copies of MB megabytes (scale reference for HBM counters)")
     return ap.parse_args()
+
+
+def copy_calib(mb):
+    import torch
+    n = int(mb * 1e6) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(20):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calib_bytes_read": n * 4, "copy_calib_bytes_written": n * 4, "launches": 20}))
 
 
 def main():
@@ -54,6 +68,10 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d, WORLD_SIZE %d). "
               "Run it with --gpus 1." % (args.gpus, world), file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_calib > 0:
+        copy_calib(args.copy_calib)
+        return
 
     import numpy as np
     import torch
@@ -119,46 +137,50 @@ def main():
     torch.cuda.synchronize()
 
     # One graph holds R consecutive steps (one per replica).  Replaying it is
-    # how a decode loop issues the block without per-kernel host overhead; the
-    # event nodes around each gate/up launch time the dominant kernel.
+    # how a decode loop issues the block without per-kernel host overhead.
+    # --no-graph launches every step eagerly instead (counter profiling).
     K = args.steps
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(R)]
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    graphs = []
-    with torch.cuda.stream(side):
-        for n in sorted({R, K % R} - {0}, reverse=True):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=side):
-                for i in range(n):
-                    step(i, events[i] if n == R else None)
-            graphs.append((n, g))
-    torch.cuda.current_stream().wait_stream(side)
-    full = [g for n, g in graphs if n == R]
-    rest = [g for n, g in graphs if n != R]
-    plan = full * (K // R) + rest
-    for g in (full or rest)[:1] * 2:
-        g.replay()
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for g in plan:
-        g.replay()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    ms_step = 1000.0 * wall / K
-    ev_src = "graph event nodes"
-    try:
-        gateup_ms = float(np.mean([a.elapsed_time(b) for a, b in events])) if full else float("nan")
-    except RuntimeError:
-        gateup_ms = float("nan")
-    if not (gateup_ms > 0):
-        # eager pass with events on the launch stream
-        ev_src = "eager events"
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4 * R)]
-        for i, e in enumerate(evs):
-            step(i, e)
+    if args.no_graph:
+        plan = []
         torch.cuda.synchronize()
-        gateup_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+        t_start = time.perf_counter()
+        for i in range(K):
+            step(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+    else:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graphs = []
+        with torch.cuda.stream(side):
+            for n in sorted({R, K % R} - {0}, reverse=True):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    for i in range(n):
+                        step(i)
+                graphs.append((n, g))
+        torch.cuda.current_stream().wait_stream(side)
+        full = [g for n, g in graphs if n == R]
+        rest = [g for n, g in graphs if n != R]
+        plan = full * (K // R) + rest
+        for g in (full or rest)[:1] * 2:
+            g.replay()
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for g in plan:
+            g.replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+    ms_step = 1000.0 * wall / K
+    # The dominant kernel's launch time: HIP events on the launch stream
+    # around stage 3, over 4R cold-cache steps issued eagerly (events inside a
+    # captured graph do not time).
+    ev_src = "HIP events around each stage-3 launch, %d eager cold-cache steps" % (4 * R)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4 * R)]
+    for i, e in enumerate(evs):
+        step(i, e)
+    torch.cuda.synchronize()
+    gateup_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     log("timed %d steps in %.3f s (%d graph replays); gate/up avg %.2f us (%s)" % (
         K, wall, len(plan), gateup_ms * 1e3, ev_src))
 

@@ -286,22 +286,27 @@ MOE_DEV float chunk_scale(const float *x, float &inv24) {
     return __uint_as_float((uint32_t)(127 + 13 - e) << 23);   // S
 }
 
-// Prepared activations for Q2K rows, one record of 18 dwords per group of 16
-// values v: hi[m], lo[m] (m < 8) = the fp16 pair (v[m], v[m+8]) * S * 4^-m'
-// split into hi + lo, with m' = m for m < 5 and m - 5 after; sx = sum of the
-// 16 values (fp32); inv = 2^24 / S.  S is a power of two per group with
-// max|v| * S in [2^13, 2^14).  A lane's 64 weights use 4 records.
+// Prepared activations for Q2K rows: one record of 20 dwords per group of 16
+// values v[0..15].  Slot m < 8 pairs v[m] with v[m+8] (the two weights whose
+// codes share bit positions in one code dword); hi[m], lo[m] hold that fp16
+// pair times S_h * 4^-m', split into hi + lo, with m' = m for m < 5 and m - 5
+// after.  The pairs form two halves h = m / 4 (positions {0-3, 8-11} and
+// {4-7, 12-15}), each with its own power-of-two scale S_h (max|v| * S_h in
+// [2^13, 2^14) over the half): so the two halves can be written by different
+// waves.  sx_h is the sum of the half's 8 values, inv_h = 2^24 / S_h.
+// Layout: hi[0..7], lo[0..7], sx0, inv0, sx1, inv1.  A lane's 64 weights use
+// 4 consecutive records.
 struct P16 {
     uint32_t hi[8], lo[8];
-    float sx, inv;
+    float sx0, inv0, sx1, inv1;
 };
-constexpr int kP16Dwords = 18;
+constexpr int kP16Dwords = 20;
 
 struct XQ2K {
     P16 g[4];
 };
 
-// scale S and 2^24/S for a group whose largest magnitude is m
+// scale S and 2^24/S for a set whose largest magnitude is m
 MOE_DEV float group_scale(float m, float &inv24) {
     int e = m > 0.f ? (int)((__float_as_uint(m) >> 23) & 0xFF) - 127 : 0;
     e = max(-100, min(100, e));
@@ -311,33 +316,50 @@ MOE_DEV float group_scale(float m, float &inv24) {
 
 MOE_DEV float p16_factor(int m) { return 1.0f / (float)(1 << (2 * (m < 5 ? m : m - 5))); }
 
+// position of the i-th value (i < 8) of half h in a group of 16
+MOE_DEV int p16_pos(int h, int i) { return (i < 4 ? 0 : 4) + 4 * h + i; }
+
 // per-lane preparation of the lane's 64 activations
 MOE_DEV void prep_q2k(const float *x, XQ2K &p) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-        float s = 0.f, m = 0.f;
+        const float *v = x + 16 * g;
+        float S[2];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            s += x[16 * g + i];
-            m = fmaxf(m, fabsf(x[16 * g + i]));
+        for (int h = 0; h < 2; ++h) {
+            float s = 0.f, m = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                s += v[p16_pos(h, i)];
+                m = fmaxf(m, fabsf(v[p16_pos(h, i)]));
+            }
+            float inv;
+            S[h] = group_scale(m, inv);
+            if (h == 0) {
+                p.g[g].sx0 = s;
+                p.g[g].inv0 = inv;
+            } else {
+                p.g[g].sx1 = s;
+                p.g[g].inv1 = inv;
+            }
         }
-        p.g[g].sx = s;
-        const float S = group_scale(m, p.g[g].inv);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const float f = S * p16_factor(j);
-            split2(x[16 * g + j] * f, x[16 * g + j + 8] * f, p.g[g].hi[j], p.g[g].lo[j]);
+            const float f = S[j >> 2] * p16_factor(j);
+            split2(v[j] * f, v[j + 8] * f, p.g[g].hi[j], p.g[g].lo[j]);
         }
     }
 }
 
-// wave-cooperative preparation: lane l holds value v of position l % 16 in
-// group l / 16; records of groups < ngroups go to out[(l / 16) * 18 ...].
-// All lanes of the wave must call it.
+// Wave-cooperative preparation of ngroups (<= 4) groups: lane l holds the
+// value at position l % 16 of group l / 16; the records go to out[(l / 16) *
+// 20 ...].  All lanes of the wave must call it.
 MOE_DEV void prep16_wave(float v, uint32_t *out, int ngroups = 4) {
-    const int lane = threadIdx.x & 63, gl = lane & 15;
+    const int lane = threadIdx.x & 63, pos = lane & 15;
     float m = fabsf(v), s = v;
-    for (int o = 1; o < 16; o <<= 1) {  // within the 16-lane group, fixed order
+#pragma unroll
+    for (int o = 1; o <= 8; o <<= 1) {  // over the 8 lanes of the half: bits 0, 1, 3 of pos
+        if (o == 4) continue;
         m = fmaxf(m, __shfl_xor(m, o, kWave));
         s += __shfl_xor(s, o, kWave);
     }
@@ -346,22 +368,23 @@ MOE_DEV void prep16_wave(float v, uint32_t *out, int ngroups = 4) {
     const float partner = __shfl_down(v, 8, kWave);
     uint32_t *rec = out + (lane >> 4) * kP16Dwords;
     if ((lane >> 4) >= ngroups) return;
-    if (gl < 8) {
-        const float f = S * p16_factor(gl);
+    if (pos < 8) {
+        const float f = S * p16_factor(pos);
         uint32_t hi, lo;
         split2(v * f, partner * f, hi, lo);
-        rec[gl] = hi;
-        rec[8 + gl] = lo;
-    } else if (gl == 8) {
-        rec[16] = __float_as_uint(s);
-        rec[17] = __float_as_uint(inv);
+        rec[pos] = hi;
+        rec[8 + pos] = lo;
+        if ((pos & 3) == 0) {  // pos 0: half 0, pos 4: half 1
+            rec[16 + (pos >> 1)] = __float_as_uint(s);
+            rec[17 + (pos >> 1)] = __float_as_uint(inv);
+        }
     }
 }
 
 MOE_DEV void load_q2k_prep(const uint32_t *rec4, XQ2K &p) {
     u32x4 *dst = (u32x4 *)&p;
 #pragma unroll
-    for (int i = 0; i < 18; ++i) dst[i] = *(const u32x4 *)(rec4 + 4 * i);
+    for (int i = 0; i < 4 * kP16Dwords / 4; ++i) dst[i] = *(const u32x4 *)(rec4 + 4 * i);
 }
 
 MOE_DEV float q2k_dot2(const Q2KChunk &c, const XQ2K &p) {
@@ -370,27 +393,31 @@ MOE_DEV float q2k_dot2(const Q2KChunk &c, const XQ2K &p) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
         const uint32_t q = c.qs[g], q5 = q >> 10;
-        float a = 0.f;
+        float a[2] = {0.f, 0.f};
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
             const uint32_t t = m < 5 ? (q & (0x00030003u << (2 * m))) : (q5 & (0x00030003u << (2 * (m - 5))));
-            a = dot2(t, p.g[g].hi[m], a);
-            a = dot2(t, p.g[g].lo[m], a);
+            a[m >> 2] = dot2(t, p.g[g].hi[m], a[m >> 2]);
+            a[m >> 2] = dot2(t, p.g[g].lo[m], a[m >> 2]);
         }
         const uint32_t smb = (c.sm >> (8 * g)) & 0xFFu;
-        acc_q = __builtin_fmaf((float)(smb & 15u), a * p.g[g].inv, acc_q);
-        acc_m = __builtin_fmaf((float)(smb >> 4), p.g[g].sx, acc_m);
+        acc_q = __builtin_fmaf((float)(smb & 15u), __builtin_fmaf(a[1], p.g[g].inv1, a[0] * p.g[g].inv0), acc_q);
+        acc_m = __builtin_fmaf((float)(smb >> 4), p.g[g].sx0 + p.g[g].sx1, acc_m);
     }
     return d * acc_q - dmin * acc_m;
 }
 
-// Activations of one lane chunk for Q8_0 codes: pair i holds
-// (x[2i], x[2i+1]) * S; int8 codes enter as the fp16 subnormal (q+128)*2^-24.
+// Activations of one lane chunk (64 values) for Q8_0 codes: pair i holds
+// (x[2i], x[2i+1]) * S split into hi + lo, S a power of two per chunk; int8
+// codes enter as the fp16 subnormal (q+128)*2^-24.  68 dwords: hi[32],
+// lo[32], the sums of the two 32-blocks, 2^24 / S, one pad dword.
 struct XQ8 {
     uint32_t hi[32], lo[32];
     float sx[2];  // sum of each 32-block of activations
     float inv;
+    float pad;
 };
+constexpr int kXQ8Dwords = 68;
 
 MOE_DEV void prep_q8(const float *x, XQ8 &p) {
     const float S = chunk_scale(x, p.inv);
@@ -403,6 +430,38 @@ MOE_DEV void prep_q8(const float *x, XQ8 &p) {
     }
 #pragma unroll
     for (int i = 0; i < 32; ++i) split2(x[2 * i] * S, x[2 * i + 1] * S, p.hi[i], p.lo[i]);
+    p.pad = 0.f;
+}
+
+// Wave-cooperative XQ8 record of one chunk: lane l holds value l.
+MOE_DEV void prep8_wave(float v, uint32_t *rec) {
+    const int lane = threadIdx.x & 63;
+    float m = fabsf(v), s = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        m = fmaxf(m, __shfl_xor(m, o, kWave));
+        if (o < 32) s += __shfl_xor(s, o, kWave);
+    }
+    float inv;
+    const float S = group_scale(m, inv);  // max|v| * S in [2^13, 2^14)
+    const float partner = __shfl_down(v, 1, kWave);
+    if ((lane & 1) == 0) {
+        uint32_t hi, lo;
+        split2(v * S, partner * S, hi, lo);
+        rec[lane >> 1] = hi;
+        rec[32 + (lane >> 1)] = lo;
+    }
+    if ((lane & 31) == 0) rec[64 + (lane >> 5)] = __float_as_uint(s);
+    if (lane == 0) {
+        rec[66] = __float_as_uint(inv);
+        rec[67] = 0u;
+    }
+}
+
+MOE_DEV void load_q8_prep(const uint32_t *rec, XQ8 &p) {
+    u32x4 *dst = (u32x4 *)&p;
+#pragma unroll
+    for (int i = 0; i < kXQ8Dwords / 4; ++i) dst[i] = *(const u32x4 *)(rec + 4 * i);
 }
 
 MOE_DEV float q8_dot2(const Q8Chunk &c, const XQ8 &p) {
@@ -429,7 +488,6 @@ MOE_DEV float q8_dot2(const Q8Chunk &c, const XQ8 &p) {
     // sum (q+128) x = sum q x + 128 sum x
     return d0 * __builtin_fmaf(p.inv, a0, -128.0f * p.sx[0]) + d1 * __builtin_fmaf(p.inv, a1, -128.0f * p.sx[1]);
 }
-
 template <int FMT>
 MOE_DEV float chunk_dot(const uint8_t *base, int64_t i0, const float *x, const uint32_t *cb_lds) {
     if constexpr (FMT == MOE_Q2K) {
@@ -439,6 +497,40 @@ MOE_DEV float chunk_dot(const uint8_t *base, int64_t i0, const float *x, const u
     } else {
         return cb2_dot(cb2_load(base, i0), x, cb_lds);
     }
+}
+
+// Per-slot record for the expert kernels of the few-token schedule: expert
+// e (-1: no expert in this slot), its first bucket position j0, its bucket
+// size n and the token of each bucket entry, so that one load gives a wave
+// everything it needs to address weights and activations.
+struct SlotRec {
+    int32_t e, j0, n, pad;
+    uint32_t tok0, tok1, tok2, tok3;  // byte i of the 16 = token of bucket entry i
+};
+
+// The record with every field made wave-uniform (the slot index is uniform).
+MOE_DEV SlotRec uniform_slot(const SlotRec *slots, int s) {
+    const SlotRec v = slots[s];
+    SlotRec r;
+    r.e = __builtin_amdgcn_readfirstlane(v.e);
+    r.j0 = __builtin_amdgcn_readfirstlane(v.j0);
+    r.n = __builtin_amdgcn_readfirstlane(v.n);
+    r.pad = 0;
+    r.tok0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)v.tok0);
+    r.tok1 = (uint32_t)__builtin_amdgcn_readfirstlane((int)v.tok1);
+    r.tok2 = (uint32_t)__builtin_amdgcn_readfirstlane((int)v.tok2);
+    r.tok3 = (uint32_t)__builtin_amdgcn_readfirstlane((int)v.tok3);
+    return r;
+}
+
+MOE_DEV int slot_token(const SlotRec &r, int j) {
+    const uint64_t w = j < 8 ? ((uint64_t)r.tok1 << 32 | r.tok0) : ((uint64_t)r.tok3 << 32 | r.tok2);
+    return (int)((w >> (8 * (j & 7))) & 0xFFu);
+}
+
+// Record of expert e, bucket start j0, size n, with the token bytes packed.
+MOE_DEV SlotRec make_slot(int e, int j0, int n, uint64_t tlo, uint64_t thi) {
+    return SlotRec{e, j0, n, 0, (uint32_t)tlo, (uint32_t)(tlo >> 32), (uint32_t)thi, (uint32_t)(thi >> 32)};
 }
 
 // ---- workspace layout -------------------------------------------------------
@@ -452,8 +544,11 @@ struct Workspace {
     float *hs;            // [T][Fs]
     float *ypart;         // [T*k][D]
     float *ys;            // [T][D]
-    uint32_t *xp16;       // [T][D/16][18] x prepared for Q2K rows
-    uint32_t *hp16;       // [T*k][F/16][18] h prepared for Q2K rows
+    uint32_t *xp16;       // [T][D/16] records: x prepared for Q2K rows
+    uint32_t *xq8;        // [T][D/64] records: x prepared for Q8_0 rows
+    uint32_t *hp16;       // [T*k][F/16] records: h prepared for Q2K rows
+    uint32_t *hsrec;      // [T][Fs] records of hs prepared for the shared down (Q2K or Q8_0)
+    SlotRec *slots;       // [T*k] per-slot records of the few-token schedule
     size_t bytes;
 };
 
@@ -484,7 +579,10 @@ __host__ inline Workspace workspace_layout(const moe_layer_desc *d, int32_t T, v
     w.ypart = (float *)take(sizeof(float) * (size_t)P * (size_t)D);
     w.ys = (float *)take(sizeof(float) * (size_t)T * (size_t)D);
     w.xp16 = (uint32_t *)take(sizeof(uint32_t) * kP16Dwords * (size_t)T * (size_t)(D / 16));
+    w.xq8 = (uint32_t *)take(sizeof(uint32_t) * kXQ8Dwords * (size_t)T * (size_t)(D / 64));
     w.hp16 = (uint32_t *)take(sizeof(uint32_t) * kP16Dwords * (size_t)P * (size_t)(F / 16));
+    w.hsrec = (uint32_t *)take(sizeof(uint32_t) * kP16Dwords * (size_t)T * (size_t)((Fs > 0 ? Fs : 16) / 16));
+    w.slots = (SlotRec *)take(sizeof(SlotRec) * (size_t)P);
     w.bytes = off;
     return w;
 }

@@ -31,9 +31,17 @@ struct FfnArgs {
     int n_router_blocks, n_slot_blocks;
     int32_t *w_topk_idx, *w_count, *w_offset, *w_perm, *w_pos, *w_active, *w_n_active;
     float *w_topk_w;
-    // prepared activations (NULL when the path does not use them)
-    uint32_t *xp16, *hp16;
-    int n_prep_blocks;
+    // prepared activations (NULL when the path does not use them): x for Q2K
+    // rows ([T][D/16] records), x for Q8_0 rows ([T][D/64] records), h for the
+    // routed Q2K down ([T*k][F/16] records)
+    uint32_t *xp16, *xq8, *hp16;
+    uint32_t *hsrec;  // hs prepared for the shared down ([T][Fs/16] Q2K or [T][Fs/64] Q8_0 records)
+    int n_gu_blocks;  // K3: blocks of routed gate/up before the hs-preparing blocks
+    int shared_fmt;
+    // per-slot records (few-token schedule) and their number, min(T*k, E)
+    SlotRec *slots;
+    int nslots;
+    int build_slots;  // K1 writes the records from a given routing
 };
 
 // Load the lane's 64 activations at element offset off of x (fp32 or bf16).
@@ -120,61 +128,205 @@ MOE_DEV RowPlan row_plan(int n_in, int lane) {
     return p;
 }
 
-// One wave's rows [row0, row0+nrows) of matrix m0 (and m1 when TWO): the
-// row chunks are loaded into registers first (load), the dots with the
-// lane's prepared activations come after (compute).  All loads are
-// unconditional: rows past the end are clamped to the last one.
-template <int FMT, bool TWO, int NB>
-struct WaveRows {
-    RawChunk<FMT> g[NB], u[NB];
-    int iters;
-    RowPlan rp;
+// LDS ordering between the lanes of one wave: LDS operations of a wave
+// execute in issue order, so only the compiler has to be kept from moving
+// them across this point.
+MOE_DEV void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
-    MOE_DEV void load(const uint8_t *m0, const uint8_t *m1, int n_in, int row0, int nrows, int lane) {
-        rp = row_plan(n_in, lane);
-        iters = (nrows + rp.rpi - 1) / rp.rpi;
+// Sum of lanes xor 1 and xor 2 (quad permutations) and xor 4.. via shuffles.
+MOE_DEV float xor_sum(float s, int L) {
+    if (L > 1) s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, false));
+    if (L > 2) s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x4E, 0xF, 0xF, false));
+    for (int m = 4; m < L; m <<= 1) s += __shfl_xor(s, m, kWave);
+    return s;
+}
+
+// Segment sums of NV per-lane partials through a wave-private LDS area red
+// (NV * 64 floats, 16-byte aligned).  Lanes form segments of cpr consecutive
+// lanes (cpr a power of two <= 64).  Afterwards red[i * 64 + r] holds the sum
+// of partial i over segment r (r < 64 / cpr).  The partials of one output are
+// added in a fixed order (runs of consecutive lanes, then a fixed butterfly),
+// the same for every output.  All lanes of the wave must call it.
+template <int NV>
+MOE_DEV void seg_reduce_lds(const float (&v)[NV], int cpr, float *red) {
+    const int lane = threadIdx.x & 63;
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const int r = min(b * rp.rpi + rp.lr, nrows - 1);
-            const int64_t i0 = (int64_t)(row0 + r) * n_in + 64 * rp.c;
-            g[b].load(m0, i0);
-            if constexpr (TWO) u[b].load(m1, i0);
+    for (int i = 0; i < NV; ++i) red[i * 64 + lane] = v[i];
+    wave_lds_sync();
+    const int rpi = 64 / cpr;
+    float res[NV];
+    int dst[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) dst[j] = -1;
+    if (cpr >= NV) {  // L lanes per output, each adds a run of NV partials
+        const int L = cpr / NV, o = lane / L, sub = lane % L;
+        const int i = o / rpi, r = o % rpi;
+        const float *p = red + i * 64 + r * cpr + sub * NV;
+        float s = 0.f;
+        if constexpr (NV % 4 == 0) {
+#pragma unroll
+            for (int j = 0; j < NV; j += 4) {
+                const f32x4 q = *(const f32x4 *)(p + j);
+                s += q[0];
+                s += q[1];
+                s += q[2];
+                s += q[3];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NV; ++j) s += p[j];
         }
-    }
-
-    // emit(r, v0, v1) on the lane holding row r's full sums
-    template <typename Emit>
-    MOE_DEV void compute(const typename RawChunk<FMT>::Prep &xr, const uint32_t *cb, int nrows, Emit emit) const {
+        res[0] = xor_sum(s, L);
+        if (sub == 0) dst[0] = i * 64 + r;
+    } else {  // each lane owns NV / cpr outputs and adds all cpr partials of each
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            if (b < iters) {  // uniform over the wave
-                const float s0 = seg_sum(g[b].dot(xr, cb), rp.cpr);
-                float s1 = 0.f;
-                if constexpr (TWO) s1 = seg_sum(u[b].dot(xr, cb), rp.cpr);
-                const int r = b * rp.rpi + rp.lr;
-                if (rp.c == 0 && r < nrows) emit(r, s0, s1);
+        for (int j = 0; j < NV; ++j) {
+            const int o = lane + 64 * j;
+            if (o < NV * rpi) {
+                const int i = o / rpi, r = o % rpi;
+                const float *p = red + i * 64 + r * cpr;
+                float s = 0.f;
+                for (int q = 0; q < cpr; ++q) s += p[q];
+                res[j] = s;
+                dst[j] = i * 64 + r;
             }
         }
     }
-};
+    wave_lds_sync();
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+        if (dst[j] >= 0) red[dst[j]] = res[j];
+    wave_lds_sync();
+}
 
-// Rows of one wave iteration per format: enough to cover the wave's rows in
-// one load batch (4 rows of 4096 weights, or 2 rows of 2048 for the down).
+// One wave: dots of rows rowof(l), l < nrows, of m0 (and m1 when TWO) over
+// the columns [col0, col0 + ncols) (rows ld weights apart) with the lane's
+// prepared activations.  A lane takes 64 consecutive columns of a row, cpr =
+// ncols/64 lanes a row, 64/cpr rows per iteration; NB iterations per load
+// batch.  Every weight load of a batch is issued first (unconditionally, rows
+// past the end clamped to the last one), then loadprep(xr) issues the loads
+// of the activations (first batch only), so that a wave waits for one memory
+// round trip, not two.  The partial sums go through red (LDS, 2*NB*64 floats
+// per wave, 16-byte aligned); then emit(l, s0, s1) runs once per row, on
+// some lane.
+template <int FMT, bool TWO, int NB, typename RowOf, typename LoadPrep, typename Emit>
+MOE_DEV void rows_dot(const uint8_t *m0, const uint8_t *m1, int64_t ld, int col0, int ncols, int nrows, RowOf rowof,
+                      LoadPrep loadprep, const uint32_t *cb, int lane, float *red, Emit emit) {
+    constexpr int NV = (TWO ? 2 : 1) * NB;
+    const int cpr = ncols >> 6, rpi = 64 / cpr, lr = lane / cpr, c = lane % cpr;
+    typename RawChunk<FMT>::Prep xr;
+    for (int b0 = 0; b0 < nrows; b0 += NB * rpi) {
+        RawChunk<FMT> g[NB], u[NB];
+#pragma unroll
+        for (int it = 0; it < NB; ++it) {
+            const int l = min(b0 + it * rpi + lr, nrows - 1);
+            const int64_t i0 = (int64_t)rowof(l) * ld + col0 + 64 * c;
+            g[it].load(m0, i0);
+            if constexpr (TWO) u[it].load(m1, i0);
+        }
+        if (b0 == 0) loadprep(xr);
+        float v[NV];
+#pragma unroll
+        for (int it = 0; it < NB; ++it) {
+            const bool ok = b0 + it * rpi < nrows;  // uniform over the wave
+            v[(TWO ? 2 : 1) * it] = ok ? g[it].dot(xr, cb) : 0.f;
+            if constexpr (TWO) v[2 * it + 1] = ok ? u[it].dot(xr, cb) : 0.f;
+        }
+        seg_reduce_lds<NV>(v, cpr, red);
+        for (int o = lane; o < NB * rpi; o += 64) {
+            const int it = o / rpi, r = o % rpi, l = b0 + o;
+            if (l < nrows) {
+                const float s0 = red[(TWO ? 2 : 1) * it * 64 + r];
+                const float s1 = TWO ? red[(2 * it + 1) * 64 + r] : 0.f;
+                emit(l, s0, s1);
+            }
+        }
+        wave_lds_sync();
+    }
+}
+
+// Barrier that orders LDS only: global loads still in flight are not waited
+// for (a plain __syncthreads also waits for every outstanding global access).
+MOE_DEV void block_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// One wave: dots of the rows row0 + l (l < nrows) of matrices staged in LDS
+// (m0, and m1 when TWO; rows of n_in weights blocked over the flat index from
+// the staged start, as in memory) over the columns [col0, col0 + ncols) with
+// the lane's prepared activations.  A lane takes 64 consecutive columns of a
+// row, cpr = ncols/64 lanes a row, 64/cpr rows per iteration, NB iterations
+// per reduction.  emit(l, s0, s1) runs once per row, on some lane.
+template <int FMT, bool TWO, int NB, typename Emit>
+MOE_DEV void lds_rows_dot(const uint8_t *m0, const uint8_t *m1, int n_in, int row0, int col0, int ncols, int nrows,
+                          const typename RawChunk<FMT>::Prep &xr, const uint32_t *cb, int lane, float *red,
+                          Emit emit) {
+    constexpr int NV = (TWO ? 2 : 1) * NB;
+    const int cpr = ncols >> 6, rpi = 64 / cpr, lr = lane / cpr, col = col0 + 64 * (lane % cpr);
+    for (int b0 = 0; b0 < nrows; b0 += NB * rpi) {
+        float v[NV];
+#pragma unroll
+        for (int it = 0; it < NB; ++it) {
+            const bool ok = b0 + it * rpi < nrows;  // uniform over the wave
+            const int i0 = (row0 + min(b0 + it * rpi + lr, nrows - 1)) * n_in + col;
+            RawChunk<FMT> g;
+            g.load(m0, i0);
+            v[(TWO ? 2 : 1) * it] = ok ? g.dot(xr, cb) : 0.f;
+            if constexpr (TWO) {
+                RawChunk<FMT> u;
+                u.load(m1, i0);
+                v[2 * it + 1] = ok ? u.dot(xr, cb) : 0.f;
+            }
+        }
+        seg_reduce_lds<NV>(v, cpr, red);
+        for (int o = lane; o < NB * rpi; o += 64) {
+            const int it = o / rpi, r = o % rpi, l = b0 + o;
+            if (l < nrows) {
+                const float s0 = red[(TWO ? 2 : 1) * it * 64 + r];
+                const float s1 = TWO ? red[(2 * it + 1) * 64 + r] : 0.f;
+                emit(l, s0, s1);
+            }
+        }
+        wave_lds_sync();
+    }
+}
+
+// Rows of one load batch for the batched (many-token) path.
 template <int FMT>
 constexpr int wave_batch() { return FMT == MOE_Q8_0 ? 1 : 4; }
 
-// One wave: dots of rows [row0, row0+nrows) with the lane's activations,
-// in batches of wave_batch() row iterations.
+// One wave: dots of rows [row0, row0+nrows) with the lane's activations
+// (batched path): wave_batch() row iterations per load batch, the lanes of a
+// row combined by a butterfly.
 template <int FMT, bool TWO, typename Emit>
 MOE_DEV void wave_rows(const uint8_t *m0, const uint8_t *m1, int n_in, int row0, int nrows,
                        const typename RawChunk<FMT>::Prep &xr, const uint32_t *cb, int lane, Emit emit) {
     constexpr int NB = wave_batch<FMT>();
-    const int rpi = 64 / (n_in >> 6);
-    for (int r0 = 0; r0 < nrows; r0 += NB * rpi) {
-        WaveRows<FMT, TWO, NB> w;
-        const int n = min(nrows - r0, NB * rpi);
-        w.load(m0, m1, n_in, row0 + r0, n, lane);
-        w.compute(xr, cb, n, [&](int r, float v0, float v1) { emit(r0 + r, v0, v1); });
+    const RowPlan rp = row_plan(n_in, lane);
+    for (int b0 = 0; b0 < nrows; b0 += NB * rp.rpi) {
+        RawChunk<FMT> g[NB], u[NB];
+#pragma unroll
+        for (int it = 0; it < NB; ++it)
+            if (b0 + it * rp.rpi < nrows) {
+                const int64_t i0 = (int64_t)(row0 + min(b0 + it * rp.rpi + rp.lr, nrows - 1)) * n_in + 64 * rp.c;
+                g[it].load(m0, i0);
+                if constexpr (TWO) u[it].load(m1, i0);
+            }
+#pragma unroll
+        for (int it = 0; it < NB; ++it)
+            if (b0 + it * rp.rpi < nrows) {
+                const float s0 = seg_sum(g[it].dot(xr, cb), rp.cpr);
+                float s1 = 0.f;
+                if constexpr (TWO) s1 = seg_sum(u[it].dot(xr, cb), rp.cpr);
+                const int l = b0 + it * rp.rpi + rp.lr;
+                if (rp.c == 0 && l < nrows) emit(l, s0, s1);
+            }
     }
 }
 
@@ -184,50 +336,23 @@ MOE_DEV float swiglu_h(float g, float u, int round_bf16) {
 }
 
 // h rows for one routed expert e (rows [row0, row0+nrows) of its gate/up),
-// every token of its bucket.  The weight loads are issued before the
-// activations are read.  With prepared x (Q2K) the activations come from the
-// workspace records; otherwise each wave prepares its own.
-// tile (LDS, 16 floats, or NULL): when set, the block's 4 waves cover the 16
-// rows [tile_row0, tile_row0+16) and after each token wave 0 writes the
-// prepared h record of those 16 rows (for a Q2K down projection).
-template <int FMT, bool PREPPED = false>
-MOE_DEV void routed_gateup(const FfnArgs &a, int e, int row0, int nrows, const uint32_t *cb, int lane,
-                           float *tile = nullptr, int tile_row0 = 0) {
+// every token of its bucket, activations prepared in the lane.  The weight
+// loads sit inside the token loop so that the compiler does not hoist every
+// decoded code out of it; later tokens hit the cache.
+template <int FMT>
+MOE_DEV void routed_gateup(const FfnArgs &a, int e, int row0, int nrows, const uint32_t *cb, int lane) {
     const uint8_t *g = a.gate + (int64_t)e * a.gu_expert_bytes, *u = a.up + (int64_t)e * a.gu_expert_bytes;
     const int j0 = a.offset[e], n = a.count[e];
     const RowPlan rp = row_plan(a.D, lane);
-    constexpr int NB = wave_batch<FMT>();
-    // nrows <= 4: for the formats with NB >= 4 one load batch covers the rows
-    // (the weight loads sit inside the token loop so that the compiler does not
-    // hoist every decoded code out of it; later tokens hit the cache)
-    constexpr bool ONE = NB >= 4;
     for (int j = 0; j < n; ++j) {
-        WaveRows<FMT, true, NB> w;
-        if constexpr (ONE) w.load(g, u, a.D, row0, nrows, lane);
         const int t = a.perm[j0 + j] / a.k;
         typename RawChunk<FMT>::Prep xr;
-        if constexpr (FMT == MOE_Q2K && PREPPED) {
-            load_q2k_prep(a.xp16 + ((int64_t)t * (a.D / 16) + 4 * rp.c) * kP16Dwords, xr);
-        } else {
-            float xf[64];
-            load_x64(a.x, a.x_bf16, (int64_t)t * a.D + 64 * rp.c, xf);
-            RawChunk<FMT>::prep(xf, xr);
-        }
+        float xf[64];
+        load_x64(a.x, a.x_bf16, (int64_t)t * a.D + 64 * rp.c, xf);
+        RawChunk<FMT>::prep(xf, xr);
         float *dst = a.h + (int64_t)(j0 + j) * a.F + row0;
-        auto emit = [&](int r, float gs, float us) {
-            const float hv = swiglu_h(gs, us, a.x_bf16);
-            dst[r] = hv;
-            if (tile) tile[row0 + r - tile_row0] = hv;
-        };
-        if constexpr (ONE) w.compute(xr, cb, nrows, emit);
-        else wave_rows<FMT, true>(g, u, a.D, row0, nrows, xr, cb, lane, emit);
-        if (tile) {  // uniform over the block
-            __syncthreads();
-            if ((threadIdx.x >> 6) == 0)
-                prep16_wave(lane < 16 ? tile[lane] : 0.f,
-                            a.hp16 + ((int64_t)(j0 + j) * (a.F / 16) + tile_row0 / 16) * kP16Dwords, 1);
-            __syncthreads();
-        }
+        wave_rows<FMT, true>(g, u, a.D, row0, nrows, xr, cb, lane,
+                             [&](int r, float gs, float us) { dst[r] = swiglu_h(gs, us, a.x_bf16); });
     }
 }
 
@@ -263,7 +388,7 @@ MOE_DEV void shared_down(const FfnArgs &a, int row0, int nrows, const uint32_t *
 
 // Down rows [row0, row0+nrows) of routed expert e for its bucket, into
 // out[q * stride + (row - row0)] for bucket positions q.
-template <int FMT, bool PREPPED = false>
+template <int FMT>
 MOE_DEV void routed_down(const FfnArgs &a, int e, int row0, int nrows, const uint32_t *cb, int lane, float *out,
                          int stride) {
     const uint8_t *m = a.down + (int64_t)e * a.down_expert_bytes;
@@ -271,13 +396,9 @@ MOE_DEV void routed_down(const FfnArgs &a, int e, int row0, int nrows, const uin
     const RowPlan rp = row_plan(a.F, lane);
     for (int j = 0; j < n; ++j) {
         typename RawChunk<FMT>::Prep xr;
-        if constexpr (FMT == MOE_Q2K && PREPPED) {
-            load_q2k_prep(a.hp16 + ((int64_t)(j0 + j) * (a.F / 16) + 4 * rp.c) * kP16Dwords, xr);
-        } else {
-            float xf[64];
-            load_x64(a.h + (int64_t)(j0 + j) * a.F, 0, 64 * rp.c, xf);
-            RawChunk<FMT>::prep(xf, xr);
-        }
+        float xf[64];
+        load_x64(a.h + (int64_t)(j0 + j) * a.F, 0, 64 * rp.c, xf);
+        RawChunk<FMT>::prep(xf, xr);
         float *dst = out + (int64_t)(j0 + j) * stride;
         wave_rows<FMT, false>(m, nullptr, a.F, row0, nrows, xr, cb, lane, [&](int r, float s, float) { dst[r] = s; });
     }

@@ -3,14 +3,22 @@
 // with bandwidth-bound expert work ("Understanding Dwarf Star", 5.3.7 steps
 // 1-5; 5.3.4 the shared expert runs alongside the routed ones; 3.5 a
 // schedule built once and replayed per token):
-//   K1  router logits (a wave per expert row) + x prepared for the dot2 path
-//   K2  top-k, weights, bucketing (block 0)  || shared expert gate/up -> hs
-//   K3  routed gate/up + SwiGLU (4 waves x 4 rows of one active expert per
-//       block; writes h and its prepared form) || shared expert down -> ys
-//   K4  routed down, then y = ys + sum_s w_s * down_s in slot order
-//       (block = 4 output rows x every active expert, combined in LDS)
-// No routing result ever travels back to the host: K3/K4 read n_active and
-// the active list from device memory and idle blocks return at once.
+//   K1  router logits (one block per expert row) || x prepared for the dot2
+//       paths (one wave per 64 activations)
+//   K2  top-k, weights, bucketing (block 0) || shared expert gate/up -> hs
+//   K3  routed gate/up + SwiGLU: one block per (active expert, group of 16
+//       rows); writes h and, for a Q2K down, its prepared form
+//   K4  per block of 16 output rows: routed down of every active expert and
+//       the shared down, then y = ys + sum_s w_s * down_s in slot order
+// Weight rows are contiguous in memory, so every expert kernel first copies
+// the rows it needs into LDS with aligned 16-byte loads (each wave
+// instruction reads 1 KB of consecutive bytes), then reads its 64-weight
+// chunks from LDS: a 16-byte load per lane straight from the 84-byte Q2K
+// blocks would be misaligned and split.  The waves of a block split the
+// columns, so that each lane reuses its prepared activations over many rows.
+// No routing result ever travels back to the host: the finisher leaves one
+// record per slot (expert, bucket start and size, tokens), and each K3/K4
+// block reads its slot's record in one load; empty slots return at once.
 #include <algorithm>
 #include <type_traits>
 
@@ -19,91 +27,340 @@
 
 namespace moe {
 
-constexpr int kGatherRows = 4;    // output rows per K4 block
-constexpr int kGatherWaves = 8;   // waves per K4 block, one active expert each at a time
-constexpr int kMaxGatherPairs = 1024;
+constexpr int kDecRows = 16;      // output rows per K4 block
+constexpr int kDecWaves = 8;      // waves per K4 block
+constexpr int kMaxDecPairs = 256;  // token-slot pairs the decode schedule takes (T*k)
+constexpr int kMaxDecTokens = 16;
 
-template <int XT>
-__global__ void __launch_bounds__(256) dec_k1_kernel(FfnArgs a) {
-    int b = blockIdx.x;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    if (b < a.n_router_blocks) {
-        router_rows_wave<XT>(a.router_w, a.router_bias, a.x, a.T, a.D, a.E, a.logits, b * 4 + wave);
-        return;
-    }
-    b -= a.n_router_blocks;
-    const int item = b * 4 + wave, per_t = a.D / 64;  // x prepared for the routed Q2K gate/up
-    if (item < a.T * per_t) {
-        const int t = item / per_t, c = item % per_t;
-        const float v = XT == MOE_BF16 ? bf16_bits_to_float(((const uint16_t *)a.x)[(int64_t)t * a.D + 64 * c + lane])
-                                       : ((const float *)a.x)[(int64_t)t * a.D + 64 * c + lane];
-        prep16_wave(v, a.xp16 + ((int64_t)t * (a.D / 16) + 4 * c) * kP16Dwords);
+// Formats the staged decode kernels take for the routed experts (their 16
+// rows of gate and up fit in LDS), and the bytes of 16 rows at n_embd or
+// n_ff_exp <= 4096.
+constexpr bool staged_fmt(int f) { return f == MOE_Q2K || f == MOE_CB2; }
+template <int FMT>
+constexpr int rows16_bytes_max() { return 16 * 16 * (FMT == MOE_Q8_0 ? 2 * kQ8Bytes * 4 : (FMT == MOE_CB2 ? kCB2Bytes : kQ2KBytes)); }
+// shared gate/up rows per K2 block
+template <int FMT>
+constexpr int shared_gu_rows() { return FMT == MOE_Q8_0 ? 8 : 16; }
+constexpr int kK4StageUnits = 6528;  // 16-byte units of K4's weight stage (102 KB)
+constexpr int kK4SlotsMax = 16;
+
+// The lane's prepared activations (64-column chunk c of row `row` of an
+// [.][n] input): from the records written by an earlier kernel (REC: Q2K or
+// Q8_0 records), else prepared in the lane from the fp32 / bf16 values.
+template <int FMT, bool REC>
+MOE_DEV void lane_prep(const uint32_t *rec, const void *src, int src_bf16, int64_t row, int n, int c,
+                       typename RawChunk<FMT>::Prep &p) {
+    if constexpr (REC && FMT == MOE_Q2K) {
+        load_q2k_prep(rec + (row * (n / 16) + 4 * c) * kP16Dwords, p);
+    } else if constexpr (REC && FMT == MOE_Q8_0) {
+        load_q8_prep(rec + (row * (n / 64) + c) * kXQ8Dwords, p);
+    } else {
+        float xf[64];
+        load_x64(src, src_bf16, row * n + 64 * c, xf);
+        RawChunk<FMT>::prep(xf, p);
     }
 }
 
-template <int SFMT>
-__global__ void __launch_bounds__(256) dec_k2_kernel(FfnArgs a, int do_route) {
-    __shared__ uint32_t cb_lds[512];
+// Per-slot records from a routing given by the caller (no routing in K1/K2).
+MOE_DEV void build_slot_records(const FfnArgs &a) {
+    const int na = a.n_active[0];
+    for (int s = threadIdx.x; s < a.nslots; s += blockDim.x) {
+        SlotRec r = make_slot(-1, 0, 0, 0, 0);
+        if (s < na) {
+            const int e = a.active[s], j0 = a.offset[e];
+            const int n = min(a.count[e], kMaxDecTokens);  // one entry per token at most
+            uint64_t tlo = 0, thi = 0;
+            for (int i = 0; i < n; ++i) {
+                const uint64_t t = (uint64_t)(a.perm[j0 + i] / a.k);
+                if (i < 8) tlo |= t << (8 * i);
+                else thi |= t << (8 * (i - 8));
+            }
+            r = make_slot(e, j0, n, tlo, thi);
+        }
+        a.slots[s] = r;
+    }
+}
+
+template <int XT>
+__global__ void __launch_bounds__(256) dec_k1_kernel(FfnArgs a) {
+    __shared__ double part[4 * 16];
     int b = blockIdx.x;
-    if (do_route) {
+    if (a.build_slots) {
         if (b == 0) {
-            route_finish_small(a.logits, a.T, a.E, a.k, a.route_scale, a.w_topk_idx, a.w_topk_w, a.w_count,
-                               a.w_offset, a.w_perm, a.w_pos, a.w_active, a.w_n_active);
+            build_slot_records(a);
             return;
         }
         b -= 1;
     }
-    load_codebook(SFMT == MOE_CB2 ? a.codebook : nullptr, cb_lds);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int rpw = 4096 / a.D;  // rows per wave: one wave iteration
-    const int row0 = (b * 4 + wave) * rpw;
-    if (row0 >= a.Fs) return;
-    shared_gateup<SFMT>(a, row0, min(rpw, a.Fs - row0), cb_lds, lane);
-}
-
-// blocks [0, n_slot_blocks): 16 rows of one active expert; then shared down
-template <int GFMT, int SFMT>
-__global__ void __launch_bounds__(256) dec_k3_kernel(FfnArgs a) {
-    __shared__ uint32_t cb_lds[512];
-    __shared__ float tile[16];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    int b = blockIdx.x;
-    if (b < a.n_slot_blocks) {
-        const int nrb = a.F / 16, slot = b / nrb, rb = b % nrb;
-        if (slot >= a.n_active[0]) return;
-        load_codebook(GFMT == MOE_CB2 ? a.codebook : nullptr, cb_lds);
-        const int row0 = rb * 16 + wave * 4;  // F is a multiple of 64: every wave has its 4 rows
-        routed_gateup<GFMT, GFMT == MOE_Q2K>(a, a.active[slot], row0, 4, cb_lds, lane, a.hp16 ? tile : nullptr,
-                                             rb * 16);
+    if (b < a.n_router_blocks) {
+        router_row_block<XT>(a.router_w, a.router_bias, a.x, a.T, a.D, a.E, a.logits, b, part);
         return;
     }
-    b -= a.n_slot_blocks;
-    load_codebook(SFMT == MOE_CB2 ? a.codebook : nullptr, cb_lds);
-    const int rpw = 4096 / a.Fs;
-    const int row0 = (b * 4 + wave) * rpw;
-    if (row0 >= a.D) return;
-    shared_down<SFMT>(a, row0, min(rpw, a.D - row0), cb_lds, lane);
+    b -= a.n_router_blocks;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int item = b * 4 + wave, per_t = a.D / 64;  // one wave per 64 activations of a token
+    if (item >= a.T * per_t) return;
+    const int t = item / per_t, c = item % per_t;
+    const int64_t i = (int64_t)t * a.D + 64 * c + lane;
+    const float v = XT == MOE_BF16 ? bf16_bits_to_float(((const uint16_t *)a.x)[i]) : ((const float *)a.x)[i];
+    if (a.xp16) prep16_wave(v, a.xp16 + ((int64_t)t * (a.D / 16) + 4 * c) * kP16Dwords);
+    if (a.xq8) prep8_wave(v, a.xq8 + ((int64_t)t * (a.D / 64) + c) * kXQ8Dwords);
 }
 
-template <int DFMT>
-__global__ void __launch_bounds__(64 * kGatherWaves) dec_k4_kernel(FfnArgs a) {
-    __shared__ uint32_t cb_lds[512];
-    __shared__ float part[kMaxGatherPairs * kGatherRows];
-    load_codebook(DFMT == MOE_CB2 ? a.codebook : nullptr, cb_lds);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int row0 = blockIdx.x * kGatherRows;
-    const int nrows = min(kGatherRows, a.D - row0);
-    const int na = a.n_active[0];
-    for (int s = wave; s < na; s += kGatherWaves)
-        routed_down<DFMT, DFMT == MOE_Q2K>(a, a.active[s], row0, nrows, cb_lds, lane, part, kGatherRows);
-    __syncthreads();
-    for (int i = threadIdx.x; i < a.T * nrows; i += blockDim.x) {
-        const int t = i / nrows, r = i % nrows;
+// Column parts of a staged block of 4 waves: P = min(4, n/256) parts of the
+// n columns, the 4/P row groups of rows_per_block rows spread over the rest.
+struct ColSplit {
+    int P, RW, cp, rg, ncol, cpr, rpi;
+};
+MOE_DEV ColSplit col_split(int n, int rows_per_block, int wave) {
+    ColSplit s;
+    s.P = min(4, n >> 8);
+    s.RW = rows_per_block * s.P / 4;
+    s.cp = wave % s.P;
+    s.rg = wave / s.P;
+    s.ncol = n / s.P;
+    s.cpr = s.ncol >> 6;
+    s.rpi = 64 / s.cpr;
+    return s;
+}
+
+// block 0 (when routing): the finisher; then shared gate/up, R rows of gate
+// and of up per block, staged in LDS, 4 waves over column parts.
+template <int SFMT>
+__global__ void __launch_bounds__(256) dec_k2_kernel(FfnArgs a, int do_route) {
+    constexpr int R = shared_gu_rows<SFMT>();
+    constexpr int kU = 2 * R * (rows16_bytes_max<SFMT>() / 16) / 16;
+    constexpr int kNI = (kU + 255) / 256;
+    __shared__ __align__(16) u32x4 wbuf[kU];
+    __shared__ uint32_t cb_lds[SFMT == MOE_CB2 ? 512 : 1];
+    __shared__ __align__(16) float red[4][2 * 4 * 64];
+    __shared__ float part[4][2 * R];
+    int b = blockIdx.x;
+    if (do_route) {
+        if (b == 0) {
+            route_finish_block(a.logits, a.T, a.E, a.k, a.route_scale, a.w_topk_idx, a.w_topk_w, a.w_count,
+                               a.w_offset, a.w_perm, a.w_pos, a.w_active, a.w_n_active, a.slots, a.nslots);
+            return;
+        }
+        b -= 1;
+    }
+    if constexpr (SFMT == MOE_CB2) load_codebook(a.codebook, cb_lds);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int row0 = b * R, nrows = min(R, a.Fs - row0);
+    const int U = (int)fmt_bytes(SFMT, (int64_t)nrows * a.D) / 16;  // rows are whole blocks: 16-byte units
+    const u32x4 *sg = (const u32x4 *)(a.sh_gate + fmt_bytes(SFMT, (int64_t)row0 * a.D));
+    const u32x4 *su = (const u32x4 *)(a.sh_up + fmt_bytes(SFMT, (int64_t)row0 * a.D));
+    const ColSplit cs = col_split(a.D, R, wave);
+    const int col = cs.cp * cs.ncol, chunk = (col >> 6) + lane % cs.cpr;
+    typename RawChunk<SFMT>::Prep xr;  // token 0's activations, in flight with the weights
+    lane_prep<SFMT, SFMT != MOE_CB2>(SFMT == MOE_Q2K ? a.xp16 : a.xq8, a.x, a.x_bf16, 0, a.D, chunk, xr);
+    u32x4 v[kNI];
+#pragma unroll
+    for (int i = 0; i < kNI; ++i) {
+        const int u = i * 256 + tid;
+        if (u < 2 * U) v[i] = u < U ? sg[u] : su[u - U];
+    }
+#pragma unroll
+    for (int i = 0; i < kNI; ++i) {
+        const int u = i * 256 + tid;
+        if (u < 2 * U) wbuf[u] = v[i];
+    }
+    block_lds_sync();
+    const int r0 = cs.rg * cs.RW, nr = max(0, min(cs.RW, nrows - r0));
+    const uint8_t *wb = (const uint8_t *)wbuf;
+    for (int t = 0; t < a.T; ++t) {
+        if (t > 0) lane_prep<SFMT, SFMT != MOE_CB2>(SFMT == MOE_Q2K ? a.xp16 : a.xq8, a.x, a.x_bf16, t, a.D, chunk, xr);
+        if (nr > 0)
+            lds_rows_dot<SFMT, true, 4>(wb, wb + U * 16, a.D, r0, col, cs.ncol, nr, xr, cb_lds, lane, red[wave],
+                                        [&](int l, float gs, float us) {
+                                            part[wave][2 * l] = gs;
+                                            part[wave][2 * l + 1] = us;
+                                        });
+        block_lds_sync();
+        if (tid < nrows) {  // add the column parts in order
+            const int rg = tid / cs.RW, rl = tid % cs.RW;
+            float gs = 0.f, us = 0.f;
+            for (int q = 0; q < cs.P; ++q) {
+                gs += part[rg * cs.P + q][2 * rl];
+                us += part[rg * cs.P + q][2 * rl + 1];
+            }
+            a.hs[(int64_t)t * a.Fs + row0 + tid] = swiglu_h(gs, us, a.x_bf16);
+        }
+        block_lds_sync();
+    }
+}
+
+// One block per (active slot, group g of 16 rows of the expert's gate and up):
+// the 16 rows of both are staged in LDS, wave w takes column part w % P of
+// the rows of row group w / P; the parts of a row are added in LDS in column
+// order, then wave 0 applies SwiGLU and writes h and the group's prepared
+// record.  The staged rows serve every token of the bucket.
+template <int GFMT>
+__global__ void __launch_bounds__(256) dec_k3_kernel(FfnArgs a) {
+    static_assert(staged_fmt(GFMT), "staged formats only");
+    constexpr int kU = 2 * rows16_bytes_max<GFMT>() / 16;
+    constexpr int kNI = (kU + 255) / 256;
+    __shared__ __align__(16) u32x4 wbuf[kU];
+    __shared__ uint32_t cb_lds[GFMT == MOE_CB2 ? 512 : 1];
+    __shared__ __align__(16) float red[4][2 * 4 * 64];
+    __shared__ float part[4][32];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if ((int)blockIdx.x >= a.n_gu_blocks) {  // hs prepared for the shared down: one wave per 64 values
+        const int item = ((int)blockIdx.x - a.n_gu_blocks) * 4 + wave, per_t = a.Fs / 64;
+        if (item >= a.T * per_t) return;
+        const int t = item / per_t, c = item % per_t;
+        const float v = a.hs[(int64_t)t * a.Fs + 64 * c + lane];
+        if (a.shared_fmt == MOE_Q2K) prep16_wave(v, a.hsrec + ((int64_t)t * (a.Fs / 16) + 4 * c) * kP16Dwords);
+        else prep8_wave(v, a.hsrec + ((int64_t)t * (a.Fs / 64) + c) * kXQ8Dwords);
+        return;
+    }
+    if constexpr (GFMT == MOE_CB2) load_codebook(a.codebook, cb_lds);
+    const int gpe = a.F / 16, slot = blockIdx.x / gpe, g = blockIdx.x % gpe;
+    const SlotRec rec = uniform_slot(a.slots, slot);
+    if (rec.e < 0) return;  // uniform over the block
+    const int U = (int)fmt_bytes(GFMT, (int64_t)16 * a.D) / 16;  // 16 rows in 16-byte units
+    const int64_t goff = (int64_t)rec.e * a.gu_expert_bytes + fmt_bytes(GFMT, (int64_t)16 * g * a.D);
+    const u32x4 *sg = (const u32x4 *)(a.gate + goff), *su = (const u32x4 *)(a.up + goff);
+    const ColSplit cs = col_split(a.D, 16, wave);
+    const int col = cs.cp * cs.ncol, chunk = (col >> 6) + lane % cs.cpr;
+    typename RawChunk<GFMT>::Prep xr;  // the first token's activations, in flight with the weights
+    lane_prep<GFMT, GFMT == MOE_Q2K>(a.xp16, a.x, a.x_bf16, slot_token(rec, 0), a.D, chunk, xr);
+    {
+        u32x4 v[kNI];
+#pragma unroll
+        for (int i = 0; i < kNI; ++i) {
+            const int u = i * 256 + tid;
+            if (u < 2 * U) v[i] = u < U ? sg[u] : su[u - U];
+        }
+#pragma unroll
+        for (int i = 0; i < kNI; ++i) {
+            const int u = i * 256 + tid;
+            if (u < 2 * U) wbuf[u] = v[i];
+        }
+    }
+    block_lds_sync();
+    const uint8_t *wb = (const uint8_t *)wbuf;
+    for (int j = 0; j < rec.n; ++j) {
+        if (j > 0) lane_prep<GFMT, GFMT == MOE_Q2K>(a.xp16, a.x, a.x_bf16, slot_token(rec, j), a.D, chunk, xr);
+        lds_rows_dot<GFMT, true, 4>(wb, wb + U * 16, a.D, cs.rg * cs.RW, col, cs.ncol, cs.RW, xr, cb_lds, lane,
+                                    red[wave], [&](int l, float gs, float us) {
+                                        part[wave][2 * l] = gs;
+                                        part[wave][2 * l + 1] = us;
+                                    });
+        block_lds_sync();
+        if (wave == 0) {
+            float hv = 0.f;
+            if (lane < 16) {
+                const int rg = lane / cs.RW, rl = lane % cs.RW;
+                float gs = 0.f, us = 0.f;
+                for (int q = 0; q < cs.P; ++q) {
+                    gs += part[rg * cs.P + q][2 * rl];
+                    us += part[rg * cs.P + q][2 * rl + 1];
+                }
+                hv = swiglu_h(gs, us, a.x_bf16);
+                a.h[(int64_t)(rec.j0 + j) * a.F + 16 * g + lane] = hv;
+            }
+            if (a.hp16) prep16_wave(hv, a.hp16 + ((int64_t)(rec.j0 + j) * (a.F / 16) + g) * kP16Dwords, 1);
+        }
+        block_lds_sync();
+    }
+}
+
+// One block per 16 output rows.  The 16 rows of the shared down and of each
+// active expert's down are staged in LDS (experts in batches that fit), then
+// waves take units in turn: a routed slot (its 16 rows for every token of its
+// bucket, into part[bucket position]) or one half of the shared rows (8 rows,
+// every token, into ysl).  Then the combine adds, per output, ys and the k
+// routed terms in slot order.
+template <int DFMT, int SFMT>
+__global__ void __launch_bounds__(64 * kDecWaves) dec_k4_kernel(FfnArgs a) {
+    static_assert(staged_fmt(DFMT), "staged formats only");
+    __shared__ __align__(16) u32x4 stage[kK4StageUnits];
+    __shared__ uint32_t cb_lds[(DFMT == MOE_CB2 || SFMT == MOE_CB2) ? 512 : 1];
+    __shared__ __align__(16) float red[kDecWaves][8 * 64];
+    __shared__ float part[kMaxDecPairs][kDecRows];
+    __shared__ float ysl[kMaxDecTokens][kDecRows];
+    __shared__ float wl[kMaxDecPairs];
+    __shared__ int32_t posl[kMaxDecPairs];
+    __shared__ int32_t bslot[kK4SlotsMax];  // slots of the current batch
+    if constexpr (DFMT == MOE_CB2 || SFMT == MOE_CB2) load_codebook(a.codebook, cb_lds);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int row0 = blockIdx.x * kDecRows;
+    const int nsh = a.Fs > 0 ? 2 : 0;
+    for (int p = tid; p < a.T * a.k; p += blockDim.x) {  // for the combine, read early
+        wl[p] = a.topk_w[p];
+        posl[p] = a.pos[p];
+    }
+    const int UF = (int)fmt_bytes(DFMT, (int64_t)kDecRows * a.F) / 16;  // 16 rows of a routed down, 16-byte units
+    const int US = a.Fs > 0 ? (int)fmt_bytes(SFMT, (int64_t)kDecRows * a.Fs) / 16 : 0;
+    const int64_t offF = fmt_bytes(DFMT, (int64_t)row0 * a.F), offS = a.Fs > 0 ? fmt_bytes(SFMT, (int64_t)row0 * a.Fs) : 0;
+    const int nsb = min(kK4SlotsMax, max(1, (kK4StageUnits - US) / UF));
+    constexpr int kNI = (kK4StageUnits + 64 * kDecWaves - 1) / (64 * kDecWaves);
+    const uint8_t *st = (const uint8_t *)stage;
+    for (int s0 = 0; s0 < a.nslots; s0 += nsb) {
+        const int s1 = min(a.nslots, s0 + nsb), first = s0 == 0;
+        const int ush = first ? US : 0, nunits = ush + (s1 - s0) * UF;
+        if (tid < s1 - s0) bslot[tid] = a.slots[s0 + tid].e;
+        block_lds_sync();
+        const int nr = s1 - s0, nu = nr + (first ? nsh : 0);
+        const int c = lane % (a.F >> 6);
+        {
+            u32x4 v[kNI];
+#pragma unroll
+            for (int i = 0; i < kNI; ++i) {
+                const int u = i * 64 * kDecWaves + tid;
+                if (u < nunits) {
+                    const u32x4 *src;
+                    if (u < ush) {
+                        src = (const u32x4 *)(a.sh_down + offS) + u;
+                    } else {
+                        const int q = (u - ush) / UF, off = (u - ush) % UF;
+                        const int e = max(bslot[q], 0);
+                        src = (const u32x4 *)(a.down + (int64_t)e * a.down_expert_bytes + offF) + off;
+                    }
+                    v[i] = *src;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kNI; ++i) {
+                const int u = i * 64 * kDecWaves + tid;
+                if (u < nunits) stage[u] = v[i];
+            }
+        }
+        block_lds_sync();
+        for (int u = wave; u < nu; u += kDecWaves) {
+            if (u < nr) {
+                const SlotRec rec = uniform_slot(a.slots, s0 + u);
+                if (rec.e < 0) continue;
+                const uint8_t *m = st + (ush + u * UF) * 16;
+                for (int j = 0; j < rec.n; ++j) {
+                    typename RawChunk<DFMT>::Prep hr;
+                    lane_prep<DFMT, DFMT == MOE_Q2K>(a.hp16, a.h, 0, rec.j0 + j, a.F, c, hr);
+                    float *dst = part[rec.j0 + j];
+                    lds_rows_dot<DFMT, false, 4>(m, nullptr, a.F, 0, 0, a.F, kDecRows, hr, cb_lds, lane, red[wave],
+                                                 [&](int l, float s, float) { dst[l] = s; });
+                }
+            } else {
+                const int half = u - nr;
+                const int cs = lane % (a.Fs >> 6);
+                for (int t = 0; t < a.T; ++t) {
+                    typename RawChunk<SFMT>::Prep hr;
+                    lane_prep<SFMT, SFMT != MOE_CB2>(a.hsrec, a.hs, 0, t, a.Fs, cs, hr);
+                    float *dst = &ysl[t][8 * half];
+                    lds_rows_dot<SFMT, false, 2>(st, nullptr, a.Fs, 8 * half, 0, a.Fs, 8, hr, cb_lds, lane, red[wave],
+                                                 [&](int l, float s, float) { dst[l] = s; });
+                }
+            }
+        }
+        block_lds_sync();
+    }
+    for (int i = tid; i < a.T * kDecRows; i += blockDim.x) {
+        const int t = i / kDecRows, r = i % kDecRows;
         const int64_t o = (int64_t)t * a.D + row0 + r;
-        float acc = a.Fs > 0 ? a.ys[o] : 0.f;
+        float acc = nsh ? ysl[t][r] : 0.f;
         for (int s = 0; s < a.k; ++s) {
             const int p = t * a.k + s;
-            acc = __builtin_fmaf(a.topk_w[p], part[a.pos[p] * kGatherRows + r], acc);
+            acc = __builtin_fmaf(wl[p], part[posl[p]][r], acc);
         }
         if (a.flags & MOE_ACCUMULATE) acc += a.y[o];
         a.y[o] = acc;
@@ -148,51 +405,60 @@ FfnArgs make_ffn_args(const moe_layer_desc *d, const void *x, int32_t T, int32_t
     a.router_bias = d->router_bias;
     a.route_scale = d->route_scale;
     a.logits = ws.logits;
-    a.xp16 = nullptr;
-    a.hp16 = nullptr;
+    a.xp16 = a.xq8 = a.hp16 = a.hsrec = nullptr;
     return a;
 }
 
 bool small_path_ok(const moe_layer_desc *d, int32_t T) {
-    return T <= 16 && (int64_t)T * d->n_expert_used <= kMaxGatherPairs;
+    return T <= kMaxDecTokens && (int64_t)T * d->n_expert_used <= kMaxDecPairs && staged_fmt(d->gate_type) &&
+           staged_fmt(d->down_type);
 }
 
 bool small_route_ok(const moe_layer_desc *d, int32_t T) { return route_small_ok(T, d->n_expert, d->n_expert_used); }
 
 // stage 0 = all; 1..4 = K1..K4.  route: also compute the routing (K1's router
-// waves and K2's block 0); otherwise the routing in r is given.
+// blocks and K2's block 0); otherwise the routing in r is given.
 hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
                         float *y, uint32_t flags, const Workspace &ws, hipStream_t s, int stage, bool route) {
     FfnArgs a = make_ffn_args(d, x, T, x_type, r, y, flags, ws);
-    const int sf = a.Fs > 0 ? d->shared_type : MOE_Q8_0;
-    a.n_router_blocks = route ? (a.E + 4 * (4096 / a.D) - 1) / (4 * (4096 / a.D)) : 0;
-    int prep_blocks = 0;
-    if (d->gate_type == MOE_Q2K) {  // x prepared once per token for the routed gate/up
-        a.xp16 = ws.xp16;
-        prep_blocks = (T * (a.D / 64) + 3) / 4;
-    }
-    if (d->down_type == MOE_Q2K) a.hp16 = ws.hp16;  // h prepared by K3 for the routed down
+    const bool has_sh = a.Fs > 0;
+    const int sf = has_sh ? d->shared_type : MOE_Q8_0;
+    a.n_router_blocks = route ? a.E : 0;
+    a.slots = ws.slots;
+    a.nslots = (int)std::min<int64_t>((int64_t)T * a.k, a.E);
+    a.build_slots = route ? 0 : 1;
+    // x records for the dot2 formats, written by K1
+    if (d->gate_type == MOE_Q2K || (has_sh && sf == MOE_Q2K)) a.xp16 = ws.xp16;
+    if (d->gate_type == MOE_Q8_0 || (has_sh && sf == MOE_Q8_0)) a.xq8 = ws.xq8;
+    if (d->down_type == MOE_Q2K) a.hp16 = ws.hp16;  // h records, written by K3
+    const int prep_blocks = (a.xp16 || a.xq8) ? (T * (a.D / 64) + 3) / 4 : 0;
     const int max_slots = (int)std::min<int64_t>((int64_t)T * a.k, a.E);
-    a.n_slot_blocks = max_slots * (a.F / 16);
-    const int sh_gu_blocks = a.Fs > 0 ? (a.Fs + 4 * (4096 / a.D) - 1) / (4 * (4096 / a.D)) : 0;
-    const int sh_dn_blocks = a.Fs > 0 ? (a.D + 4 * (4096 / a.Fs) - 1) / (4 * (4096 / a.Fs)) : 0;
-    const int k1 = a.n_router_blocks + prep_blocks, k2 = (route ? 1 : 0) + sh_gu_blocks;
+    a.n_gu_blocks = max_slots * (a.F / 16);
+    a.hsrec = (has_sh && sf != MOE_CB2) ? ws.hsrec : nullptr;
+    a.shared_fmt = sf;
+    const int k3_blocks = a.n_gu_blocks + (a.hsrec ? (T * (a.Fs / 64) + 3) / 4 : 0);
+    int sh_rows = 8;
+    with_fmt(sf, [&](auto S) { sh_rows = shared_gu_rows<decltype(S)::value>(); });
+    const int sh_gu_blocks = has_sh ? (a.Fs + sh_rows - 1) / sh_rows : 0;
+    const int k1 = a.build_slots + a.n_router_blocks + prep_blocks, k2 = (route ? 1 : 0) + sh_gu_blocks;
     if ((stage == 0 || stage == 1) && k1 > 0) {
         if (x_type == MOE_BF16) dec_k1_kernel<MOE_BF16><<<k1, 256, 0, s>>>(a);
         else dec_k1_kernel<MOE_F32><<<k1, 256, 0, s>>>(a);
     }
     if ((stage == 0 || stage == 2) && k2 > 0)
         with_fmt(sf, [&](auto S) { dec_k2_kernel<decltype(S)::value><<<k2, 256, 0, s>>>(a, route ? 1 : 0); });
-    if (stage == 0 || stage == 3)
-        with_fmt(d->gate_type, [&](auto G) {
-            with_fmt(sf, [&](auto S) {
-                dec_k3_kernel<decltype(G)::value, decltype(S)::value><<<a.n_slot_blocks + sh_dn_blocks, 256, 0, s>>>(a);
-            });
+    if (stage == 0 || stage == 3) {
+        if (d->gate_type == MOE_CB2) dec_k3_kernel<MOE_CB2><<<k3_blocks, 256, 0, s>>>(a);
+        else dec_k3_kernel<MOE_Q2K><<<k3_blocks, 256, 0, s>>>(a);
+    }
+    if (stage == 0 || stage == 4) {
+        with_fmt(sf, [&](auto S) {
+            if (d->down_type == MOE_CB2)
+                dec_k4_kernel<MOE_CB2, decltype(S)::value><<<a.D / kDecRows, 64 * kDecWaves, 0, s>>>(a);
+            else
+                dec_k4_kernel<MOE_Q2K, decltype(S)::value><<<a.D / kDecRows, 64 * kDecWaves, 0, s>>>(a);
         });
-    if (stage == 0 || stage == 4)
-        with_fmt(d->down_type, [&](auto DN) {
-            dec_k4_kernel<decltype(DN)::value><<<(a.D + kGatherRows - 1) / kGatherRows, 64 * kGatherWaves, 0, s>>>(a);
-        });
+    }
     return hipGetLastError();
 }
 

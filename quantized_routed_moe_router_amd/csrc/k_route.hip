@@ -6,10 +6,11 @@
 namespace moe {
 
 template <int XT>
-__global__ void __launch_bounds__(256) router_rows_kernel(const float *__restrict__ W, const float *__restrict__ bias,
-                                                          const void *__restrict__ xin, int T, int D, int E,
-                                                          double *__restrict__ logits) {
-    router_rows_wave<XT>(W, bias, xin, T, D, E, logits, blockIdx.x * 4 + (threadIdx.x >> 6));
+__global__ void __launch_bounds__(256) router_row_kernel(const float *__restrict__ W, const float *__restrict__ bias,
+                                                         const void *__restrict__ xin, int T, int D, int E,
+                                                         double *__restrict__ logits) {
+    __shared__ double part[4 * 16];
+    router_row_block<XT>(W, bias, xin, T, D, E, logits, blockIdx.x, part);
 }
 
 template <int XT>
@@ -19,28 +20,26 @@ __global__ void __launch_bounds__(256) router_tile_kernel(const float *__restric
     router_tile_block<XT>(W, bias, xin, T, D, E, logits, blockIdx.x, blockIdx.y);
 }
 
-__global__ void __launch_bounds__(1024) route_finish_small_kernel(const double *__restrict__ logits, int T, int E,
-                                                                  int k, float route_scale,
-                                                                  int32_t *__restrict__ topk_idx,
-                                                                  float *__restrict__ topk_w,
-                                                                  int32_t *__restrict__ count,
-                                                                  int32_t *__restrict__ offset,
-                                                                  int32_t *__restrict__ perm, int32_t *__restrict__ pos,
-                                                                  int32_t *__restrict__ active,
-                                                                  int32_t *__restrict__ n_active) {
-    route_finish_small(logits, T, E, k, route_scale, topk_idx, topk_w, count, offset, perm, pos, active, n_active);
+__global__ void __launch_bounds__(256) route_finish_small_kernel(const double *__restrict__ logits, int T, int E,
+                                                                 int k, float route_scale,
+                                                                 int32_t *__restrict__ topk_idx,
+                                                                 float *__restrict__ topk_w,
+                                                                 int32_t *__restrict__ count,
+                                                                 int32_t *__restrict__ offset,
+                                                                 int32_t *__restrict__ perm, int32_t *__restrict__ pos,
+                                                                 int32_t *__restrict__ active,
+                                                                 int32_t *__restrict__ n_active) {
+    route_finish_block(logits, T, E, k, route_scale, topk_idx, topk_w, count, offset, perm, pos, active, n_active,
+                       nullptr, 0);
 }
 
 // One wave per token: top-k of its logit row.
 __global__ void __launch_bounds__(256) router_topk_kernel(const double *__restrict__ logits, int T, int E, int k,
                                                           float route_scale, int32_t *__restrict__ topk_idx,
                                                           float *__restrict__ topk_w) {
-    __shared__ double lg[4][kMaxExperts];
-    const int wave = threadIdx.x >> 6, t = blockIdx.x * 4 + wave;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    for (int e = threadIdx.x & 63; e < E; e += 64) lg[wave][e] = logits[(int64_t)t * E + e];
-    __builtin_amdgcn_wave_barrier();
-    select_topk(lg[wave], E, k, route_scale, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k, nullptr, nullptr);
+    select_topk(logits + (int64_t)t * E, E, k, route_scale, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
 }
 
 __global__ void __launch_bounds__(1024) bucket_small_kernel(const int32_t *__restrict__ topk_idx, int P, int E,
@@ -51,7 +50,7 @@ __global__ void __launch_bounds__(1024) bucket_small_kernel(const int32_t *__res
     __shared__ int32_t sidx[1024];
     for (int p = threadIdx.x; p < P; p += blockDim.x) sidx[p] = topk_idx[p];
     __syncthreads();
-    bucket_small(sidx, P, E, count, offset, perm, pos, active, n_active);
+    bucket_small(sidx, P, E, 1, count, offset, perm, pos, active, n_active, nullptr, 0);
 }
 
 // Stable counting sort of the P = T*k pairs by expert, one block of 8 waves.
@@ -144,19 +143,17 @@ __global__ void __launch_bounds__(512) bucket_kernel(const int32_t *__restrict__
     if (tid == 0) n_active[0] = na;
 }
 
-// rows kernel for few tokens, tiles for many
+// one block per expert row for few tokens, 16 x 16 tiles for many
 bool router_rows_ok(int T) { return T <= 16; }
 
 hipError_t launch_router_logits(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type,
                                 const Workspace &ws, hipStream_t s) {
     const int D = d->n_embd, E = d->n_expert;
     if (router_rows_ok(T)) {
-        const int per_block = 4 * (4096 / D);
-        const int blocks = (E + per_block - 1) / per_block;
         if (x_type == MOE_BF16)
-            router_rows_kernel<MOE_BF16><<<blocks, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E, ws.logits);
+            router_row_kernel<MOE_BF16><<<E, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E, ws.logits);
         else
-            router_rows_kernel<MOE_F32><<<blocks, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E, ws.logits);
+            router_row_kernel<MOE_F32><<<E, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E, ws.logits);
     } else {
         dim3 g((T + 15) / 16, (E + 15) / 16);
         if (x_type == MOE_BF16)
@@ -171,7 +168,7 @@ hipError_t launch_route_finish(const moe_layer_desc *d, int32_t T, const Routing
                                hipStream_t s) {
     const int E = d->n_expert, k = d->n_expert_used, P = T * k;
     if (route_small_ok(T, E, k)) {
-        route_finish_small_kernel<<<1, 1024, 0, s>>>(ws.logits, T, E, k, d->route_scale, r.topk_idx, r.topk_w,
+        route_finish_small_kernel<<<1, 256, 0, s>>>(ws.logits, T, E, k, d->route_scale, r.topk_idx, r.topk_w,
                                                      r.count, r.offset, r.perm, r.pos, r.active, r.n_active);
         return hipGetLastError();
     }

@@ -118,18 +118,13 @@ def main():
     torch.cuda.synchronize()
     log("%d replicas resident (%.1f GB)" % (R, R * (base.gate.numel() * 3 + base.sh_gate.numel() * 3) / 1e9))
 
-    # The four stages of one forward; events bracket stage 3 (gate/up), the
-    # kernel that moves the most bytes.
-    def step(i, ev=None):
+    # The four stages of one forward.
+    def step(i):
         W = reps[i % R]
         x = xin[i % n_x]
         moe.layer_forward_stage(W, x, y, ws, moe.STAGE_ROUTER, routing=r)
         moe.layer_forward_stage(W, x, y, ws, moe.STAGE_ROUTE, routing=r)
-        if ev is not None:
-            ev[0].record()
         moe.layer_forward_stage(W, x, y, ws, moe.STAGE_GATE_UP, routing=r)
-        if ev is not None:
-            ev[1].record()
         moe.layer_forward_stage(W, x, y, ws, moe.STAGE_DOWN_COMBINE, routing=r)
 
     for i in range(args.warmup):
@@ -174,13 +169,26 @@ def main():
     ms_step = 1000.0 * wall / K
     # The dominant kernel's launch time: HIP events on the launch stream
     # around stage 3, over 4R cold-cache steps issued eagerly (events inside a
-    # captured graph do not time).
-    ev_src = "HIP events around each stage-3 launch, %d eager cold-cache steps" % (4 * R)
+    # captured graph do not time).  A bounded spin kernel runs before each
+    # bracket, so that the host has queued event, kernel, event before the GPU
+    # reaches them and the bracket holds the kernel alone.
+    ev_src = ("HIP events around each stage-3 launch, %d eager cold-cache steps, queue kept ahead by a "
+              "spin kernel" % (4 * R))
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4 * R)]
     for i, e in enumerate(evs):
-        step(i, e)
+        W = reps[i % R]
+        x = xin[i % n_x]
+        moe.layer_forward_stage(W, x, y, ws, moe.STAGE_ROUTER, routing=r)
+        moe.layer_forward_stage(W, x, y, ws, moe.STAGE_ROUTE, routing=r)
+        torch.cuda._sleep(1000000)
+        e[0].record()
+        moe.layer_forward_stage(W, x, y, ws, moe.STAGE_GATE_UP, routing=r)
+        e[1].record()
+        moe.layer_forward_stage(W, x, y, ws, moe.STAGE_DOWN_COMBINE, routing=r)
     torch.cuda.synchronize()
-    gateup_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    times = sorted(a.elapsed_time(b) for a, b in evs)
+    gateup_ms = float(np.median(times))
+    gateup_p10, gateup_p90 = float(np.percentile(times, 10)), float(np.percentile(times, 90))
     log("timed %d steps in %.3f s (%d graph replays); gate/up avg %.2f us (%s)" % (
         K, wall, len(plan), gateup_ms * 1e3, ev_src))
 
@@ -206,6 +214,7 @@ def main():
     if not small:
         gateup_bytes += sh_gu + T * Fs * 4
     achieved = gateup_bytes / (gateup_ms * 1e-3) / 1e9
+    kernel_name = "dec_k3_kernel" if small else "large_gateup_kernel"
     tokens_s = T / (ms_step * 1e-3)
     flops = 2.0 * T * (k * 3 * D * F + 3 * D * Fs)
 
@@ -239,21 +248,43 @@ def main():
         "tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "unique_experts_per_step": nu,
         "roofline": {
-            "kernel": ("dec_k3_kernel (routed gate/up dequant-GEMV + SwiGLU)" if small else
-                       "large_gateup_kernel (gate/up dequant-GEMV + SwiGLU, routed and shared)"),
+            "kernel": kernel_name,
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(kernel_name, args.workload),
             "bytes_per_launch": int(gateup_bytes),
             "avg_launch_us": round(gateup_ms * 1e3, 3),
-            "timing": ev_src,
+            "launch_us_p10_p90": [round(gateup_p10 * 1e3, 3), round(gateup_p90 * 1e3, 3)],
+            "timing": ev_src + "; median",
         },
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of the kernel from the committed counter summary
+    (profiles/<kernel>_<workload>_hbm_counters.md), or None when there is
+    none or it was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_hbm_counters.md" % (kernel, workload))
+    try:
+        with open(path) as f:
+            text = f.read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if line.startswith("- traffic_bytes_per_launch:"):
+            vals["bytes"] = float(line.split(":", 1)[1])
+        elif line.startswith("- kernel_source_sha256:"):
+            vals["sha"] = line.split(":", 1)[1].strip()
+    from quantized_routed_moe_router_amd.profsum import kernel_source_digest
+    if "bytes" not in vals or vals.get("sha") != kernel_source_digest():
+        return None
+    return vals["bytes"]
 
 
 def cpu_baseline(L, x_all, T, mode, budget_s):

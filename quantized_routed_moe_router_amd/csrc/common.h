@@ -547,7 +547,6 @@ struct Workspace {
     uint32_t *xp16;       // [T][D/16] records: x prepared for Q2K rows
     uint32_t *xq8;        // [T][D/64] records: x prepared for Q8_0 rows
     uint32_t *hp16;       // [T*k][F/16] records: h prepared for Q2K rows
-    uint32_t *hsrec;      // [T][Fs] records of hs prepared for the shared down (Q2K or Q8_0)
     SlotRec *slots;       // [T*k] per-slot records of the few-token schedule
     size_t bytes;
 };
@@ -581,7 +580,6 @@ __host__ inline Workspace workspace_layout(const moe_layer_desc *d, int32_t T, v
     w.xp16 = (uint32_t *)take(sizeof(uint32_t) * kP16Dwords * (size_t)T * (size_t)(D / 16));
     w.xq8 = (uint32_t *)take(sizeof(uint32_t) * kXQ8Dwords * (size_t)T * (size_t)(D / 64));
     w.hp16 = (uint32_t *)take(sizeof(uint32_t) * kP16Dwords * (size_t)P * (size_t)(F / 16));
-    w.hsrec = (uint32_t *)take(sizeof(uint32_t) * kP16Dwords * (size_t)T * (size_t)((Fs > 0 ? Fs : 16) / 16));
     w.slots = (SlotRec *)take(sizeof(SlotRec) * (size_t)P);
     w.bytes = off;
     return w;

@@ -35,8 +35,8 @@ struct FfnArgs {
     // rows ([T][D/16] records), x for Q8_0 rows ([T][D/64] records), h for the
     // routed Q2K down ([T*k][F/16] records)
     uint32_t *xp16, *xq8, *hp16;
-    uint32_t *hsrec;  // hs prepared for the shared down ([T][Fs/16] Q2K or [T][Fs/64] Q8_0 records)
-    int n_gu_blocks;  // K3: blocks of routed gate/up before the hs-preparing blocks
+    int n_prep_blocks, n_shgu_blocks;  // K1: x-preparing and shared gate/up blocks
+    int n_shd_blocks;                  // K2: shared down blocks
     int shared_fmt;
     // per-slot records (few-token schedule) and their number, min(T*k, E)
     SlotRec *slots;
@@ -213,14 +213,14 @@ MOE_DEV void seg_reduce_lds(const float (&v)[NV], int cpr, float *red) {
 // round trip, not two.  The partial sums go through red (LDS, 2*NB*64 floats
 // per wave, 16-byte aligned); then emit(l, s0, s1) runs once per row, on
 // some lane.
-template <int FMT, bool TWO, int NB, typename RowOf, typename LoadPrep, typename Emit>
-MOE_DEV void rows_dot(const uint8_t *m0, const uint8_t *m1, int64_t ld, int col0, int ncols, int nrows, RowOf rowof,
-                      LoadPrep loadprep, const uint32_t *cb, int lane, float *red, Emit emit) {
+template <class CH, bool TWO, int NB, typename RowOf, typename LoadPrep, typename Emit>
+MOE_DEV void rows_dot_ch(const uint8_t *m0, const uint8_t *m1, int64_t ld, int col0, int ncols, int nrows, RowOf rowof,
+                         LoadPrep loadprep, const uint32_t *cb, int lane, float *red, Emit emit) {
     constexpr int NV = (TWO ? 2 : 1) * NB;
     const int cpr = ncols >> 6, rpi = 64 / cpr, lr = lane / cpr, c = lane % cpr;
-    typename RawChunk<FMT>::Prep xr;
+    typename CH::Prep xr;
     for (int b0 = 0; b0 < nrows; b0 += NB * rpi) {
-        RawChunk<FMT> g[NB], u[NB];
+        CH g[NB], u[NB];
 #pragma unroll
         for (int it = 0; it < NB; ++it) {
             const int l = min(b0 + it * rpi + lr, nrows - 1);
@@ -248,6 +248,31 @@ MOE_DEV void rows_dot(const uint8_t *m0, const uint8_t *m1, int64_t ld, int col0
         wave_lds_sync();
     }
 }
+
+template <int FMT, bool TWO, int NB, typename RowOf, typename LoadPrep, typename Emit>
+MOE_DEV void rows_dot(const uint8_t *m0, const uint8_t *m1, int64_t ld, int col0, int ncols, int nrows, RowOf rowof,
+                      LoadPrep loadprep, const uint32_t *cb, int lane, float *red, Emit emit) {
+    rows_dot_ch<RawChunk<FMT>, TWO, NB>(m0, m1, ld, col0, ncols, nrows, rowof, loadprep, cb, lane, red, emit);
+}
+
+// A 64-weight chunk of any format dotted with plain fp32 activations (each
+// product rounded once in fp32): for the shared expert, whose activations
+// are not prepared.
+template <int FMT>
+struct F32Chunk {
+    typedef XF32 Prep;
+    typename std::conditional<FMT == MOE_Q2K, Q2KChunk, typename std::conditional<FMT == MOE_Q8_0, Q8Chunk, CB2Chunk>::type>::type c;
+    MOE_DEV void load(const uint8_t *b, int64_t i0) {
+        if constexpr (FMT == MOE_Q2K) c = q2k_load(b, i0);
+        else if constexpr (FMT == MOE_Q8_0) c = q8_load(b, i0);
+        else c = cb2_load(b, i0);
+    }
+    MOE_DEV float dot(const Prep &p, const uint32_t *cb) const {
+        if constexpr (FMT == MOE_Q2K) return q2k_dot(c, p.x);
+        else if constexpr (FMT == MOE_Q8_0) return q8_dot(c, p.x);
+        else return cb2_dot(c, p.x, cb);
+    }
+};
 
 // Barrier that orders LDS only: global loads still in flight are not waited
 // for (a plain __syncthreads also waits for every outstanding global access).

@@ -1,21 +1,19 @@
 // k_decode.hip - the block for a handful of token rows (decode, micro-batched
 // decode) in four dependent kernels, each pairing latency-bound routing work
 // with bandwidth-bound expert work ("Understanding Dwarf Star", 5.3.7 steps
-// 1-5; 5.3.4 the shared expert runs alongside the routed ones; 3.5 a
-// schedule built once and replayed per token):
-//   K1  router logits (one block per expert row) || x prepared for the dot2
-//       paths (one wave per 64 activations)
-//   K2  top-k, weights, bucketing (block 0) || shared expert gate/up -> hs
+// 1-5; 5.3.4 the shared expert needs no routing, so it runs beside the
+// router and the finisher; 3.5 a schedule built once and replayed per token):
+//   K1  router logits (one block per expert row) || x prepared for the routed
+//       dot2 path || shared expert gate/up -> hs
+//   K2  top-k, weights, bucketing (block 0) || shared expert down -> ys
 //   K3  routed gate/up + SwiGLU: one block per (active expert, group of 16
 //       rows); writes h and, for a Q2K down, its prepared form
-//   K4  per block of 16 output rows: routed down of every active expert and
-//       the shared down, then y = ys + sum_s w_s * down_s in slot order
-// Weight rows are contiguous in memory, so every expert kernel first copies
-// the rows it needs into LDS with aligned 16-byte loads (each wave
-// instruction reads 1 KB of consecutive bytes), then reads its 64-weight
-// chunks from LDS: a 16-byte load per lane straight from the 84-byte Q2K
-// blocks would be misaligned and split.  The waves of a block split the
-// columns, so that each lane reuses its prepared activations over many rows.
+//   K4  per block of 16 output rows: routed down of every active expert,
+//       then y = ys + sum_s w_s * down_s in slot order
+// Routed weight rows are copied into LDS with aligned 16-byte loads (each
+// wave instruction reads 1 KB of consecutive bytes) before their 64-weight
+// chunks are read from LDS: a 16-byte load per lane straight from the
+// 84-byte Q2K blocks would be misaligned and split.
 // No routing result ever travels back to the host: the finisher leaves one
 // record per slot (expert, bucket start and size, tokens), and each K3/K4
 // block reads its slot's record in one load; empty slots return at once.
@@ -38,11 +36,10 @@ constexpr int kMaxDecTokens = 16;
 constexpr bool staged_fmt(int f) { return f == MOE_Q2K || f == MOE_CB2; }
 template <int FMT>
 constexpr int rows16_bytes_max() { return 16 * 16 * (FMT == MOE_Q8_0 ? 2 * kQ8Bytes * 4 : (FMT == MOE_CB2 ? kCB2Bytes : kQ2KBytes)); }
-// shared gate/up rows per K2 block
-template <int FMT>
-constexpr int shared_gu_rows() { return FMT == MOE_Q8_0 ? 8 : 16; }
-constexpr int kK4StageUnits = 6528;  // 16-byte units of K4's weight stage (102 KB)
-constexpr int kK4SlotsMax = 16;
+// shared expert rows per wave (gate/up in K1, down in K2)
+constexpr int kShGuRows = 2, kShDownRows = 4;
+// K4: LDS units (16 bytes) a wave stages at once: 16 rows of 2048 Q2K weights
+constexpr int kK4WaveUnits = 672;
 
 // The lane's prepared activations (64-column chunk c of row `row` of an
 // [.][n] input): from the records written by an earlier kernel (REC: Q2K or
@@ -81,9 +78,11 @@ MOE_DEV void build_slot_records(const FfnArgs &a) {
     }
 }
 
-template <int XT>
+template <int XT, int SFMT>
 __global__ void __launch_bounds__(256) dec_k1_kernel(FfnArgs a) {
     __shared__ double part[4 * 16];
+    __shared__ uint32_t cb_lds[SFMT == MOE_CB2 ? 512 : 1];
+    __shared__ __align__(16) float red[4][2 * kShGuRows * 64];
     int b = blockIdx.x;
     if (a.build_slots) {
         if (b == 0) {
@@ -98,6 +97,20 @@ __global__ void __launch_bounds__(256) dec_k1_kernel(FfnArgs a) {
     }
     b -= a.n_router_blocks;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (b >= a.n_prep_blocks) {  // shared gate/up: kShGuRows rows per wave, fp32 activations
+        if constexpr (SFMT == MOE_CB2) load_codebook(a.codebook, cb_lds);  // uniform over the block
+        const int row0 = ((b - a.n_prep_blocks) * 4 + wave) * kShGuRows;
+        if (row0 >= a.Fs) return;
+        const int nrows = min(kShGuRows, a.Fs - row0), c = lane % (a.D >> 6);
+        for (int t = 0; t < a.T; ++t) {
+            float *dst = a.hs + (int64_t)t * a.Fs + row0;
+            rows_dot_ch<F32Chunk<SFMT>, true, kShGuRows>(
+                a.sh_gate, a.sh_up, a.D, 0, a.D, nrows, [&](int l) { return row0 + l; },
+                [&](XF32 &xr) { load_x64(a.x, a.x_bf16, (int64_t)t * a.D + 64 * c, xr.x); }, cb_lds, lane,
+                red[wave], [&](int l, float gs, float us) { dst[l] = swiglu_h(gs, us, a.x_bf16); });
+        }
+        return;
+    }
     const int item = b * 4 + wave, per_t = a.D / 64;  // one wave per 64 activations of a token
     if (item >= a.T * per_t) return;
     const int t = item / per_t, c = item % per_t;
@@ -124,17 +137,12 @@ MOE_DEV ColSplit col_split(int n, int rows_per_block, int wave) {
     return s;
 }
 
-// block 0 (when routing): the finisher; then shared gate/up, R rows of gate
-// and of up per block, staged in LDS, 4 waves over column parts.
+// block 0 (when routing): the finisher; then the shared expert's down,
+// kShDownRows rows per wave, fp32 activations hs -> ys.
 template <int SFMT>
 __global__ void __launch_bounds__(256) dec_k2_kernel(FfnArgs a, int do_route) {
-    constexpr int R = shared_gu_rows<SFMT>();
-    constexpr int kU = 2 * R * (rows16_bytes_max<SFMT>() / 16) / 16;
-    constexpr int kNI = (kU + 255) / 256;
-    __shared__ __align__(16) u32x4 wbuf[kU];
     __shared__ uint32_t cb_lds[SFMT == MOE_CB2 ? 512 : 1];
-    __shared__ __align__(16) float red[4][2 * 4 * 64];
-    __shared__ float part[4][2 * R];
+    __shared__ __align__(16) float red[4][kShDownRows * 64];
     int b = blockIdx.x;
     if (do_route) {
         if (b == 0) {
@@ -145,48 +153,16 @@ __global__ void __launch_bounds__(256) dec_k2_kernel(FfnArgs a, int do_route) {
         b -= 1;
     }
     if constexpr (SFMT == MOE_CB2) load_codebook(a.codebook, cb_lds);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int row0 = b * R, nrows = min(R, a.Fs - row0);
-    const int U = (int)fmt_bytes(SFMT, (int64_t)nrows * a.D) / 16;  // rows are whole blocks: 16-byte units
-    const u32x4 *sg = (const u32x4 *)(a.sh_gate + fmt_bytes(SFMT, (int64_t)row0 * a.D));
-    const u32x4 *su = (const u32x4 *)(a.sh_up + fmt_bytes(SFMT, (int64_t)row0 * a.D));
-    const ColSplit cs = col_split(a.D, R, wave);
-    const int col = cs.cp * cs.ncol, chunk = (col >> 6) + lane % cs.cpr;
-    typename RawChunk<SFMT>::Prep xr;  // token 0's activations, in flight with the weights
-    lane_prep<SFMT, SFMT != MOE_CB2>(SFMT == MOE_Q2K ? a.xp16 : a.xq8, a.x, a.x_bf16, 0, a.D, chunk, xr);
-    u32x4 v[kNI];
-#pragma unroll
-    for (int i = 0; i < kNI; ++i) {
-        const int u = i * 256 + tid;
-        if (u < 2 * U) v[i] = u < U ? sg[u] : su[u - U];
-    }
-#pragma unroll
-    for (int i = 0; i < kNI; ++i) {
-        const int u = i * 256 + tid;
-        if (u < 2 * U) wbuf[u] = v[i];
-    }
-    block_lds_sync();
-    const int r0 = cs.rg * cs.RW, nr = max(0, min(cs.RW, nrows - r0));
-    const uint8_t *wb = (const uint8_t *)wbuf;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int row0 = (b * 4 + wave) * kShDownRows;
+    if (row0 >= a.D) return;
+    const int nrows = min(kShDownRows, a.D - row0), c = lane % (a.Fs >> 6);
     for (int t = 0; t < a.T; ++t) {
-        if (t > 0) lane_prep<SFMT, SFMT != MOE_CB2>(SFMT == MOE_Q2K ? a.xp16 : a.xq8, a.x, a.x_bf16, t, a.D, chunk, xr);
-        if (nr > 0)
-            lds_rows_dot<SFMT, true, 4>(wb, wb + U * 16, a.D, r0, col, cs.ncol, nr, xr, cb_lds, lane, red[wave],
-                                        [&](int l, float gs, float us) {
-                                            part[wave][2 * l] = gs;
-                                            part[wave][2 * l + 1] = us;
-                                        });
-        block_lds_sync();
-        if (tid < nrows) {  // add the column parts in order
-            const int rg = tid / cs.RW, rl = tid % cs.RW;
-            float gs = 0.f, us = 0.f;
-            for (int q = 0; q < cs.P; ++q) {
-                gs += part[rg * cs.P + q][2 * rl];
-                us += part[rg * cs.P + q][2 * rl + 1];
-            }
-            a.hs[(int64_t)t * a.Fs + row0 + tid] = swiglu_h(gs, us, a.x_bf16);
-        }
-        block_lds_sync();
+        float *dst = a.ys + (int64_t)t * a.D + row0;
+        rows_dot_ch<F32Chunk<SFMT>, false, kShDownRows>(
+            a.sh_down, nullptr, a.Fs, 0, a.Fs, nrows, [&](int l) { return row0 + l; },
+            [&](XF32 &hr) { load_x64(a.hs, 0, (int64_t)t * a.Fs + 64 * c, hr.x); }, cb_lds, lane, red[wave],
+            [&](int l, float s, float) { dst[l] = s; });
     }
 }
 
@@ -196,7 +172,7 @@ __global__ void __launch_bounds__(256) dec_k2_kernel(FfnArgs a, int do_route) {
 // order, then wave 0 applies SwiGLU and writes h and the group's prepared
 // record.  The staged rows serve every token of the bucket.
 template <int GFMT>
-__global__ void __launch_bounds__(256) dec_k3_kernel(FfnArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) dec_k3_kernel(FfnArgs a) {
     static_assert(staged_fmt(GFMT), "staged formats only");
     constexpr int kU = 2 * rows16_bytes_max<GFMT>() / 16;
     constexpr int kNI = (kU + 255) / 256;
@@ -205,15 +181,6 @@ __global__ void __launch_bounds__(256) dec_k3_kernel(FfnArgs a) {
     __shared__ __align__(16) float red[4][2 * 4 * 64];
     __shared__ float part[4][32];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    if ((int)blockIdx.x >= a.n_gu_blocks) {  // hs prepared for the shared down: one wave per 64 values
-        const int item = ((int)blockIdx.x - a.n_gu_blocks) * 4 + wave, per_t = a.Fs / 64;
-        if (item >= a.T * per_t) return;
-        const int t = item / per_t, c = item % per_t;
-        const float v = a.hs[(int64_t)t * a.Fs + 64 * c + lane];
-        if (a.shared_fmt == MOE_Q2K) prep16_wave(v, a.hsrec + ((int64_t)t * (a.Fs / 16) + 4 * c) * kP16Dwords);
-        else prep8_wave(v, a.hsrec + ((int64_t)t * (a.Fs / 64) + c) * kXQ8Dwords);
-        return;
-    }
     if constexpr (GFMT == MOE_CB2) load_codebook(a.codebook, cb_lds);
     const int gpe = a.F / 16, slot = blockIdx.x / gpe, g = blockIdx.x % gpe;
     const SlotRec rec = uniform_slot(a.slots, slot);
@@ -266,98 +233,67 @@ __global__ void __launch_bounds__(256) dec_k3_kernel(FfnArgs a) {
     }
 }
 
-// One block per 16 output rows.  The 16 rows of the shared down and of each
-// active expert's down are staged in LDS (experts in batches that fit), then
-// waves take units in turn: a routed slot (its 16 rows for every token of its
-// bucket, into part[bucket position]) or one half of the shared rows (8 rows,
-// every token, into ysl).  Then the combine adds, per output, ys and the k
-// routed terms in slot order.
-template <int DFMT, int SFMT>
+// One block per 16 output rows, a wave per active slot in turn: the wave
+// copies the slot expert's 16 down rows into its own LDS area with aligned
+// 16-byte loads (no block barrier: every wave starts on its dots as soon as
+// its own rows have landed), then dots them with the prepared h of every
+// token of its bucket, into part[bucket position].  Then the combine adds,
+// per output, ys and the k routed terms in slot order.
+template <int DFMT>
 __global__ void __launch_bounds__(64 * kDecWaves) dec_k4_kernel(FfnArgs a) {
     static_assert(staged_fmt(DFMT), "staged formats only");
-    __shared__ __align__(16) u32x4 stage[kK4StageUnits];
-    __shared__ uint32_t cb_lds[(DFMT == MOE_CB2 || SFMT == MOE_CB2) ? 512 : 1];
+    __shared__ __align__(16) u32x4 wstage[kDecWaves][kK4WaveUnits];
+    __shared__ uint32_t cb_lds[DFMT == MOE_CB2 ? 512 : 1];
     __shared__ __align__(16) float red[kDecWaves][8 * 64];
     __shared__ float part[kMaxDecPairs][kDecRows];
-    __shared__ float ysl[kMaxDecTokens][kDecRows];
     __shared__ float wl[kMaxDecPairs];
     __shared__ int32_t posl[kMaxDecPairs];
-    __shared__ int32_t bslot[kK4SlotsMax];  // slots of the current batch
-    if constexpr (DFMT == MOE_CB2 || SFMT == MOE_CB2) load_codebook(a.codebook, cb_lds);
+    if constexpr (DFMT == MOE_CB2) load_codebook(a.codebook, cb_lds);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int row0 = blockIdx.x * kDecRows;
-    const int nsh = a.Fs > 0 ? 2 : 0;
     for (int p = tid; p < a.T * a.k; p += blockDim.x) {  // for the combine, read early
         wl[p] = a.topk_w[p];
         posl[p] = a.pos[p];
     }
-    const int UF = (int)fmt_bytes(DFMT, (int64_t)kDecRows * a.F) / 16;  // 16 rows of a routed down, 16-byte units
-    const int US = a.Fs > 0 ? (int)fmt_bytes(SFMT, (int64_t)kDecRows * a.Fs) / 16 : 0;
-    const int64_t offF = fmt_bytes(DFMT, (int64_t)row0 * a.F), offS = a.Fs > 0 ? fmt_bytes(SFMT, (int64_t)row0 * a.Fs) : 0;
-    const int nsb = min(kK4SlotsMax, max(1, (kK4StageUnits - US) / UF));
-    constexpr int kNI = (kK4StageUnits + 64 * kDecWaves - 1) / (64 * kDecWaves);
-    const uint8_t *st = (const uint8_t *)stage;
-    for (int s0 = 0; s0 < a.nslots; s0 += nsb) {
-        const int s1 = min(a.nslots, s0 + nsb), first = s0 == 0;
-        const int ush = first ? US : 0, nunits = ush + (s1 - s0) * UF;
-        if (tid < s1 - s0) bslot[tid] = a.slots[s0 + tid].e;
-        block_lds_sync();
-        const int nr = s1 - s0, nu = nr + (first ? nsh : 0);
-        const int c = lane % (a.F >> 6);
-        {
-            u32x4 v[kNI];
+    // rows per staged batch: 16, or fewer when 16 rows exceed the wave's area
+    const int64_t b16 = fmt_bytes(DFMT, (int64_t)kDecRows * a.F);
+    const int rb = b16 <= 16 * kK4WaveUnits ? kDecRows : kDecRows * 16 * kK4WaveUnits / (int)b16;
+    const int c = lane % (a.F >> 6);
+    const uint8_t *ws = (const uint8_t *)wstage[wave];
+    for (int u = wave; u < a.nslots; u += kDecWaves) {
+        const SlotRec rec = uniform_slot(a.slots, u);
+        if (rec.e < 0) continue;
+        const uint8_t *m = a.down + (int64_t)rec.e * a.down_expert_bytes;
+        for (int r0 = 0; r0 < kDecRows; r0 += rb) {
+            const int nunits = (int)(fmt_bytes(DFMT, (int64_t)rb * a.F) / 16);
+            typename RawChunk<DFMT>::Prep hr;  // the first token's prepared h, in flight with the rows
+            lane_prep<DFMT, DFMT == MOE_Q2K>(a.hp16, a.h, 0, rec.j0, a.F, c, hr);
+            {
+                const u32x4 *src = (const u32x4 *)(m + fmt_bytes(DFMT, (int64_t)(row0 + r0) * a.F));
+                constexpr int kNI = (kK4WaveUnits + 63) / 64;
+                u32x4 v[kNI];
 #pragma unroll
-            for (int i = 0; i < kNI; ++i) {
-                const int u = i * 64 * kDecWaves + tid;
-                if (u < nunits) {
-                    const u32x4 *src;
-                    if (u < ush) {
-                        src = (const u32x4 *)(a.sh_down + offS) + u;
-                    } else {
-                        const int q = (u - ush) / UF, off = (u - ush) % UF;
-                        const int e = max(bslot[q], 0);
-                        src = (const u32x4 *)(a.down + (int64_t)e * a.down_expert_bytes + offF) + off;
-                    }
-                    v[i] = *src;
-                }
-            }
+                for (int i = 0; i < kNI; ++i)
+                    if (i * 64 + lane < nunits) v[i] = src[i * 64 + lane];
 #pragma unroll
-            for (int i = 0; i < kNI; ++i) {
-                const int u = i * 64 * kDecWaves + tid;
-                if (u < nunits) stage[u] = v[i];
+                for (int i = 0; i < kNI; ++i)
+                    if (i * 64 + lane < nunits) wstage[wave][i * 64 + lane] = v[i];
+                wave_lds_sync();
             }
-        }
-        block_lds_sync();
-        for (int u = wave; u < nu; u += kDecWaves) {
-            if (u < nr) {
-                const SlotRec rec = uniform_slot(a.slots, s0 + u);
-                if (rec.e < 0) continue;
-                const uint8_t *m = st + (ush + u * UF) * 16;
-                for (int j = 0; j < rec.n; ++j) {
-                    typename RawChunk<DFMT>::Prep hr;
-                    lane_prep<DFMT, DFMT == MOE_Q2K>(a.hp16, a.h, 0, rec.j0 + j, a.F, c, hr);
-                    float *dst = part[rec.j0 + j];
-                    lds_rows_dot<DFMT, false, 4>(m, nullptr, a.F, 0, 0, a.F, kDecRows, hr, cb_lds, lane, red[wave],
-                                                 [&](int l, float s, float) { dst[l] = s; });
-                }
-            } else {
-                const int half = u - nr;
-                const int cs = lane % (a.Fs >> 6);
-                for (int t = 0; t < a.T; ++t) {
-                    typename RawChunk<SFMT>::Prep hr;
-                    lane_prep<SFMT, SFMT != MOE_CB2>(a.hsrec, a.hs, 0, t, a.Fs, cs, hr);
-                    float *dst = &ysl[t][8 * half];
-                    lds_rows_dot<SFMT, false, 2>(st, nullptr, a.Fs, 8 * half, 0, a.Fs, 8, hr, cb_lds, lane, red[wave],
-                                                 [&](int l, float s, float) { dst[l] = s; });
-                }
+            for (int j = 0; j < rec.n; ++j) {
+                if (j > 0) lane_prep<DFMT, DFMT == MOE_Q2K>(a.hp16, a.h, 0, rec.j0 + j, a.F, c, hr);
+                float *dst = part[rec.j0 + j] + r0;
+                lds_rows_dot<DFMT, false, 8>(ws, nullptr, a.F, 0, 0, a.F, rb, hr, cb_lds, lane, red[wave],
+                                             [&](int l, float s, float) { dst[l] = s; });
             }
+            wave_lds_sync();  // the area is rewritten by the next batch
         }
-        block_lds_sync();
     }
+    block_lds_sync();
     for (int i = tid; i < a.T * kDecRows; i += blockDim.x) {
         const int t = i / kDecRows, r = i % kDecRows;
         const int64_t o = (int64_t)t * a.D + row0 + r;
-        float acc = nsh ? ysl[t][r] : 0.f;
+        float acc = a.Fs > 0 ? a.ys[o] : 0.f;
         for (int s = 0; s < a.k; ++s) {
             const int p = t * a.k + s;
             acc = __builtin_fmaf(wl[p], part[posl[p]][r], acc);
@@ -405,7 +341,7 @@ FfnArgs make_ffn_args(const moe_layer_desc *d, const void *x, int32_t T, int32_t
     a.router_bias = d->router_bias;
     a.route_scale = d->route_scale;
     a.logits = ws.logits;
-    a.xp16 = a.xq8 = a.hp16 = a.hsrec = nullptr;
+    a.xp16 = a.xq8 = a.hp16 = nullptr;
     return a;
 }
 
@@ -422,42 +358,33 @@ hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32
                         float *y, uint32_t flags, const Workspace &ws, hipStream_t s, int stage, bool route) {
     FfnArgs a = make_ffn_args(d, x, T, x_type, r, y, flags, ws);
     const bool has_sh = a.Fs > 0;
-    const int sf = has_sh ? d->shared_type : MOE_Q8_0;
+    a.shared_fmt = has_sh ? d->shared_type : MOE_Q8_0;
     a.n_router_blocks = route ? a.E : 0;
     a.slots = ws.slots;
     a.nslots = (int)std::min<int64_t>((int64_t)T * a.k, a.E);
     a.build_slots = route ? 0 : 1;
-    // x records for the dot2 formats, written by K1
-    if (d->gate_type == MOE_Q2K || (has_sh && sf == MOE_Q2K)) a.xp16 = ws.xp16;
-    if (d->gate_type == MOE_Q8_0 || (has_sh && sf == MOE_Q8_0)) a.xq8 = ws.xq8;
-    if (d->down_type == MOE_Q2K) a.hp16 = ws.hp16;  // h records, written by K3
-    const int prep_blocks = (a.xp16 || a.xq8) ? (T * (a.D / 64) + 3) / 4 : 0;
-    const int max_slots = (int)std::min<int64_t>((int64_t)T * a.k, a.E);
-    a.n_gu_blocks = max_slots * (a.F / 16);
-    a.hsrec = (has_sh && sf != MOE_CB2) ? ws.hsrec : nullptr;
-    a.shared_fmt = sf;
-    const int k3_blocks = a.n_gu_blocks + (a.hsrec ? (T * (a.Fs / 64) + 3) / 4 : 0);
-    int sh_rows = 8;
-    with_fmt(sf, [&](auto S) { sh_rows = shared_gu_rows<decltype(S)::value>(); });
-    const int sh_gu_blocks = has_sh ? (a.Fs + sh_rows - 1) / sh_rows : 0;
-    const int k1 = a.build_slots + a.n_router_blocks + prep_blocks, k2 = (route ? 1 : 0) + sh_gu_blocks;
-    if ((stage == 0 || stage == 1) && k1 > 0) {
-        if (x_type == MOE_BF16) dec_k1_kernel<MOE_BF16><<<k1, 256, 0, s>>>(a);
-        else dec_k1_kernel<MOE_F32><<<k1, 256, 0, s>>>(a);
-    }
+    if (d->gate_type == MOE_Q2K) a.xp16 = ws.xp16;  // x records for the routed gate/up, written by K1
+    if (d->down_type == MOE_Q2K) a.hp16 = ws.hp16;  // h records for the routed down, written by K3
+    a.n_prep_blocks = a.xp16 ? (T * (a.D / 64) + 3) / 4 : 0;
+    a.n_shgu_blocks = has_sh ? (a.Fs + 4 * kShGuRows - 1) / (4 * kShGuRows) : 0;
+    a.n_shd_blocks = has_sh ? (a.D + 4 * kShDownRows - 1) / (4 * kShDownRows) : 0;
+    const int k1 = a.build_slots + a.n_router_blocks + a.n_prep_blocks + a.n_shgu_blocks;
+    const int k2 = (route ? 1 : 0) + a.n_shd_blocks;
+    const int k3 = a.nslots * (a.F / 16);
+    if ((stage == 0 || stage == 1) && k1 > 0)
+        with_fmt(a.shared_fmt, [&](auto S) {
+            if (x_type == MOE_BF16) dec_k1_kernel<MOE_BF16, decltype(S)::value><<<k1, 256, 0, s>>>(a);
+            else dec_k1_kernel<MOE_F32, decltype(S)::value><<<k1, 256, 0, s>>>(a);
+        });
     if ((stage == 0 || stage == 2) && k2 > 0)
-        with_fmt(sf, [&](auto S) { dec_k2_kernel<decltype(S)::value><<<k2, 256, 0, s>>>(a, route ? 1 : 0); });
+        with_fmt(a.shared_fmt, [&](auto S) { dec_k2_kernel<decltype(S)::value><<<k2, 256, 0, s>>>(a, route ? 1 : 0); });
     if (stage == 0 || stage == 3) {
-        if (d->gate_type == MOE_CB2) dec_k3_kernel<MOE_CB2><<<k3_blocks, 256, 0, s>>>(a);
-        else dec_k3_kernel<MOE_Q2K><<<k3_blocks, 256, 0, s>>>(a);
+        if (d->gate_type == MOE_CB2) dec_k3_kernel<MOE_CB2><<<k3, 256, 0, s>>>(a);
+        else dec_k3_kernel<MOE_Q2K><<<k3, 256, 0, s>>>(a);
     }
     if (stage == 0 || stage == 4) {
-        with_fmt(sf, [&](auto S) {
-            if (d->down_type == MOE_CB2)
-                dec_k4_kernel<MOE_CB2, decltype(S)::value><<<a.D / kDecRows, 64 * kDecWaves, 0, s>>>(a);
-            else
-                dec_k4_kernel<MOE_Q2K, decltype(S)::value><<<a.D / kDecRows, 64 * kDecWaves, 0, s>>>(a);
-        });
+        if (d->down_type == MOE_CB2) dec_k4_kernel<MOE_CB2><<<a.D / kDecRows, 64 * kDecWaves, 0, s>>>(a);
+        else dec_k4_kernel<MOE_Q2K><<<a.D / kDecRows, 64 * kDecWaves, 0, s>>>(a);
     }
     return hipGetLastError();
 }

@@ -8,6 +8,16 @@ becomes a table of per-kernel launch counts and durations, and every
 ``*counter_collection.csv`` (from ``--pmc``) a table of each counter's mean
 value per dispatch, per kernel.  ``--match`` keeps only kernels whose name
 contains one of the given strings.
+
+    python -m quantized_routed_moe_router_amd.profsum --hbm KERNEL \
+        --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --copy-bytes N
+
+turns a FETCH_SIZE pass and a WRITE_SIZE pass over a kernel into HBM bytes
+per launch.  The counters' units are fixed by the same counters read over a
+plain device copy of N bytes (``bench.py --copy-calib``): bytes per counter
+unit = N / (copy kernel's mean counter value).  The summary ends with
+``- traffic_bytes_per_launch:`` and ``- kernel_source_sha256:`` lines, the
+latter a digest of the HIP sources the counters were taken on.
 """
 import argparse
 import collections
@@ -57,11 +67,74 @@ def counters(path, match):
     return out
 
 
+COPY_KERNEL = "copyBuffer"
+
+
+def kernel_source_digest():
+    """SHA-256 over the library's HIP sources (csrc/), in file-name order."""
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+    for f in sorted(os.listdir(root)):
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def _mean_counter(d, counter, match):
+    """Mean value of ``counter`` per dispatch over kernels whose name contains ``match``."""
+    tot, disp = 0.0, set()
+    for p in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(p, newline="") as f:
+            for r in csv.DictReader(f):
+                if match in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                    tot += float(r["Counter_Value"])
+                    disp.add((p, r["Dispatch_Id"]))
+    if not disp:
+        raise SystemExit("no %s values for a kernel named *%s* under %s" % (counter, match, d))
+    return tot / len(disp), len(disp)
+
+
+def hbm(a):
+    fetch, nf = _mean_counter(a.fetch, "FETCH_SIZE", a.hbm)
+    write, nw = _mean_counter(a.write, "WRITE_SIZE", a.hbm)
+    cfetch, ncf = _mean_counter(a.copy_fetch, "FETCH_SIZE", COPY_KERNEL)
+    cwrite, ncw = _mean_counter(a.copy_write, "WRITE_SIZE", COPY_KERNEL)
+    bf, bw = a.copy_bytes / cfetch, a.copy_bytes / cwrite
+    traffic = fetch * bf + write * bw
+    print("HBM traffic of %s per launch, from rocprofv3 FETCH_SIZE and WRITE_SIZE passes.\n" % a.hbm)
+    print("| counter | kernel mean per dispatch | dispatches | copy of %d B: mean | bytes per unit | bytes |"
+          % a.copy_bytes)
+    print("|---|---:|---:|---:|---:|---:|")
+    print("| FETCH_SIZE | %.6g | %d | %.6g (%d) | %.2f | %.0f |" % (fetch, nf, cfetch, ncf, bf, fetch * bf))
+    print("| WRITE_SIZE | %.6g | %d | %.6g (%d) | %.2f | %.0f |" % (write, nw, cwrite, ncw, bw, write * bw))
+    if a.algorithmic_bytes:
+        print("\nalgorithmic bytes per launch %d; traffic / algorithmic = %.4f"
+              % (a.algorithmic_bytes, traffic / a.algorithmic_bytes))
+    print()
+    print("- traffic_bytes_per_launch: %.0f" % traffic)
+    print("- kernel_source_sha256: %s" % kernel_source_digest())
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("dir")
+    ap.add_argument("dir", nargs="?")
     ap.add_argument("--match", nargs="*", default=[])
+    ap.add_argument("--hbm", metavar="KERNEL", help="kernel-name substring for the HBM traffic summary")
+    ap.add_argument("--fetch")
+    ap.add_argument("--write")
+    ap.add_argument("--copy-fetch")
+    ap.add_argument("--copy-write")
+    ap.add_argument("--copy-bytes", type=float)
+    ap.add_argument("--algorithmic-bytes", type=int, default=0)
     a = ap.parse_args(argv)
+    if a.hbm:
+        if not (a.fetch and a.write and a.copy_fetch and a.copy_write and a.copy_bytes):
+            ap.error("--hbm needs --fetch, --write, --copy-fetch, --copy-write and --copy-bytes")
+        return hbm(a)
+    if not a.dir:
+        ap.error("a rocprofv3 output directory is needed")
     found = False
     for p in sorted(glob.glob(os.path.join(a.dir, "**", "*kernel_stats.csv"), recursive=True)):
         found = True

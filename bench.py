@@ -168,25 +168,28 @@ def main():
         wall = time.perf_counter() - t_start
     ms_step = 1000.0 * wall / K
     # The dominant kernel's launch time: HIP events on the launch stream
-    # around stage 3, over 4R cold-cache steps issued eagerly (events inside a
-    # captured graph do not time).  A bounded spin kernel runs before each
-    # bracket, so that the host has queued event, kernel, event before the GPU
-    # reaches them and the bracket holds the kernel alone.
-    ev_src = ("HIP events around each stage-3 launch, %d eager cold-cache steps, queue kept ahead by a "
-              "spin kernel" % (4 * R))
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4 * R)]
+    # around a run of R back-to-back stage-3 launches, one per weight replica
+    # (each reads cold weights), after stages 1-2 of one input; 8 such runs
+    # over different inputs.  Events inside a captured graph do not time, and
+    # a pair of events around a single launch also holds its dispatch
+    # latency, so the run is long and a bounded spin kernel ahead of it lets
+    # the host queue the whole run before the GPU reaches it.
+    n_runs = 8
+    ev_src = ("HIP events around runs of %d back-to-back stage-3 launches on cold replicas, %d runs, "
+              "median per launch" % (R, n_runs))
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_runs)]
     for i, e in enumerate(evs):
-        W = reps[i % R]
         x = xin[i % n_x]
-        moe.layer_forward_stage(W, x, y, ws, moe.STAGE_ROUTER, routing=r)
-        moe.layer_forward_stage(W, x, y, ws, moe.STAGE_ROUTE, routing=r)
+        moe.layer_forward_stage(base, x, y, ws, moe.STAGE_ROUTER, routing=r)
+        moe.layer_forward_stage(base, x, y, ws, moe.STAGE_ROUTE, routing=r)
         torch.cuda._sleep(1000000)
         e[0].record()
-        moe.layer_forward_stage(W, x, y, ws, moe.STAGE_GATE_UP, routing=r)
+        for W in reps:
+            moe.layer_forward_stage(W, x, y, ws, moe.STAGE_GATE_UP, routing=r)
         e[1].record()
-        moe.layer_forward_stage(W, x, y, ws, moe.STAGE_DOWN_COMBINE, routing=r)
+        moe.layer_forward_stage(base, x, y, ws, moe.STAGE_DOWN_COMBINE, routing=r)
     torch.cuda.synchronize()
-    times = sorted(a.elapsed_time(b) for a, b in evs)
+    times = [a.elapsed_time(b) / R for a, b in evs]
     gateup_ms = float(np.median(times))
     gateup_p10, gateup_p90 = float(np.percentile(times, 10)), float(np.percentile(times, 90))
     log("timed %d steps in %.3f s (%d graph replays); gate/up avg %.2f us (%s)" % (
@@ -258,7 +261,7 @@ def main():
             "bytes_per_launch": int(gateup_bytes),
             "avg_launch_us": round(gateup_ms * 1e3, 3),
             "launch_us_p10_p90": [round(gateup_p10 * 1e3, 3), round(gateup_p90 * 1e3, 3)],
-            "timing": ev_src + "; median",
+            "timing": ev_src,
         },
         "cpu_baseline": cpu,
     }

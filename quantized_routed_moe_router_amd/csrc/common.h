@@ -286,25 +286,121 @@ MOE_DEV float chunk_scale(const float *x, float &inv24) {
     return __uint_as_float((uint32_t)(127 + 13 - e) << 23);   // S
 }
 
-// Prepared activations for Q2K rows: one record of 20 dwords per group of 16
-// values v[0..15].  Slot m < 8 pairs v[m] with v[m+8] (the two weights whose
-// codes share bit positions in one code dword); hi[m], lo[m] hold that fp16
-// pair times S_h * 4^-m', split into hi + lo, with m' = m for m < 5 and m - 5
-// after.  The pairs form two halves h = m / 4 (positions {0-3, 8-11} and
-// {4-7, 12-15}), each with its own power-of-two scale S_h (max|v| * S_h in
-// [2^13, 2^14) over the half): so the two halves can be written by different
-// waves.  sx_h is the sum of the half's 8 values, inv_h = 2^24 / S_h.
-// Layout: hi[0..7], lo[0..7], sx0, inv0, sx1, inv1.  A lane's 64 weights use
-// 4 consecutive records.
-struct P16 {
-    uint32_t hi[8], lo[8];
-    float sx0, inv0, sx1, inv1;
+// Prepared activations for Q2K rows, in integers: a record of 10 dwords per
+// group of 16 values v.  With S = 32512 / max|v|, c_i = rint(v_i * S) is split
+// as c_i = 256 * a_i + b_i, a_i in [-127, 127], b_i in [-128, 127]; dword j of
+// a[] holds a of positions j, 4+j, 8+j, 12+j in bytes 0..3 (the same order as
+// the Q2K codes of one group after a shift by 2j and a byte mask), likewise
+// b[].  sx is the fp32 sum of the 16 values, inv = 1 / S.  The dot of 16
+// codes with the group is then inv * (256 * sum q*a + sum q*b), the two sums
+// from v_dot4_i32_i8; |v_i - inv * c_i| <= inv / 2, a 2^-16 fraction of the
+// group's largest magnitude.  A lane's 64 weights use 4 consecutive records.
+struct Rec16 {
+    uint32_t a[4], b[4];
+    float sx, inv;
 };
-constexpr int kP16Dwords = 20;
+constexpr int kRec16Dwords = 10;
+constexpr float kRec16Max = 32512.f;
 
 struct XQ2K {
-    P16 g[4];
+    Rec16 g[4];
 };
+
+// integer code of v for a group scale S, as (a, b) bytes
+MOE_DEV void rec16_split(float v, float S, int &hi, int &lo) {
+    const int c = (int)__builtin_rintf(v * S);
+    hi = (c + 128) >> 8;
+    lo = c - 256 * hi;
+}
+
+// per-lane preparation of the lane's 64 activations
+MOE_DEV void prep_q2k(const float *x, XQ2K &p) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const float *v = x + 16 * g;
+        float m = 0.f, s = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            m = fmaxf(m, fabsf(v[i]));
+            s += v[i];
+        }
+        const float S = m > 0.f ? kRec16Max / m : 0.f;
+        p.g[g].sx = s;
+        p.g[g].inv = m / kRec16Max;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            uint32_t A = 0, B = 0;
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                int hi, lo;
+                rec16_split(v[4 * n + j], S, hi, lo);
+                A |= (uint32_t)(hi & 0xFF) << (8 * n);
+                B |= (uint32_t)(lo & 0xFF) << (8 * n);
+            }
+            p.g[g].a[j] = A;
+            p.g[g].b[j] = B;
+        }
+    }
+}
+
+// Wave-cooperative preparation of ngroups (<= 4) groups: lane l holds the
+// value at position l % 16 of group l / 16; the records go to out[(l / 16) *
+// 10 ...].  All lanes of the wave must call it.
+MOE_DEV void prep16_wave(float v, uint32_t *out, int ngroups = 4) {
+    const int lane = threadIdx.x & 63, pos = lane & 15;
+    float m = fabsf(v), s = v;
+#pragma unroll
+    for (int o = 1; o <= 8; o <<= 1) {  // over the 16 lanes of the group
+        m = fmaxf(m, __shfl_xor(m, o, kWave));
+        s += __shfl_xor(s, o, kWave);
+    }
+    const float S = m > 0.f ? kRec16Max / m : 0.f;
+    int hi, lo;
+    rec16_split(v, S, hi, lo);
+    // byte pos / 4 of dword pos % 4, gathered over the lanes of one residue
+    uint32_t A = (uint32_t)(hi & 0xFF) << (8 * (pos >> 2)), B = (uint32_t)(lo & 0xFF) << (8 * (pos >> 2));
+    A |= __shfl_xor(A, 4, kWave);
+    B |= __shfl_xor(B, 4, kWave);
+    A |= __shfl_xor(A, 8, kWave);
+    B |= __shfl_xor(B, 8, kWave);
+    if ((lane >> 4) >= ngroups) return;
+    uint32_t *rec = out + (lane >> 4) * kRec16Dwords;
+    if (pos < 4) rec[pos] = A;
+    else if (pos < 8) rec[pos] = B;  // dword pos - 4 of b[], at offset 4 + (pos - 4)
+    else if (pos == 8) rec[8] = __float_as_uint(s);
+    else if (pos == 9) rec[9] = __float_as_uint(m / kRec16Max);
+}
+
+MOE_DEV void load_q2k_prep(const uint32_t *rec4, XQ2K &p) {
+    u32x4 *dst = (u32x4 *)&p;
+#pragma unroll
+    for (int i = 0; i < 4 * kRec16Dwords / 4; ++i) dst[i] = *(const u32x4 *)(rec4 + 4 * i);
+}
+
+MOE_DEV int sdot4(uint32_t a, uint32_t b, int c) { return __builtin_amdgcn_sdot4((int)a, (int)b, c, false); }
+
+// sum_g inv_g * (d*sc_g*sum_i q_i c_i) - dmin * sum_g m_g * sx_g, the integer
+// dot of each group exact in int32 (|sum| < 2^21)
+MOE_DEV float q2k_dot2(const Q2KChunk &c, const XQ2K &p) {
+    const float d = half_bits_to_float(c.dd), dmin = half_bits_to_float(c.dd >> 16);
+    float acc_q = 0.f, acc_m = 0.f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const uint32_t q = c.qs[g];
+        int A = 0, B = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t t = (q >> (2 * j)) & 0x03030303u;
+            A = sdot4(t, p.g[g].a[j], A);
+            B = sdot4(t, p.g[g].b[j], B);
+        }
+        const uint32_t smb = (c.sm >> (8 * g)) & 0xFFu;
+        const float sq = (float)(256 * A + B);
+        acc_q = __builtin_fmaf((float)(smb & 15u) * p.g[g].inv, sq, acc_q);
+        acc_m = __builtin_fmaf((float)(smb >> 4), p.g[g].sx, acc_m);
+    }
+    return d * acc_q - dmin * acc_m;
+}
 
 // scale S and 2^24/S for a set whose largest magnitude is m
 MOE_DEV float group_scale(float m, float &inv24) {
@@ -312,99 +408,6 @@ MOE_DEV float group_scale(float m, float &inv24) {
     e = max(-100, min(100, e));
     inv24 = __uint_as_float((uint32_t)(127 + 11 + e) << 23);
     return __uint_as_float((uint32_t)(127 + 13 - e) << 23);
-}
-
-MOE_DEV float p16_factor(int m) { return 1.0f / (float)(1 << (2 * (m < 5 ? m : m - 5))); }
-
-// position of the i-th value (i < 8) of half h in a group of 16
-MOE_DEV int p16_pos(int h, int i) { return (i < 4 ? 0 : 4) + 4 * h + i; }
-
-// per-lane preparation of the lane's 64 activations
-MOE_DEV void prep_q2k(const float *x, XQ2K &p) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const float *v = x + 16 * g;
-        float S[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            float s = 0.f, m = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                s += v[p16_pos(h, i)];
-                m = fmaxf(m, fabsf(v[p16_pos(h, i)]));
-            }
-            float inv;
-            S[h] = group_scale(m, inv);
-            if (h == 0) {
-                p.g[g].sx0 = s;
-                p.g[g].inv0 = inv;
-            } else {
-                p.g[g].sx1 = s;
-                p.g[g].inv1 = inv;
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const float f = S[j >> 2] * p16_factor(j);
-            split2(v[j] * f, v[j + 8] * f, p.g[g].hi[j], p.g[g].lo[j]);
-        }
-    }
-}
-
-// Wave-cooperative preparation of ngroups (<= 4) groups: lane l holds the
-// value at position l % 16 of group l / 16; the records go to out[(l / 16) *
-// 20 ...].  All lanes of the wave must call it.
-MOE_DEV void prep16_wave(float v, uint32_t *out, int ngroups = 4) {
-    const int lane = threadIdx.x & 63, pos = lane & 15;
-    float m = fabsf(v), s = v;
-#pragma unroll
-    for (int o = 1; o <= 8; o <<= 1) {  // over the 8 lanes of the half: bits 0, 1, 3 of pos
-        if (o == 4) continue;
-        m = fmaxf(m, __shfl_xor(m, o, kWave));
-        s += __shfl_xor(s, o, kWave);
-    }
-    float inv;
-    const float S = group_scale(m, inv);
-    const float partner = __shfl_down(v, 8, kWave);
-    uint32_t *rec = out + (lane >> 4) * kP16Dwords;
-    if ((lane >> 4) >= ngroups) return;
-    if (pos < 8) {
-        const float f = S * p16_factor(pos);
-        uint32_t hi, lo;
-        split2(v * f, partner * f, hi, lo);
-        rec[pos] = hi;
-        rec[8 + pos] = lo;
-        if ((pos & 3) == 0) {  // pos 0: half 0, pos 4: half 1
-            rec[16 + (pos >> 1)] = __float_as_uint(s);
-            rec[17 + (pos >> 1)] = __float_as_uint(inv);
-        }
-    }
-}
-
-MOE_DEV void load_q2k_prep(const uint32_t *rec4, XQ2K &p) {
-    u32x4 *dst = (u32x4 *)&p;
-#pragma unroll
-    for (int i = 0; i < 4 * kP16Dwords / 4; ++i) dst[i] = *(const u32x4 *)(rec4 + 4 * i);
-}
-
-MOE_DEV float q2k_dot2(const Q2KChunk &c, const XQ2K &p) {
-    const float d = half_bits_to_float(c.dd), dmin = half_bits_to_float(c.dd >> 16);
-    float acc_q = 0.f, acc_m = 0.f;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const uint32_t q = c.qs[g], q5 = q >> 10;
-        float a[2] = {0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const uint32_t t = m < 5 ? (q & (0x00030003u << (2 * m))) : (q5 & (0x00030003u << (2 * (m - 5))));
-            a[m >> 2] = dot2(t, p.g[g].hi[m], a[m >> 2]);
-            a[m >> 2] = dot2(t, p.g[g].lo[m], a[m >> 2]);
-        }
-        const uint32_t smb = (c.sm >> (8 * g)) & 0xFFu;
-        acc_q = __builtin_fmaf((float)(smb & 15u), __builtin_fmaf(a[1], p.g[g].inv1, a[0] * p.g[g].inv0), acc_q);
-        acc_m = __builtin_fmaf((float)(smb >> 4), p.g[g].sx0 + p.g[g].sx1, acc_m);
-    }
-    return d * acc_q - dmin * acc_m;
 }
 
 // Activations of one lane chunk (64 values) for Q8_0 codes: pair i holds
@@ -577,9 +580,9 @@ __host__ inline Workspace workspace_layout(const moe_layer_desc *d, int32_t T, v
     w.hs = (float *)take(sizeof(float) * (size_t)T * (size_t)(Fs > 0 ? Fs : 1));
     w.ypart = (float *)take(sizeof(float) * (size_t)P * (size_t)D);
     w.ys = (float *)take(sizeof(float) * (size_t)T * (size_t)D);
-    w.xp16 = (uint32_t *)take(sizeof(uint32_t) * kP16Dwords * (size_t)T * (size_t)(D / 16));
+    w.xp16 = (uint32_t *)take(sizeof(uint32_t) * kRec16Dwords * (size_t)T * (size_t)(D / 16));
     w.xq8 = (uint32_t *)take(sizeof(uint32_t) * kXQ8Dwords * (size_t)T * (size_t)(D / 64));
-    w.hp16 = (uint32_t *)take(sizeof(uint32_t) * kP16Dwords * (size_t)P * (size_t)(F / 16));
+    w.hp16 = (uint32_t *)take(sizeof(uint32_t) * kRec16Dwords * (size_t)P * (size_t)(F / 16));
     w.slots = (SlotRec *)take(sizeof(SlotRec) * (size_t)P);
     w.bytes = off;
     return w;

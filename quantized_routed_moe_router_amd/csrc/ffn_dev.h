@@ -131,6 +131,18 @@ MOE_DEV RowPlan row_plan(int n_in, int lane) {
 // LDS ordering between the lanes of one wave: LDS operations of a wave
 // execute in issue order, so only the compiler has to be kept from moving
 // them across this point.
+// 16 bytes from global memory straight into LDS (no registers held): lane l
+// of the wave writes lds_wave + 16 * l.  lds_wave must be the same for every
+// lane of the wave; lanes switched off by a branch write nothing.
+MOE_DEV void lds_dma16(const void *g, void *lds_wave) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                     (__attribute__((address_space(3))) void *)lds_wave, 16, 0, 0);
+}
+
+// Wait until every vector memory load of the wave, LDS-bound ones included,
+// has landed (vmcnt 0; the export and LDS counters left alone).
+MOE_DEV void vmem_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 MOE_DEV void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();

@@ -48,7 +48,7 @@ template <int FMT, bool REC>
 MOE_DEV void lane_prep(const uint32_t *rec, const void *src, int src_bf16, int64_t row, int n, int c,
                        typename RawChunk<FMT>::Prep &p) {
     if constexpr (REC && FMT == MOE_Q2K) {
-        load_q2k_prep(rec + (row * (n / 16) + 4 * c) * kP16Dwords, p);
+        load_q2k_prep(rec + (row * (n / 16) + 4 * c) * kRec16Dwords, p);
     } else if constexpr (REC && FMT == MOE_Q8_0) {
         load_q8_prep(rec + (row * (n / 64) + c) * kXQ8Dwords, p);
     } else {
@@ -116,7 +116,7 @@ __global__ void __launch_bounds__(256) dec_k1_kernel(FfnArgs a) {
     const int t = item / per_t, c = item % per_t;
     const int64_t i = (int64_t)t * a.D + 64 * c + lane;
     const float v = XT == MOE_BF16 ? bf16_bits_to_float(((const uint16_t *)a.x)[i]) : ((const float *)a.x)[i];
-    if (a.xp16) prep16_wave(v, a.xp16 + ((int64_t)t * (a.D / 16) + 4 * c) * kP16Dwords);
+    if (a.xp16) prep16_wave(v, a.xp16 + ((int64_t)t * (a.D / 16) + 4 * c) * kRec16Dwords);
     if (a.xq8) prep8_wave(v, a.xq8 + ((int64_t)t * (a.D / 64) + c) * kXQ8Dwords);
 }
 
@@ -192,24 +192,18 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
     const int col = cs.cp * cs.ncol, chunk = (col >> 6) + lane % cs.cpr;
     typename RawChunk<GFMT>::Prep xr;  // the first token's activations, in flight with the weights
     lane_prep<GFMT, GFMT == MOE_Q2K>(a.xp16, a.x, a.x_bf16, slot_token(rec, 0), a.D, chunk, xr);
-    {
-        u32x4 v[kNI];
+    // round i: lane l of wave w copies unit i * 256 + 64 * w + l of gate ++ up
 #pragma unroll
-        for (int i = 0; i < kNI; ++i) {
-            const int u = i * 256 + tid;
-            if (u < 2 * U) v[i] = u < U ? sg[u] : su[u - U];
-        }
-#pragma unroll
-        for (int i = 0; i < kNI; ++i) {
-            const int u = i * 256 + tid;
-            if (u < 2 * U) wbuf[u] = v[i];
-        }
+    for (int i = 0; i < kNI; ++i) {
+        const int u = i * 256 + tid;
+        if (u < 2 * U) lds_dma16(u < U ? sg + u : su + (u - U), wbuf + i * 256 + 64 * wave);
     }
+    vmem_wait_all();
     block_lds_sync();
     const uint8_t *wb = (const uint8_t *)wbuf;
     for (int j = 0; j < rec.n; ++j) {
         if (j > 0) lane_prep<GFMT, GFMT == MOE_Q2K>(a.xp16, a.x, a.x_bf16, slot_token(rec, j), a.D, chunk, xr);
-        lds_rows_dot<GFMT, true, 4>(wb, wb + U * 16, a.D, cs.rg * cs.RW, col, cs.ncol, cs.RW, xr, cb_lds, lane,
+        lds_rows_dot<GFMT, true, GFMT == MOE_Q2K ? 4 : 2>(wb, wb + U * 16, a.D, cs.rg * cs.RW, col, cs.ncol, cs.RW, xr, cb_lds, lane,
                                     red[wave], [&](int l, float gs, float us) {
                                         part[wave][2 * l] = gs;
                                         part[wave][2 * l + 1] = us;
@@ -227,7 +221,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
                 hv = swiglu_h(gs, us, a.x_bf16);
                 a.h[(int64_t)(rec.j0 + j) * a.F + 16 * g + lane] = hv;
             }
-            if (a.hp16) prep16_wave(hv, a.hp16 + ((int64_t)(rec.j0 + j) * (a.F / 16) + g) * kP16Dwords, 1);
+            if (a.hp16) prep16_wave(hv, a.hp16 + ((int64_t)(rec.j0 + j) * (a.F / 16) + g) * kRec16Dwords, 1);
         }
         block_lds_sync();
     }
@@ -271,13 +265,10 @@ __global__ void __launch_bounds__(64 * kDecWaves) dec_k4_kernel(FfnArgs a) {
             {
                 const u32x4 *src = (const u32x4 *)(m + fmt_bytes(DFMT, (int64_t)(row0 + r0) * a.F));
                 constexpr int kNI = (kK4WaveUnits + 63) / 64;
-                u32x4 v[kNI];
 #pragma unroll
                 for (int i = 0; i < kNI; ++i)
-                    if (i * 64 + lane < nunits) v[i] = src[i * 64 + lane];
-#pragma unroll
-                for (int i = 0; i < kNI; ++i)
-                    if (i * 64 + lane < nunits) wstage[wave][i * 64 + lane] = v[i];
+                    if (i * 64 + lane < nunits) lds_dma16(src + i * 64 + lane, &wstage[wave][i * 64]);
+                vmem_wait_all();
                 wave_lds_sync();
             }
             for (int j = 0; j < rec.n; ++j) {

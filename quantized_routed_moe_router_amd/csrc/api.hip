@@ -100,7 +100,9 @@ hipError_t forward(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_
     hipError_t e = hipSuccess;
     if (stage == 0 || stage == 1) e = launch_router_logits(d, x, T, x_type, w, s);
     if (e == hipSuccess && (stage == 0 || stage == 2)) e = launch_route_finish(d, T, r, w, s);
-    if (e == hipSuccess && (stage == 0 || stage >= 3)) e = launch_ffn_large(d, x, T, x_type, r, y, flags, w, s, stage);
+    if (e == hipSuccess && (stage == 0 || stage >= 3))
+        e = prefill_path_ok(d, T, x_type) ? launch_prefill(d, x, T, r, y, flags, w, s, stage)
+                                          : launch_ffn_large(d, x, T, x_type, r, y, flags, w, s, stage);
     return e;
 }
 
@@ -144,8 +146,9 @@ int moe_expert_ffn(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_
     if (!aligned16(y)) return fail(err, errlen, MOE_EALIGN, "y must be 16-byte aligned");
     Workspace w = workspace_layout(d, T, ws);
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = small_path_ok(d, T) ? launch_small(d, x, T, x_type, from_routing(r), y, flags, w, s, 0, false)
-                                       : launch_ffn_large(d, x, T, x_type, from_routing(r), y, flags, w, s, 0);
+    hipError_t e = small_path_ok(d, T)                ? launch_small(d, x, T, x_type, from_routing(r), y, flags, w, s, 0, false)
+                   : prefill_path_ok(d, T, x_type) ? launch_prefill(d, x, T, from_routing(r), y, flags, w, s, 0)
+                                                   : launch_ffn_large(d, x, T, x_type, from_routing(r), y, flags, w, s, 0);
     return device_status(e, err, errlen);
 }
 

@@ -551,8 +551,28 @@ struct Workspace {
     uint32_t *xq8;        // [T][D/64] records: x prepared for Q8_0 rows
     uint32_t *hp16;       // [T*k][F/16] records: h prepared for Q2K rows
     SlotRec *slots;       // [T*k] per-slot records of the few-token schedule
+    // many-row bf16 path: int16 activation codes as two int8 planes per
+    // 256-column block ([rows][n/256][512] bytes), group sums as bf16 pairs
+    // ([rows][n/256][16] dwords) and scales, for x (gate/up) and h (down)
+    uint8_t *pf_xq;
+    uint32_t *pf_xs;
+    float *pf_xinv;       // [T]
+    int4 *pf_tiles;       // {expert, first bucket position, rows, 0}
+    int32_t *pf_ntiles;
+    uint16_t *pf_hb;      // [T*k][F] bf16 h by bucket position
+    uint8_t *pf_hq;
+    uint32_t *pf_hs;
+    float *pf_hinv;       // [T*k]
     size_t bytes;
 };
+
+constexpr int kPfTileRows = 64;  // pair rows per tile of the many-row bf16 path
+
+// tiles of at most kPfTileRows pairs over the active experts
+__host__ inline int pf_max_tiles(int32_t T, int k, int E) {
+    const int64_t P = (int64_t)T * k;
+    return (int)((P + kPfTileRows - 1) / kPfTileRows + (P < E ? P : E));
+}
 
 __host__ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
@@ -584,6 +604,15 @@ __host__ inline Workspace workspace_layout(const moe_layer_desc *d, int32_t T, v
     w.xq8 = (uint32_t *)take(sizeof(uint32_t) * kXQ8Dwords * (size_t)T * (size_t)(D / 64));
     w.hp16 = (uint32_t *)take(sizeof(uint32_t) * kRec16Dwords * (size_t)P * (size_t)(F / 16));
     w.slots = (SlotRec *)take(sizeof(SlotRec) * (size_t)P);
+    w.pf_xq = (uint8_t *)take((size_t)T * (size_t)D * 2);
+    w.pf_xs = (uint32_t *)take((size_t)T * (size_t)(D / 256 + 1) * 64);
+    w.pf_xinv = (float *)take(sizeof(float) * (size_t)T);
+    w.pf_tiles = (int4 *)take(sizeof(int4) * (size_t)pf_max_tiles(T, k, E));
+    w.pf_ntiles = (int32_t *)take(sizeof(int32_t) * 4);
+    w.pf_hb = (uint16_t *)take((size_t)P * (size_t)F * 2);
+    w.pf_hq = (uint8_t *)take((size_t)P * (size_t)F * 2);
+    w.pf_hs = (uint32_t *)take((size_t)P * (size_t)(F / 256 + 1) * 64);
+    w.pf_hinv = (float *)take(sizeof(float) * (size_t)P);
     w.bytes = off;
     return w;
 }
@@ -610,6 +639,14 @@ hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32
 // any number of rows: stage 3 = gate/up, 4 = down + combine, 0 = both
 hipError_t launch_ffn_large(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
                             float *y, uint32_t flags, const Workspace &ws, hipStream_t s, int stage);
+// shared expert alone on the batched kernels: stage 3 writes hs, 4 writes ys
+hipError_t launch_ffn_large_shared(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type,
+                                   const RoutingPtrs &r, float *y, uint32_t flags, const Workspace &ws, hipStream_t s,
+                                   int stage);
+// many rows in bf16 mode with Q2K experts: MFMA grouped GEMMs
+bool prefill_path_ok(const moe_layer_desc *d, int32_t T, int32_t x_type);
+hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, const RoutingPtrs &r, float *y,
+                          uint32_t flags, const Workspace &ws, hipStream_t s, int stage);
 hipError_t launch_rmsnorm(const float *x, const float *gamma, float eps, int32_t T, int32_t D, float *out,
                           hipStream_t s);
 hipError_t launch_dequant(int32_t type, const void *src, int64_t n, const int8_t *cb, int32_t out_type, void *dst,

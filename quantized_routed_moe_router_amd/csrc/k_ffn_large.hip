@@ -83,4 +83,23 @@ hipError_t launch_ffn_large(const moe_layer_desc *d, const void *x, int32_t T, i
     return hipGetLastError();
 }
 
+hipError_t launch_ffn_large_shared(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type,
+                                   const RoutingPtrs &r, float *y, uint32_t flags, const Workspace &ws, hipStream_t s,
+                                   int stage) {
+    FfnArgs a = make_ffn_args(d, x, T, x_type, r, y, flags, ws);
+    if (a.Fs <= 0) return hipSuccess;
+    dim3 g1((a.Fs + kLargeRows - 1) / kLargeRows, 1);
+    dim3 g2((a.D + kLargeRows - 1) / kLargeRows, 1);
+    const int sf = d->shared_type;
+    if (stage == 3)
+        with_fmt(d->gate_type, [&](auto G) {
+            with_fmt(sf, [&](auto S) { large_gateup_kernel<decltype(G)::value, decltype(S)::value><<<g1, 256, 0, s>>>(a); });
+        });
+    if (stage == 4)
+        with_fmt(d->down_type, [&](auto DN) {
+            with_fmt(sf, [&](auto S) { large_down_kernel<decltype(DN)::value, decltype(S)::value><<<g2, 256, 0, s>>>(a); });
+        });
+    return hipGetLastError();
+}
+
 }  // namespace moe

@@ -1,0 +1,511 @@
+// k_prefill.hip - the routed experts of many token rows in bf16 mode as
+// grouped GEMMs on the matrix cores ("Understanding Dwarf Star", 5.3.7 steps
+// 3-5: each active expert's bucket of pairs runs gate/up, SwiGLU, down and a
+// weighted scatter into y; 2.8.2 the dequant-dot over 256-weight super-blocks;
+// the Q2_K subsection for w = d*sc*q - dmin*m).
+//
+// A tile is up to 64 pairs of one expert (two 32-row MFMA subtiles).  A block
+// of 8 waves streams one 256-weight super-block column of 256 weight rows
+// (gate and up, or down) per step through two LDS stages filled by
+// global-to-LDS DMA; each wave owns 32 weight rows for both subtiles.  Per
+// super-block column:
+//   sum_k w_k a_k = d * sum_k (sc*q)_k a_k - sum_g (dmin*m_g) * (sum_{k in g} a_k)
+// The first sum runs on v_mfma_i32_32x32x32_i8: the codes sc*q (0..45) are
+// exact int8 and the activations are int16 codes c = rint(a*S) split as
+// c = 256*hi + lo (two int8 passes).  The integer result, exact in int32, is
+// scaled by d in fp32.  The second sum runs on v_mfma_f32_32x32x16_bf16 with
+// dmin*m (exact as a bf16 pair) against the group sums (a bf16 pair).
+#include <type_traits>
+
+#include "ffn_dev.h"
+
+namespace moe {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int kPfM = 64;                // pair rows per tile
+constexpr int kPfWaves = 8;
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kPfBRows = 256;           // weight rows staged per super-block column
+constexpr int kPfAUnits = kPfM * 32;    // 16-byte units of codes per column: hi 16 + lo 16 per row
+constexpr int kPfSDwords = kPfM * 16;   // group sums: 8 dwords sH + 8 dwords sL per row
+constexpr float kPfCodeMax = 32512.f;   // |c| <= 32512 keeps hi in [-127, 127]
+
+// One super-block column in LDS.  Codes of row r, unit u (0..15 hi, 16..31
+// lo) sit at a[r*32 + (u ^ (r & 7))]; group sums of row r, unit u (0, 1 sH;
+// 2, 3 sL) at s[4*(r*4 + (u ^ ((r >> 1) & 3)))...]; weight row R: scale
+// bytes and codes (the 80 bytes after d, dmin) at b[5R..5R+4], d and dmin at
+// dd[R].  The XOR swizzles keep 8 consecutive rows on distinct LDS banks.
+constexpr int kPfBI = (kPfBRows * 5 + kPfThreads - 1) / kPfThreads;  // B units per thread (padded)
+struct PfStage {
+    u32x4 a[kPfAUnits];
+    uint32_t s[kPfSDwords];
+    u32x4 b[kPfBI * kPfThreads];    // rows past kPfBRows: padding the DMA fills with copies
+    uint32_t dd[kPfThreads];        // entries past kPfBRows: padding
+};
+
+struct PfArgs {
+    const uint8_t *w0, *w1;  // gate and up (mode 0) or down (mode 1), expert-major Q2K
+    int64_t expert_bytes;
+    int n_in;                // reduction length: D (mode 0) or F (mode 1)
+    const uint8_t *aq;       // activation codes [rows][n_in/256][512]
+    const uint32_t *as;      // group sums in code units [rows][n_in/256][16]
+    const float *ainv;       // 1/S of each row: [T] (mode 0) or [T*k] by bucket position (mode 1)
+    const int4 *tiles;       // {expert, first bucket position, rows, 0}
+    const int32_t *n_tiles;
+    const int32_t *perm;
+    const float *topk_w;
+    int k;
+    int D, F;
+    uint16_t *hb;            // mode 0 output: h in bf16, [T*k][F] by bucket position
+    float *y;                // mode 1 output
+};
+
+// Global-to-LDS copies of 16 and 4 bytes per lane (lane l writes lds_wave +
+// size * l; lds_wave uniform over the wave), issued as inline assembly: the
+// compiler then sees no LDS store to order against the reads of the other
+// stage (its own tracking of such copies falls back to waiting for all of
+// them), and the kernel counts them with explicit vmcnt waits instead.  One
+// wait state separates the m0 write from the copy.
+MOE_DEV uint32_t lds_addr(const void *p) { return (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)p; }
+
+MOE_DEV void pf_dma16(const void *g, void *lds_wave) {
+    __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :
+                     : "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave))), "v"(g)
+                     : "memory");
+}
+
+MOE_DEV void pf_dma4(const void *g, void *lds_wave) {
+    __asm__ volatile("s_nop 0\n\tglobal_load_lds_dword %1, off"
+                     :
+                     : "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave))), "v"(g)
+                     : "memory");
+}
+
+// wait until at most N vector memory operations of the wave are outstanding
+// (vmcnt is 6 bits: low 4 at [3:0], high 2 at [15:14])
+template <int N>
+MOE_DEV void vmem_wait_at_most() {
+    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+MOE_DEV uint16_t bf16_rne(float f) { return (uint16_t)float_to_bf16_bits(f); }
+
+// 16 activations -> t-ordered int8 halves (byte 4j+n of the unit holds value
+// 4n+j, the order the code dwords of a Q2K group take after >> 2j & 0x03030303)
+MOE_DEV void pf_codes16(const float *v, float S, u32x4 &hi, u32x4 &lo) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t H = 0, L = 0;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const int c = (int)__builtin_rintf(v[4 * n + j] * S);
+            const int hv = (c + 128) >> 8;
+            H |= (uint32_t)(hv & 0xFF) << (8 * n);
+            L |= (uint32_t)((c - 256 * hv) & 0xFF) << (8 * n);
+        }
+        hi[j] = H;
+        lo[j] = L;
+    }
+}
+
+// Activation codes of rows of n bf16 values (x for gate/up, h for down): one
+// block per row, a thread per group of 16.  S = 32512 / max|row|; the group
+// sums are kept in code units (sum * S), so a whole product stays in code
+// units until the row's 1/S at the end.
+__global__ void __launch_bounds__(256) pf_prep_rows_kernel(const uint16_t *x, int n, uint8_t *xq, uint32_t *xs,
+                                                           float *xinv) {
+    __shared__ float wmax[4];
+    const int t = blockIdx.x, ng = n >> 4;
+    float mt = 0.f;
+    for (int g = threadIdx.x; g < ng; g += 256) {
+        const u32x4 *src = (const u32x4 *)(x + (int64_t)t * n + 16 * g);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const u32x4 w = src[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                mt = fmaxf(mt, fmaxf(fabsf(bf16_bits_to_float(w[j] & 0xFFFFu)), fabsf(bf16_bits_to_float(w[j] >> 16))));
+        }
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) mt = fmaxf(mt, __shfl_xor(mt, o, kWave));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mt;
+    __syncthreads();
+    const float m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float S = m > 0.f ? kPfCodeMax / m : 0.f;
+    if (threadIdx.x == 0) xinv[t] = m / kPfCodeMax;
+    const int nkb = n >> 8;
+    for (int g = threadIdx.x; g < ng; g += 256) {
+        float v[16];
+        const u32x4 *src = (const u32x4 *)(x + (int64_t)t * n + 16 * g);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const u32x4 w = src[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[8 * i + 2 * j] = bf16_bits_to_float(w[j] & 0xFFFFu);
+                v[8 * i + 2 * j + 1] = bf16_bits_to_float(w[j] >> 16);
+            }
+        }
+        const int kb = g >> 4, gi = g & 15;
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sum += v[i];
+        const float sc = sum * S;
+        const uint16_t sh = bf16_rne(sc);
+        const uint16_t sl = bf16_rne(sc - bf16_bits_to_float(sh));
+        u32x4 hi, lo;
+        pf_codes16(v, S, hi, lo);
+        uint8_t *base = xq + ((int64_t)t * nkb + kb) * 512;
+        const int unit = 2 * (gi & 7) + (gi >> 3);
+        *(u32x4 *)(base + 16 * unit) = hi;
+        *(u32x4 *)(base + 256 + 16 * unit) = lo;
+        uint16_t *sb = (uint16_t *)(xs + ((int64_t)t * nkb + kb) * 16);
+        sb[gi] = sh;
+        sb[16 + gi] = sl;
+    }
+}
+
+// Tiles of at most 64 pairs over the active experts, ascending expert id.
+__global__ void pf_tiles_kernel(const int32_t *active, const int32_t *n_active, const int32_t *count,
+                                const int32_t *offset, int4 *tiles, int32_t *n_tiles) {
+    if (threadIdx.x != 0) return;
+    const int n = n_active[0];
+    int nt = 0;
+    for (int i = 0; i < n; ++i) {
+        const int e = active[i], c = count[e], o = offset[e];
+        for (int s = 0; s < c; s += kPfM) tiles[nt++] = make_int4(e, o + s, min(kPfM, c - s), 0);
+    }
+    n_tiles[0] = nt;
+}
+
+// y = ys (+ y when accumulating), or 0 / y without a shared expert: the
+// routed pairs are then added by the down pass.
+__global__ void __launch_bounds__(256) pf_y_init_kernel(const float *ys, float *y, int64_t n, int accumulate) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float v = ys ? ys[i] : 0.f;
+    if (accumulate) v += y[i];
+    y[i] = v;
+}
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// four byte codes (each <= 3) times sc (<= 15) bytewise, no carries: one
+// packed 16-bit multiply
+MOE_DEV uint32_t mul_bytes(uint32_t t, uint32_t sc) {
+    const u16x2 p = __builtin_bit_cast(u16x2, t) * (u16x2){(unsigned short)sc, (unsigned short)sc};
+    return __builtin_bit_cast(uint32_t, p);
+}
+
+MOE_DEV v8bf as_v8bf(const uint32_t (&w)[4]) {
+    v8bf r;
+    __builtin_memcpy(&r, w, 16);
+    return r;
+}
+
+// Barrier for the LDS stages: a compiler-level memory fence only.  Each wave
+// has already waited for its own DMA (vmcnt) and consumed its LDS reads, and
+// a hardware fence here would also wait for the DMA of the next stage.
+MOE_DEV void stage_barrier() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
+// Mode 0: blockIdx.x = 128 F-rows; wave w < 4 owns gate rows 32w..32w+31,
+// wave w >= 4 the same rows of up; writes h = silu(g) * u in bf16.  Mode 1:
+// blockIdx.x = 256 D-columns, wave w owns columns 32w..32w+31; adds
+// w * y_pair into y.  blockIdx.y = tile.
+template <int MODE>
+__global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
+    __shared__ PfStage st0, st1;
+    __shared__ int32_t row_tok[kPfM];
+    __shared__ float row_f[kPfM];
+    const int tile = blockIdx.y;
+    if (tile >= a.n_tiles[0]) return;
+    const int4 ti = a.tiles[tile];
+    const int e = ti.x, start = ti.y, cnt = ti.z;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, c = lane & 31, h = lane >> 5;
+    const int nkb = a.n_in >> 8;
+    const int o0 = blockIdx.x * (MODE == 0 ? 128 : 256);
+    const int64_t rowbytes = (int64_t)nkb * kQ2KBytes;
+
+    if (tid < kPfM) {
+        const int pos = start + min(tid, cnt - 1);
+        const int pair = a.perm[pos];
+        row_tok[tid] = pair / a.k;
+        row_f[tid] = MODE == 0 ? a.ainv[pair / a.k] : a.ainv[pos] * a.topk_w[pair];
+    }
+    block_lds_sync();
+
+    // DMA sources, fixed over the columns (32-bit offsets from uniform bases)
+    auto arow = [&](int r) { return MODE == 0 ? row_tok[r] : start + min(r, cnt - 1); };
+    constexpr int kAI = kPfAUnits / kPfThreads, kSI = kPfSDwords / kPfThreads;
+    uint32_t aoff[kAI], soff[kSI], boff[kPfBI];
+#pragma unroll
+    for (int i = 0; i < kAI; ++i) {
+        const int u = i * kPfThreads + tid, r = u >> 5;
+        aoff[i] = (uint32_t)(arow(r) * nkb * 512 + (((u & 31) ^ (r & 7)) * 16));
+    }
+#pragma unroll
+    for (int i = 0; i < kSI; ++i) {
+        const int q = i * kPfThreads + tid, r = q >> 4;
+        const int unit = ((q >> 2) & 3) ^ ((r >> 1) & 3);
+        soff[i] = (uint32_t)(arow(r) * nkb * 64 + unit * 16 + (q & 3) * 4);
+    }
+    const uint8_t *wb0 = a.w0 + (int64_t)e * a.expert_bytes, *wb1 = a.w1 + (int64_t)e * a.expert_bytes;
+    // staged row R: mode 0 rows < 128 are gate, the rest up; mode 1 all down
+    auto wrow = [&](int R) -> uint32_t { return (uint32_t)((o0 + (MODE == 0 ? (R & 127) : R)) * rowbytes); };
+    bool bup[kPfBI];
+#pragma unroll
+    for (int i = 0; i < kPfBI; ++i) {
+        const int u = min(i * kPfThreads + tid, kPfBRows * 5 - 1), R = u / 5, part = u % 5;
+        boff[i] = wrow(R) + 4 + 16 * part;
+        bup[i] = MODE == 0 && R >= 128;
+    }
+    const int ddr = tid & (kPfBRows - 1);
+    const uint32_t ddoff = wrow(ddr);
+    const bool ddup = MODE == 0 && ddr >= 128;
+
+    auto issue = [&](PfStage &S, int kb) {
+#pragma unroll
+        for (int i = 0; i < kAI; ++i) pf_dma16(a.aq + aoff[i] + kb * 512, &S.a[i * kPfThreads + 64 * wave]);
+#pragma unroll
+        for (int i = 0; i < kSI; ++i)
+            pf_dma4((const uint8_t *)a.as + soff[i] + kb * 64, &S.s[i * kPfThreads + 64 * wave]);
+#pragma unroll
+        for (int i = 0; i < kPfBI; ++i)
+            pf_dma16((bup[i] ? wb1 : wb0) + boff[i] + kb * kQ2KBytes, &S.b[i * kPfThreads + 64 * wave]);
+        pf_dma4((ddup ? wb1 : wb0) + ddoff + kb * kQ2KBytes, &S.dd[64 * wave]);
+    };
+    constexpr int kIssued = kAI + kSI + kPfBI + 1;
+
+    const int nsub = cnt > 32 ? 2 : 1;
+    // this wave's weight rows in the stage
+    const int R = MODE == 0 ? (wave >> 2) * 128 + (wave & 3) * 32 + c : wave * 32 + c;
+    v16f tot[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) tot[q][v] = 0.f;
+
+    auto run = [&](auto nsub_c) {
+    constexpr int NSUB = decltype(nsub_c)::value;
+    auto compute = [&](PfStage &S) {
+        v4i bq[8];
+        uint32_t bmh[4], bml[4];
+        const uint8_t *rb = (const uint8_t *)&S.b[R * 5];
+        const uint2 sm = *(const uint2 *)(rb + 8 * h);
+        const u32x4 q0 = *(const u32x4 *)(rb + 16 + 32 * h), q1 = *(const u32x4 *)(rb + 32 + 32 * h);
+        const uint32_t dd = S.dd[R];
+        const float dsc = half_bits_to_float(dd), dmin = half_bits_to_float(dd >> 16);
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const uint32_t Q = p < 4 ? q0[p] : q1[p - 4];
+            const uint32_t sc = ((p < 4 ? sm.x : sm.y) >> (8 * (p & 3))) & 15u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) bq[p][j] = (int)mul_bytes((Q >> (2 * j)) & 0x03030303u, sc);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t hw = 0, lw = 0;
+#pragma unroll
+            for (int z = 0; z < 2; ++z) {
+                const int gi = 2 * i + z;
+                const uint32_t m = ((gi < 4 ? sm.x : sm.y) >> (8 * (gi & 3) + 4)) & 15u;
+                const float cf = -(dmin * (float)m);
+                const uint16_t hb = bf16_rne(cf);
+                const uint16_t lb = bf16_rne(cf - bf16_bits_to_float(hb));
+                hw |= (uint32_t)hb << (16 * z);
+                lw |= (uint32_t)lb << (16 * z);
+            }
+            bmh[i] = hw;
+            bml[i] = lw;
+        }
+        const u32x4 *abase[2][4];
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int row = q * 32 + c;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) abase[q][j] = &S.a[row * 32 + ((2 * j + h) ^ (row & 7))];
+        }
+        // two independent accumulation chains, one per subtile
+        v16i acc[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[q][v] = 0;
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            if (pass == 1) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[q][v] <<= 8;
+            }
+#pragma unroll
+            for (int p = 0; p < 8; ++p) {
+#pragma unroll
+                for (int q = 0; q < NSUB; ++q) {
+                    // unit 16*pass + 2p + h of row q*32 + c: the swizzle only
+                    // permutes within aligned groups of 8 units, so p + 4 and
+                    // the lo half are constant byte offsets from abase
+                    const u32x4 av = *(const u32x4 *)((const uint8_t *)abase[q][p & 3] + 128 * (p >> 2) + 256 * pass);
+                    v4i ai;
+                    __builtin_memcpy(&ai, &av, 16);
+                    acc[q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ai, bq[p], acc[q], 0, 0, 0);
+                }
+            }
+        }
+        const v8bf ch = as_v8bf(bmh), cl = as_v8bf(bml);
+#pragma unroll
+        for (int q = 0; q < NSUB; ++q) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) tot[q][v] = __builtin_fmaf((float)acc[q][v], dsc, tot[q][v]);
+            const int row = q * 32 + c, sw = (row >> 1) & 3;
+            const u32x4 shu = *(const u32x4 *)&S.s[4 * (row * 4 + (h ^ sw))];
+            const u32x4 slu = *(const u32x4 *)&S.s[4 * (row * 4 + ((2 + h) ^ sw))];
+            v8bf sh, sl;
+            __builtin_memcpy(&sh, &shu, 16);
+            __builtin_memcpy(&sl, &slu, 16);
+            tot[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sh, ch, tot[q], 0, 0, 0);
+            tot[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sl, ch, tot[q], 0, 0, 0);
+            tot[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sh, cl, tot[q], 0, 0, 0);
+        }
+    };
+
+    issue(st0, 0);
+    for (int kb = 0; kb < nkb; kb += 2) {
+        if (kb + 1 < nkb) {
+            issue(st1, kb + 1);
+            vmem_wait_at_most<kIssued>();
+        } else {
+            vmem_wait_at_most<0>();
+        }
+        stage_barrier();
+        compute(st0);
+        stage_barrier();
+        if (kb + 1 >= nkb) break;
+        if (kb + 2 < nkb) {
+            issue(st0, kb + 2);
+            vmem_wait_at_most<kIssued>();
+        } else {
+            vmem_wait_at_most<0>();
+        }
+        stage_barrier();
+        compute(st1);
+        stage_barrier();
+    }
+    };
+    if (nsub == 2) run(std::integral_constant<int, 2>{});
+    else run(std::integral_constant<int, 1>{});
+
+    if constexpr (MODE == 0) {
+        // up waves hand their values to the gate waves of the same rows
+        float *U = (float *)&st0;  // [64 rows][128 columns]
+        if (wave >= 4) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                if (q == 1 && nsub < 2) continue;
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    U[(q * 32 + 8 * (v >> 2) + 4 * h + (v & 3)) * 128 + (wave & 3) * 32 + c] = tot[q][v];
+            }
+        }
+        block_lds_sync();
+        if (wave < 4) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                if (q == 1 && nsub < 2) continue;
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int r = q * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                    if (r >= cnt) continue;
+                    const float f = row_f[r];
+                    const float hv = silu(tot[q][v] * f) * (U[r * 128 + wave * 32 + c] * f);
+                    a.hb[(int64_t)(start + r) * a.F + o0 + wave * 32 + c] = bf16_rne(hv);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            if (q == 1 && nsub < 2) continue;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = q * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                if (r < cnt)
+                    unsafeAtomicAdd(&a.y[(int64_t)row_tok[r] * a.D + o0 + wave * 32 + c], row_f[r] * tot[q][v]);
+            }
+        }
+    }
+}
+
+bool prefill_path_ok(const moe_layer_desc *d, int32_t T, int32_t x_type) {
+    return x_type == MOE_BF16 && T > 0 && d->gate_type == MOE_Q2K && d->down_type == MOE_Q2K &&
+           d->n_embd % 256 == 0 && d->n_ff_exp % 256 == 0;
+}
+
+// stage 3: x codes, tiles, shared gate/up, routed gate/up; stage 4: h codes,
+// shared down, y init, routed down; 0: all
+hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, const RoutingPtrs &r, float *y,
+                          uint32_t flags, const Workspace &ws, hipStream_t s, int stage) {
+    const int D = d->n_embd, F = d->n_ff_exp, k = d->n_expert_used, E = d->n_expert;
+    const int ntmax = pf_max_tiles(T, k, E);
+    static_assert(kPfM == kPfTileRows, "tile rows");
+    const int64_t P = (int64_t)T * k;
+    PfArgs a{};
+    a.tiles = (const int4 *)ws.pf_tiles;
+    a.n_tiles = ws.pf_ntiles;
+    a.perm = r.perm;
+    a.topk_w = r.topk_w;
+    a.k = k;
+    a.D = D;
+    a.F = F;
+    a.hb = ws.pf_hb;
+    a.y = y;
+    a.expert_bytes = fmt_bytes(MOE_Q2K, (int64_t)F * D);
+    if (stage == 0 || stage == 3) {
+        pf_prep_rows_kernel<<<T, 256, 0, s>>>((const uint16_t *)x, D, ws.pf_xq, ws.pf_xs, ws.pf_xinv);
+        pf_tiles_kernel<<<1, 64, 0, s>>>(r.active, r.n_active, r.count, r.offset, ws.pf_tiles, ws.pf_ntiles);
+        if (d->n_ff_shared > 0) {
+            hipError_t e = launch_ffn_large_shared(d, x, T, MOE_BF16, r, y, flags, ws, s, 3);
+            if (e != hipSuccess) return e;
+        }
+        PfArgs g = a;
+        g.w0 = (const uint8_t *)d->gate;
+        g.w1 = (const uint8_t *)d->up;
+        g.n_in = D;
+        g.aq = ws.pf_xq;
+        g.as = ws.pf_xs;
+        g.ainv = ws.pf_xinv;
+        pf_gemm_kernel<0><<<dim3(F / 128, ntmax), kPfThreads, 0, s>>>(g);
+    }
+    if (stage == 0 || stage == 4) {
+        pf_prep_rows_kernel<<<(unsigned)P, 256, 0, s>>>(ws.pf_hb, F, ws.pf_hq, ws.pf_hs, ws.pf_hinv);
+        if (d->n_ff_shared > 0) {
+            hipError_t e = launch_ffn_large_shared(d, x, T, MOE_BF16, r, y, flags, ws, s, 4);
+            if (e != hipSuccess) return e;
+        }
+        const int64_t n = (int64_t)T * D;
+        pf_y_init_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(d->n_ff_shared > 0 ? ws.ys : nullptr, y, n,
+                                                                      (flags & MOE_ACCUMULATE) ? 1 : 0);
+        PfArgs dn = a;
+        dn.w0 = dn.w1 = (const uint8_t *)d->down;
+        dn.n_in = F;
+        dn.aq = ws.pf_hq;
+        dn.as = ws.pf_hs;
+        dn.ainv = ws.pf_hinv;
+        pf_gemm_kernel<1><<<dim3(D / 256, ntmax), kPfThreads, 0, s>>>(dn);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -71,6 +71,30 @@ def test_bf16_small(T):
     _check_layer(L, T, 71, bf16=True)
 
 
+@pytest.mark.parametrize("D,F,E,k,T,Fs", [
+    (512, 512, 8, 2, 150, 256),   # 1- and 2-subtile tiles with ragged rows
+    (256, 256, 4, 2, 300, 0),     # several tiles per expert; one super-block column
+    (1024, 256, 16, 6, 57, 128),
+])
+def test_bf16_many_rows_matrix_cores(D, F, E, k, T, Fs):
+    # bf16 batches beyond the decode schedule run as grouped GEMMs on the
+    # matrix cores; outputs within tolerance of the oracle's bf16 mode
+    L = synth.make_layer(74 + T, 0, D=D, E=E, k=k, F=F, Fs=Fs)
+    worst, _, _ = _check_layer(L, T, 75 + T, bf16=True)
+    print("bf16 D=%d F=%d E=%d k=%d T=%d: worst relative error %.3g" % (D, F, E, k, T, worst))
+
+
+def test_bf16_many_rows_accumulate():
+    L = synth.make_layer(76, 0, D=512, E=8, k=2, F=512, Fs=256)
+    x = synth.activations(77, 40, 512)
+    xb = synth.to_bf16_bits(x)
+    y_ref, _, _ = oracle.moe_forward(L, x_bf16=xb)
+    W = gu.upload(L)
+    y0 = torch.full((40, 512), -0.5, dtype=torch.float32, device="cuda")
+    y, _ = gu.run_forward(W, gu.x_to_device(x_bf16=xb), accumulate=True, y0=y0)
+    gu.assert_close(y.cpu().numpy(), y_ref - np.float32(0.5))
+
+
 def test_cb2_gate_up_layer():
     cb = synth.codebook(4)
     L = synth.make_layer(72, 0, D=1024, E=16, k=6, F=512, Fs=256, gate_fmt=synth.CB2, cb=cb)

@@ -410,6 +410,7 @@ __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
     if constexpr (MODE == 0) {
         // up waves hand their values to the gate waves of the same rows
         float *U = (float *)&st0;  // [64 rows][128 columns]
+        static_assert(sizeof(PfStage) >= kPfM * 128 * sizeof(float), "exchange area");
         if (wave >= 4) {
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
@@ -448,16 +449,192 @@ __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
     }
 }
 
+// ---- shared expert: bf16 GEMM on exactly split weights -------------------------
+// Each Q8_0 weight w = d*q (at most 18 significant bits) is split once per
+// call into bf16 hi = rne(w) and lo = rne(w - hi), so w = hi + lo to 2^-17
+// relative; gate/up and down then run as bf16 GEMMs over both halves
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulation): bf16 activations times
+// either half are exact products.
+
+__global__ void __launch_bounds__(256) pf_q8_split_kernel(const uint8_t *src, int64_t nblocks, uint16_t *hi,
+                                                          uint16_t *lo) {
+    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (b >= nblocks) return;
+    const uint8_t *blk = src + b * kQ8Bytes;
+    const float d = half_bits_to_float((uint32_t)blk[0] | ((uint32_t)blk[1] << 8));
+#pragma unroll
+    for (int i0 = 0; i0 < 32; i0 += 8) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+            uint32_t hh = 0, ll = 0;
+#pragma unroll
+            for (int z = 0; z < 2; ++z) {
+                const float w = d * (float)(int8_t)blk[2 + i0 + j + z];
+                const uint16_t wh = bf16_rne(w);
+                const uint16_t wl = bf16_rne(w - bf16_bits_to_float(wh));
+                hh |= (uint32_t)wh << (16 * z);
+                ll |= (uint32_t)wl << (16 * z);
+            }
+            hw[j / 2] = hh;
+            lw[j / 2] = ll;
+        }
+        *(u32x4 *)(hi + b * 32 + i0) = u32x4{hw[0], hw[1], hw[2], hw[3]};
+        *(u32x4 *)(lo + b * 32 + i0) = u32x4{lw[0], lw[1], lw[2], lw[3]};
+    }
+}
+
+constexpr int kSgM = 128;            // token rows per block (four 32-row subtiles)
+constexpr int kSgKc = 32;            // reduction columns per stage
+constexpr int kSgRowUnits = kSgKc * 2 / 16;   // 16-byte units per row per stage (4)
+
+struct SgStage {
+    u32x4 a[kSgM * kSgRowUnits];       // activation rows: unit u of row r at r*4 + (u ^ ((r >> 1) & 3))
+    u32x4 bh[256 * kSgRowUnits];       // weight rows, hi halves, same swizzle
+    u32x4 bl[256 * kSgRowUnits];       // lo halves
+};
+
+struct SgArgs {
+    const uint16_t *a;          // [T][K] bf16
+    const uint16_t *wh, *wl;    // mode 0: gate rows then up rows [2*Fs][D]; mode 1: down [D][Fs]
+    int T, K, Fs, D;
+    uint16_t *hs;               // mode 0 output [T][Fs] bf16
+    float *y;                   // mode 1 output [T][D]
+    int accumulate;
+};
+
+MOE_DEV int sg_unit(int r, int u) { return r * kSgRowUnits + (u ^ ((r >> 1) & 3)); }
+
+// Mode 0: blockIdx.x = 128 F-rows (waves 0-3 gate, 4-7 up), writes bf16
+// h = silu(g) * u.  Mode 1: blockIdx.x = 256 D-columns, y = (y if
+// accumulating) + shared output.  blockIdx.y = 128 token rows.
+template <int MODE>
+__global__ void __launch_bounds__(512) pf_sg_gemm_kernel(SgArgs a) {
+    __shared__ SgStage st0, st1;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, c = lane & 31, h = lane >> 5;
+    const int m0 = blockIdx.y * kSgM;
+    const int nkc = a.K / kSgKc;
+    auto wrow = [&](int R) -> int64_t {
+        if (MODE == 0) return (int64_t)((R >> 7) * a.Fs + blockIdx.x * 128 + (R & 127));
+        return (int64_t)(blockIdx.x * 256 + R);
+    };
+    // one 16-byte unit per thread for A (512 units), two for each weight half (1024 units)
+    static_assert(kSgM * kSgRowUnits == 512 && 256 * kSgRowUnits == 1024, "stage shape");
+    const int ar = tid >> 2;
+    const uint16_t *asrc = a.a + (int64_t)min(m0 + ar, a.T - 1) * a.K + 8 * ((tid & 3) ^ ((ar >> 1) & 3));
+    int64_t boff[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int u = i * 512 + tid, R = u >> 2;
+        boff[i] = wrow(R) * a.K + 8 * ((u & 3) ^ ((R >> 1) & 3));
+    }
+    auto issue = [&](SgStage &S, int kc) {
+        pf_dma16(asrc + kc * kSgKc, &S.a[64 * wave]);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            pf_dma16(a.wh + boff[i] + kc * kSgKc, &S.bh[i * 512 + 64 * wave]);
+            pf_dma16(a.wl + boff[i] + kc * kSgKc, &S.bl[i * 512 + 64 * wave]);
+        }
+    };
+    constexpr int kIssued = 5;
+    v16f tot[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) tot[q][v] = 0.f;
+    const int R = MODE == 0 ? (wave >> 2) * 128 + (wave & 3) * 32 + c : wave * 32 + c;
+    auto compute = [&](SgStage &S) {
+#pragma unroll
+        for (int ks = 0; ks < kSgKc / 16; ++ks) {
+            const int u = 2 * ks + h;
+            const u32x4 bw = S.bh[sg_unit(R, u)], bx = S.bl[sg_unit(R, u)];
+            v8bf bvh, bvl;
+            __builtin_memcpy(&bvh, &bw, 16);
+            __builtin_memcpy(&bvl, &bx, 16);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x4 aw = S.a[sg_unit(q * 32 + c, u)];
+                v8bf av;
+                __builtin_memcpy(&av, &aw, 16);
+                tot[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bvh, tot[q], 0, 0, 0);
+                tot[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bvl, tot[q], 0, 0, 0);
+            }
+        }
+    };
+    issue(st0, 0);
+    for (int kc = 0; kc < nkc; kc += 2) {
+        if (kc + 1 < nkc) {
+            issue(st1, kc + 1);
+            vmem_wait_at_most<kIssued>();
+        } else {
+            vmem_wait_at_most<0>();
+        }
+        stage_barrier();
+        compute(st0);
+        stage_barrier();
+        if (kc + 1 >= nkc) break;
+        if (kc + 2 < nkc) {
+            issue(st0, kc + 2);
+            vmem_wait_at_most<kIssued>();
+        } else {
+            vmem_wait_at_most<0>();
+        }
+        stage_barrier();
+        compute(st1);
+        stage_barrier();
+    }
+    if constexpr (MODE == 0) {
+        // up waves hand their values to the gate waves, 64 rows at a time
+        float *U = (float *)&st0;  // [64 rows][128 columns], 32 KB of the 40 KB stage
+        static_assert(sizeof(SgStage) >= 64 * 128 * sizeof(float), "exchange area");
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            if (wave >= 4) {
+#pragma unroll
+                for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        U[(qq * 32 + 8 * (v >> 2) + 4 * h + (v & 3)) * 128 + (wave & 3) * 32 + c] =
+                            tot[2 * half + qq][v];
+            }
+            block_lds_sync();
+            if (wave < 4) {
+#pragma unroll
+                for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int rl = qq * 32 + 8 * (v >> 2) + 4 * h + (v & 3), r = 64 * half + rl;
+                        if (m0 + r >= a.T) continue;
+                        const float hv = silu(tot[2 * half + qq][v]) * U[rl * 128 + wave * 32 + c];
+                        a.hs[(int64_t)(m0 + r) * a.Fs + blockIdx.x * 128 + wave * 32 + c] = bf16_rne(hv);
+                    }
+            }
+            block_lds_sync();
+        }
+    } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = q * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                if (m0 + r >= a.T) continue;
+                float *dst = a.y + (int64_t)(m0 + r) * a.D + blockIdx.x * 256 + wave * 32 + c;
+                *dst = a.accumulate ? *dst + tot[q][v] : tot[q][v];
+            }
+    }
+}
+
 bool prefill_path_ok(const moe_layer_desc *d, int32_t T, int32_t x_type) {
     return x_type == MOE_BF16 && T > 0 && d->gate_type == MOE_Q2K && d->down_type == MOE_Q2K &&
-           d->n_embd % 256 == 0 && d->n_ff_exp % 256 == 0;
+           d->n_embd % 256 == 0 && d->n_ff_exp % 256 == 0 &&
+           (d->n_ff_shared == 0 || (d->shared_type == MOE_Q8_0 && d->n_ff_shared % 128 == 0));
 }
 
 // stage 3: x codes, tiles, shared gate/up, routed gate/up; stage 4: h codes,
 // shared down, y init, routed down; 0: all
 hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, const RoutingPtrs &r, float *y,
                           uint32_t flags, const Workspace &ws, hipStream_t s, int stage) {
-    const int D = d->n_embd, F = d->n_ff_exp, k = d->n_expert_used, E = d->n_expert;
+    const int D = d->n_embd, F = d->n_ff_exp, k = d->n_expert_used, E = d->n_expert, Fs = d->n_ff_shared;
     const int ntmax = pf_max_tiles(T, k, E);
     static_assert(kPfM == kPfTileRows, "tile rows");
     const int64_t P = (int64_t)T * k;
@@ -475,9 +652,24 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, con
     if (stage == 0 || stage == 3) {
         pf_prep_rows_kernel<<<T, 256, 0, s>>>((const uint16_t *)x, D, ws.pf_xq, ws.pf_xs, ws.pf_xinv);
         pf_tiles_kernel<<<1, 64, 0, s>>>(r.active, r.n_active, r.count, r.offset, ws.pf_tiles, ws.pf_ntiles);
-        if (d->n_ff_shared > 0) {
-            hipError_t e = launch_ffn_large_shared(d, x, T, MOE_BF16, r, y, flags, ws, s, 3);
-            if (e != hipSuccess) return e;
+        if (Fs > 0) {
+            // shared weights split into bf16 halves, then the shared gate/up GEMM
+            const int64_t nw = (int64_t)Fs * D, nb = nw / 32;
+            uint16_t *hi = ws.pf_shw, *lo = ws.pf_shw + 3 * nw;
+            const unsigned g = (unsigned)((nb + 255) / 256);
+            pf_q8_split_kernel<<<g, 256, 0, s>>>((const uint8_t *)d->sh_gate, nb, hi, lo);
+            pf_q8_split_kernel<<<g, 256, 0, s>>>((const uint8_t *)d->sh_up, nb, hi + nw, lo + nw);
+            pf_q8_split_kernel<<<g, 256, 0, s>>>((const uint8_t *)d->sh_down, nb, hi + 2 * nw, lo + 2 * nw);
+            SgArgs sg{};
+            sg.a = (const uint16_t *)x;
+            sg.wh = hi;
+            sg.wl = lo;
+            sg.T = T;
+            sg.K = D;
+            sg.Fs = Fs;
+            sg.D = D;
+            sg.hs = ws.pf_hsb;
+            pf_sg_gemm_kernel<0><<<dim3(Fs / 128, (T + kSgM - 1) / kSgM), 512, 0, s>>>(sg);
         }
         PfArgs g = a;
         g.w0 = (const uint8_t *)d->gate;
@@ -490,13 +682,23 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, con
     }
     if (stage == 0 || stage == 4) {
         pf_prep_rows_kernel<<<(unsigned)P, 256, 0, s>>>(ws.pf_hb, F, ws.pf_hq, ws.pf_hs, ws.pf_hinv);
-        if (d->n_ff_shared > 0) {
-            hipError_t e = launch_ffn_large_shared(d, x, T, MOE_BF16, r, y, flags, ws, s, 4);
-            if (e != hipSuccess) return e;
+        if (Fs > 0) {
+            const int64_t nw = (int64_t)Fs * D;
+            SgArgs sg{};
+            sg.a = ws.pf_hsb;
+            sg.wh = ws.pf_shw + 2 * nw;
+            sg.wl = ws.pf_shw + 5 * nw;
+            sg.T = T;
+            sg.K = Fs;
+            sg.Fs = Fs;
+            sg.D = D;
+            sg.y = y;
+            sg.accumulate = (flags & MOE_ACCUMULATE) ? 1 : 0;
+            pf_sg_gemm_kernel<1><<<dim3(D / 256, (T + kSgM - 1) / kSgM), 512, 0, s>>>(sg);
+        } else if (!(flags & MOE_ACCUMULATE)) {
+            const int64_t n = (int64_t)T * D;
+            pf_y_init_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(nullptr, y, n, 0);
         }
-        const int64_t n = (int64_t)T * D;
-        pf_y_init_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(d->n_ff_shared > 0 ? ws.ys : nullptr, y, n,
-                                                                      (flags & MOE_ACCUMULATE) ? 1 : 0);
         PfArgs dn = a;
         dn.w0 = dn.w1 = (const uint8_t *)d->down;
         dn.n_in = F;

@@ -79,6 +79,32 @@ MOE_DEV void pf_dma16(const void *g, void *lds_wave) {
                      : "memory");
 }
 
+// a pointer that is the same in every lane, moved to scalar registers
+MOE_DEV const void *wave_uniform(const void *p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const void *)(((uint64_t)hi << 32) | lo);
+}
+
+// The same with a wave-uniform base in scalar registers and a 32-bit lane
+// offset.  The base usually comes from v_readfirstlane, and a VALU write of an
+// SGPR needs 5 wait states before a vector memory instruction reads that SGPR;
+// the compiler cannot see that the assembly is such an instruction, so the
+// wait states are part of it (s_nop 4 = 5, which also covers the m0 write).
+MOE_DEV void pf_dma16s(const void *base, uint32_t off, void *lds_wave) {
+    __asm__ volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %1, %2"
+                     :
+                     : "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave))), "v"(off), "s"(wave_uniform(base))
+                     : "memory");
+}
+
+MOE_DEV void pf_dma4s(const void *base, uint32_t off, void *lds_wave) {
+    __asm__ volatile("s_nop 4\n\tglobal_load_lds_dword %1, %2"
+                     :
+                     : "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave))), "v"(off), "s"(wave_uniform(base))
+                     : "memory");
+}
+
 MOE_DEV void pf_dma4(const void *g, void *lds_wave) {
     __asm__ volatile("s_nop 0\n\tglobal_load_lds_dword %1, off"
                      :
@@ -94,7 +120,15 @@ MOE_DEV void vmem_wait_at_most() {
     __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
-MOE_DEV uint16_t bf16_rne(float f) { return (uint16_t)float_to_bf16_bits(f); }
+// fp32 -> bf16, round to nearest even (the hardware conversion; inputs here
+// are finite)
+MOE_DEV uint16_t bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+MOE_DEV uint32_t bf16x2_rne(float lo, float hi) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){lo, hi}, b2));
+}
 
 // 16 activations -> t-ordered int8 halves (byte 4j+n of the unit holds value
 // 4n+j, the order the code dwords of a Q2K group take after >> 2j & 0x03030303)
@@ -248,7 +282,7 @@ __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
     // DMA sources, fixed over the columns (32-bit offsets from uniform bases)
     auto arow = [&](int r) { return MODE == 0 ? row_tok[r] : start + min(r, cnt - 1); };
     constexpr int kAI = kPfAUnits / kPfThreads, kSI = kPfSDwords / kPfThreads;
-    uint32_t aoff[kAI], soff[kSI], boff[kPfBI];
+    uint32_t aoff[kAI], soff[kSI];
 #pragma unroll
     for (int i = 0; i < kAI; ++i) {
         const int u = i * kPfThreads + tid, r = u >> 5;
@@ -261,35 +295,40 @@ __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
         soff[i] = (uint32_t)(arow(r) * nkb * 64 + unit * 16 + (q & 3) * 4);
     }
     const uint8_t *wb0 = a.w0 + (int64_t)e * a.expert_bytes, *wb1 = a.w1 + (int64_t)e * a.expert_bytes;
-    // staged row R: mode 0 rows < 128 are gate, the rest up; mode 1 all down
-    auto wrow = [&](int R) -> uint32_t { return (uint32_t)((o0 + (MODE == 0 ? (R & 127) : R)) * rowbytes); };
-    bool bup[kPfBI];
+    // Weight rows: each wave copies from one matrix (mode 0: waves 0-3 gate,
+    // 4-7 up, 128 rows each; mode 1: all waves down, 256 rows).  Per matrix
+    // the units (5 per row) are padded to whole wave copies; B index of unit
+    // (row, part) = mat * kBMatStride + 5 * row + part.
+    constexpr int kBMatRows = MODE == 0 ? 128 : 256;
+    constexpr int kBMatUnits = kBMatRows * 5;
+    constexpr int kBWavesPerMat = MODE == 0 ? 4 : 8;
+    constexpr int kBMatStride = kPfBI * 64 * kBWavesPerMat;
+    static_assert(kBMatUnits <= kBMatStride && kBMatStride * (8 / kBWavesPerMat) <= kPfBI * kPfThreads, "B stage");
+    const int bmat = MODE == 0 ? wave >> 2 : 0, bw = MODE == 0 ? (wave & 3) : wave;
+    const uint8_t *wbm = bmat ? wb1 : wb0;
+    uint32_t boff[kPfBI];
 #pragma unroll
-    for (int i = 0; i < kPfBI; ++i) {
-        const int u = min(i * kPfThreads + tid, kPfBRows * 5 - 1), R = u / 5, part = u % 5;
-        boff[i] = wrow(R) + 4 + 16 * part;
-        bup[i] = MODE == 0 && R >= 128;
+    for (int j = 0; j < kPfBI; ++j) {
+        const int idx = min((bw * kPfBI + j) * 64 + lane, kBMatUnits - 1), row = idx / 5, part = idx % 5;
+        boff[j] = (uint32_t)((o0 + row) * rowbytes) + 4 + 16 * part;
     }
-    const int ddr = tid & (kPfBRows - 1);
-    const uint32_t ddoff = wrow(ddr);
-    const bool ddup = MODE == 0 && ddr >= 128;
+    const uint32_t ddoff = (uint32_t)((o0 + ((bw * 64 + lane) & (kBMatRows - 1))) * rowbytes);
 
     auto issue = [&](PfStage &S, int kb) {
+        const uint8_t *ab = a.aq + kb * 512, *sb = (const uint8_t *)a.as + kb * 64, *wbk = wbm + kb * kQ2KBytes;
 #pragma unroll
-        for (int i = 0; i < kAI; ++i) pf_dma16(a.aq + aoff[i] + kb * 512, &S.a[i * kPfThreads + 64 * wave]);
+        for (int i = 0; i < kAI; ++i) pf_dma16s(ab, aoff[i], &S.a[i * kPfThreads + 64 * wave]);
 #pragma unroll
-        for (int i = 0; i < kSI; ++i)
-            pf_dma4((const uint8_t *)a.as + soff[i] + kb * 64, &S.s[i * kPfThreads + 64 * wave]);
+        for (int i = 0; i < kSI; ++i) pf_dma4s(sb, soff[i], &S.s[i * kPfThreads + 64 * wave]);
 #pragma unroll
-        for (int i = 0; i < kPfBI; ++i)
-            pf_dma16((bup[i] ? wb1 : wb0) + boff[i] + kb * kQ2KBytes, &S.b[i * kPfThreads + 64 * wave]);
-        pf_dma4((ddup ? wb1 : wb0) + ddoff + kb * kQ2KBytes, &S.dd[64 * wave]);
+        for (int j = 0; j < kPfBI; ++j) pf_dma16s(wbk, boff[j], &S.b[bmat * kBMatStride + (bw * kPfBI + j) * 64]);
+        pf_dma4s(wbk, ddoff, &S.dd[64 * wave]);
     };
     constexpr int kIssued = kAI + kSI + kPfBI + 1;
 
     const int nsub = cnt > 32 ? 2 : 1;
-    // this wave's weight rows in the stage
-    const int R = MODE == 0 ? (wave >> 2) * 128 + (wave & 3) * 32 + c : wave * 32 + c;
+    // this wave's weight rows in the stage: matrix and row within it
+    const int Rmat = MODE == 0 ? wave >> 2 : 0, Rrow = MODE == 0 ? (wave & 3) * 32 + c : wave * 32 + c;
     v16f tot[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q)
@@ -301,10 +340,10 @@ __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
     auto compute = [&](PfStage &S) {
         v4i bq[8];
         uint32_t bmh[4], bml[4];
-        const uint8_t *rb = (const uint8_t *)&S.b[R * 5];
+        const uint8_t *rb = (const uint8_t *)&S.b[Rmat * kBMatStride + 5 * Rrow];
         const uint2 sm = *(const uint2 *)(rb + 8 * h);
         const u32x4 q0 = *(const u32x4 *)(rb + 16 + 32 * h), q1 = *(const u32x4 *)(rb + 32 + 32 * h);
-        const uint32_t dd = S.dd[R];
+        const uint32_t dd = S.dd[Rmat * 256 + Rrow];
         const float dsc = half_bits_to_float(dd), dmin = half_bits_to_float(dd >> 16);
 #pragma unroll
         for (int p = 0; p < 8; ++p) {
@@ -313,21 +352,16 @@ __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) bq[p][j] = (int)mul_bytes((Q >> (2 * j)) & 0x03030303u, sc);
         }
+        // -dmin * m_g of the lane's 8 groups, exactly as bf16 hi + lo
+        const uint32_t mA = (sm.x >> 4) & 0x0F0F0F0Fu, mB = (sm.y >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            uint32_t hw = 0, lw = 0;
-#pragma unroll
-            for (int z = 0; z < 2; ++z) {
-                const int gi = 2 * i + z;
-                const uint32_t m = ((gi < 4 ? sm.x : sm.y) >> (8 * (gi & 3) + 4)) & 15u;
-                const float cf = -(dmin * (float)m);
-                const uint16_t hb = bf16_rne(cf);
-                const uint16_t lb = bf16_rne(cf - bf16_bits_to_float(hb));
-                hw |= (uint32_t)hb << (16 * z);
-                lw |= (uint32_t)lb << (16 * z);
-            }
+            const uint32_t mw = i < 2 ? mA : mB;
+            const float c0 = -dmin * (float)((mw >> (16 * (i & 1))) & 0xFFu);
+            const float c1 = -dmin * (float)((mw >> (16 * (i & 1) + 8)) & 0xFFu);
+            const uint32_t hw = bf16x2_rne(c0, c1);
             bmh[i] = hw;
-            bml[i] = lw;
+            bml[i] = bf16x2_rne(c0 - __uint_as_float(hw << 16), c1 - __uint_as_float(hw & 0xFFFF0000u));
         }
         const u32x4 *abase[2][4];
 #pragma unroll

@@ -15,6 +15,7 @@
 // c = 256*hi + lo (two int8 passes).  The integer result, exact in int32, is
 // scaled by d in fp32.  The second sum runs on v_mfma_f32_32x32x16_bf16 with
 // dmin*m (exact as a bf16 pair) against the group sums (a bf16 pair).
+#include <cstddef>
 #include <type_traits>
 
 #include "ffn_dev.h"
@@ -29,22 +30,28 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 constexpr int kPfM = 64;                // pair rows per tile
 constexpr int kPfWaves = 8;
 constexpr int kPfThreads = 64 * kPfWaves;
-constexpr int kPfBRows = 256;           // weight rows staged per super-block column
-constexpr int kPfAUnits = kPfM * 32;    // 16-byte units of codes per column: hi 16 + lo 16 per row
+constexpr int kPfWaveRows = 64;         // weight rows per wave (two 32-column MFMA subtiles)
+constexpr int kPfBRows = kPfWaveRows * kPfWaves;  // weight rows staged per super-block column
+constexpr int kPfARow = 33;             // 16-byte units per code row in LDS: hi 16 + lo 16 + 1 pad
+constexpr int kPfAUnits = kPfM * kPfARow;
 constexpr int kPfSDwords = kPfM * 16;   // group sums: 8 dwords sH + 8 dwords sL per row
 constexpr float kPfCodeMax = 32512.f;   // |c| <= 32512 keeps hi in [-127, 127]
 
+// 4-unit rows (64 bytes): distinct banks for 8 and for 16 consecutive rows
+MOE_DEV int sum_swz(int r) { return ((r >> 1) + (r >> 3)) & 3; }
+
 // One super-block column in LDS.  Codes of row r, unit u (0..15 hi, 16..31
-// lo) sit at a[r*32 + (u ^ (r & 7))]; group sums of row r, unit u (0, 1 sH;
-// 2, 3 sL) at s[4*(r*4 + (u ^ ((r >> 1) & 3)))...]; weight row R: scale
-// bytes and codes (the 80 bytes after d, dmin) at b[5R..5R+4], d and dmin at
-// dd[R].  The XOR swizzles keep 8 consecutive rows on distinct LDS banks.
-constexpr int kPfBI = (kPfBRows * 5 + kPfThreads - 1) / kPfThreads;  // B units per thread (padded)
+// lo) sit at a[33 r + u] (one pad unit per row); group sums of row r, unit u
+// (0, 1 sH; 2, 3 sL) at s[4*(r*4 + (u ^ sum_swz(r)))...]; staged weight row R
+// (wave R / 64 copies rows 64w..64w+63): scale bytes and codes (the 80 bytes
+// after d, dmin) at b[5R..5R+4], d and dmin at dd[R].  The pad and the
+// swizzle put the 16-byte reads of 16 consecutive rows on distinct banks
+// (and of any 8 consecutive rows).
 struct PfStage {
     u32x4 a[kPfAUnits];
     uint32_t s[kPfSDwords];
-    u32x4 b[kPfBI * kPfThreads];    // rows past kPfBRows: padding the DMA fills with copies
-    uint32_t dd[kPfThreads];        // entries past kPfBRows: padding
+    u32x4 b[kPfBRows * 5];
+    uint32_t dd[kPfBRows];
 };
 
 struct PfArgs {
@@ -103,6 +110,15 @@ MOE_DEV void pf_dma4s(const void *base, uint32_t off, void *lds_wave) {
                      :
                      : "{m0}"(__builtin_amdgcn_readfirstlane(lds_addr(lds_wave))), "v"(off), "s"(wave_uniform(base))
                      : "memory");
+}
+
+// the same with the LDS address (m0) already wave-uniform
+MOE_DEV void pf_dma16u(const void *base, uint32_t off, uint32_t m0) {
+    __asm__ volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %1, %2" : : "{m0}"(m0), "v"(off), "s"(base) : "memory");
+}
+
+MOE_DEV void pf_dma4u(const void *base, uint32_t off, uint32_t m0) {
+    __asm__ volatile("s_nop 4\n\tglobal_load_lds_dword %1, %2" : : "{m0}"(m0), "v"(off), "s"(base) : "memory");
 }
 
 MOE_DEV void pf_dma4(const void *g, void *lds_wave) {
@@ -206,17 +222,28 @@ __global__ void __launch_bounds__(256) pf_prep_rows_kernel(const uint16_t *x, in
     }
 }
 
-// Tiles of at most 64 pairs over the active experts, ascending expert id.
-__global__ void pf_tiles_kernel(const int32_t *active, const int32_t *n_active, const int32_t *count,
-                                const int32_t *offset, int4 *tiles, int32_t *n_tiles) {
-    if (threadIdx.x != 0) return;
-    const int n = n_active[0];
-    int nt = 0;
-    for (int i = 0; i < n; ++i) {
-        const int e = active[i], c = count[e], o = offset[e];
-        for (int s = 0; s < c; s += kPfM) tiles[nt++] = make_int4(e, o + s, min(kPfM, c - s), 0);
+// Tiles of at most 64 pairs over the active experts, ascending expert id:
+// one wave, 64 experts at a time, tile offsets by a prefix sum over lanes.
+__global__ void __launch_bounds__(64) pf_tiles_kernel(const int32_t *active, const int32_t *n_active,
+                                                      const int32_t *count, const int32_t *offset, int4 *tiles,
+                                                      int32_t *n_tiles) {
+    const int lane = threadIdx.x, n = n_active[0];
+    int base = 0;
+    for (int i0 = 0; i0 < n; i0 += 64) {
+        const int i = i0 + lane;
+        const int e = i < n ? active[i] : 0, c = i < n ? count[e] : 0, o = i < n ? offset[e] : 0;
+        const int nt = (c + kPfM - 1) / kPfM;
+        int incl = nt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(incl, d, kWave);
+            if (lane >= d) incl += v;
+        }
+        const int first = base + incl - nt;
+        for (int t = 0; t < nt; ++t) tiles[first + t] = make_int4(e, o + t * kPfM, min(kPfM, c - t * kPfM), 0);
+        base += __shfl(incl, 63, kWave);
     }
-    n_tiles[0] = nt;
+    if (lane == 0) n_tiles[0] = base;
 }
 
 // y = ys (+ y when accumulating), or 0 / y without a shared expert: the
@@ -253,22 +280,39 @@ MOE_DEV void stage_barrier() {
     __asm__ volatile("" ::: "memory");
 }
 
-// Mode 0: blockIdx.x = 128 F-rows; wave w < 4 owns gate rows 32w..32w+31,
-// wave w >= 4 the same rows of up; writes h = silu(g) * u in bf16.  Mode 1:
-// blockIdx.x = 256 D-columns, wave w owns columns 32w..32w+31; adds
-// w * y_pair into y.  blockIdx.y = tile.
+// Mode 0: a column block is 128 F-rows; wave w < 4 owns gate rows
+// 32w..32w+31, wave w >= 4 the same rows of up; writes h = silu(g) * u in
+// bf16.  Mode 1: a column block is 256 D-columns, wave w owns columns
+// 32w..32w+31; adds w * y_pair into y.
+// Linear block id -> (tile, column block), so that the column blocks of one
+// tile run on one XCD (blocks go round-robin to the 8 XCDs): its activation
+// rows are then fetched into that XCD's L2 once instead of into all of them.
+// nb = column blocks per tile; the grid holds 8 * ceil(tiles / 8) * nb blocks.
+MOE_DEV void xcd_tile_map(int L, int nb, int &tile, int &col) {
+    const int xcd = L & 7, j = L >> 3;
+    tile = xcd + 8 * (j / nb);
+    col = j % nb;
+}
+
+// Mode 0: a column block is 256 F-rows; wave w < 4 owns gate rows
+// 64w..64w+63, wave w >= 4 the same rows of up; writes h = silu(g) * u in
+// bf16.  Mode 1: a column block is 512 D-columns, wave w owns columns
+// 64w..64w+63; adds w * y_pair into y.
 template <int MODE>
 __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
     __shared__ PfStage st0, st1;
     __shared__ int32_t row_tok[kPfM];
     __shared__ float row_f[kPfM];
-    const int tile = blockIdx.y;
+    constexpr int kColRows = MODE == 0 ? kPfBRows / 2 : kPfBRows;  // output columns per block
+    const int nb = (MODE == 0 ? a.F : a.D) / kColRows;
+    int tile, colblk;
+    xcd_tile_map(blockIdx.x, nb, tile, colblk);
     if (tile >= a.n_tiles[0]) return;
     const int4 ti = a.tiles[tile];
     const int e = ti.x, start = ti.y, cnt = ti.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, c = lane & 31, h = lane >> 5;
     const int nkb = a.n_in >> 8;
-    const int o0 = blockIdx.x * (MODE == 0 ? 128 : 256);
+    const int o0 = colblk * kColRows;
     const int64_t rowbytes = (int64_t)nkb * kQ2KBytes;
 
     if (tid < kPfM) {
@@ -279,147 +323,156 @@ __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
     }
     block_lds_sync();
 
-    // DMA sources, fixed over the columns (32-bit offsets from uniform bases)
+    // DMA sources, fixed over the columns (32-bit offsets from uniform bases).
+    // Code rows: 33 wave copies of 64 units; wave w takes copies w, w+8,
+    // w+16, w+24 and wave 0 also copy 32; a pad unit loads a copy of unit 31.
     auto arow = [&](int r) { return MODE == 0 ? row_tok[r] : start + min(r, cnt - 1); };
-    constexpr int kAI = kPfAUnits / kPfThreads, kSI = kPfSDwords / kPfThreads;
+    constexpr int kACopies = kPfAUnits / 64, kAI = kACopies / kPfWaves + 1, kSI = kPfSDwords / kPfThreads;
+    static_assert(kACopies == 4 * kPfWaves + 1, "A copies");
     uint32_t aoff[kAI], soff[kSI];
 #pragma unroll
     for (int i = 0; i < kAI; ++i) {
-        const int u = i * kPfThreads + tid, r = u >> 5;
-        aoff[i] = (uint32_t)(arow(r) * nkb * 512 + (((u & 31) ^ (r & 7)) * 16));
+        const int L = min((i * kPfWaves + wave) * 64 + lane, kPfAUnits - 1), r = L / kPfARow, u = min(L % kPfARow, 31);
+        aoff[i] = (uint32_t)(arow(r) * nkb * 512 + u * 16);
     }
 #pragma unroll
     for (int i = 0; i < kSI; ++i) {
         const int q = i * kPfThreads + tid, r = q >> 4;
-        const int unit = ((q >> 2) & 3) ^ ((r >> 1) & 3);
+        const int unit = ((q >> 2) & 3) ^ sum_swz(r);
         soff[i] = (uint32_t)(arow(r) * nkb * 64 + unit * 16 + (q & 3) * 4);
     }
-    const uint8_t *wb0 = a.w0 + (int64_t)e * a.expert_bytes, *wb1 = a.w1 + (int64_t)e * a.expert_bytes;
-    // Weight rows: each wave copies from one matrix (mode 0: waves 0-3 gate,
-    // 4-7 up, 128 rows each; mode 1: all waves down, 256 rows).  Per matrix
-    // the units (5 per row) are padded to whole wave copies; B index of unit
-    // (row, part) = mat * kBMatStride + 5 * row + part.
-    constexpr int kBMatRows = MODE == 0 ? 128 : 256;
-    constexpr int kBMatUnits = kBMatRows * 5;
-    constexpr int kBWavesPerMat = MODE == 0 ? 4 : 8;
-    constexpr int kBMatStride = kPfBI * 64 * kBWavesPerMat;
-    static_assert(kBMatUnits <= kBMatStride && kBMatStride * (8 / kBWavesPerMat) <= kPfBI * kPfThreads, "B stage");
-    const int bmat = MODE == 0 ? wave >> 2 : 0, bw = MODE == 0 ? (wave & 3) : wave;
-    const uint8_t *wbm = bmat ? wb1 : wb0;
-    uint32_t boff[kPfBI];
+    // Weight rows: wave w copies its own 64 rows (5 units each = 5 copies of
+    // 64 units) and their d, dmin (one copy); mode 0 waves 0-3 from gate,
+    // 4-7 from up.
+    const int wrow0 = MODE == 0 ? (wave & 3) * kPfWaveRows : wave * kPfWaveRows;  // first row in its matrix block
+    const uint8_t *wbm = (MODE == 0 && wave >= 4 ? a.w1 : a.w0) + (int64_t)e * a.expert_bytes;
+    uint32_t boff[5];
 #pragma unroll
-    for (int j = 0; j < kPfBI; ++j) {
-        const int idx = min((bw * kPfBI + j) * 64 + lane, kBMatUnits - 1), row = idx / 5, part = idx % 5;
-        boff[j] = (uint32_t)((o0 + row) * rowbytes) + 4 + 16 * part;
+    for (int j = 0; j < 5; ++j) {
+        const int idx = j * 64 + lane, row = idx / 5, part = idx % 5;
+        boff[j] = (uint32_t)((o0 + wrow0 + row) * rowbytes) + 4 + 16 * part;
     }
-    const uint32_t ddoff = (uint32_t)((o0 + ((bw * 64 + lane) & (kBMatRows - 1))) * rowbytes);
+    const uint32_t ddoff = (uint32_t)((o0 + wrow0 + lane) * rowbytes);
 
-    auto issue = [&](PfStage &S, int kb) {
-        const uint8_t *ab = a.aq + kb * 512, *sb = (const uint8_t *)a.as + kb * 64, *wbk = wbm + kb * kQ2KBytes;
+    // uniform (scalar) DMA operands: stage LDS addresses, this wave's
+    // destinations within a stage, the weight base of this wave's rows
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    const uint32_t lds_st[2] = {(uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(&st0)),
+                                (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(&st1))};
+    const uint8_t *wbm_u = (const uint8_t *)wave_uniform(wbm);
+    auto issue = [&](int st, int kb) {
+        const uint8_t *ab = a.aq + kb * 512, *sb = (const uint8_t *)a.as + kb * 64, *wbk = wbm_u + kb * kQ2KBytes;
+        const uint32_t L = lds_st[st];
 #pragma unroll
-        for (int i = 0; i < kAI; ++i) pf_dma16s(ab, aoff[i], &S.a[i * kPfThreads + 64 * wave]);
+        for (int i = 0; i < kAI - 1; ++i)
+            pf_dma16u(ab, aoff[i], L + (uint32_t)offsetof(PfStage, a) + (uint32_t)((i * kPfWaves + wv) * 64 * 16));
+        if (wv == 0) pf_dma16u(ab, aoff[kAI - 1], L + (uint32_t)offsetof(PfStage, a) + (uint32_t)((kACopies - 1) * 64 * 16));
 #pragma unroll
-        for (int i = 0; i < kSI; ++i) pf_dma4s(sb, soff[i], &S.s[i * kPfThreads + 64 * wave]);
+        for (int i = 0; i < kSI; ++i)
+            pf_dma4u(sb, soff[i], L + (uint32_t)offsetof(PfStage, s) + (uint32_t)((i * kPfThreads + 64 * wv) * 4));
 #pragma unroll
-        for (int j = 0; j < kPfBI; ++j) pf_dma16s(wbk, boff[j], &S.b[bmat * kBMatStride + (bw * kPfBI + j) * 64]);
-        pf_dma4s(wbk, ddoff, &S.dd[64 * wave]);
+        for (int j = 0; j < 5; ++j)
+            pf_dma16u(wbk, boff[j], L + (uint32_t)offsetof(PfStage, b) + (uint32_t)((wv * kPfWaveRows * 5 + j * 64) * 16));
+        pf_dma4u(wbk, ddoff, L + (uint32_t)offsetof(PfStage, dd) + (uint32_t)(wv * kPfWaveRows * 4));
     };
-    constexpr int kIssued = kAI + kSI + kPfBI + 1;
+    constexpr int kIssued = (kAI - 1) + kSI + 5 + 1;  // wave 0: one more
+    auto wait_stage = [&]() {
+        if (wave == 0) vmem_wait_at_most<kIssued + 1>();
+        else vmem_wait_at_most<kIssued>();
+    };
 
     const int nsub = cnt > 32 ? 2 : 1;
-    // this wave's weight rows in the stage: matrix and row within it
-    const int Rmat = MODE == 0 ? wave >> 2 : 0, Rrow = MODE == 0 ? (wave & 3) * 32 + c : wave * 32 + c;
-    v16f tot[2];
+    v16f tot[2][2];  // [column subtile][row subtile]
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int n = 0; n < 2; ++n)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) tot[q][v] = 0.f;
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) tot[n][q][v] = 0.f;
 
     auto run = [&](auto nsub_c) {
     constexpr int NSUB = decltype(nsub_c)::value;
     auto compute = [&](PfStage &S) {
-        v4i bq[8];
-        uint32_t bmh[4], bml[4];
-        const uint8_t *rb = (const uint8_t *)&S.b[Rmat * kBMatStride + 5 * Rrow];
-        const uint2 sm = *(const uint2 *)(rb + 8 * h);
-        const u32x4 q0 = *(const u32x4 *)(rb + 16 + 32 * h), q1 = *(const u32x4 *)(rb + 32 + 32 * h);
-        const uint32_t dd = S.dd[Rmat * 256 + Rrow];
-        const float dsc = half_bits_to_float(dd), dmin = half_bits_to_float(dd >> 16);
+        // unit 16*pass + 2p + h of row q*32 + c: constant offsets from abase
+        const u32x4 *abase = &S.a[c * kPfARow + h];
 #pragma unroll
-        for (int p = 0; p < 8; ++p) {
-            const uint32_t Q = p < 4 ? q0[p] : q1[p - 4];
-            const uint32_t sc = ((p < 4 ? sm.x : sm.y) >> (8 * (p & 3))) & 15u;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) bq[p][j] = (int)mul_bytes((Q >> (2 * j)) & 0x03030303u, sc);
-        }
-        // -dmin * m_g of the lane's 8 groups, exactly as bf16 hi + lo
-        const uint32_t mA = (sm.x >> 4) & 0x0F0F0F0Fu, mB = (sm.y >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t mw = i < 2 ? mA : mB;
-            const float c0 = -dmin * (float)((mw >> (16 * (i & 1))) & 0xFFu);
-            const float c1 = -dmin * (float)((mw >> (16 * (i & 1) + 8)) & 0xFFu);
-            const uint32_t hw = bf16x2_rne(c0, c1);
-            bmh[i] = hw;
-            bml[i] = bf16x2_rne(c0 - __uint_as_float(hw << 16), c1 - __uint_as_float(hw & 0xFFFF0000u));
-        }
-        const u32x4 *abase[2][4];
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            const int row = q * 32 + c;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) abase[q][j] = &S.a[row * 32 + ((2 * j + h) ^ (row & 7))];
-        }
-        // two independent accumulation chains, one per subtile
-        v16i acc[2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) acc[q][v] = 0;
-#pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-            if (pass == 1) {
-#pragma unroll
-                for (int q = 0; q < 2; ++q)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) acc[q][v] <<= 8;
-            }
+        for (int n = 0; n < 2; ++n) {
+            // keep the two column subtiles apart in the schedule (registers)
+            __builtin_amdgcn_sched_barrier(0);
+            const int R = wave * kPfWaveRows + 32 * n + c;
+            v4i bq[8];
+            uint32_t bmh[4], bml[4];
+            const uint8_t *rb = (const uint8_t *)&S.b[R * 5];
+            const uint2 sm = *(const uint2 *)(rb + 8 * h);
+            const u32x4 q0 = *(const u32x4 *)(rb + 16 + 32 * h), q1 = *(const u32x4 *)(rb + 32 + 32 * h);
+            const uint32_t dd = S.dd[R];
+            const float dsc = half_bits_to_float(dd), dmin = half_bits_to_float(dd >> 16);
 #pragma unroll
             for (int p = 0; p < 8; ++p) {
+                const uint32_t Q = p < 4 ? q0[p] : q1[p - 4];
+                const uint32_t sc = ((p < 4 ? sm.x : sm.y) >> (8 * (p & 3))) & 15u;
 #pragma unroll
-                for (int q = 0; q < NSUB; ++q) {
-                    // unit 16*pass + 2p + h of row q*32 + c: the swizzle only
-                    // permutes within aligned groups of 8 units, so p + 4 and
-                    // the lo half are constant byte offsets from abase
-                    const u32x4 av = *(const u32x4 *)((const uint8_t *)abase[q][p & 3] + 128 * (p >> 2) + 256 * pass);
-                    v4i ai;
-                    __builtin_memcpy(&ai, &av, 16);
-                    acc[q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ai, bq[p], acc[q], 0, 0, 0);
+                for (int j = 0; j < 4; ++j) bq[p][j] = (int)mul_bytes((Q >> (2 * j)) & 0x03030303u, sc);
+            }
+            // -dmin * m_g of the lane's 8 groups, exactly as bf16 hi + lo
+            const uint32_t mA = (sm.x >> 4) & 0x0F0F0F0Fu, mB = (sm.y >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t mw = i < 2 ? mA : mB;
+                const float c0 = -dmin * (float)((mw >> (16 * (i & 1))) & 0xFFu);
+                const float c1 = -dmin * (float)((mw >> (16 * (i & 1) + 8)) & 0xFFu);
+                const uint32_t hw = bf16x2_rne(c0, c1);
+                bmh[i] = hw;
+                bml[i] = bf16x2_rne(c0 - __uint_as_float(hw << 16), c1 - __uint_as_float(hw & 0xFFFF0000u));
+            }
+            // two independent accumulation chains, one per row subtile
+            v16i acc[2];
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[q][v] = 0;
+#pragma unroll
+            for (int pass = 0; pass < 2; ++pass) {
+                if (pass == 1) {
+#pragma unroll
+                    for (int q = 0; q < NSUB; ++q)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) acc[q][v] <<= 8;
+                }
+#pragma unroll
+                for (int p = 0; p < 8; ++p) {
+#pragma unroll
+                    for (int q = 0; q < NSUB; ++q) {
+                        const u32x4 av = abase[32 * kPfARow * q + 16 * pass + 2 * p];
+                        v4i ai;
+                        __builtin_memcpy(&ai, &av, 16);
+                        acc[q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ai, bq[p], acc[q], 0, 0, 0);
+                    }
                 }
             }
-        }
-        const v8bf ch = as_v8bf(bmh), cl = as_v8bf(bml);
+            const v8bf ch = as_v8bf(bmh), cl = as_v8bf(bml);
 #pragma unroll
-        for (int q = 0; q < NSUB; ++q) {
+            for (int q = 0; q < NSUB; ++q) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) tot[q][v] = __builtin_fmaf((float)acc[q][v], dsc, tot[q][v]);
-            const int row = q * 32 + c, sw = (row >> 1) & 3;
-            const u32x4 shu = *(const u32x4 *)&S.s[4 * (row * 4 + (h ^ sw))];
-            const u32x4 slu = *(const u32x4 *)&S.s[4 * (row * 4 + ((2 + h) ^ sw))];
-            v8bf sh, sl;
-            __builtin_memcpy(&sh, &shu, 16);
-            __builtin_memcpy(&sl, &slu, 16);
-            tot[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sh, ch, tot[q], 0, 0, 0);
-            tot[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sl, ch, tot[q], 0, 0, 0);
-            tot[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sh, cl, tot[q], 0, 0, 0);
+                for (int v = 0; v < 16; ++v) tot[n][q][v] = __builtin_fmaf((float)acc[q][v], dsc, tot[n][q][v]);
+                const int row = q * 32 + c, sw = sum_swz(row);
+                const u32x4 shu = *(const u32x4 *)&S.s[4 * (row * 4 + (h ^ sw))];
+                const u32x4 slu = *(const u32x4 *)&S.s[4 * (row * 4 + ((2 + h) ^ sw))];
+                v8bf sh, sl;
+                __builtin_memcpy(&sh, &shu, 16);
+                __builtin_memcpy(&sl, &slu, 16);
+                tot[n][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sh, ch, tot[n][q], 0, 0, 0);
+                tot[n][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sl, ch, tot[n][q], 0, 0, 0);
+                tot[n][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sh, cl, tot[n][q], 0, 0, 0);
+            }
         }
     };
 
-    issue(st0, 0);
+    issue(0, 0);
     for (int kb = 0; kb < nkb; kb += 2) {
         if (kb + 1 < nkb) {
-            issue(st1, kb + 1);
-            vmem_wait_at_most<kIssued>();
+            issue(1, kb + 1);
+            wait_stage();
         } else {
             vmem_wait_at_most<0>();
         }
@@ -428,8 +481,8 @@ __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
         stage_barrier();
         if (kb + 1 >= nkb) break;
         if (kb + 2 < nkb) {
-            issue(st0, kb + 2);
-            vmem_wait_at_most<kIssued>();
+            issue(0, kb + 2);
+            wait_stage();
         } else {
             vmem_wait_at_most<0>();
         }
@@ -443,43 +496,51 @@ __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
 
     if constexpr (MODE == 0) {
         // up waves hand their values to the gate waves of the same rows
-        float *U = (float *)&st0;  // [64 rows][128 columns]
-        static_assert(sizeof(PfStage) >= kPfM * 128 * sizeof(float), "exchange area");
+        float *U = (float *)&st0;  // [64 rows][256 columns]
+        static_assert(sizeof(PfStage) >= kPfM * 256 * sizeof(float), "exchange area");
         if (wave >= 4) {
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                if (q == 1 && nsub < 2) continue;
+            for (int n = 0; n < 2; ++n)
 #pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    U[(q * 32 + 8 * (v >> 2) + 4 * h + (v & 3)) * 128 + (wave & 3) * 32 + c] = tot[q][v];
-            }
+                for (int q = 0; q < 2; ++q) {
+                    if (q == 1 && nsub < 2) continue;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        U[(q * 32 + 8 * (v >> 2) + 4 * h + (v & 3)) * 256 + (wave & 3) * 64 + 32 * n + c] = tot[n][q][v];
+                }
         }
         block_lds_sync();
         if (wave < 4) {
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    if (q == 1 && nsub < 2) continue;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int r = q * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+                        if (r >= cnt) continue;
+                        const float f = row_f[r];
+                        const int col = wave * 64 + 32 * n + c;
+                        const float hv = silu(tot[n][q][v] * f) * (U[r * 256 + col] * f);
+                        a.hb[(int64_t)(start + r) * a.F + o0 + col] = bf16_rne(hv);
+                    }
+                }
+        }
+    } else {
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 if (q == 1 && nsub < 2) continue;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int r = q * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                    if (r >= cnt) continue;
-                    const float f = row_f[r];
-                    const float hv = silu(tot[q][v] * f) * (U[r * 128 + wave * 32 + c] * f);
-                    a.hb[(int64_t)(start + r) * a.F + o0 + wave * 32 + c] = bf16_rne(hv);
+                    if (r < cnt)
+                        unsafeAtomicAdd(&a.y[(int64_t)row_tok[r] * a.D + o0 + wave * 64 + 32 * n + c],
+                                        row_f[r] * tot[n][q][v]);
                 }
             }
-        }
-    } else {
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            if (q == 1 && nsub < 2) continue;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int r = q * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                if (r < cnt)
-                    unsafeAtomicAdd(&a.y[(int64_t)row_tok[r] * a.D + o0 + wave * 32 + c], row_f[r] * tot[q][v]);
-            }
-        }
     }
 }
 
@@ -523,7 +584,7 @@ constexpr int kSgKc = 32;            // reduction columns per stage
 constexpr int kSgRowUnits = kSgKc * 2 / 16;   // 16-byte units per row per stage (4)
 
 struct SgStage {
-    u32x4 a[kSgM * kSgRowUnits];       // activation rows: unit u of row r at r*4 + (u ^ ((r >> 1) & 3))
+    u32x4 a[kSgM * kSgRowUnits];       // activation rows: unit u of row r at r*4 + (u ^ sum_swz(r))
     u32x4 bh[256 * kSgRowUnits];       // weight rows, hi halves, same swizzle
     u32x4 bl[256 * kSgRowUnits];       // lo halves
 };
@@ -537,7 +598,7 @@ struct SgArgs {
     int accumulate;
 };
 
-MOE_DEV int sg_unit(int r, int u) { return r * kSgRowUnits + (u ^ ((r >> 1) & 3)); }
+MOE_DEV int sg_unit(int r, int u) { return r * kSgRowUnits + (u ^ sum_swz(r)); }
 
 // Mode 0: blockIdx.x = 128 F-rows (waves 0-3 gate, 4-7 up), writes bf16
 // h = silu(g) * u.  Mode 1: blockIdx.x = 256 D-columns, y = (y if
@@ -555,12 +616,12 @@ __global__ void __launch_bounds__(512) pf_sg_gemm_kernel(SgArgs a) {
     // one 16-byte unit per thread for A (512 units), two for each weight half (1024 units)
     static_assert(kSgM * kSgRowUnits == 512 && 256 * kSgRowUnits == 1024, "stage shape");
     const int ar = tid >> 2;
-    const uint16_t *asrc = a.a + (int64_t)min(m0 + ar, a.T - 1) * a.K + 8 * ((tid & 3) ^ ((ar >> 1) & 3));
+    const uint16_t *asrc = a.a + (int64_t)min(m0 + ar, a.T - 1) * a.K + 8 * ((tid & 3) ^ sum_swz(ar));
     int64_t boff[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int u = i * 512 + tid, R = u >> 2;
-        boff[i] = wrow(R) * a.K + 8 * ((u & 3) ^ ((R >> 1) & 3));
+        boff[i] = wrow(R) * a.K + 8 * ((u & 3) ^ sum_swz(R));
     }
     auto issue = [&](SgStage &S, int kc) {
         pf_dma16(asrc + kc * kSgKc, &S.a[64 * wave]);
@@ -660,7 +721,7 @@ __global__ void __launch_bounds__(512) pf_sg_gemm_kernel(SgArgs a) {
 
 bool prefill_path_ok(const moe_layer_desc *d, int32_t T, int32_t x_type) {
     return x_type == MOE_BF16 && T > 0 && d->gate_type == MOE_Q2K && d->down_type == MOE_Q2K &&
-           d->n_embd % 256 == 0 && d->n_ff_exp % 256 == 0 &&
+           d->n_embd % 512 == 0 && d->n_ff_exp % 256 == 0 &&
            (d->n_ff_shared == 0 || (d->shared_type == MOE_Q8_0 && d->n_ff_shared % 128 == 0));
 }
 
@@ -712,7 +773,7 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, con
         g.aq = ws.pf_xq;
         g.as = ws.pf_xs;
         g.ainv = ws.pf_xinv;
-        pf_gemm_kernel<0><<<dim3(F / 128, ntmax), kPfThreads, 0, s>>>(g);
+        pf_gemm_kernel<0><<<(unsigned)(((ntmax + 7) / 8) * 8 * (F / 256)), kPfThreads, 0, s>>>(g);
     }
     if (stage == 0 || stage == 4) {
         pf_prep_rows_kernel<<<(unsigned)P, 256, 0, s>>>(ws.pf_hb, F, ws.pf_hq, ws.pf_hs, ws.pf_hinv);
@@ -739,7 +800,7 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, con
         dn.aq = ws.pf_hq;
         dn.as = ws.pf_hs;
         dn.ainv = ws.pf_hinv;
-        pf_gemm_kernel<1><<<dim3(D / 256, ntmax), kPfThreads, 0, s>>>(dn);
+        pf_gemm_kernel<1><<<(unsigned)(((ntmax + 7) / 8) * 8 * (D / 512)), kPfThreads, 0, s>>>(dn);
     }
     return hipGetLastError();
 }

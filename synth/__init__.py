@@ -260,6 +260,32 @@ def stack_layer(l, cb, nthreads=None, E=None):
                       down_fmt=Q2K, shared_fmt=Q8_0, cb=cb, gamma=True, nthreads=nthreads)
 
 
+def stack_layer_sampled(l, cb, nthreads=None):
+    """One block of the stack with every expert and shared tensor drawn as
+    random codes (sampled_tensor: each field uniform, block scales set for a
+    weight spread near the N(0, 0.02) of the quantized recipe): the formats,
+    shapes and byte counts of stack_layer without running the encoders (the
+    codebook encoder takes minutes per full layer).  Router and RMSNorm
+    weights as in stack_layer."""
+    s = DS4_FLASH
+    D, E, k, F, Fs = s["D"], s["E"], s["k"], s["F"], s["Fs"]
+    nt = nthreads or default_threads()
+    L = Layer(
+        n_embd=D, n_expert=E, n_expert_used=k, n_ff_exp=F, n_ff_shared=Fs,
+        gate_fmt=CB2, up_fmt=CB2, down_fmt=Q2K, shared_fmt=Q8_0,
+        router_w=normal(4, l, TAG_ROUTER, 0, D * E, WEIGHT_SIGMA).reshape(E, D),
+        gate=sampled_tensor(CB2, 4, l, TAG_GATE, E, F, D, codebook=cb, nthreads=nt),
+        up=sampled_tensor(CB2, 4, l, TAG_UP, E, F, D, codebook=cb, nthreads=nt),
+        down=sampled_tensor(Q2K, 4, l, TAG_DOWN, E, D, F, nthreads=nt),
+        codebook=cb,
+    )
+    L.sh_gate = sampled_tensor(Q8_0, 4, l, TAG_SH_GATE, 1, Fs, D, nthreads=nt)
+    L.sh_up = sampled_tensor(Q8_0, 4, l, TAG_SH_UP, 1, Fs, D, nthreads=nt)
+    L.sh_down = sampled_tensor(Q8_0, 4, l, TAG_SH_DOWN, 1, D, Fs, nthreads=nt)
+    L.gamma = (0.9 + 0.2 * uniform(4, l, TAG_GAMMA, 0, D)).astype(np.float32)
+    return L
+
+
 def stack43(B=1, n_layer=43, nthreads=None, layer_fn=None):
     """The 43-block stack; layers are generated one by one through layer_fn
     (default: keep them all in host memory)."""

@@ -55,3 +55,41 @@ def test_decode_b32_zipf(flash):
 def test_prefill_2048(flash):
     L, W = flash
     _run(synth.prefill_2048(L), W, [0, 1, 511, 1024, 2047])
+
+
+@pytest.fixture(scope="module")
+def stack3():
+    # three blocks of the 43-block stack at full width (n_embd 4096, FFN 2048,
+    # top-6, CB2 gate/up, Q2K down, Q8_0 shared, RMSNorm weights), 16 experts
+    # per layer to keep the codebook encoding short
+    t = time.time()
+    cb = synth.codebook(4)
+    layers = [synth.stack_layer(l, cb, E=16) for l in range(3)]
+    _log("stack layers generated in %.1f s" % (time.time() - t))
+    return layers, [gu.upload(L) for L in layers]
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_stack_rmsnorm_residual_teacher_forced(stack3, B):
+    # x <- x + MoE(RMSNorm(x)) layer by layer through the C ABI (rmsnorm, then
+    # layer_forward accumulating into x); each layer's output is compared with
+    # the oracle's on the same input (teacher forcing), so errors do not compound
+    import torch
+
+    import quantized_routed_moe_router_amd as moe
+    layers, Ws = stack3
+    x = synth.stack43(B=B).x
+    xd = gu.dev(x)
+    xn = torch.empty_like(xd)
+    ws = moe.alloc_workspace(Ws[0], B)
+    outs = []
+    for W in Ws:
+        moe.rmsnorm(xd, W.gamma, xn, 1e-6)
+        moe.layer_forward(W, xn, xd, ws, accumulate=True)
+        outs.append(xd.cpu().numpy().copy())
+    t = time.time()
+    ref = oracle.stack_forward(layers, x, teacher=[x] + outs[:-1])
+    _log("stack B=%d: oracle %.1f s" % (B, time.time() - t))
+    for l in range(len(layers)):
+        worst = gu.assert_close(outs[l], ref[l], what="layer %d output" % l)
+        _log("stack B=%d layer %d: worst relative error %.3g" % (B, l, worst))

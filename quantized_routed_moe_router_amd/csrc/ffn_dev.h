@@ -143,6 +143,47 @@ MOE_DEV void lds_dma16(const void *g, void *lds_wave) {
 // has landed (vmcnt 0; the export and LDS counters left alone).
 MOE_DEV void vmem_wait_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// LDS address of a pointer into a __shared__ array.
+MOE_DEV uint32_t lds_addr(const void *p) { return (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)p; }
+
+// 16 bytes per lane from global address g into LDS at m0 + 16 * lane (m0
+// wave-uniform).  Issued as assembly so that the compiler's wait counting
+// does not see it: the caller waits with s_waitcnt on vmcnt itself, counting
+// these copies with every vector load issued after them.  The s_nop covers
+// the wait state between the write of m0 and the copy that reads it.
+MOE_DEV void dma16_m0(const void *g, uint32_t m0) {
+    __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, off" : : "{m0}"(m0), "v"(g) : "memory");
+}
+
+// Wait until at most N vector memory loads of the wave are outstanding.
+template <int N>
+MOE_DEV void vmem_wait_le() {
+    static_assert(N >= 0 && N < 64, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Block barrier that orders the compiler's memory accesses around it but
+// waits for no counter (the copies above are waited for by vmem_wait_le).
+MOE_DEV void barrier_only() {
+    __asm__ volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ volatile("" ::: "memory");
+}
+
+// Sum over the 16 lanes of each row of the wave, returned to all of them
+// (DPP row rotations by 8, 4, 2 and 1).
+template <int CTRL>
+MOE_DEV float dpp_row_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+MOE_DEV float row16_sum(float v) {
+    v += dpp_row_f32<0x128>(v);
+    v += dpp_row_f32<0x124>(v);
+    v += dpp_row_f32<0x122>(v);
+    v += dpp_row_f32<0x121>(v);
+    return v;
+}
+
 MOE_DEV void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();

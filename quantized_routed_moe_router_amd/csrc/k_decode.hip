@@ -227,6 +227,109 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
     }
 }
 
+// K3 for Q2K gate/up rows of 4096 weights.  The block issues all of its
+// copies into LDS at once, in the order [x records of the first token]
+// [gate rows 0-3][up rows 0-3][gate rows 4-7]...[up rows 12-15]: 13 copies of
+// 256 units of 16 bytes, lane-contiguous, so that no copy is partial.  The
+// waves then work through the 4-row groups in that order, each as soon as
+// every copy that covers it has landed (the block's copies land in issue
+// order per wave; a barrier joins the waves), so the dot products of one
+// group run under the copies of the next.  Wave w takes column quarter w of
+// every row: lane (r, c) one 64-weight chunk of row r of the group; the 16
+// lanes of a row are added by DPP, the quarters in LDS.
+constexpr int kK3PXu = 640;                      // units of one token's records at n_embd 4096
+constexpr int kK3PHu = 336;                      // units of 4 rows of 4096 Q2K weights
+constexpr int kK3PUnits = kK3PXu + 8 * kK3PHu;  // 3328
+constexpr int kK3PCopies = kK3PUnits / 256;      // 13 per lane
+static_assert(kK3PUnits % 256 == 0, "whole copies");
+
+// vmcnt that guarantees units [0, end) of the block have landed: a wave's
+// copy i covers units [256 i + 64 w, +64), so at most ceil(end / 256) of its
+// copies are needed; the rest may still be in flight.
+// The scheduling barriers keep the dot products of the previous group in
+// front of the wait.
+template <int END>
+MOE_DEV void k3p_wait() {
+    __builtin_amdgcn_sched_barrier(0);
+    vmem_wait_le<kK3PCopies - (END + 255) / 256>();
+    barrier_only();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) dec_k3_q2k4096_kernel(FfnArgs a) {
+    __shared__ __align__(16) u32x4 wbuf[kK3PUnits];
+    __shared__ float part[4][32];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int gpe = a.F / 16, slot = blockIdx.x / gpe, g = blockIdx.x % gpe;
+    const SlotRec rec = uniform_slot(a.slots, slot);
+    if (rec.e < 0) return;  // uniform over the block
+    constexpr int RB = 16 * kQ2KBytes;  // bytes of one row
+    const int64_t goff = (int64_t)rec.e * a.gu_expert_bytes + (int64_t)16 * g * RB;
+    const uint8_t *gm = a.gate + goff, *um = a.up + goff;
+    {
+        const u32x4 *xs = (const u32x4 *)(a.xp16 + (int64_t)slot_token(rec, 0) * (4096 / 16) * kRec16Dwords);
+        const uint32_t lb = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(wbuf) + 1024 * wave);
+#pragma unroll
+        for (int i = 0; i < kK3PCopies; ++i) {
+            const int u = 256 * i + tid;
+            const void *src;
+            if (u < kK3PXu) {
+                src = xs + u;
+            } else {
+                const int v = u - kK3PXu, hgrp = v / kK3PHu, o = v - hgrp * kK3PHu;
+                src = ((hgrp & 1) ? um : gm) + (hgrp >> 1) * (4 * RB) + 16 * o;
+            }
+            dma16_m0(src, lb + 4096 * i);
+        }
+    }
+    const int c = lane & 15, lr = lane >> 4, cidx = 16 * wave + c;  // chunk of the row: 64 * cidx
+    const uint8_t *wb = (const uint8_t *)wbuf;
+    XQ2K xr;
+    float v[8];
+    k3p_wait<kK3PXu>();
+    load_q2k_prep((const uint32_t *)wbuf + 40 * cidx, xr);
+#pragma unroll
+    for (int hgrp = 0; hgrp < 8; ++hgrp) {
+        if (hgrp == 0) k3p_wait<kK3PXu + 1 * kK3PHu>();
+        if (hgrp == 1) k3p_wait<kK3PXu + 2 * kK3PHu>();
+        if (hgrp == 2) k3p_wait<kK3PXu + 3 * kK3PHu>();
+        if (hgrp == 3) k3p_wait<kK3PXu + 4 * kK3PHu>();
+        if (hgrp == 4) k3p_wait<kK3PXu + 5 * kK3PHu>();
+        if (hgrp == 5) k3p_wait<kK3PXu + 6 * kK3PHu>();
+        if (hgrp == 6) k3p_wait<kK3PXu + 7 * kK3PHu>();
+        if (hgrp == 7) k3p_wait<kK3PXu + 8 * kK3PHu>();
+        v[hgrp] = q2k_dot2(q2k_load(wb + 16 * (kK3PXu + kK3PHu * hgrp), (int64_t)lr * 4096 + 64 * cidx), xr);
+    }
+    for (int j = 0;;) {
+#pragma unroll
+        for (int hgrp = 0; hgrp < 8; ++hgrp) {
+            const float s = row16_sum(v[hgrp]);
+            if (c == 0) part[wave][2 * (4 * (hgrp >> 1) + lr) + (hgrp & 1)] = s;
+        }
+        block_lds_sync();
+        if (wave == 0) {
+            float hv = 0.f;
+            if (lane < 16) {
+                float gs = 0.f, us = 0.f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    gs += part[q][2 * lane];
+                    us += part[q][2 * lane + 1];
+                }
+                hv = swiglu_h(gs, us, a.x_bf16);
+                a.h[(int64_t)(rec.j0 + j) * a.F + 16 * g + lane] = hv;
+            }
+            if (a.hp16) prep16_wave(hv, a.hp16 + ((int64_t)(rec.j0 + j) * (a.F / 16) + g) * kRec16Dwords, 1);
+        }
+        if (++j >= rec.n) break;
+        block_lds_sync();  // part is rewritten for the next token
+        load_q2k_prep(a.xp16 + ((int64_t)slot_token(rec, j) * 256 + 4 * cidx) * kRec16Dwords, xr);
+#pragma unroll
+        for (int hgrp = 0; hgrp < 8; ++hgrp)
+            v[hgrp] = q2k_dot2(q2k_load(wb + 16 * (kK3PXu + kK3PHu * hgrp), (int64_t)lr * 4096 + 64 * cidx), xr);
+    }
+}
+
 // One block per 16 output rows, a wave per active slot in turn: the wave
 // copies the slot expert's 16 down rows into its own LDS area with aligned
 // 16-byte loads (no block barrier: every wave starts on its dots as soon as
@@ -371,6 +474,7 @@ hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32
         with_fmt(a.shared_fmt, [&](auto S) { dec_k2_kernel<decltype(S)::value><<<k2, 256, 0, s>>>(a, route ? 1 : 0); });
     if (stage == 0 || stage == 3) {
         if (d->gate_type == MOE_CB2) dec_k3_kernel<MOE_CB2><<<k3, 256, 0, s>>>(a);
+        else if (a.D == 4096) dec_k3_q2k4096_kernel<<<k3, 256, 0, s>>>(a);
         else dec_k3_kernel<MOE_Q2K><<<k3, 256, 0, s>>>(a);
     }
     if (stage == 0 || stage == 4) {

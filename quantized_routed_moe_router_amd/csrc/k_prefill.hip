@@ -77,7 +77,6 @@ struct PfArgs {
 // stage (its own tracking of such copies falls back to waiting for all of
 // them), and the kernel counts them with explicit vmcnt waits instead.  One
 // wait state separates the m0 write from the copy.
-MOE_DEV uint32_t lds_addr(const void *p) { return (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)p; }
 
 MOE_DEV void pf_dma16(const void *g, void *lds_wave) {
     __asm__ volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, off"

@@ -52,6 +52,20 @@ def test_decode_b32_zipf(flash):
     _run(synth.decode_b32(L), W, [0, 5, 17, 31])
 
 
+@pytest.mark.parametrize("T,zipf", [(8, False), (16, True)])
+def test_decode_small_batches(flash, T, zipf):
+    # the few-token path at full width with several tokens per bucket (the
+    # Zipf router bias crowds the batch onto a few experts)
+    import copy
+    L, W = flash
+    Lb = copy.copy(L)
+    if zipf:
+        Lb.router_bias = synth.zipf_bias(2, L.n_expert)
+    wl = synth.Workload("decode_b%d%s" % (T, "_zipf" if zipf else ""), T, synth.F32, [Lb],
+                        x=synth.activations(6, T, L.n_embd))
+    _run(wl, W, [0, T // 2, T - 1])
+
+
 def test_prefill_2048(flash):
     L, W = flash
     _run(synth.prefill_2048(L), W, [0, 1, 511, 1024, 2047])

@@ -137,10 +137,12 @@ int moe_layer_forward(const moe_layer_desc *desc, const void *x, int32_t T, int3
 /* The four stages moe_layer_forward runs, callable one by one with the same
  * arguments (so that each can be timed with events on the caller's stream);
  * running stages 1, 2, 3, 4 in order equals one moe_layer_forward call.
- *   1  router partial sums (and, for a few rows, the shared expert's gate/up)
- *   2  logits, top-k, weights, bucketing (and the shared expert's down)
+ *   1  router logits
+ *   2  top-k, weights, bucketing (for a few rows, also the shared expert's
+ *      gate/up)
  *   3  gate/up with SwiGLU
- *   4  down projection and the weighted combine into y */
+ *   4  down projection and the weighted combine into y (for a few rows, also
+ *      the shared expert's down) */
 int moe_layer_forward_stage(const moe_layer_desc *desc, const void *x, int32_t T, int32_t x_type, float *y,
                             uint32_t flags, const moe_routing *routing, int32_t stage, void *ws, size_t ws_bytes,
                             void *stream, char *err, size_t errlen);

@@ -35,8 +35,8 @@ struct FfnArgs {
     // rows ([T][D/16] records), x for Q8_0 rows ([T][D/64] records), h for the
     // routed Q2K down ([T*k][F/16] records)
     uint32_t *xp16, *xq8, *hp16;
-    int n_prep_blocks, n_shgu_blocks;  // K1: x-preparing and shared gate/up blocks
-    int n_shd_blocks;                  // K2: shared down blocks
+    int n_prep_blocks;  // K1: x-preparing blocks
+    int n_shgu_blocks;  // K2: shared gate/up blocks
     int shared_fmt;
     // per-slot records (few-token schedule) and their number, min(T*k, E)
     SlotRec *slots;

@@ -4,12 +4,13 @@
 // 1-5; 5.3.4 the shared expert needs no routing, so it runs beside the
 // router and the finisher; 3.5 a schedule built once and replayed per token):
 //   K1  router logits (one block per expert row) || x prepared for the routed
-//       dot2 path || shared expert gate/up -> hs
-//   K2  top-k, weights, bucketing (block 0) || shared expert down -> ys
+//       dot2 path
+//   K2  top-k, weights, bucketing (block 0) || shared expert gate/up -> hs
 //   K3  routed gate/up + SwiGLU: one block per (active expert, group of 16
 //       rows); writes h and, for a Q2K down, its prepared form
-//   K4  per block of 16 output rows: routed down of every active expert,
-//       then y = ys + sum_s w_s * down_s in slot order
+//   K4  per block of 16 output rows: routed down of every active expert and
+//       the shared expert's down (two rows per wave), then
+//       y = shared + sum_s w_s * down_s in slot order
 // Routed weight rows are copied into LDS with aligned 16-byte loads (each
 // wave instruction reads 1 KB of consecutive bytes) before their 64-weight
 // chunks are read from LDS: a 16-byte load per lane straight from the
@@ -37,7 +38,9 @@ constexpr bool staged_fmt(int f) { return f == MOE_Q2K || f == MOE_CB2; }
 template <int FMT>
 constexpr int rows16_bytes_max() { return 16 * 16 * (FMT == MOE_Q8_0 ? 2 * kQ8Bytes * 4 : (FMT == MOE_CB2 ? kCB2Bytes : kQ2KBytes)); }
 // shared expert rows per wave (gate/up in K1, down in K2)
-constexpr int kShGuRows = 2, kShDownRows = 4;
+constexpr int kShGuRows = 2;
+// K4: shared expert down rows per wave (kDecRows over kDecWaves waves)
+constexpr int kShDownRowsK4 = 2;
 // K4: LDS units (16 bytes) a wave stages at once: 16 rows of 2048 Q2K weights
 constexpr int kK4WaveUnits = 672;
 
@@ -78,11 +81,9 @@ MOE_DEV void build_slot_records(const FfnArgs &a) {
     }
 }
 
-template <int XT, int SFMT>
+template <int XT>
 __global__ void __launch_bounds__(256) dec_k1_kernel(FfnArgs a) {
     __shared__ double part[4 * 16];
-    __shared__ uint32_t cb_lds[SFMT == MOE_CB2 ? 512 : 1];
-    __shared__ __align__(16) float red[4][2 * kShGuRows * 64];
     int b = blockIdx.x;
     if (a.build_slots) {
         if (b == 0) {
@@ -97,20 +98,6 @@ __global__ void __launch_bounds__(256) dec_k1_kernel(FfnArgs a) {
     }
     b -= a.n_router_blocks;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    if (b >= a.n_prep_blocks) {  // shared gate/up: kShGuRows rows per wave, fp32 activations
-        if constexpr (SFMT == MOE_CB2) load_codebook(a.codebook, cb_lds);  // uniform over the block
-        const int row0 = ((b - a.n_prep_blocks) * 4 + wave) * kShGuRows;
-        if (row0 >= a.Fs) return;
-        const int nrows = min(kShGuRows, a.Fs - row0), c = lane % (a.D >> 6);
-        for (int t = 0; t < a.T; ++t) {
-            float *dst = a.hs + (int64_t)t * a.Fs + row0;
-            rows_dot_ch<F32Chunk<SFMT>, true, kShGuRows>(
-                a.sh_gate, a.sh_up, a.D, 0, a.D, nrows, [&](int l) { return row0 + l; },
-                [&](XF32 &xr) { load_x64(a.x, a.x_bf16, (int64_t)t * a.D + 64 * c, xr.x); }, cb_lds, lane,
-                red[wave], [&](int l, float gs, float us) { dst[l] = swiglu_h(gs, us, a.x_bf16); });
-        }
-        return;
-    }
     const int item = b * 4 + wave, per_t = a.D / 64;  // one wave per 64 activations of a token
     if (item >= a.T * per_t) return;
     const int t = item / per_t, c = item % per_t;
@@ -137,12 +124,14 @@ MOE_DEV ColSplit col_split(int n, int rows_per_block, int wave) {
     return s;
 }
 
-// block 0 (when routing): the finisher; then the shared expert's down,
-// kShDownRows rows per wave, fp32 activations hs -> ys.
+// Block 0 (when routing): top-k, weights and bucketing; the other blocks
+// run the shared expert's gate/up, kShGuRows rows per wave, fp32
+// activations x -> hs.  The finisher's latency hides under the shared
+// expert's weight stream.
 template <int SFMT>
 __global__ void __launch_bounds__(256) dec_k2_kernel(FfnArgs a, int do_route) {
     __shared__ uint32_t cb_lds[SFMT == MOE_CB2 ? 512 : 1];
-    __shared__ __align__(16) float red[4][kShDownRows * 64];
+    __shared__ __align__(16) float red[4][2 * kShGuRows * 64];
     int b = blockIdx.x;
     if (do_route) {
         if (b == 0) {
@@ -152,17 +141,17 @@ __global__ void __launch_bounds__(256) dec_k2_kernel(FfnArgs a, int do_route) {
         }
         b -= 1;
     }
-    if constexpr (SFMT == MOE_CB2) load_codebook(a.codebook, cb_lds);
+    if constexpr (SFMT == MOE_CB2) load_codebook(a.codebook, cb_lds);  // uniform over the block
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int row0 = (b * 4 + wave) * kShDownRows;
-    if (row0 >= a.D) return;
-    const int nrows = min(kShDownRows, a.D - row0), c = lane % (a.Fs >> 6);
+    const int row0 = (b * 4 + wave) * kShGuRows;
+    if (row0 >= a.Fs) return;
+    const int nrows = min(kShGuRows, a.Fs - row0), c = lane % (a.D >> 6);
     for (int t = 0; t < a.T; ++t) {
-        float *dst = a.ys + (int64_t)t * a.D + row0;
-        rows_dot_ch<F32Chunk<SFMT>, false, kShDownRows>(
-            a.sh_down, nullptr, a.Fs, 0, a.Fs, nrows, [&](int l) { return row0 + l; },
-            [&](XF32 &hr) { load_x64(a.hs, 0, (int64_t)t * a.Fs + 64 * c, hr.x); }, cb_lds, lane, red[wave],
-            [&](int l, float s, float) { dst[l] = s; });
+        float *dst = a.hs + (int64_t)t * a.Fs + row0;
+        rows_dot_ch<F32Chunk<SFMT>, true, kShGuRows>(
+            a.sh_gate, a.sh_up, a.D, 0, a.D, nrows, [&](int l) { return row0 + l; },
+            [&](XF32 &xr) { load_x64(a.x, a.x_bf16, (int64_t)t * a.D + 64 * c, xr.x); }, cb_lds, lane, red[wave],
+            [&](int l, float gs, float us) { dst[l] = swiglu_h(gs, us, a.x_bf16); });
     }
 }
 
@@ -335,19 +324,34 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
 // 16-byte loads (no block barrier: every wave starts on its dots as soon as
 // its own rows have landed), then dots them with the prepared h of every
 // token of its bucket, into part[bucket position].  Then the combine adds,
-// per output, ys and the k routed terms in slot order.
-template <int DFMT>
+// per output, the shared expert's term and the k routed terms in slot order.
+template <int DFMT, int SFMT>
 __global__ void __launch_bounds__(64 * kDecWaves) dec_k4_kernel(FfnArgs a) {
     static_assert(staged_fmt(DFMT), "staged formats only");
+    static_assert(kDecRows == kShDownRowsK4 * kDecWaves, "shared rows per wave");
     __shared__ __align__(16) u32x4 wstage[kDecWaves][kK4WaveUnits];
-    __shared__ uint32_t cb_lds[DFMT == MOE_CB2 ? 512 : 1];
+    __shared__ uint32_t cb_lds[DFMT == MOE_CB2 || SFMT == MOE_CB2 ? 512 : 1];
     __shared__ __align__(16) float red[kDecWaves][8 * 64];
     __shared__ float part[kMaxDecPairs][kDecRows];
+    __shared__ float ysl[kMaxDecTokens][kDecRows];
     __shared__ float wl[kMaxDecPairs];
     __shared__ int32_t posl[kMaxDecPairs];
-    if constexpr (DFMT == MOE_CB2) load_codebook(a.codebook, cb_lds);
+    if constexpr (DFMT == MOE_CB2 || SFMT == MOE_CB2) load_codebook(a.codebook, cb_lds);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int row0 = blockIdx.x * kDecRows;
+    // The shared expert's down for rows row0 + 2 wave, +1 and every token
+    // (fp32 activations hs), into ysl.  A wave with a routed slot runs it
+    // while the copies of its first slot's rows are in flight.
+    bool sh_pending = a.Fs > 0;
+    auto shared_down = [&]() {
+        const int r0 = row0 + kShDownRowsK4 * wave, c = lane % (a.Fs >> 6);
+        for (int t = 0; t < a.T; ++t)
+            rows_dot_ch<F32Chunk<SFMT>, false, 1>(
+                a.sh_down, nullptr, a.Fs, 0, a.Fs, kShDownRowsK4, [&](int l) { return r0 + l; },
+                [&](XF32 &hr) { load_x64(a.hs, 0, (int64_t)t * a.Fs + 64 * c, hr.x); }, cb_lds, lane, red[wave],
+                [&](int l, float v, float) { ysl[t][kShDownRowsK4 * wave + l] = v; });
+        sh_pending = false;
+    };
     for (int p = tid; p < a.T * a.k; p += blockDim.x) {  // for the combine, read early
         wl[p] = a.topk_w[p];
         posl[p] = a.pos[p];
@@ -371,6 +375,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) dec_k4_kernel(FfnArgs a) {
 #pragma unroll
                 for (int i = 0; i < kNI; ++i)
                     if (i * 64 + lane < nunits) lds_dma16(src + i * 64 + lane, &wstage[wave][i * 64]);
+                if (sh_pending) shared_down();
                 vmem_wait_all();
                 wave_lds_sync();
             }
@@ -383,11 +388,12 @@ __global__ void __launch_bounds__(64 * kDecWaves) dec_k4_kernel(FfnArgs a) {
             wave_lds_sync();  // the area is rewritten by the next batch
         }
     }
+    if (sh_pending) shared_down();
     block_lds_sync();
     for (int i = tid; i < a.T * kDecRows; i += blockDim.x) {
         const int t = i / kDecRows, r = i % kDecRows;
         const int64_t o = (int64_t)t * a.D + row0 + r;
-        float acc = a.Fs > 0 ? a.ys[o] : 0.f;
+        float acc = a.Fs > 0 ? ysl[t][r] : 0.f;
         for (int s = 0; s < a.k; ++s) {
             const int p = t * a.k + s;
             acc = __builtin_fmaf(wl[p], part[posl[p]][r], acc);
@@ -461,15 +467,14 @@ hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32
     if (d->down_type == MOE_Q2K) a.hp16 = ws.hp16;  // h records for the routed down, written by K3
     a.n_prep_blocks = a.xp16 ? (T * (a.D / 64) + 3) / 4 : 0;
     a.n_shgu_blocks = has_sh ? (a.Fs + 4 * kShGuRows - 1) / (4 * kShGuRows) : 0;
-    a.n_shd_blocks = has_sh ? (a.D + 4 * kShDownRows - 1) / (4 * kShDownRows) : 0;
-    const int k1 = a.build_slots + a.n_router_blocks + a.n_prep_blocks + a.n_shgu_blocks;
-    const int k2 = (route ? 1 : 0) + a.n_shd_blocks;
+    const int k1 = a.build_slots + a.n_router_blocks + a.n_prep_blocks;
+    const int k2 = (route ? 1 : 0) + a.n_shgu_blocks;
     const int k3 = a.nslots * (a.F / 16);
     if ((stage == 0 || stage == 1) && k1 > 0)
-        with_fmt(a.shared_fmt, [&](auto S) {
-            if (x_type == MOE_BF16) dec_k1_kernel<MOE_BF16, decltype(S)::value><<<k1, 256, 0, s>>>(a);
-            else dec_k1_kernel<MOE_F32, decltype(S)::value><<<k1, 256, 0, s>>>(a);
-        });
+    {
+        if (x_type == MOE_BF16) dec_k1_kernel<MOE_BF16><<<k1, 256, 0, s>>>(a);
+        else dec_k1_kernel<MOE_F32><<<k1, 256, 0, s>>>(a);
+    }
     if ((stage == 0 || stage == 2) && k2 > 0)
         with_fmt(a.shared_fmt, [&](auto S) { dec_k2_kernel<decltype(S)::value><<<k2, 256, 0, s>>>(a, route ? 1 : 0); });
     if (stage == 0 || stage == 3) {
@@ -478,8 +483,11 @@ hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32
         else dec_k3_kernel<MOE_Q2K><<<k3, 256, 0, s>>>(a);
     }
     if (stage == 0 || stage == 4) {
-        if (d->down_type == MOE_CB2) dec_k4_kernel<MOE_CB2><<<a.D / kDecRows, 64 * kDecWaves, 0, s>>>(a);
-        else dec_k4_kernel<MOE_Q2K><<<a.D / kDecRows, 64 * kDecWaves, 0, s>>>(a);
+        with_fmt(a.shared_fmt, [&](auto S) {
+            constexpr int SF = decltype(S)::value;
+            if (d->down_type == MOE_CB2) dec_k4_kernel<MOE_CB2, SF><<<a.D / kDecRows, 64 * kDecWaves, 0, s>>>(a);
+            else dec_k4_kernel<MOE_Q2K, SF><<<a.D / kDecRows, 64 * kDecWaves, 0, s>>>(a);
+        });
     }
     return hipGetLastError();
 }

@@ -170,6 +170,10 @@ MOE_DEV void barrier_only() {
     __asm__ volatile("" ::: "memory");
 }
 
+// Make v appear used and changed here: the compiler then computes it before
+// this point and cannot sink the computation below a later wait.
+MOE_DEV void pin_value(float &v) { __asm__ volatile("" : "+v"(v)); }
+
 // Sum over the 16 lanes of each row of the wave, returned to all of them
 // (DPP row rotations by 8, 4, 2 and 1).
 template <int CTRL>

@@ -288,6 +288,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
         if (hgrp == 6) k3p_wait<kK3PXu + 7 * kK3PHu>();
         if (hgrp == 7) k3p_wait<kK3PXu + 8 * kK3PHu>();
         v[hgrp] = q2k_dot2(q2k_load(wb + 16 * (kK3PXu + kK3PHu * hgrp), (int64_t)lr * 4096 + 64 * cidx), xr);
+        pin_value(v[hgrp]);
     }
     for (int j = 0;;) {
 #pragma unroll
@@ -403,6 +404,160 @@ __global__ void __launch_bounds__(64 * kDecWaves) dec_k4_kernel(FfnArgs a) {
     }
 }
 
+// K4 for one token (k <= 6 slots; routed down Q2K and shared down Q8_0,
+// both of width 2048).  Wave s < k takes slot s (16 rows of its expert's
+// down matrix); waves 6 and 7 take 8 rows each of the shared expert's down.
+// Each wave copies what it reads into its own LDS area, all copies issued at
+// once: first the activations (the pair's prepared h row; for the shared
+// waves, hs), then its rows in order, and starts on each group of rows as
+// soon as the copies covering it have landed.  With one token, slot s
+// (ascending expert) holds bucket position s.  The activations are placed
+// in LDS permuted (the permutation is applied to the copy sources) so that
+// the lanes of a 16-lane group read 16 different bank groups.
+constexpr int kK4T1Hu = 320;                // units of a prepared h row of 2048 (32 chunks of 10 units)
+constexpr int kK4T1Ru = 672;                // units of 16 Q2K rows of 2048
+constexpr int kK4T1SlotCopies = 16;         // (320 + 672 = 992) -> 16 copies of 64 units
+constexpr int kK4T1Hsu = 512;               // units of hs: 2048 fp32 (32 chunks of 16 units)
+constexpr int kK4T1Su = 8 * 136;            // units of 8 Q8_0 rows of 2048
+constexpr int kK4T1ShCopies = 25;           // (512 + 1088 = 1600) -> 25 copies of 64 units
+static_assert(kK4T1Hu + kK4T1Ru <= 64 * kK4T1SlotCopies && kK4T1Hsu + kK4T1Su == 64 * kK4T1ShCopies, "areas");
+
+template <int NC, int END>  // the wave's copies covering its units [0, end) have landed
+MOE_DEV void k4t1_wait() {
+    __builtin_amdgcn_sched_barrier(0);
+    vmem_wait_le<NC - (END + 63) / 64>();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+MOE_DEV float sum32(float v) {  // over lanes [32 r, 32 r + 32)
+    v = row16_sum(v);
+    return v + __shfl_xor(v, 16, kWave);
+}
+
+__global__ void __launch_bounds__(512) dec_k4_t1_kernel(FfnArgs a) {
+    __shared__ __align__(16) u32x4 sarea[6][64 * kK4T1SlotCopies];
+    __shared__ __align__(16) u32x4 harea[2][64 * kK4T1ShCopies];
+    __shared__ float part[6][kDecRows];
+    __shared__ float ysl[kDecRows];
+    __shared__ float wl[6];
+    __shared__ int32_t posl[6];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int row0 = blockIdx.x * kDecRows, k = a.k;
+    const int r = lane >> 5, c = lane & 31;  // row parity, 64-weight chunk of the row
+    if (tid < k) {
+        wl[tid] = a.topk_w[tid];
+        posl[tid] = a.pos[tid];
+    }
+    if (wave < 6) {
+        const SlotRec rec = wave < k ? uniform_slot(a.slots, wave) : make_slot(-1, 0, 0, 0, 0);
+        if (rec.e >= 0) {
+            constexpr int RB = 8 * kQ2KBytes;  // bytes of a row
+            const uint8_t *hrow = (const uint8_t *)(a.hp16 + (int64_t)rec.j0 * (2048 / 16) * kRec16Dwords);
+            const uint8_t *rows = a.down + (int64_t)rec.e * a.down_expert_bytes + (int64_t)row0 * RB;
+            const uint32_t lb = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(sarea[wave]));
+#pragma unroll
+            for (int i = 0; i < kK4T1SlotCopies; ++i) {
+                const int u = 64 * i + lane;
+                const uint8_t *src;
+                if (u < kK4T1Hu) {  // record unit m of chunk cc sits at (m + (cc >> 3 & 1)) % 10
+                    const int cc = u / 10, m = u - 10 * cc, g = (cc >> 3) & 1;
+                    src = hrow + 16 * (10 * cc + (m + 10 - g) % 10);
+                } else {
+                    src = rows + 16 * min(u - kK4T1Hu, kK4T1Ru - 1);
+                }
+                dma16_m0(src, lb + 1024 * i);
+            }
+            const uint8_t *ab = (const uint8_t *)sarea[wave];
+            const uint8_t *wb = ab + 16 * kK4T1Hu;
+            XQ2K xr;
+            float v[8];
+            auto group = [&](int gq) {  // rows 4 gq + 2 i + r
+                if (gq == 0) {
+                    const int g = (c >> 3) & 1;
+                    u32x4 *dst = (u32x4 *)&xr;
+#pragma unroll
+                    for (int m = 0; m < 10; ++m) dst[m] = *(const u32x4 *)(ab + 16 * (10 * c + (m + g) % 10));
+                }
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    v[2 * gq + i] = q2k_dot2(q2k_load(wb + RB * (4 * gq + 2 * i + r), 64 * c), xr);
+                pin_value(v[2 * gq]);  // computed here, not sunk below the next wait
+                pin_value(v[2 * gq + 1]);
+            };
+            k4t1_wait<kK4T1SlotCopies, kK4T1Hu + 4 * RB / 16>();
+            group(0);
+            k4t1_wait<kK4T1SlotCopies, kK4T1Hu + 8 * RB / 16>();
+            group(1);
+            k4t1_wait<kK4T1SlotCopies, kK4T1Hu + 12 * RB / 16>();
+            group(2);
+            k4t1_wait<kK4T1SlotCopies, kK4T1Hu + 16 * RB / 16>();
+            group(3);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const float sv = sum32(v[q]);
+                if (c == 0) part[rec.j0][4 * (q >> 1) + 2 * (q & 1) + r] = sv;
+            }
+        }
+    } else if (a.Fs > 0) {
+        const int h = wave - 6;  // rows row0 + 8 h .. + 8
+        constexpr int SB = 2048 / 32 * kQ8Bytes;  // bytes of a row
+        const uint8_t *hsb = (const uint8_t *)a.hs;
+        const uint8_t *rows = a.sh_down + (int64_t)(row0 + 8 * h) * SB;
+        const uint32_t lb = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(harea[h]));
+#pragma unroll
+        for (int i = 0; i < kK4T1ShCopies; ++i) {
+            const int u = 64 * i + lane;
+            const uint8_t *src;
+            if (u < kK4T1Hsu) {  // float4 j of chunk cc sits at j ^ (cc & 15)
+                const int cc = u >> 4, j = u & 15;
+                src = hsb + 16 * (16 * cc + (j ^ (cc & 15)));
+            } else {
+                src = rows + 16 * (u - kK4T1Hsu);
+            }
+            dma16_m0(src, lb + 1024 * i);
+        }
+        const uint8_t *ab = (const uint8_t *)harea[h];
+        const uint8_t *wb = ab + 16 * kK4T1Hsu;
+        float xv[64];
+        float v[4];
+        auto pair = [&](int q) {  // rows 2 q + r
+            if (q == 0) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const f32x4 t4 = *(const f32x4 *)(ab + 16 * (16 * c + (j ^ (c & 15))));
+                    xv[4 * j] = t4[0];
+                    xv[4 * j + 1] = t4[1];
+                    xv[4 * j + 2] = t4[2];
+                    xv[4 * j + 3] = t4[3];
+                }
+            }
+            v[q] = q8_dot(q8_load(wb + SB * (2 * q + r), 64 * c), xv);
+            pin_value(v[q]);
+        };
+        k4t1_wait<kK4T1ShCopies, kK4T1Hsu + 2 * SB / 16>();
+        pair(0);
+        k4t1_wait<kK4T1ShCopies, kK4T1Hsu + 4 * SB / 16>();
+        pair(1);
+        k4t1_wait<kK4T1ShCopies, kK4T1Hsu + 6 * SB / 16>();
+        pair(2);
+        k4t1_wait<kK4T1ShCopies, kK4T1Hsu + 8 * SB / 16>();
+        pair(3);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float sv = sum32(v[q]);
+            if (c == 0) ysl[8 * h + 2 * q + r] = sv;
+        }
+    }
+    __syncthreads();
+    if (tid < kDecRows) {
+        const int64_t o = row0 + tid;
+        float acc = a.Fs > 0 ? ysl[tid] : 0.f;
+        for (int q = 0; q < k; ++q) acc = __builtin_fmaf(wl[q], part[posl[q]][tid], acc);
+        if (a.flags & MOE_ACCUMULATE) acc += a.y[o];
+        a.y[o] = acc;
+    }
+}
+
 FfnArgs make_ffn_args(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
                       float *y, uint32_t flags, const Workspace &ws) {
     FfnArgs a{};
@@ -483,7 +638,10 @@ hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32
         else dec_k3_kernel<MOE_Q2K><<<k3, 256, 0, s>>>(a);
     }
     if (stage == 0 || stage == 4) {
-        with_fmt(a.shared_fmt, [&](auto S) {
+        const bool t1 = T == 1 && d->down_type == MOE_Q2K && a.F == 2048 && a.k <= 6 && a.D % kDecRows == 0 &&
+                        (a.Fs == 0 || (a.Fs == 2048 && a.shared_fmt == MOE_Q8_0));
+        if (t1) dec_k4_t1_kernel<<<a.D / kDecRows, 64 * kDecWaves, 0, s>>>(a);
+        else with_fmt(a.shared_fmt, [&](auto S) {
             constexpr int SF = decltype(S)::value;
             if (d->down_type == MOE_CB2) dec_k4_kernel<MOE_CB2, SF><<<a.D / kDecRows, 64 * kDecWaves, 0, s>>>(a);
             else dec_k4_kernel<MOE_Q2K, SF><<<a.D / kDecRows, 64 * kDecWaves, 0, s>>>(a);

@@ -66,6 +66,25 @@ def test_decode_small_batches(flash, T, zipf):
     _run(wl, W, [0, T // 2, T - 1])
 
 
+@pytest.mark.parametrize("E,k,Fs,accumulate", [(16, 4, 0, False), (12, 6, 2048, True), (8, 1, 2048, False)])
+def test_one_token_full_width(E, k, Fs, accumulate):
+    # one token through full-width experts (n_embd 4096, FFN 2048) with fewer
+    # slots than waves, with and without the shared expert, and adding into y
+    import torch
+
+    import quantized_routed_moe_router_amd as moe
+    L = synth.make_layer(7, 0, D=4096, E=E, k=k, F=2048, Fs=Fs)
+    x = synth.activations(8, 1, 4096)
+    y0 = synth.activations(9, 1, 4096) if accumulate else np.zeros((1, 4096), np.float32)
+    W = gu.upload(L)
+    y = gu.dev(y0)
+    ws = moe.alloc_workspace(W, 1)
+    moe.layer_forward(W, gu.dev(x), y, ws, accumulate=accumulate)
+    y_ref, _, _ = oracle.moe_forward(L, x=x)
+    worst = gu.assert_close(y.cpu().numpy(), y_ref + y0)
+    _log("one token E=%d k=%d Fs=%d: worst relative error %.3g" % (E, k, Fs, worst))
+
+
 def test_prefill_2048(flash):
     L, W = flash
     _run(synth.prefill_2048(L), W, [0, 1, 511, 1024, 2047])

@@ -155,6 +155,102 @@ __global__ void __launch_bounds__(256) dec_k2_kernel(FfnArgs a, int do_route) {
     }
 }
 
+// K2 with a Q8_0 shared expert at n_embd 4096: block 0 finishes the routing
+// (when routing); every other block takes 8 rows of the shared gate and the
+// same 8 rows of up, wave w their column quarter w.  Each wave copies into
+// its own LDS area, all at once: the first token's prepared x for its
+// quarter (16 chunk records), then rows in groups of four ([gate 2q, 2q+1,
+// up 2q, 2q+1] for q = 0..3), and starts on each group once it has landed.
+// Lane (r, c) dots row r of a group with chunk c of the quarter (packed fp16
+// products of the int8 codes with the hi/lo split activations); the 16 lanes
+// of a row are added by DPP, the quarters in LDS.
+constexpr int kSgXu = 16 * kXQ8Dwords / 4;   // 272 units: 16 chunk records
+constexpr int kSgRu = 1024 / 32 * kQ8Bytes / 16;  // 68 units: a row quarter
+constexpr int kSgCopies = 22;                 // 272 + 16 x 68 = 1360 units -> 22 copies of 64
+static_assert(kSgXu + 16 * kSgRu <= 64 * kSgCopies, "area");
+
+template <int END>
+MOE_DEV void sg_wait() {
+    __builtin_amdgcn_sched_barrier(0);
+    vmem_wait_le<kSgCopies - (END + 63) / 64>();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+__global__ void __launch_bounds__(256) dec_k2_q8sg4096_kernel(FfnArgs a, int do_route) {
+    __shared__ __align__(16) u32x4 area[4][64 * kSgCopies];
+    __shared__ float part[4][16];
+    int b = blockIdx.x;
+    if (do_route) {
+        if (b == 0) {
+            route_finish_block(a.logits, a.T, a.E, a.k, a.route_scale, a.w_topk_idx, a.w_topk_w, a.w_count,
+                               a.w_offset, a.w_perm, a.w_pos, a.w_active, a.w_n_active, a.slots, a.nslots);
+            return;
+        }
+        b -= 1;
+    }
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int row0 = 8 * b;  // rows row0 .. row0 + 7 of gate and of up
+    constexpr int RB = 4096 / 32 * kQ8Bytes;  // bytes of a row: 4352
+    {
+        const uint8_t *xs = (const uint8_t *)(a.xq8 + (int64_t)(16 * wave) * kXQ8Dwords);  // token 0, quarter w
+        const uint8_t *gm = a.sh_gate + (int64_t)row0 * RB + 1088 * wave, *um = a.sh_up + (int64_t)row0 * RB + 1088 * wave;
+        const uint32_t lb = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(area[wave]));
+#pragma unroll
+        for (int i = 0; i < kSgCopies; ++i) {
+            const int u = 64 * i + lane;
+            const uint8_t *src;
+            if (u < kSgXu) {
+                src = xs + 16 * u;
+            } else {
+                const int v = min(u - kSgXu, 16 * kSgRu - 1), rw = v / kSgRu, o = v - rw * kSgRu;
+                const int q = rw >> 2, j = rw & 3;  // group q: gate 2q, 2q+1, up 2q, 2q+1
+                src = ((j & 2) ? um : gm) + (int64_t)(2 * q + (j & 1)) * RB + 16 * o;
+            }
+            dma16_m0(src, lb + 1024 * i);
+        }
+    }
+    const int r = lane >> 4, c = lane & 15;
+    const uint8_t *ab = (const uint8_t *)area[wave];
+    XQ8 xr;
+    float v[4];
+    auto group = [&](int q) {
+        if (q == 0) load_q8_prep((const uint32_t *)(ab + 272 * c), xr);
+        v[q] = q8_dot2(q8_load(ab + 16 * (kSgXu + kSgRu * (4 * q + r)), 64 * c), xr);
+        pin_value(v[q]);
+    };
+    sg_wait<kSgXu + 4 * kSgRu>();
+    group(0);
+    sg_wait<kSgXu + 8 * kSgRu>();
+    group(1);
+    sg_wait<kSgXu + 12 * kSgRu>();
+    group(2);
+    sg_wait<kSgXu + 16 * kSgRu>();
+    group(3);
+    for (int t = 0;;) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float sv = row16_sum(v[q]);
+            if (c == 0) part[wave][4 * q + r] = sv;  // [group][gate 2q, 2q+1, up 2q, 2q+1]
+        }
+        __syncthreads();
+        if (tid < 8) {
+            const int q = tid >> 1, j = tid & 1;
+            float gs = 0.f, us = 0.f;
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                gs += part[w][4 * q + j];
+                us += part[w][4 * q + 2 + j];
+            }
+            a.hs[(int64_t)t * a.Fs + row0 + tid] = swiglu_h(gs, us, a.x_bf16);
+        }
+        if (++t >= a.T) break;
+        __syncthreads();  // part is rewritten
+        load_q8_prep(a.xq8 + ((int64_t)t * 64 + 16 * wave + c) * kXQ8Dwords, xr);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = q8_dot2(q8_load(ab + 16 * (kSgXu + kSgRu * (4 * q + r)), 64 * c), xr);
+    }
+}
+
 // One block per (active slot, group g of 16 rows of the expert's gate and up):
 // the 16 rows of both are staged in LDS, wave w takes column part w % P of
 // the rows of row group w / P; the parts of a row are added in LDS in column
@@ -620,7 +716,10 @@ hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32
     a.build_slots = route ? 0 : 1;
     if (d->gate_type == MOE_Q2K) a.xp16 = ws.xp16;  // x records for the routed gate/up, written by K1
     if (d->down_type == MOE_Q2K) a.hp16 = ws.hp16;  // h records for the routed down, written by K3
-    a.n_prep_blocks = a.xp16 ? (T * (a.D / 64) + 3) / 4 : 0;
+    // a Q8_0 shared expert at n_embd 4096 takes the staged K2, on x records written by K1
+    const bool sg_staged = has_sh && a.shared_fmt == MOE_Q8_0 && a.D == 4096 && a.Fs % 8 == 0;
+    if (sg_staged) a.xq8 = ws.xq8;
+    a.n_prep_blocks = a.xp16 || a.xq8 ? (T * (a.D / 64) + 3) / 4 : 0;
     a.n_shgu_blocks = has_sh ? (a.Fs + 4 * kShGuRows - 1) / (4 * kShGuRows) : 0;
     const int k1 = a.build_slots + a.n_router_blocks + a.n_prep_blocks;
     const int k2 = (route ? 1 : 0) + a.n_shgu_blocks;
@@ -631,7 +730,10 @@ hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32
         else dec_k1_kernel<MOE_F32><<<k1, 256, 0, s>>>(a);
     }
     if ((stage == 0 || stage == 2) && k2 > 0)
-        with_fmt(a.shared_fmt, [&](auto S) { dec_k2_kernel<decltype(S)::value><<<k2, 256, 0, s>>>(a, route ? 1 : 0); });
+    {
+        if (sg_staged) dec_k2_q8sg4096_kernel<<<(route ? 1 : 0) + a.Fs / 8, 256, 0, s>>>(a, route ? 1 : 0);
+        else with_fmt(a.shared_fmt, [&](auto S) { dec_k2_kernel<decltype(S)::value><<<k2, 256, 0, s>>>(a, route ? 1 : 0); });
+    }
     if (stage == 0 || stage == 3) {
         if (d->gate_type == MOE_CB2) dec_k3_kernel<MOE_CB2><<<k3, 256, 0, s>>>(a);
         else if (a.D == 4096) dec_k3_q2k4096_kernel<<<k3, 256, 0, s>>>(a);

@@ -85,6 +85,32 @@ def test_one_token_full_width(E, k, Fs, accumulate):
     _log("one token E=%d k=%d Fs=%d: worst relative error %.3g" % (E, k, Fs, worst))
 
 
+def test_one_token_stages_and_repeats_are_bitwise_equal(flash):
+    # the one-token schedule at full width: stages 1-4 one by one, and the
+    # same call repeated on one workspace, give bitwise the same y and routing
+    import torch
+
+    import quantized_routed_moe_router_amd as moe
+    L, W = flash
+    x = gu.x_to_device(x=synth.activations(10, 1, L.n_embd))
+    ws = moe.alloc_workspace(W, 1)
+    r = moe.Routing(1, L.n_expert_used, L.n_expert)
+    y = torch.zeros((1, L.n_embd), dtype=torch.float32, device="cuda")
+    for st in (1, 2, 3, 4):
+        moe.layer_forward_stage(W, x, y, ws, st, routing=r)
+    outs = []
+    for _ in range(3):
+        y2 = torch.zeros_like(y)
+        r2 = moe.Routing(1, L.n_expert_used, L.n_expert)
+        moe.layer_forward(W, x, y2, ws, routing=r2)
+        outs.append((y2, r2))
+    torch.cuda.synchronize()
+    for y2, r2 in outs:
+        assert torch.equal(y, y2) and torch.equal(r.topk_idx, r2.topk_idx) and torch.equal(r.topk_w, r2.topk_w)
+    y_ref, _, _ = oracle.moe_forward(L, x=x.cpu().numpy())
+    gu.assert_close(y.cpu().numpy(), y_ref)
+
+
 def test_prefill_2048(flash):
     L, W = flash
     _run(synth.prefill_2048(L), W, [0, 1, 511, 1024, 2047])

@@ -7,6 +7,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "../../include/moe.h"
 
 #define MOE_DEV __device__ __forceinline__
@@ -381,24 +383,46 @@ MOE_DEV int sdot4(uint32_t a, uint32_t b, int c) { return __builtin_amdgcn_sdot4
 
 // sum_g inv_g * (d*sc_g*sum_i q_i c_i) - dmin * sum_g m_g * sx_g, the integer
 // dot of each group exact in int32 (|sum| < 2^21)
+// Byte N of v as a float, in one instruction (the compiler would extract
+// the byte first).
+template <int N>
+MOE_DEV float byte_to_float(uint32_t v) {
+    float f;
+    if constexpr (N == 0) __asm__("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(v));
+    else if constexpr (N == 1) __asm__("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(v));
+    else if constexpr (N == 2) __asm__("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(v));
+    else __asm__("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(v));
+    return f;
+}
+
+// the scale nibbles (low) and min nibbles (high) of the 4 group bytes, each
+// byte converted in place
 MOE_DEV float q2k_dot2(const Q2KChunk &c, const XQ2K &p) {
     const float d = half_bits_to_float(c.dd), dmin = half_bits_to_float(c.dd >> 16);
+    const uint32_t scs = c.sm & 0x0F0F0F0Fu, mns = (c.sm >> 4) & 0x0F0F0F0Fu;
     float acc_q = 0.f, acc_m = 0.f;
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
+    auto group = [&](auto G) {
+        constexpr int g = decltype(G)::value;
         const uint32_t q = c.qs[g];
-        int A = 0, B = 0;
+        uint32_t t[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t t = (q >> (2 * j)) & 0x03030303u;
-            A = sdot4(t, p.g[g].a[j], A);
-            B = sdot4(t, p.g[g].b[j], B);
-        }
-        const uint32_t smb = (c.sm >> (8 * g)) & 0xFFu;
-        const float sq = (float)(256 * A + B);
-        acc_q = __builtin_fmaf((float)(smb & 15u) * p.g[g].inv, sq, acc_q);
-        acc_m = __builtin_fmaf((float)(smb >> 4), p.g[g].sx, acc_m);
-    }
+        for (int j = 0; j < 4; ++j) t[j] = (q >> (2 * j)) & 0x03030303u;
+        // sum_i q_i c_i = 256 A + B: the B chain starts from 256 A, so the
+        // combination costs one shift and no zeroed accumulator
+        int A = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) A = sdot4(t[j], p.g[g].a[j], A);
+        int S = A << 8;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S = sdot4(t[j], p.g[g].b[j], S);
+        const float sq = (float)S;
+        acc_q = __builtin_fmaf(byte_to_float<g>(scs) * p.g[g].inv, sq, acc_q);
+        acc_m = __builtin_fmaf(byte_to_float<g>(mns), p.g[g].sx, acc_m);
+    };
+    group(std::integral_constant<int, 0>());
+    group(std::integral_constant<int, 1>());
+    group(std::integral_constant<int, 2>());
+    group(std::integral_constant<int, 3>());
     return d * acc_q - dmin * acc_m;
 }
 

@@ -314,9 +314,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
 
 // K3 for Q2K gate/up rows of 4096 weights.  The block issues all of its
 // copies into LDS at once, in the order [x records of the first token]
-// [gate rows 0-3][up rows 0-3][gate rows 4-7]...[up rows 12-15]: 13 copies of
-// 256 units of 16 bytes, lane-contiguous, so that no copy is partial.  The
-// waves then work through the 4-row groups in that order, each as soon as
+// [gate rows 0-15][up rows 0-15] (each a contiguous range of the matrix, so
+// a lane's source address is one add per copy): 13 copies of 256 units of
+// 16 bytes, lane-contiguous, so that no copy is partial.  The waves then
+// work through the 4-row groups in that order, each as soon as
 // every copy that covers it has landed (the block's copies land in issue
 // order per wave; a barrier joins the waves), so the dot products of one
 // group run under the copies of the next.  Wave w takes column quarter w of
@@ -358,12 +359,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
         for (int i = 0; i < kK3PCopies; ++i) {
             const int u = 256 * i + tid;
             const void *src;
-            if (u < kK3PXu) {
-                src = xs + u;
-            } else {
-                const int v = u - kK3PXu, hgrp = v / kK3PHu, o = v - hgrp * kK3PHu;
-                src = ((hgrp & 1) ? um : gm) + (hgrp >> 1) * (4 * RB) + 16 * o;
-            }
+            if (u < kK3PXu) src = xs + u;
+            else if (u < kK3PXu + 4 * kK3PHu) src = gm + 16 * (u - kK3PXu);
+            else src = um + 16 * (u - kK3PXu - 4 * kK3PHu);
             dma16_m0(src, lb + 4096 * i);
         }
     }
@@ -390,7 +388,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
 #pragma unroll
         for (int hgrp = 0; hgrp < 8; ++hgrp) {
             const float s = row16_sum(v[hgrp]);
-            if (c == 0) part[wave][2 * (4 * (hgrp >> 1) + lr) + (hgrp & 1)] = s;
+            if (c == 0) part[wave][2 * (4 * (hgrp & 3) + lr) + (hgrp >> 2)] = s;  // groups 0-3 gate, 4-7 up
         }
         block_lds_sync();
         if (wave == 0) {

@@ -176,11 +176,16 @@ MOE_DEV void sg_wait() {
     __builtin_amdgcn_sched_barrier(0);
 }
 
-__global__ void __launch_bounds__(256) dec_k2_q8sg4096_kernel(FfnArgs a, int do_route) {
+// do_route 1: block 0 (a block of its own) finishes the routing; 2 (one
+// token): a fifth wave of block 0 does, so that the grid is one block per
+// 8 shared rows and every block gets a compute unit of its own (the LDS
+// areas allow one block per unit).
+__global__ void __launch_bounds__(320) dec_k2_q8sg4096_kernel(FfnArgs a, int do_route) {
     __shared__ __align__(16) u32x4 area[4][64 * kSgCopies];
     __shared__ float part[4][16];
     int b = blockIdx.x;
-    if (do_route) {
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if (do_route == 1) {
         if (b == 0) {
             route_finish_block(a.logits, a.T, a.E, a.k, a.route_scale, a.w_topk_idx, a.w_topk_w, a.w_count,
                                a.w_offset, a.w_perm, a.w_pos, a.w_active, a.w_n_active, a.slots, a.nslots);
@@ -188,7 +193,18 @@ __global__ void __launch_bounds__(256) dec_k2_q8sg4096_kernel(FfnArgs a, int do_
         }
         b -= 1;
     }
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    if (wave == 4) {  // joins the block's barriers below: one per token, one between tokens
+        if (do_route == 2 && b == 0) {
+            const int my_e = select_topk(a.logits, a.E, a.k, a.route_scale, a.w_topk_idx, a.w_topk_w);
+            bucket_one_token(my_e, a.k, a.E, a.w_count, a.w_offset, a.w_perm, a.w_pos, a.w_active, a.w_n_active,
+                             a.slots, a.nslots);
+        }
+        for (int t = 0; t < a.T; ++t) {
+            __syncthreads();
+            if (t + 1 < a.T) __syncthreads();
+        }
+        return;
+    }
     const int row0 = 8 * b;  // rows row0 .. row0 + 7 of gate and of up
     constexpr int RB = 4096 / 32 * kQ8Bytes;  // bytes of a row: 4352
     {
@@ -729,7 +745,10 @@ hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32
     }
     if ((stage == 0 || stage == 2) && k2 > 0)
     {
-        if (sg_staged) dec_k2_q8sg4096_kernel<<<(route ? 1 : 0) + a.Fs / 8, 256, 0, s>>>(a, route ? 1 : 0);
+        if (sg_staged) {
+            const int mode = !route ? 0 : (T == 1 && a.k <= 16 ? 2 : 1);
+            dec_k2_q8sg4096_kernel<<<(mode == 1 ? 1 : 0) + a.Fs / 8, 320, 0, s>>>(a, mode);
+        }
         else with_fmt(a.shared_fmt, [&](auto S) { dec_k2_kernel<decltype(S)::value><<<k2, 256, 0, s>>>(a, route ? 1 : 0); });
     }
     if (stage == 0 || stage == 3) {

@@ -209,7 +209,11 @@ MOE_DEV int select_topk_per(const double *lg, int E, int k, float route_scale, i
     int my_e = 0;
     for (int s = 0; s < k; ++s) {
         const double wv = wave_max_f64(bv);
-        const int we = wave_min_i32(bv == wv ? be : NONE);
+        // Usually one lane offers the maximum: take its expert by ballot;
+        // only an exact tie needs the lowest index across lanes.
+        const uint64_t tied = __ballot(bv == wv);
+        const int we = __popcll(tied) == 1 ? __builtin_amdgcn_readlane(be, (int)__builtin_ctzll(tied))
+                                           : wave_min_i32(bv == wv ? be : NONE);
         if (we == be) {  // the one lane whose candidate won
             avail &= ~(1u << ((be - lane) >> 6));
             rescan();
@@ -242,6 +246,45 @@ MOE_DEV int select_topk(const double *lg, int E, int k, float route_scale, int32
 // pair p.  Every count, offset and slot is a count over the P pairs (the
 // stable counting sort); the active list comes from ballots in expert order.
 // slots (optional): records of slots [0, nslots).
+// Bucketing of one token's k distinct experts by one wave (lanes < k hold
+// slot s's expert ep): rank = number of selected experts below ep is the
+// pair's bucket position; count and offset of every expert come from k
+// comparisons each.  Same outputs as bucket_wave with P = k.
+MOE_DEV void bucket_one_token(int ep, int k, int E, int32_t *__restrict__ count, int32_t *__restrict__ offset,
+                              int32_t *__restrict__ perm, int32_t *__restrict__ pos, int32_t *__restrict__ active,
+                              int32_t *__restrict__ n_active, SlotRec *__restrict__ slots, int nslots) {
+    const int lane = threadIdx.x & 63;
+    int eq[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) eq[q] = q < k ? __builtin_amdgcn_readlane(ep, q) : 0x7FFFFFFF;
+    if (lane < k) {
+        int rank = 0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) rank += eq[q] < ep;
+        perm[rank] = lane;
+        pos[lane] = rank;
+        active[rank] = ep;
+        if (slots && rank < nslots) slots[rank] = make_slot(ep, rank, 1, 0, 0);
+    }
+    for (int e = lane; e < E; e += 64) {
+        int below = 0, hit = 0;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            below += eq[q] < e;
+            hit += eq[q] == e;
+        }
+        count[e] = hit;
+        offset[e] = below;
+        if (e >= k) active[e] = -1;
+    }
+    if (slots)
+        for (int s = k + lane; s < nslots; s += 64) slots[s] = make_slot(-1, 0, 0, 0, 0);
+    if (lane == 0) {
+        n_active[0] = k;
+        offset[E] = k;
+    }
+}
+
 MOE_DEV void bucket_wave(int ep, int P, int E, int k, int32_t *__restrict__ count, int32_t *__restrict__ offset,
                          int32_t *__restrict__ perm, int32_t *__restrict__ pos, int32_t *__restrict__ active,
                          int32_t *__restrict__ n_active, SlotRec *__restrict__ slots, int nslots) {
@@ -381,7 +424,7 @@ MOE_DEV void route_finish_block(const double *__restrict__ logits, int T, int E,
     if (T == 1 && k <= 16) {
         if (wave == 0) {
             const int my_e = select_topk(logits, E, k, route_scale, topk_idx, topk_w);
-            bucket_wave(my_e, k, E, k, count, offset, perm, pos, active, n_active, slots, nslots);
+            bucket_one_token(my_e, k, E, count, offset, perm, pos, active, n_active, slots, nslots);
         }
         return;
     }

@@ -222,7 +222,10 @@ def main():
     if not small:
         gateup_bytes += sh_gu + T * Fs * 4
     achieved = gateup_bytes / (gateup_ms * 1e-3) / 1e9
-    kernel_name = "dec_k3_kernel" if small else "large_gateup_kernel"
+    if small:  # the decode gate/up kernel this layer takes
+        kernel_name = "dec_k3_q2k4096_kernel" if L.gate_fmt == synth.Q2K and D == 4096 else "dec_k3_kernel"
+    else:
+        kernel_name = "large_gateup_kernel"
     tokens_s = T / (ms_step * 1e-3)
     flops = 2.0 * T * (k * 3 * D * F + 3 * D * Fs)
 
@@ -290,7 +293,7 @@ def measured_traffic(kernel, workload):
         elif line.startswith("- kernel_source_sha256:"):
             vals["sha"] = line.split(":", 1)[1].strip()
     from quantized_routed_moe_router_amd.profsum import kernel_source_digest
-    if "bytes" not in vals or vals.get("sha") != kernel_source_digest():
+    if "bytes" not in vals or vals.get("sha") != kernel_source_digest(kernel):
         return None
     return vals["bytes"]
 

@@ -70,12 +70,26 @@ def counters(path, match):
 COPY_KERNEL = "copyBuffer"
 
 
-def kernel_source_digest():
-    """SHA-256 over the library's HIP sources (csrc/), in file-name order."""
+# The sources each kernel family is compiled from (its translation unit and
+# the headers it includes); other kernels use every file of csrc/.
+KERNEL_SOURCES = {
+    "dec_": ("common.h", "ffn_dev.h", "route_dev.h", "k_decode.hip"),
+    "pf_": ("common.h", "ffn_dev.h", "k_prefill.hip"),
+    "large_": ("common.h", "ffn_dev.h", "k_ffn_large.hip"),
+}
+
+
+def kernel_source_digest(kernel=None):
+    """SHA-256 over the HIP sources the kernel is built from (csrc/), in
+    file-name order: a counter summary is stale once this changes."""
     import hashlib
     h = hashlib.sha256()
     root = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
-    for f in sorted(os.listdir(root)):
+    files = sorted(os.listdir(root))
+    for prefix, srcs in KERNEL_SOURCES.items():
+        if kernel and kernel.startswith(prefix):
+            files = sorted(srcs)
+    for f in files:
         with open(os.path.join(root, f), "rb") as fh:
             h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()
@@ -113,7 +127,7 @@ def hbm(a):
               % (a.algorithmic_bytes, traffic / a.algorithmic_bytes))
     print()
     print("- traffic_bytes_per_launch: %.0f" % traffic)
-    print("- kernel_source_sha256: %s" % kernel_source_digest())
+    print("- kernel_source_sha256: %s" % kernel_source_digest(a.hbm))
     return 0
 
 

@@ -47,6 +47,9 @@ def _load():
         lib.orc_moe_forward_dense.argtypes = [P, ctypes.c_int, P, P, I32, P]
         lib.orc_rmsnorm.argtypes = [P, P, D, I32, I32, P]
         lib.orc_swiglu.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P, P, I32, I32, ctypes.c_int, P, P]
+        lib.orc_count_selections.argtypes = [P, I32, I32, I32, I32, P]
+        lib.orc_hotlist.restype = I32
+        lib.orc_hotlist.argtypes = [P, I32, P]
         lib.orc_version.restype = ctypes.c_char_p
         _lib = lib
     return _lib
@@ -179,6 +182,23 @@ def rmsnorm(x, gamma, eps=1e-6):
     out = np.empty_like(x)
     _load().orc_rmsnorm(_p(x), _p(g), eps, T, D, _p(out))
     return out
+
+
+def count_selections(topk_idx, E, layer, counts):
+    """Adds the selections of one layer's routing into counts [n_layer*E] int64 (in place)."""
+    idx = _c(topk_idx, np.int32)
+    assert counts.dtype == np.int64 and counts.flags.c_contiguous
+    T, k = idx.shape
+    _load().orc_count_selections(_p(idx), T, k, E, layer, _p(counts))
+    return counts
+
+
+def hotlist(counts):
+    """(order, n_hot): indices by hits descending, ties by index; n_hot = positive counts."""
+    c = _c(counts, np.int64)
+    order = np.empty(c.shape[0], np.int32)
+    n_hot = _load().orc_hotlist(_p(c), c.shape[0], _p(order))
+    return order, n_hot
 
 
 def swiglu(fmt_gu, fmt_down, gate, up, down, D, F, x, mode=F32, codebook=None):

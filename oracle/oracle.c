@@ -385,4 +385,38 @@ int orc_rmsnorm(const float *x, const float *gamma, double eps, int32_t T, int32
     return 0;
 }
 
+/* Selections per {layer, expert} ([SPE] "Some experts run far more often than
+ * others"), added into an existing profile. */
+void orc_count_selections(const int32_t *topk_idx, int32_t T, int32_t k, int32_t E, int32_t layer, int64_t *counts) {
+    for (int64_t p = 0; p < (int64_t)T * k; ++p) {
+        const int32_t e = topk_idx[p];
+        if (e >= 0 && e < E) counts[(int64_t)layer * E + e] += 1;
+    }
+}
+
+static const int64_t *hot_counts;
+static int64_t hot_key(int32_t i) {
+    const int64_t c = hot_counts[i];
+    return c < 0 ? 0 : (c >= ((int64_t)1 << 39) ? ((int64_t)1 << 39) - 1 : c);
+}
+static int hot_cmp(const void *a, const void *b) {
+    const int32_t i = *(const int32_t *)a, j = *(const int32_t *)b;
+    const int64_t ci = hot_key(i), cj = hot_key(j);
+    if (ci != cj) return ci > cj ? -1 : 1;  /* more hits first */
+    return i < j ? -1 : (i > j);             /* then lower {layer, expert} index */
+}
+
+/* The hot list: {layer, expert} entries sorted by hits ([SPE] "Some experts run
+ * far more often than others"; ties by index, our reading). */
+int32_t orc_hotlist(const int64_t *counts, int32_t n, int32_t *order) {
+    int32_t hot = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        order[i] = i;
+        hot += counts[i] > 0;
+    }
+    hot_counts = counts;
+    qsort(order, (size_t)n, sizeof(int32_t), hot_cmp);
+    return hot;
+}
+
 const char *orc_version(void) { return "oracle-1"; }

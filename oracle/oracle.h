@@ -13,7 +13,8 @@
  *         steps, 5.6.2 RMSNorm per layer.
  *  [SPE]  "The sparsity that pays for everything else in DwarfStar": "Where the
  *         parameters actually are" (shape and parameter arithmetic), "Quantize
- *         by role, not by tensor".
+ *         by role, not by tensor", "Some experts run far more often than
+ *         others" (selection counts and the hot list).
  *  [RDM]  antirez/ds4 README mirror: the --batched-session paragraph
  *         ("batching is exact").
  * Where the pages are silent the oracle takes the readings listed in the design doc
@@ -73,6 +74,16 @@ int orc_rmsnorm(const float *x, const float *gamma, double eps, int32_t T, int32
 /* One SwiGLU FFN on one token (weights [F][D], [F][D], [D][F]); y[D] in double. */
 int orc_swiglu(int fmt_gu, int fmt_down, const uint8_t *gate, const uint8_t *up, const uint8_t *down,
                const int8_t *cb, int32_t D, int32_t F, int mode, const double *x, double *y);
+/* Expert selection counts and the hot list ([SPE] "Some experts run far
+ * more often than others": a run counts expert selections per {layer,
+ * expert}, merges them into an existing profile, sorts and writes the list).
+ * counts[layer*E + e] += the number of pairs (t, s) with topk_idx[t*k+s] == e;
+ * entries outside [0, E) are not counted. */
+void orc_count_selections(const int32_t *topk_idx, int32_t T, int32_t k, int32_t E, int32_t layer, int64_t *counts);
+/* order[0..n) = 0..n-1 sorted by counts descending, ties by index ascending
+ * (counts clamped to [0, 2^39)); returns how many counts are positive. */
+int32_t orc_hotlist(const int64_t *counts, int32_t n, int32_t *order);
+
 const char *orc_version(void);
 
 #endif

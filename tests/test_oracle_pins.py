@@ -399,3 +399,34 @@ def test_stack_teacher_forcing_is_consistent():
     forced = oracle.stack_forward(layers, x, teacher=[x] + free[:-1])
     for a, b in zip(free, forced):
         assert np.array_equal(a, b)
+
+
+# Selection counts and the hot list ("The sparsity that pays for everything
+# else in DwarfStar", "Some experts run far more often than others").
+
+def test_count_selections_is_a_histogram_and_merges():
+    rng = np.random.default_rng(5)
+    E, n_layer = 40, 3
+    counts = np.zeros(n_layer * E, np.int64)
+    expect = np.zeros(n_layer * E, np.int64)
+    for layer, T, k in ((0, 7, 3), (2, 5, 6), (0, 4, 2)):  # layer 0 twice: the second merges
+        idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
+        oracle.count_selections(idx, E, layer, counts)
+        expect[layer * E:(layer + 1) * E] += np.bincount(idx.ravel(), minlength=E)
+    assert np.array_equal(counts, expect)
+    assert counts.sum() == 7 * 3 + 5 * 6 + 4 * 2 and counts[E:2 * E].sum() == 0
+    # indices outside [0, E) are not counted
+    c2 = np.zeros(E, np.int64)
+    oracle.count_selections(np.array([[-1, 0, E, 3]], np.int32), E, 0, c2)
+    assert c2.sum() == 2 and c2[0] == 1 and c2[3] == 1
+
+
+def test_hotlist_orders_by_hits_then_index():
+    # a hand case: ties (5 at 1 and 4; 0 at 0, 3, 5) keep the lower index first
+    order, n_hot = oracle.hotlist(np.array([0, 5, 9, 0, 5, 0, 2], np.int64))
+    assert order.tolist() == [2, 1, 4, 6, 0, 3, 5] and n_hot == 4
+    rng = np.random.default_rng(6)
+    c = rng.integers(0, 12, size=43 * 256).astype(np.int64)  # many ties
+    order, n_hot = oracle.hotlist(c)
+    assert order.tolist() == sorted(range(c.size), key=lambda i: (-int(c[i]), i))
+    assert n_hot == int((c > 0).sum())

@@ -27,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE-layer tokens/s; decode HBM GB/s and prefill MFMA % of MI355X peak"
+ALU_PEAK_TOPS = 256 * 64 * 2.4e9 / 1e12  # 32-bit lane operations per second: 256 CUs x 64 lanes x 2.4 GHz
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
 
@@ -41,7 +42,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=2048)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="decode_b1",
-                    choices=["decode_b1", "decode_b32", "prefill_2048", "stack43_b1", "stack43_b8"])
+                    choices=["decode_b1", "decode_b32", "prefill_2048", "stack43_b1", "stack43_b8", "hotlist_43x256"])
     ap.add_argument("--replicas", type=int, default=16)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu", action="store_true")
@@ -76,6 +77,9 @@ def main():
 
     if args.workload.startswith("stack43"):
         run_stack(args, int(args.workload.split("_b")[1]))
+        return
+    if args.workload == "hotlist_43x256":
+        run_hotlist(args)
         return
 
     import numpy as np
@@ -442,6 +446,100 @@ def run_stack(args, B):
             "avg_launch_us": round(gu_ms * 1e3, 3),
             "timing": "HIP events around runs of 43 back-to-back stage-3 launches (one per layer), %d runs, "
                       "median per launch" % n_runs,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_hotlist(args):
+    """Hot-expert profiling over the 43-block stack: per step, the selection
+    counts of 43 layers' routings (8 tokens, top-6 of 256, a Zipf-skewed
+    choice of experts so that some run far more often) are added into the
+    profile, then the 11,008 {layer, expert} entries are sorted by hits."""
+    import numpy as np
+    import torch
+
+    import quantized_routed_moe_router_amd as moe
+    torch.cuda.set_device(0)
+    n_layer, E, k, B = 43, 256, 6, 8
+    rng = np.random.default_rng(13)
+    idx = []
+    for l in range(n_layer):
+        p = 1.0 / np.arange(1, E + 1) ** 1.1
+        p = p[rng.permutation(E)]
+        p /= p.sum()
+        idx.append(torch.from_numpy(np.stack([rng.choice(E, k, replace=False, p=p) for _ in range(B)])
+                                    .astype(np.int32)).cuda())
+    n = n_layer * E
+    counts = torch.zeros(n, dtype=torch.int64, device="cuda")
+    order = torch.empty(n, dtype=torch.int32, device="cuda")
+    n_hot = torch.empty(1, dtype=torch.int32, device="cuda")
+
+    def step():
+        for l in range(n_layer):
+            moe.count_selections(idx[l], E, l, counts)
+        moe.hotlist(counts, order, n_hot)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    g.replay()
+    torch.cuda.synchronize()
+    K = args.steps
+    t0 = time.perf_counter()
+    for _ in range(K):
+        g.replay()
+    torch.cuda.synchronize()
+    ms_step = 1000.0 * (time.perf_counter() - t0) / K
+    # the sort's launch time: events around runs of 16 back-to-back launches
+    runs = []
+    for _ in range(8):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000000)
+        a.record()
+        for _ in range(16):
+            moe.hotlist(counts, order, n_hot)
+        b.record()
+        torch.cuda.synchronize()
+        runs.append(a.elapsed_time(b) / 16)
+    sort_ms = float(np.median(runs))
+    cmps = n * n  # the list by ranks: every key against every key
+    achieved = cmps / (sort_ms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu:
+        import oracle
+        host = [t.cpu().numpy() for t in idx]
+        c = np.zeros(n, np.int64)
+        done, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0):
+            for l in range(n_layer):
+                oracle.count_selections(host[l], E, l, c)
+            oracle.hotlist(c)
+            done += 1
+        el = time.perf_counter() - t0
+        cpu = {"value": round(done / el, 2), "unit": "profile steps/s", "cores": 1, "kind": "oracle",
+               "sample": "%d step(s) of 43 layers' counts and one sort of %d entries in %.1f s" % (done, n, el)}
+    line = {
+        "metric": "hot-expert profile steps/s (43 layers' selection counts + the sorted list)",
+        "value": round(1000.0 / ms_step, 1), "unit": "profile steps/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int64", "data": "synthetic",
+        "config": {"workload": args.workload, "n_layer": n_layer, "n_expert": E, "n_expert_used": k,
+                   "tokens_per_layer": B, "entries": n, "launch": "hipGraph of one step (44 launches), replayed"},
+        "roofline": {
+            "kernel": "hotlist_kernel", "bound": "alu", "achieved": round(achieved, 4), "peak": ALU_PEAK_TOPS,
+            "unit": "T key compares/s", "frac": round(achieved / ALU_PEAK_TOPS, 5), "traffic": None,
+            "avg_launch_us": round(sort_ms * 1e3, 3),
+            "note": "each compare is a 64-bit compare and an add (about 3 lane operations); a one-launch "
+                    "list of 11,008 entries is mostly launch and LDS staging",
         },
         "cpu_baseline": cpu,
     }

@@ -147,6 +147,30 @@ int moe_layer_forward_stage(const moe_layer_desc *desc, const void *x, int32_t T
                             uint32_t flags, const moe_routing *routing, int32_t stage, void *ws, size_t ws_bytes,
                             void *stream, char *err, size_t errlen);
 
+/* Expert selection counts for the hot list ("The sparsity that pays for
+ * everything else in DwarfStar", "Some experts run far more often than
+ * others": a run counts expert selections per {layer, expert} and merges
+ * them into an existing profile).
+ * topk_idx: [T][k] int32, the routing of one layer (moe_routing.topk_idx).
+ * counts: [n_layer][E] int64, caller-owned and caller-initialised (zeros, or
+ * a profile loaded earlier): counts[layer][e] += the number of (t, s) with
+ * topk_idx[t][s] == e.  Entries outside [0, E) are not counted.  The adds
+ * are integer, so the result does not depend on their order.  T = 0
+ * enqueues nothing. */
+int moe_count_selections(const int32_t *topk_idx, int32_t T, int32_t k, int32_t E, int32_t layer, int64_t *counts,
+                         void *stream, char *err, size_t errlen);
+
+/* The hot list (same section: the profile's entries sorted by hits, which
+ * the engine walks to seed its expert cache).  counts: [n] int64 (n =
+ * n_layer * E, entry layer*E + e); order: [n] int32 receives the entry
+ * indices sorted by count descending, equal counts by index ascending;
+ * n_hot: [1] int32 receives the number of entries with a positive count (the
+ * list's length).  Counts are ordered as if clamped to [0, 2^39).  n must be
+ * in [0, 16384]; n = 0 enqueues nothing.  One workgroup sorts the entries in
+ * LDS. */
+int moe_hotlist(const int64_t *counts, int32_t n, int32_t *order, int32_t *n_hot, void *stream, char *err,
+                size_t errlen);
+
 /* out[t][i] = gamma[i] * x[t][i] / sqrt(mean_i x[t][i]^2 + eps), fp32 in and
  * out, accumulated in fp32 ("Understanding Dwarf Star", 5.2.1 and 5.6.2:
  * RMSNorm before each block).  out may equal x. */

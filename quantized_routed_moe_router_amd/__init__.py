@@ -62,7 +62,10 @@ _lib.moe_layer_forward_stage.argtypes = [ctypes.POINTER(LayerDesc), _P, _I32, _I
 _lib.moe_rmsnorm.argtypes = [_P, _P, ctypes.c_float, _I32, _I32, _P, _P, ctypes.c_char_p, _SZ]
 _lib.moe_dequant.argtypes = [_I32, _P, _I64, _P, _I32, _P, _P, ctypes.c_char_p, _SZ]
 _lib.moe_version.restype = ctypes.c_char_p
-for _f in ("moe_route", "moe_expert_ffn", "moe_layer_forward_stage", "moe_layer_forward", "moe_rmsnorm", "moe_dequant"):
+_lib.moe_count_selections.argtypes = [_P, _I32, _I32, _I32, _I32, _P, _P, ctypes.c_char_p, _SZ]
+_lib.moe_hotlist.argtypes = [_P, _I32, _P, _P, _P, ctypes.c_char_p, _SZ]
+for _f in ("moe_route", "moe_expert_ffn", "moe_layer_forward_stage", "moe_layer_forward", "moe_rmsnorm", "moe_dequant",
+           "moe_count_selections", "moe_hotlist"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -201,6 +204,23 @@ def rmsnorm(x, gamma, out, eps=1e-6, stream=None):
     err = ctypes.create_string_buffer(512)
     _check(_lib.moe_rmsnorm(_ptr(x), _ptr(gamma), eps, x.shape[0], x.shape[1], _ptr(out), _stream(stream), err,
                             512), err)
+
+
+def count_selections(topk_idx, E, layer, counts, stream=None):
+    """counts [n_layer*E] int64 (device) += selections of topk_idx [T][k] int32 in layer `layer`."""
+    assert topk_idx.dtype == torch.int32 and topk_idx.is_contiguous() and topk_idx.dim() == 2
+    assert counts.dtype == torch.int64 and counts.is_contiguous()
+    err = ctypes.create_string_buffer(512)
+    _check(_lib.moe_count_selections(_ptr(topk_idx), topk_idx.shape[0], topk_idx.shape[1], E, layer, _ptr(counts),
+                                     _stream(stream), err, 512), err)
+
+
+def hotlist(counts, order, n_hot, stream=None):
+    """order [n] int32 <- entries by hits descending, ties by index; n_hot [1] int32 <- positive entries."""
+    assert counts.dtype == torch.int64 and counts.is_contiguous()
+    assert order.dtype == torch.int32 and n_hot.dtype == torch.int32 and order.numel() == counts.numel()
+    err = ctypes.create_string_buffer(512)
+    _check(_lib.moe_hotlist(_ptr(counts), counts.numel(), _ptr(order), _ptr(n_hot), _stream(stream), err, 512), err)
 
 
 def dequant(fmt, src, n_weights, out, codebook=None, stream=None):

@@ -183,6 +183,26 @@ int moe_layer_forward_stage(const moe_layer_desc *d, const void *x, int32_t T, i
     return device_status(forward(d, x, T, x_type, r, y, flags, w, (hipStream_t)stream, stage), err, errlen);
 }
 
+int moe_count_selections(const int32_t *topk_idx, int32_t T, int32_t k, int32_t E, int32_t layer, int64_t *counts,
+                         void *stream, char *err, size_t errlen) {
+    if (T < 0 || k < 1 || E < 1 || layer < 0)
+        return fail(err, errlen, MOE_EINVAL, "need T >= 0, k >= 1, E >= 1, layer >= 0 (T=%d k=%d E=%d layer=%d)", T, k,
+                    E, layer);
+    if (T == 0) return MOE_OK;
+    if (!topk_idx || !counts) return fail(err, errlen, MOE_EINVAL, "topk_idx and counts must be set");
+    return device_status(launch_count_selections(topk_idx, T, k, E, layer, counts, (hipStream_t)stream), err,
+                         errlen);
+}
+
+int moe_hotlist(const int64_t *counts, int32_t n, int32_t *order, int32_t *n_hot, void *stream, char *err,
+                size_t errlen) {
+    if (n < 0 || n > kMaxHotlist)
+        return fail(err, errlen, MOE_EINVAL, "n must be in [0, %d] (got %d)", kMaxHotlist, n);
+    if (n == 0) return MOE_OK;
+    if (!counts || !order || !n_hot) return fail(err, errlen, MOE_EINVAL, "counts, order and n_hot must be set");
+    return device_status(launch_hotlist(counts, n, order, n_hot, (hipStream_t)stream), err, errlen);
+}
+
 int moe_rmsnorm(const float *x, const float *gamma, float eps, int32_t T, int32_t D, float *out, void *stream,
                 char *err, size_t errlen) {
     if (T < 0 || D <= 0) return fail(err, errlen, MOE_EINVAL, "need T >= 0 and D > 0 (T=%d D=%d)", T, D);

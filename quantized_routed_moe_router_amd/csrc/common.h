@@ -675,6 +675,11 @@ hipError_t launch_ffn_large_shared(const moe_layer_desc *d, const void *x, int32
 bool prefill_path_ok(const moe_layer_desc *d, int32_t T, int32_t x_type);
 hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, const RoutingPtrs &r, float *y,
                           uint32_t flags, const Workspace &ws, hipStream_t s, int stage);
+constexpr int kMaxHotlist = 16384;                  // entries one hot-list sort takes
+constexpr int64_t kHotCountMax = (int64_t)1 << 39;  // counts are clamped below this in the sort key
+hipError_t launch_count_selections(const int32_t *topk_idx, int32_t T, int32_t k, int32_t E, int32_t layer,
+                                   int64_t *counts, hipStream_t s);
+hipError_t launch_hotlist(const int64_t *counts, int32_t n, int32_t *order, int32_t *n_hot, hipStream_t s);
 hipError_t launch_rmsnorm(const float *x, const float *gamma, float eps, int32_t T, int32_t D, float *out,
                           hipStream_t s);
 hipError_t launch_dequant(int32_t type, const void *src, int64_t n, const int8_t *cb, int32_t out_type, void *dst,

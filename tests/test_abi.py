@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol():
     import quantized_routed_moe_router_amd as moe
     names = _declared()
     assert {"moe_route", "moe_expert_ffn", "moe_layer_forward", "moe_layer_forward_stage", "moe_workspace_size",
-            "moe_rmsnorm", "moe_dequant", "moe_version"} <= names
+            "moe_rmsnorm", "moe_dequant", "moe_version", "moe_count_selections", "moe_hotlist"} <= names
     for n in names:
         assert hasattr(moe._lib, n), n
     assert moe.version().startswith("moe-gfx950")
@@ -108,3 +108,14 @@ def test_other_entry_points_validate():
     for stage in (0, 5):
         assert moe._lib.moe_layer_forward_stage(ctypes.byref(d), 0x80000, 1, 0, 0x100000, 0, None, stage, 0x90000,
                                                 1 << 30, None, err, 256) == -1
+
+
+def test_hotlist_and_counts_validate_before_enqueue():
+    import quantized_routed_moe_router_amd as moe
+    err = ctypes.create_string_buffer(256)
+    assert moe._lib.moe_hotlist(None, 16385, None, None, None, err, 256) == -1
+    assert b"16384" in err.value
+    assert moe._lib.moe_hotlist(None, 0, None, None, None, err, 256) == 0  # nothing to sort
+    assert moe._lib.moe_count_selections(None, 4, 0, 8, 0, None, None, err, 256) == -1
+    assert moe._lib.moe_count_selections(None, 0, 6, 8, 0, None, None, err, 256) == 0  # T = 0
+    assert moe._lib.moe_count_selections(None, 1, 6, 8, 0, None, None, err, 256) == -1  # pointers unset

@@ -232,3 +232,39 @@ def test_graph_replays_match_eager():
         yb = torch.zeros_like(y)
         moe.layer_forward(W, xb, yb, ws)  # other eager work on the same workspace
         torch.cuda.synchronize()
+
+
+def test_selection_counts_and_hotlist_bit_exact():
+    # counts per {layer, expert} merged over 43 layers of routings (one from a
+    # real forward, with out-of-range entries mixed in elsewhere), then hot
+    # lists with many ties, a size that is not a power of two, one entry, the
+    # largest size and counts beyond the sort key's range
+    import quantized_routed_moe_router_amd as moe
+    rng = np.random.default_rng(11)
+    E, n_layer = 256, 43
+    counts = torch.zeros(n_layer * E, dtype=torch.int64, device="cuda")
+    ref = np.zeros(n_layer * E, np.int64)
+    L = synth.make_layer(105, 0, D=256, E=E, k=6, F=128, Fs=0)
+    W = gu.upload(L)
+    y, r = gu.run_forward(W, gu.x_to_device(x=synth.activations(106, 9, 256)))
+    for layer in range(n_layer):
+        if layer == 0:
+            idx = r.topk_idx.cpu().numpy()
+        else:
+            T = int(rng.integers(1, 40))
+            idx = rng.integers(-2, E + 2, size=(T, 6)).astype(np.int32)
+        moe.count_selections(gu.dev(idx), E, layer, counts)
+        oracle.count_selections(idx, E, layer, ref)
+    torch.cuda.synchronize()
+    assert np.array_equal(counts.cpu().numpy(), ref)
+    cases = [ref, rng.integers(0, 5, size=11008), rng.integers(0, 3, size=16384), np.array([7]),
+             np.array([0, 0, 0]), np.array([2 ** 40, 2 ** 39 - 1, 2 ** 39, 5, -3, 5])]
+    for c in cases:
+        c = np.asarray(c, np.int64)
+        order = torch.empty(c.size, dtype=torch.int32, device="cuda")
+        n_hot = torch.empty(1, dtype=torch.int32, device="cuda")
+        moe.hotlist(gu.dev(c), order, n_hot)
+        o_ref, nh_ref = oracle.hotlist(c)
+        torch.cuda.synchronize()
+        assert np.array_equal(order.cpu().numpy(), o_ref), c.size
+        assert int(n_hot.item()) == nh_ref

@@ -12,7 +12,7 @@ import numpy as np
 
 from . import build as _build
 
-F32, BF16, Q2K, Q8_0, CB2 = 0, 1, 2, 3, 4
+F32, BF16, Q2K, Q8_0, CB2, Q4K = 0, 1, 2, 3, 4, 5
 
 _lib = None
 

@@ -53,10 +53,10 @@ static double orc_silu(double z) { return z / (1.0 + exp(-z)); }
 /* ---- block formats ([UDS] 2.3.2-2.3.4; byte orders are this project's) -- */
 
 static int orc_block_weights(int fmt) {
-    return fmt == ORC_Q8_0 ? 32 : (fmt == ORC_Q2K || fmt == ORC_CB2) ? 256 : 0;
+    return fmt == ORC_Q8_0 ? 32 : (fmt == ORC_Q2K || fmt == ORC_CB2 || fmt == ORC_Q4K) ? 256 : 0;
 }
 static int orc_block_bytes(int fmt) {
-    return fmt == ORC_Q2K ? 84 : fmt == ORC_Q8_0 ? 34 : fmt == ORC_CB2 ? 66 : 0;
+    return fmt == ORC_Q2K ? 84 : fmt == ORC_Q8_0 ? 34 : fmt == ORC_CB2 ? 66 : fmt == ORC_Q4K ? 144 : 0;
 }
 
 int64_t orc_tensor_bytes(int fmt, int64_t n) {
@@ -74,6 +74,31 @@ static void orc_block_q2k(const uint8_t *b, float *w) {
         int g = i / 16;
         int sc = b[4 + g] & 15, mn = b[4 + g] >> 4;
         int q = (b[20 + i / 4] >> (2 * (i % 4))) & 3;
+        w[i] = (float)(d * sc * q - dmin * mn);
+    }
+}
+
+/* Q4_K super-block ([UDS] 2.3.2, the Q4_K layout): 256 weights in 8 sub-blocks
+ * of 32, fp16 d @0 and dmin @2, a 6-bit scale and a 6-bit min per sub-block
+ * packed into the 12 bytes @4, 4-bit codes @16.  The pages leave the packing
+ * order open: field f (scale of sub-block f for f < 8, min of sub-block f-8
+ * after) takes bits 6f..6f+5 of the 12 bytes read as one little-endian
+ * integer, and weight i's code takes bits 4*(i%2) of byte i/2.
+ * Weight value: d * scale_j * q - dmin * min_j. */
+static int orc_q4k_field(const uint8_t *p12, int f) {
+    int v = 0;
+    for (int b = 0; b < 6; ++b) {
+        int bit = 6 * f + b;
+        v |= ((p12[bit / 8] >> (bit % 8)) & 1) << b;
+    }
+    return v;
+}
+static void orc_block_q4k(const uint8_t *b, float *w) {
+    double d = orc_half(b), dmin = orc_half(b + 2);
+    for (int i = 0; i < 256; ++i) {
+        int j = i / 32;
+        int sc = orc_q4k_field(b + 4, j), mn = orc_q4k_field(b + 4, 8 + j);
+        int q = (b[16 + i / 2] >> (4 * (i % 2))) & 15;
         w[i] = (float)(d * sc * q - dmin * mn);
     }
 }
@@ -99,6 +124,7 @@ static void orc_block_cb2(const uint8_t *b, const int8_t *cb, float *w) {
 
 static void orc_block(int fmt, const uint8_t *b, const int8_t *cb, float *w) {
     if (fmt == ORC_Q2K) orc_block_q2k(b, w);
+    else if (fmt == ORC_Q4K) orc_block_q4k(b, w);
     else if (fmt == ORC_Q8_0) orc_block_q8_0(b, w);
     else orc_block_cb2(b, cb, w);
 }

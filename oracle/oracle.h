@@ -5,7 +5,8 @@
  * includes, links or calls it, and it includes nothing from the GPU library.
  *
  * Sources (cited by page title and section):
- *  [UDS]  "Understanding Dwarf Star" (ldazrz.com): 2.3.2 K-quant formats, the
+ *  [UDS]  "Understanding Dwarf Star" (ldazrz.com): 2.3.2 K-quant formats (the
+ *         Q4_K block layout), the
  *         Q2_K subsection (printed as 3.3.3), 2.3.4 IQ2_XXS, 2.4 the
  *         quantize-by-role table, 2.8.1-2.8.2 dequantize-on-the-fly grouped
  *         dot, 5.2.1 layer structure (norm + residual), 5.2.4 FFN, 5.3.2 MoE
@@ -27,7 +28,7 @@
 #define ORACLE_H
 #include <stdint.h>
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_Q2K = 2, ORC_Q8_0 = 3, ORC_CB2 = 4 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_Q2K = 2, ORC_Q8_0 = 3, ORC_CB2 = 4, ORC_Q4K = 5 };
 
 typedef struct {
     int32_t n_embd;        /* D */

@@ -26,9 +26,9 @@ import numpy as np
 
 from . import build as _build
 
-F32, BF16, Q2K, Q8_0, CB2 = 0, 1, 2, 3, 4
-BLOCK_WEIGHTS = {Q2K: 256, Q8_0: 32, CB2: 256}
-BLOCK_BYTES = {Q2K: 84, Q8_0: 34, CB2: 66}
+F32, BF16, Q2K, Q8_0, CB2, Q4K = 0, 1, 2, 3, 4, 5
+BLOCK_WEIGHTS = {Q2K: 256, Q8_0: 32, CB2: 256, Q4K: 256}
+BLOCK_BYTES = {Q2K: 84, Q8_0: 34, CB2: 66, Q4K: 144}
 
 # stream tags (one key per (seed, layer, tag, expert))
 TAG_X, TAG_ROUTER, TAG_GATE, TAG_UP, TAG_DOWN = 1, 2, 3, 4, 5

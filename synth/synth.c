@@ -2,7 +2,7 @@
  * synth.c - seeded synthetic inputs for the routed mixture-of-experts block.
  *
  * This module draws the random numbers (activations, router matrix, RMSNorm
- * weights, the codebook) and *encodes* Gaussian expert weights into the three
+ * weights, the codebook) and *encodes* Gaussian expert weights into the four
  * block formats the layer stores.  It holds none of the block's arithmetic: no
  * decoding of a block back to values, no routing, no products.  Both the GPU
  * library's tests and the CPU oracle read the bytes written here.
@@ -21,6 +21,10 @@
  *   Q8_0 34 B / 32 w:  d f16 @0, int8 q[32] @2.
  *   CB2  66 B / 256 w: d f16 @0, idx[32] u8 @2 (one codebook row per 8
  *        weights), sgn[32] u8 @34 (bit j flips the sign of weight j of the 8).
+ *   Q4K 144 B / 256 w: d f16 @0, dmin f16 @2, 12 bytes @4 of sixteen 6-bit
+ *        fields (bits 6f..6f+5; f < 8 the scale of sub-block f of 32 weights,
+ *        f >= 8 the min of sub-block f-8), codes @16 (weight i in bits
+ *        4*(i&1) of byte i>>1).
  * Matrices are [n_out][n_in] row-major, flattened and cut into consecutive
  * blocks.
  */
@@ -164,6 +168,49 @@ static void sy_encode_q2k(const float *v, uint8_t *blk) {
     }
 }
 
+/* Q4K (144 B): per sub-block j of 32 weights a 6-bit scale and min; field f
+ * of the 12 bytes @4 in bits 6f..6f+5 (scales f = 0..7, mins f = 8..15);
+ * weight i's 4-bit code in bits 4*(i%2) of byte 16 + i/2. */
+static void sy_put6(uint8_t *p12, int f, unsigned v) {
+    for (int b = 0; b < 6; ++b) {
+        int bit = 6 * f + b;
+        if ((v >> b) & 1u) p12[bit / 8] |= (uint8_t)(1u << (bit % 8));
+    }
+}
+
+static void sy_encode_q4k(const float *v, uint8_t *blk) {
+    float sr[8], mn[8], max_sr = 0.f, max_mn = 0.f;
+    for (int j = 0; j < 8; ++j) {
+        float lo = v[32 * j], hi = v[32 * j];
+        for (int i = 1; i < 32; ++i) {
+            float t = v[32 * j + i];
+            lo = t < lo ? t : lo;
+            hi = t > hi ? t : hi;
+        }
+        mn[j] = lo < 0.f ? -lo : 0.f;
+        sr[j] = (hi + mn[j]) / 15.f;
+        if (sr[j] > max_sr) max_sr = sr[j];
+        if (mn[j] > max_mn) max_mn = mn[j];
+    }
+    uint16_t dh = sy_f16_bits(max_sr / 63.f), mh = sy_f16_bits(max_mn / 63.f);
+    float d = sy_f16_val(dh), dmin = sy_f16_val(mh);
+    memset(blk, 0, 144);
+    memcpy(blk + 0, &dh, 2);
+    memcpy(blk + 2, &mh, 2);
+    for (int j = 0; j < 8; ++j) {
+        float sc = d > 0.f ? sy_rint_clamp(sr[j] / d, 0.f, 63.f) : 0.f;
+        float m = dmin > 0.f ? sy_rint_clamp(mn[j] / dmin, 0.f, 63.f) : 0.f;
+        sy_put6(blk + 4, j, (unsigned)sc);
+        sy_put6(blk + 4, 8 + j, (unsigned)m);
+        float step = d * sc, off = dmin * m;
+        for (int i = 0; i < 32; ++i) {
+            int idx = 32 * j + i;
+            float q = step > 0.f ? sy_rint_clamp((v[idx] + off) / step, 0.f, 15.f) : 0.f;
+            blk[16 + (idx >> 1)] |= (uint8_t)((unsigned)q << (4 * (idx & 1)));
+        }
+    }
+}
+
 static void sy_encode_q8_0(const float *v, uint8_t *blk) {
     float amax = 0.f;
     for (int i = 0; i < 32; ++i) {
@@ -236,10 +283,10 @@ static void sy_encode_cb2(const float *v, uint8_t *blk, const sy_cb_index *ix) {
 
 /* ---- parallel tensor generation ---------------------------------------- */
 
-enum { SY_Q2K = 2, SY_Q8_0 = 3, SY_CB2 = 4 };
+enum { SY_Q2K = 2, SY_Q8_0 = 3, SY_CB2 = 4, SY_Q4K = 5 };
 
 static int sy_block_w(int fmt) { return fmt == SY_Q8_0 ? 32 : 256; }
-static int sy_block_b(int fmt) { return fmt == SY_Q2K ? 84 : (fmt == SY_Q8_0 ? 34 : 66); }
+static int sy_block_b(int fmt) { return fmt == SY_Q2K ? 84 : (fmt == SY_Q8_0 ? 34 : (fmt == SY_Q4K ? 144 : 66)); }
 
 typedef struct {
     int fmt;
@@ -271,6 +318,7 @@ static void *sy_worker(void *arg) {
             sy_normals(key, b * bw, bw, J->sigma, v);
             uint8_t *dst = J->out + g * bb;
             if (J->fmt == SY_Q2K) sy_encode_q2k(v, dst);
+            else if (J->fmt == SY_Q4K) sy_encode_q4k(v, dst);
             else if (J->fmt == SY_Q8_0) sy_encode_q8_0(v, dst);
             else sy_encode_cb2(v, dst, J->cbix);
         }
@@ -286,7 +334,7 @@ static void *sy_worker(void *arg) {
 int64_t sy_gen_expert_tensor(int fmt, uint64_t seed, uint32_t layer, uint32_t tag, int64_t n_expert,
                              int64_t n_rows, int64_t n_in, double sigma, const int8_t *codebook,
                              uint8_t *out, int nthreads) {
-    if (fmt != SY_Q2K && fmt != SY_Q8_0 && fmt != SY_CB2) return -1;
+    if (fmt != SY_Q2K && fmt != SY_Q8_0 && fmt != SY_CB2 && fmt != SY_Q4K) return -1;
     int64_t bw = sy_block_w(fmt);
     if ((n_rows * n_in) % bw) return -1;
     sy_cb_index *cbix = NULL;

@@ -125,6 +125,55 @@ def test_q2k_subnormal_scale():
     assert np.all(w == np.float32(2.0 ** -24))
 
 
+def _q4k_block(d_bits, dmin_bits, sc, mn, q):
+    # written from the header's layout, apart from both encoders and decoders
+    b = np.zeros(144, np.uint8)
+    b[0:2] = np.frombuffer(np.uint16(d_bits).tobytes(), np.uint8)
+    b[2:4] = np.frombuffer(np.uint16(dmin_bits).tobytes(), np.uint8)
+    bits = 0
+    for f, v in enumerate(list(sc) + list(mn)):
+        bits |= (int(v) & 63) << (6 * f)
+    b[4:16] = np.frombuffer(bits.to_bytes(12, "little"), np.uint8)
+    for i in range(256):
+        b[16 + i // 2] |= (q[i] & 15) << (4 * (i % 2))
+    return b
+
+
+def test_q4k_closed_forms():
+    # "Understanding Dwarf Star" 2.3.2, the Q4_K layout: w = d*scale_j*q - dmin*min_j
+    z = oracle.dequant(oracle.Q4K, np.zeros(144, np.uint8), 256)
+    assert np.all(z == 0) and not np.any(np.signbit(z))
+    w = oracle.dequant(oracle.Q4K, _q4k_block(F16_ONE, 0, [63] * 8, [0] * 8, [15] * 256), 256)
+    assert np.all(w == 945.0)
+    w = oracle.dequant(oracle.Q4K, _q4k_block(F16_ONE, F16_ONE, [1] * 8, [1] * 8, [0] * 256), 256)
+    assert np.all(w == -1.0)
+    # d = 0.5, dmin = 0.25, sub-block j has scale 8j+1 and min 63-8j, code i % 16
+    sc = [8 * j + 1 for j in range(8)]
+    mn = [63 - 8 * j for j in range(8)]
+    w = oracle.dequant(oracle.Q4K, _q4k_block(F16_HALF, F16_QUARTER, sc, mn, [i % 16 for i in range(256)]), 256)
+    assert w[37] == 0.5 * 9 * 5 - 0.25 * 55     # sub-block 1, code 5
+    assert w[255] == 0.5 * 57 * 15 - 0.25 * 7   # sub-block 7, code 15
+
+
+def test_q4k_bit_positions():
+    for i in (0, 1, 30, 31, 32, 129, 255):
+        q = [0] * 256
+        q[i] = 9
+        w = oracle.dequant(oracle.Q4K, _q4k_block(F16_ONE, 0, [1] * 8, [0] * 8, q), 256)
+        expect = np.zeros(256, np.float32)
+        expect[i] = 9.0
+        assert np.array_equal(w, expect), i
+    # each 6-bit field reaches exactly its own sub-block, as scale or as min
+    for f in range(16):
+        sc, mn = [0] * 8, [0] * 8
+        (sc if f < 8 else mn)[f % 8] = 37
+        w = oracle.dequant(oracle.Q4K, _q4k_block(F16_ONE, F16_ONE, sc, mn, [2] * 256), 256)
+        j = f % 8
+        expect = np.zeros(256, np.float32)
+        expect[32 * j:32 * j + 32] = 74.0 if f < 8 else -37.0
+        assert np.array_equal(w, expect), f
+
+
 def test_q8_0_closed_form():
     b = np.zeros(34, np.uint8)
     b[0:2] = np.frombuffer(np.uint16(F16_HALF).tobytes(), np.uint8)
@@ -155,13 +204,19 @@ def test_dequant_round_trips_through_encoders():
     # a wrong byte or bit order in either breaks these bounds
     n = 64 * 256
     v = synth.normal(11, 0, 99, 0, n, 0.02)
-    for fmt in (synth.Q2K, synth.Q8_0):
+    for fmt in (synth.Q2K, synth.Q8_0, synth.Q4K):
         b = synth.expert_tensor(fmt, 11, 0, 99, 1, n // 256, 256)
         w = oracle.dequant(fmt, b, n)
         err = np.abs(w - v)
         if fmt == synth.Q8_0:
             d = np.abs(v).reshape(-1, 32).max(1) / 127
             assert np.all(err.reshape(-1, 32) <= 0.5001 * d[:, None] + 1e-7)
+        elif fmt == synth.Q4K:  # sub-blocks of 32, codes 0..15
+            blk = v.reshape(-1, 8, 32)
+            rng = blk.max(2) - np.minimum(blk.min(2), 0)
+            step = rng / 15
+            assert np.all(err.reshape(-1, 8, 32) <= 0.75 * step.max(1)[:, None, None] + 1e-4)
+            assert err.mean() < 0.1 * 0.02  # 4-bit codes: a small fraction of sigma
         else:
             blk = v.reshape(-1, 16, 16)
             rng = blk.max(2) - np.minimum(blk.min(2), 0)

@@ -27,6 +27,13 @@
  *            weights), 32 sign masks @34 (bit j negates weight j of the 8).
  *            w = d * (+/-) codebook[idx][j], codebook int8 [256][8].
  *            ("Understanding Dwarf Star", 2.3.4: 66 bytes per 256 weights.)
+ *   MOE_Q4K  144 B / 256 weights: fp16 d @0, fp16 dmin @2, 12 bytes @4 holding
+ *            sixteen 6-bit fields (field f in bits 6f..6f+5 of the 96-bit
+ *            little-endian integer; f = j is the scale and f = 8 + j the min
+ *            of sub-block j of 32 weights), 128 bytes of 4-bit codes @16
+ *            (weight i in bits 4*(i%2) of byte i/2).  w = d*scale*q - dmin*min.
+ *            Routed gate/up/down only.  ("Understanding Dwarf Star", 2.3.2,
+ *            the Q4_K block layout.)
  * A matrix [n_out][n_in] is flattened row-major and cut into consecutive
  * blocks, so blocks run along the reduction dimension.  Expert tensors are
  * expert-major: gate/up [E][F][D], down [E][D][F]; shared [Fs][D], [Fs][D],
@@ -72,7 +79,7 @@ typedef enum {
     MOE_EDEVICE = -5       /* a HIP call failed (message carries hipGetErrorString) */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_Q2K = 2, MOE_Q8_0 = 3, MOE_CB2 = 4 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_Q2K = 2, MOE_Q8_0 = 3, MOE_CB2 = 4, MOE_Q4K = 5 } moe_dtype;
 
 enum { MOE_ACCUMULATE = 1u }; /* y += block(x) instead of y = block(x) */
 
@@ -177,7 +184,7 @@ int moe_hotlist(const int64_t *counts, int32_t n, int32_t *order, int32_t *n_hot
 int moe_rmsnorm(const float *x, const float *gamma, float eps, int32_t T, int32_t D, float *out, void *stream,
                 char *err, size_t errlen);
 
-/* Decode n_weights of a block tensor (type MOE_Q2K, MOE_Q8_0 or MOE_CB2) to
+/* Decode n_weights of a block tensor (type MOE_Q2K, MOE_Q8_0, MOE_CB2 or MOE_Q4K) to
  * fp32 (out_type MOE_F32) or bf16 (MOE_BF16, round to nearest even).  The
  * fp32 result is exact: every product in the formats fits in fp32.  A test
  * hook for the decoders the kernels use ("Understanding Dwarf Star", 2.8.2

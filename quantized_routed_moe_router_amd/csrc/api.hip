@@ -23,6 +23,7 @@ int fail(char *err, size_t errlen, int code, const char *fmt, ...) {
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 bool pow2(int v) { return v > 0 && (v & (v - 1)) == 0; }
 bool block_fmt(int f) { return f == MOE_Q2K || f == MOE_Q8_0 || f == MOE_CB2; }
+bool routed_fmt(int f) { return block_fmt(f) || f == MOE_Q4K; }
 
 // Rows are split into 64-weight chunks, one per lane, up to 64 lanes per row.
 bool row_ok(int n_in) { return n_in > 0 && n_in % 64 == 0 && pow2(n_in / 64) && n_in / 64 <= 64; }
@@ -38,10 +39,10 @@ int check_desc(const moe_layer_desc *d, char *err, size_t errlen) {
         return fail(err, errlen, MOE_EUNSUPPORTED,
                     "D must be a multiple of 256 and D, F, Fs of the form 64*2^j <= 4096 (D=%d F=%d Fs=%d)", D, F,
                     Fs);
-    if (!block_fmt(d->gate_type) || d->up_type != d->gate_type || !block_fmt(d->down_type) ||
+    if (!routed_fmt(d->gate_type) || d->up_type != d->gate_type || !routed_fmt(d->down_type) ||
         (Fs && !block_fmt(d->shared_type)))
         return fail(err, errlen, MOE_EUNSUPPORTED,
-                    "formats: gate = up in {Q2K, Q8_0, CB2}, down and shared in {Q2K, Q8_0, CB2}");
+                    "formats: gate = up and down in {Q2K, Q8_0, CB2, Q4K}, shared in {Q2K, Q8_0, CB2}");
     if (!d->router_w || !d->gate || !d->up || !d->down)
         return fail(err, errlen, MOE_EINVAL, "router_w, gate, up and down must be set");
     if (Fs && (!d->sh_gate || !d->sh_up || !d->sh_down))
@@ -214,7 +215,7 @@ int moe_rmsnorm(const float *x, const float *gamma, float eps, int32_t T, int32_
 
 int moe_dequant(int32_t type, const void *src, int64_t n, const int8_t *codebook, int32_t out_type, void *dst,
                 void *stream, char *err, size_t errlen) {
-    if (!block_fmt(type)) return fail(err, errlen, MOE_EUNSUPPORTED, "type must be Q2K, Q8_0 or CB2");
+    if (!routed_fmt(type)) return fail(err, errlen, MOE_EUNSUPPORTED, "type must be Q2K, Q8_0, CB2 or Q4K");
     if (out_type != MOE_F32 && out_type != MOE_BF16)
         return fail(err, errlen, MOE_EUNSUPPORTED, "out_type must be MOE_F32 or MOE_BF16");
     int64_t unit = type == MOE_Q8_0 ? 32 : 256;

@@ -23,11 +23,11 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxUsed = 16;
 
 // Block geometry of the three weight formats.
-constexpr int kQ2KBytes = 84, kQ8Bytes = 34, kCB2Bytes = 66;
+constexpr int kQ2KBytes = 84, kQ8Bytes = 34, kCB2Bytes = 66, kQ4KBytes = 144;
 
 __host__ __device__ inline int64_t fmt_block_weights(int fmt) { return fmt == MOE_Q8_0 ? 32 : 256; }
 __host__ __device__ inline int64_t fmt_block_bytes(int fmt) {
-    return fmt == MOE_Q2K ? kQ2KBytes : (fmt == MOE_Q8_0 ? kQ8Bytes : kCB2Bytes);
+    return fmt == MOE_Q2K ? kQ2KBytes : (fmt == MOE_Q8_0 ? kQ8Bytes : (fmt == MOE_Q4K ? kQ4KBytes : kCB2Bytes));
 }
 __host__ __device__ inline int64_t fmt_bytes(int fmt, int64_t n) {
     return n / fmt_block_weights(fmt) * fmt_block_bytes(fmt);
@@ -59,6 +59,18 @@ MOE_DEV u32x4 load_u32x4(const void *p) {
     return v;
 }
 MOE_DEV uint32_t load_u32(const void *p) { return *(const uint32_t *)__builtin_assume_aligned(p, 4); }
+
+// Byte N of v as a float, in one instruction (the compiler would extract
+// the byte first).
+template <int N>
+MOE_DEV float byte_to_float(uint32_t v) {
+    float f;
+    if constexpr (N == 0) __asm__("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(v));
+    else if constexpr (N == 1) __asm__("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(v));
+    else if constexpr (N == 2) __asm__("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(v));
+    else __asm__("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(v));
+    return f;
+}
 
 // 8 bytes starting at a 2-byte aligned address, assembled from aligned dwords.
 MOE_DEV void load_8_at_even(const uint8_t *p, uint32_t &lo, uint32_t &hi) {
@@ -165,6 +177,83 @@ MOE_DEV float q8_dot(const Q8Chunk &c, const float *x) {
         for (int n = 0; n < 4; ++n) s1 = __builtin_fmaf((float)(int8_t)(v >> (8 * n)), x[32 + 4 * i + n], s1);
     }
     return d0 * s0 + d1 * s1;
+}
+
+// Q4K: 64 weights = sub-blocks 2s and 2s+1 of one 144-byte block: 32 code
+// bytes (weight i in bits 4*(i%2) of byte i/2), the two 6-bit scales and
+// mins from the packed 12 bytes, and d, dmin.
+struct Q4KChunk {
+    u32x4 qa, qb;       // code bytes 0-15 and 16-31 of the chunk
+    uint32_t sc, mn;    // scale and min of the two sub-blocks (bytes 0 and 1)
+    uint32_t dd;        // fp16 d (low half) and dmin (high half)
+};
+
+MOE_DEV uint32_t six_bits(uint32_t w0, uint32_t w1, uint32_t w2, int f) {  // field f of the 96-bit scales
+    const int bit = 6 * f, word = bit >> 5, sh = bit & 31;
+    const uint32_t lo = word == 0 ? w0 : (word == 1 ? w1 : w2);
+    const uint32_t hi = word == 0 ? w1 : (word == 1 ? w2 : 0u);
+    const uint32_t v = sh == 0 ? lo : ((lo >> sh) | (hi << (32 - sh)));
+    return v & 63u;
+}
+
+MOE_DEV Q4KChunk q4k_load(const uint8_t *base, int64_t i0) {
+    const uint8_t *blk = base + (i0 >> 8) * kQ4KBytes;
+    const int sub = (int)((i0 >> 6) & 3);
+    Q4KChunk c;
+    c.qa = load_u32x4(blk + 16 + 32 * sub);
+    c.qb = load_u32x4(blk + 32 + 32 * sub);
+    const uint32_t w0 = load_u32(blk + 4), w1 = load_u32(blk + 8), w2 = load_u32(blk + 12);
+    c.sc = six_bits(w0, w1, w2, 2 * sub) | (six_bits(w0, w1, w2, 2 * sub + 1) << 8);
+    c.mn = six_bits(w0, w1, w2, 8 + 2 * sub) | (six_bits(w0, w1, w2, 9 + 2 * sub) << 8);
+    c.dd = load_u32(blk);
+    return c;
+}
+
+// code byte j of the chunk (weights 2j, 2j+1)
+MOE_DEV uint32_t q4k_byte_word(const Q4KChunk &c, int w) { return w < 4 ? c.qa[w] : c.qb[w - 4]; }
+
+MOE_DEV void q4k_values(const Q4KChunk &c, float *w) {
+    const float d = half_bits_to_float(c.dd), dmin = half_bits_to_float(c.dd >> 16);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // sub-block: weights 32h .. 32h+31
+        const float sc = (float)((c.sc >> (8 * h)) & 63u), off = dmin * (float)((c.mn >> (8 * h)) & 63u);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const int k = 32 * h + i;
+            const float q = (float)((q4k_byte_word(c, k >> 3) >> (8 * ((k >> 1) & 3) + 4 * (k & 1))) & 15u);
+            w[k] = __builtin_fmaf(d, sc * q, -off);
+        }
+    }
+}
+
+// sum_i (d*sc_j*q_i - dmin*m_j) x_i over the two sub-blocks, fp32
+MOE_DEV float q4k_dot(const Q4KChunk &c, const float *x) {
+    const float d = half_bits_to_float(c.dd), dmin = half_bits_to_float(c.dd >> 16);
+    float acc = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float sq = 0.f, sx = 0.f;
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {  // 4 words of code bytes: weights 32h + 8wd .. +7
+            const uint32_t v = q4k_byte_word(c, 4 * h + wd);
+            const uint32_t ev = v & 0x0F0F0F0Fu, od = (v >> 4) & 0x0F0F0F0Fu;
+            const float *xs = x + 32 * h + 8 * wd;
+            sq = __builtin_fmaf(byte_to_float<0>(ev), xs[0], sq);
+            sq = __builtin_fmaf(byte_to_float<0>(od), xs[1], sq);
+            sq = __builtin_fmaf(byte_to_float<1>(ev), xs[2], sq);
+            sq = __builtin_fmaf(byte_to_float<1>(od), xs[3], sq);
+            sq = __builtin_fmaf(byte_to_float<2>(ev), xs[4], sq);
+            sq = __builtin_fmaf(byte_to_float<2>(od), xs[5], sq);
+            sq = __builtin_fmaf(byte_to_float<3>(ev), xs[6], sq);
+            sq = __builtin_fmaf(byte_to_float<3>(od), xs[7], sq);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sx += xs[i];
+        }
+        const float sc = (float)((c.sc >> (8 * h)) & 63u), mn = (float)((c.mn >> (8 * h)) & 63u);
+        acc = __builtin_fmaf(d * sc, sq, acc);
+        acc = __builtin_fmaf(-dmin * mn, sx, acc);
+    }
+    return acc;
 }
 
 // CB2: 64 weights = 8 groups of 8 inside one 66-byte block; the codebook
@@ -383,17 +472,6 @@ MOE_DEV int sdot4(uint32_t a, uint32_t b, int c) { return __builtin_amdgcn_sdot4
 
 // sum_g inv_g * (d*sc_g*sum_i q_i c_i) - dmin * sum_g m_g * sx_g, the integer
 // dot of each group exact in int32 (|sum| < 2^21)
-// Byte N of v as a float, in one instruction (the compiler would extract
-// the byte first).
-template <int N>
-MOE_DEV float byte_to_float(uint32_t v) {
-    float f;
-    if constexpr (N == 0) __asm__("v_cvt_f32_ubyte0 %0, %1" : "=v"(f) : "v"(v));
-    else if constexpr (N == 1) __asm__("v_cvt_f32_ubyte1 %0, %1" : "=v"(f) : "v"(v));
-    else if constexpr (N == 2) __asm__("v_cvt_f32_ubyte2 %0, %1" : "=v"(f) : "v"(v));
-    else __asm__("v_cvt_f32_ubyte3 %0, %1" : "=v"(f) : "v"(v));
-    return f;
-}
 
 // the scale nibbles (low) and min nibbles (high) of the 4 group bytes, each
 // byte converted in place

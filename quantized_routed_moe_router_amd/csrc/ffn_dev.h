@@ -113,6 +113,18 @@ struct RawChunk<MOE_CB2> {
     MOE_DEV float dot(const Prep &p, const uint32_t *cb) const { return cb2_dot(c, p.x, cb); }
 };
 
+template <>
+struct RawChunk<MOE_Q4K> {
+    typedef XF32 Prep;
+    Q4KChunk c;
+    MOE_DEV static void prep(const float *x, Prep &p) {
+#pragma unroll
+        for (int i = 0; i < 64; ++i) p.x[i] = x[i];
+    }
+    MOE_DEV void load(const uint8_t *b, int64_t i0) { c = q4k_load(b, i0); }
+    MOE_DEV float dot(const Prep &p, const uint32_t *) const { return q4k_dot(c, p.x); }
+};
+
 // Lane layout over rows of n_in weights: cpr = n_in/64 lanes per row, rpi =
 // 64/cpr rows per wave iteration; lane -> (row lane/cpr, chunk lane%cpr).
 struct RowPlan {
@@ -491,6 +503,7 @@ template <typename Fn>
 inline void with_fmt(int f, Fn &&fn) {
     if (f == MOE_Q2K) fn(std::integral_constant<int, MOE_Q2K>{});
     else if (f == MOE_Q8_0) fn(std::integral_constant<int, MOE_Q8_0>{});
+    else if (f == MOE_Q4K) fn(std::integral_constant<int, MOE_Q4K>{});
     else fn(std::integral_constant<int, MOE_CB2>{});
 }
 

@@ -34,9 +34,12 @@ constexpr int kMaxDecTokens = 16;
 // Formats the staged decode kernels take for the routed experts (their 16
 // rows of gate and up fit in LDS), and the bytes of 16 rows at n_embd or
 // n_ff_exp <= 4096.
-constexpr bool staged_fmt(int f) { return f == MOE_Q2K || f == MOE_CB2; }
+constexpr bool staged_fmt(int f) { return f == MOE_Q2K || f == MOE_CB2 || f == MOE_Q4K; }
 template <int FMT>
-constexpr int rows16_bytes_max() { return 16 * 16 * (FMT == MOE_Q8_0 ? 2 * kQ8Bytes * 4 : (FMT == MOE_CB2 ? kCB2Bytes : kQ2KBytes)); }
+constexpr int rows16_bytes_max() {
+    return 16 * 16 *
+           (FMT == MOE_Q8_0 ? 2 * kQ8Bytes * 4 : (FMT == MOE_CB2 ? kCB2Bytes : (FMT == MOE_Q4K ? kQ4KBytes : kQ2KBytes)));
+}
 // shared expert rows per wave (gate/up in K1, down in K2)
 constexpr int kShGuRows = 2;
 // K4: shared expert down rows per wave (kDecRows over kDecWaves waves)
@@ -469,7 +472,8 @@ __global__ void __launch_bounds__(64 * kDecWaves) dec_k4_kernel(FfnArgs a) {
     }
     // rows per staged batch: 16, or fewer when 16 rows exceed the wave's area
     const int64_t b16 = fmt_bytes(DFMT, (int64_t)kDecRows * a.F);
-    const int rb = b16 <= 16 * kK4WaveUnits ? kDecRows : kDecRows * 16 * kK4WaveUnits / (int)b16;
+    int rb = kDecRows;  // a power of two that divides kDecRows
+    while ((int64_t)rb * b16 > (int64_t)kDecRows * 16 * kK4WaveUnits) rb >>= 1;
     const int c = lane % (a.F >> 6);
     const uint8_t *ws = (const uint8_t *)wstage[wave];
     for (int u = wave; u < a.nslots; u += kDecWaves) {
@@ -753,6 +757,7 @@ hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32
     }
     if (stage == 0 || stage == 3) {
         if (d->gate_type == MOE_CB2) dec_k3_kernel<MOE_CB2><<<k3, 256, 0, s>>>(a);
+        else if (d->gate_type == MOE_Q4K) dec_k3_kernel<MOE_Q4K><<<k3, 256, 0, s>>>(a);
         else if (a.D == 4096) dec_k3_q2k4096_kernel<<<k3, 256, 0, s>>>(a);
         else dec_k3_kernel<MOE_Q2K><<<k3, 256, 0, s>>>(a);
     }
@@ -763,6 +768,7 @@ hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32
         else with_fmt(a.shared_fmt, [&](auto S) {
             constexpr int SF = decltype(S)::value;
             if (d->down_type == MOE_CB2) dec_k4_kernel<MOE_CB2, SF><<<a.D / kDecRows, 64 * kDecWaves, 0, s>>>(a);
+            else if (d->down_type == MOE_Q4K) dec_k4_kernel<MOE_Q4K, SF><<<a.D / kDecRows, 64 * kDecWaves, 0, s>>>(a);
             else dec_k4_kernel<MOE_Q2K, SF><<<a.D / kDecRows, 64 * kDecWaves, 0, s>>>(a);
         });
     }

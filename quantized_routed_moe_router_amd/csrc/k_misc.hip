@@ -39,7 +39,7 @@ MOE_DEV void store_vals(void *dst, int out_bf16, int64_t at, const float *w, int
     }
 }
 
-// One thread per 64-weight chunk (Q2K, CB2) or per 32-weight block (Q8_0).
+// One thread per 64-weight chunk (Q2K, CB2, Q4K) or per 32-weight block (Q8_0).
 __global__ void __launch_bounds__(256) dequant_kernel(int type, const uint8_t *__restrict__ src, int64_t nunits,
                                                       const int8_t *__restrict__ cb, int out_bf16, void *dst) {
     __shared__ uint32_t cb_lds[512];
@@ -55,6 +55,9 @@ __global__ void __launch_bounds__(256) dequant_kernel(int type, const uint8_t *_
         store_vals(dst, out_bf16, 64 * u, w, 64);
     } else if (type == MOE_CB2) {
         cb2_values(cb2_load(src, 64 * u), cb_lds, w);
+        store_vals(dst, out_bf16, 64 * u, w, 64);
+    } else if (type == MOE_Q4K) {
+        q4k_values(q4k_load(src, 64 * u), w);
         store_vals(dst, out_bf16, 64 * u, w, 64);
     } else {
         q8_block_values(src + u * kQ8Bytes, w);

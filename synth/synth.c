@@ -414,11 +414,13 @@ void sy_f32_to_bf16(const float *in, int64_t n, uint16_t *out) {
  *         d*sc_g*(q - 1.5) for uniform q, i.e. symmetric about zero.
  *   Q8_0: q uniform in -127..127.
  *   CB2 : idx and sign bits uniform.
+ *   Q4K : sc_j uniform in 32..63, m_j = sc_j, dmin = fp16(7.5 d): weights are
+ *         d*sc_j*(q - 7.5) for uniform q.
  * Block b of expert e uses stream sy_key(seed, layer, tag, e), values
  * [b*64, b*64+64). */
 static void sy_sample_block(int fmt, uint64_t key, int64_t b, double sigma, const double cb_rms, uint8_t *blk) {
     uint64_t r[64];
-    int need = fmt == SY_Q2K ? 25 : (fmt == SY_Q8_0 ? 33 : 9);
+    int need = fmt == SY_Q2K || fmt == SY_Q4K ? 25 : (fmt == SY_Q8_0 ? 33 : 9);
     for (int i = 0; i < need; ++i) r[i] = sy_at(key, (uint64_t)b * 64u + (uint64_t)i);
     double jit = 0.8 + 0.4 * sy_u01(r[0]);
     if (fmt == SY_Q2K) {
@@ -431,6 +433,18 @@ static void sy_sample_block(int fmt, uint64_t key, int64_t b, double sigma, cons
             blk[4 + g] = (uint8_t)(sc | (sc << 4));
         }
         for (int i = 0; i < 64; ++i) blk[20 + i] = (uint8_t)(r[17 + (i >> 3)] >> (8 * (i & 7)));
+    } else if (fmt == SY_Q4K) {
+        uint16_t dh = sy_f16_bits((float)(sigma * jit / (47.5 * 4.6097722286464435)));
+        uint16_t mh = sy_f16_bits(7.5f * sy_f16_val(dh));
+        memset(blk, 0, 144);
+        memcpy(blk, &dh, 2);
+        memcpy(blk + 2, &mh, 2);
+        for (int j = 0; j < 8; ++j) {
+            unsigned sc = 32u + (unsigned)((r[1 + j] >> 40) & 31u);
+            sy_put6(blk + 4, j, sc);
+            sy_put6(blk + 4, 8 + j, sc);
+        }
+        for (int i = 0; i < 128; ++i) blk[16 + i] = (uint8_t)(r[9 + (i >> 3)] >> (8 * (i & 7)));
     } else if (fmt == SY_Q8_0) {
         uint16_t dh = sy_f16_bits((float)(sigma * jit / 73.33333333333333));
         memcpy(blk, &dh, 2);
@@ -476,7 +490,7 @@ static void *sy_sworker(void *arg) {
 int64_t sy_sample_expert_tensor(int fmt, uint64_t seed, uint32_t layer, uint32_t tag, int64_t n_expert,
                                 int64_t n_rows, int64_t n_in, double sigma, const int8_t *codebook,
                                 uint8_t *out, int nthreads) {
-    if (fmt != SY_Q2K && fmt != SY_Q8_0 && fmt != SY_CB2) return -1;
+    if (fmt != SY_Q2K && fmt != SY_Q8_0 && fmt != SY_CB2 && fmt != SY_Q4K) return -1;
     int64_t bw = sy_block_w(fmt);
     if ((n_rows * n_in) % bw) return -1;
     double cb_rms = 1.0;

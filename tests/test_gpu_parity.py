@@ -17,7 +17,7 @@ def _bf16_bits_of(f32):
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
-@pytest.mark.parametrize("fmt", [synth.Q2K, synth.Q8_0, synth.CB2])
+@pytest.mark.parametrize("fmt", [synth.Q2K, synth.Q8_0, synth.CB2, synth.Q4K])
 def test_dequant_bit_exact(fmt):
     import quantized_routed_moe_router_amd as moe
     cb = synth.codebook(4)
@@ -51,6 +51,14 @@ def _check_layer(L, T, seed, bf16=False, rows=None):
     yg = y.cpu().numpy()
     sel = slice(None) if rows is None else rows
     return gu.assert_close(yg[sel], y_ref[sel]), W, y
+
+
+@pytest.mark.parametrize("T", [1, 5, 37])
+def test_q4k_routed_layers(T):
+    # Q4_K routed gate/up/down with a Q8_0 shared expert: one token and a few
+    # (the staged decode kernels) and a batch (the batched kernels)
+    L = synth.make_layer(110, 0, D=512, E=32, k=4, F=256, Fs=128, gate_fmt=synth.Q4K, down_fmt=synth.Q4K)
+    _check_layer(L, T, 111 + T)
 
 
 def test_tiny_workload():

@@ -85,6 +85,16 @@ def test_one_token_full_width(E, k, Fs, accumulate):
     _log("one token E=%d k=%d Fs=%d: worst relative error %.3g" % (E, k, Fs, worst))
 
 
+@pytest.mark.parametrize("T", [1, 8])
+def test_q4k_full_width(T):
+    # Q4_K routed experts at full width (n_embd 4096, FFN 2048, top-6 of 16,
+    # Q8_0 shared expert): the staged gate/up and down kernels take 144-byte
+    # blocks (the down rows in batches of 8)
+    L = synth.make_layer(12, 0, D=4096, E=16, k=6, F=2048, Fs=2048, gate_fmt=synth.Q4K, down_fmt=synth.Q4K)
+    wl = synth.Workload("q4k_b%d" % T, T, synth.F32, [L], x=synth.activations(13, T, 4096))
+    _run(wl, gu.upload(L), list(range(T)))
+
+
 def test_one_token_stages_and_repeats_are_bitwise_equal(flash):
     # the one-token schedule at full width: stages 1-4 one by one, and the
     # same call repeated on one workspace, give bitwise the same y and routing

@@ -42,7 +42,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=2048)
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="decode_b1",
-                    choices=["decode_b1", "decode_b32", "prefill_2048", "stack43_b1", "stack43_b8", "hotlist_43x256"])
+                    choices=["decode_b1", "decode_b32", "prefill_2048", "stack43_b1", "stack43_b8", "hotlist_43x256",
+                             "decode_b1_q4k"])
     ap.add_argument("--replicas", type=int, default=16)
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu", action="store_true")
@@ -90,9 +91,14 @@ def main():
 
     torch.cuda.set_device(0)
     t0 = time.time()
-    L = synth.flash_layer()
+    if args.workload == "decode_b1_q4k":  # the flash shape with Q4_K routed experts
+        s = synth.DS4_FLASH
+        L = synth.make_layer(synth.WEIGHTS_SEED, 0, D=s["D"], E=s["E"], k=s["k"], F=s["F"], Fs=s["Fs"],
+                             gate_fmt=synth.Q4K, down_fmt=synth.Q4K)
+    else:
+        L = synth.flash_layer()
     log("layer generated in %.1f s" % (time.time() - t0))
-    if args.workload == "decode_b1":
+    if args.workload in ("decode_b1", "decode_b1_q4k"):
         T, n_x = 1, 64
         x_all = synth.activations(1, n_x, L.n_embd)
         mode = moe.F32
@@ -254,7 +260,7 @@ def main():
             "workload": args.workload,
             "tokens_per_step": T,
             "n_embd": D, "n_expert": L.n_expert, "n_expert_used": k, "n_ff_exp": F, "n_ff_shared": Fs,
-            "formats": "Q2K gate/up/down, Q8_0 shared, fp32 router",
+            "formats": "%s gate/up/down, Q8_0 shared, fp32 router" % ("Q4K" if L.gate_fmt == synth.Q4K else "Q2K"),
             "cache": "cold: %d device replicas rotated, %d distinct inputs" % (R, n_x),
             "launch": "hipGraph of %d steps, replayed" % R,
         },

@@ -1,6 +1,8 @@
 // k_route.hip - routing kernels for moe_route and for batches too large for
 // the one-block finisher ("Understanding Dwarf Star", 5.3.2 router and top-k;
 // 5.3.7 step 1 and the sparse indexing of step 2).
+#include <type_traits>
+
 #include "route_dev.h"
 
 namespace moe {
@@ -18,6 +20,89 @@ __global__ void __launch_bounds__(256) router_tile_kernel(const float *__restric
                                                           const void *__restrict__ xin, int T, int D, int E,
                                                           double *__restrict__ logits) {
     router_tile_block<XT>(W, bias, xin, T, D, E, logits, blockIdx.x, blockIdx.y);
+}
+
+// Many tokens: the logits on the fp64 matrix cores (v_mfma_f64_16x16x4_f64),
+// the router contraction of "Understanding Dwarf Star", 5.3.2.  A wave owns a
+// 16-token x 16-expert tile over the whole reduction; the 4 waves of a block
+// share the token rows and take 4 adjacent expert tiles.  Per 16-wide slice
+// of k, lane l loads 4 consecutive values of token row (l & 15) and of expert
+// row (l & 15), both at k0 + 4 (l >> 4); matrix instruction j takes component
+// j of both, so each product x[t][k] W[e][k] enters the sum exactly once.
+// Products of fp32 (or bf16) values are exact in fp64: only the order of the
+// fp64 additions differs from a plain ascending sum.  Register r of the
+// accumulator holds token (l >> 4) + 4r, expert l & 15.
+// Linear block id -> tiles: the blocks of one XCD (ids round-robin over the 8)
+// take one contiguous range of token rows, so its L2 holds those rows and the
+// router matrix.
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// raw 4 activations of one lane (bf16 bits or fp32), converted where used so
+// that a load in flight is not waited for before the products that precede
+// its use
+template <int XT>
+using RouterX = typename std::conditional<XT == MOE_BF16, uint2, f32x4>::type;
+
+template <int XT>
+MOE_DEV float router_x(const RouterX<XT> &v, int q) {
+    if constexpr (XT == MOE_BF16) {
+        const uint32_t u = q < 2 ? v.x : v.y;
+        return bf16_bits_to_float((q & 1) ? (u >> 16) : (u & 0xFFFFu));
+    } else {
+        return v[q];
+    }
+}
+
+template <int XT>
+__global__ void __launch_bounds__(256) router_mfma_kernel(const float *__restrict__ W, const float *__restrict__ bias,
+                                                          const void *__restrict__ xin, int T, int D, int E,
+                                                          double *__restrict__ logits, int n_ttx, int n_eq) {
+    const int L = blockIdx.x, xcd = L & 7, j = L >> 3;
+    const int tt = xcd * n_ttx + j / n_eq, eq = j % n_eq;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int t0 = tt * 16, e0 = (eq * 4 + wave) * 16;
+    if (t0 >= T || e0 >= E) return;
+    const int row = lane & 15, kq = 4 * (lane >> 4);
+    const int t = min(t0 + row, T - 1), e = min(e0 + row, E - 1);
+    const void *xrow = XT == MOE_BF16 ? (const void *)((const uint16_t *)xin + (int64_t)t * D + kq)
+                                      : (const void *)((const float *)xin + (int64_t)t * D + kq);
+    const float *wrow = W + (int64_t)e * D + kq;
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+    // 64 k per half step from two register sets: the loads of one set are in
+    // flight while the other's products run (D is a multiple of 128 here)
+    RouterX<XT> xa[4], xb[4];
+    f32x4 wa[4], wb[4];
+    auto load = [&](RouterX<XT> (&xv)[4], f32x4 (&wv)[4], int k) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            xv[c] = *(const RouterX<XT> *)((const char *)xrow + (int64_t)(k + 16 * c) * (XT == MOE_BF16 ? 2 : 4));
+            wv[c] = *(const f32x4 *)(wrow + k + 16 * c);
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the products
+    };
+    auto mma = [&](const RouterX<XT> (&xv)[4], const f32x4 (&wv)[4]) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)router_x<XT>(xv[c], q), (double)wv[c][q], acc, 0,
+                                                           0, 0);
+    };
+    load(xa, wa, 0);
+    for (int k0 = 0; k0 < D; k0 += 128) {
+        load(xb, wb, k0 + 64);
+        mma(xa, wa);
+        load(xa, wa, min(k0 + 128, D - 64));  // the last step re-reads a slice: no branch, so the waits stay exact
+        mma(xb, wb);
+    }
+    const int ex = e0 + (lane & 15);
+    if (ex >= E) return;
+    const double b = bias ? (double)bias[ex] : 0.0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int tok = t0 + (lane >> 4) + 4 * r;
+        if (tok < T) logits[(int64_t)tok * E + ex] = acc[r] + b;
+    }
 }
 
 __global__ void __launch_bounds__(256) route_finish_small_kernel(const double *__restrict__ logits, int T, int E,
@@ -145,6 +230,9 @@ __global__ void __launch_bounds__(512) bucket_kernel(const int32_t *__restrict__
 
 // one block per expert row for few tokens, 16 x 16 tiles for many
 bool router_rows_ok(int T) { return T <= 16; }
+// the matrix-core router from 128 rows on (fewer rows leave most of the chip
+// idle with one wave per 16 x 16 tile); the k steps need D % 128 == 0
+bool router_mfma_ok(int T, int D) { return T >= 128 && D % 128 == 0; }
 
 hipError_t launch_router_logits(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type,
                                 const Workspace &ws, hipStream_t s) {
@@ -154,6 +242,15 @@ hipError_t launch_router_logits(const moe_layer_desc *d, const void *x, int32_t 
             router_row_kernel<MOE_BF16><<<E, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E, ws.logits);
         else
             router_row_kernel<MOE_F32><<<E, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E, ws.logits);
+    } else if (router_mfma_ok(T, D)) {
+        const int n_tt = (T + 15) / 16, n_ttx = (n_tt + 7) / 8, n_eq = ((E + 15) / 16 + 3) / 4;
+        const int grid = 8 * n_ttx * n_eq;
+        if (x_type == MOE_BF16)
+            router_mfma_kernel<MOE_BF16><<<grid, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E, ws.logits,
+                                                               n_ttx, n_eq);
+        else
+            router_mfma_kernel<MOE_F32><<<grid, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E, ws.logits,
+                                                              n_ttx, n_eq);
     } else {
         dim3 g((T + 15) / 16, (E + 15) / 16);
         if (x_type == MOE_BF16)

@@ -129,6 +129,28 @@ def test_exact_ties_go_to_lower_index():
     assert np.all(idx == [3, 9, 12])
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("T", [128, 203])
+def test_route_many_rows_matrix_cores(T, bf16):
+    # from 128 rows the logits run on the fp64 matrix cores: ragged token and
+    # expert tiles (E = 40 is 2.5 tiles of 16), a Zipf bias, fp32 and bf16 x;
+    # indices and bucketing bit-exact, weights within tolerance
+    import quantized_routed_moe_router_amd as moe
+    L = synth.make_layer(94, 0, D=512, E=40, k=6, F=128, Fs=0)
+    L.router_bias = synth.zipf_bias(95, 40)
+    x = synth.activations(96 + T, T, 512)
+    kw = dict(x_bf16=synth.to_bf16_bits(x)) if bf16 else dict(x=x)
+    idx_ref, w_ref, gap = oracle.route(L, **kw)
+    print("route T=%d bf16=%s: smallest k/k+1 logit gap %.3g" % (T, bf16, float(np.min(gap))))
+    W = gu.upload(L)
+    xd = gu.x_to_device(**kw)
+    ws = moe.alloc_workspace(W, T, moe.BF16 if bf16 else moe.F32)
+    r = moe.Routing(T, L.n_expert_used, L.n_expert)
+    moe.route(W, xd, r, ws)
+    torch.cuda.synchronize()
+    gu.check_routing(r, idx_ref, w_ref, L.n_expert)
+
+
 def test_route_scale_and_accumulate():
     L = synth.make_layer(92, 0, D=512, E=32, k=4, F=256, Fs=128)
     L.route_scale = 1.5

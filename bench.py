@@ -190,17 +190,23 @@ def main():
     # latency, so the run is long and a bounded spin kernel ahead of it lets
     # the host queue the whole run before the GPU reaches it.
     n_runs = 8
-    ev_src = ("HIP events around runs of %d back-to-back stage-3 launches on cold replicas, %d runs, "
-              "median per launch" % (R, n_runs))
+    # the grouped-GEMM path (many rows, Q2K experts): stage 5 is its routed
+    # gate/up kernel alone; elsewhere stage 3 is the gate/up kernel
+    gemm = T > 16 and L.gate_fmt == synth.Q2K and L.down_fmt == synth.Q2K
+    st_gu = moe.STAGE_ROUTED_GATE_UP if gemm else moe.STAGE_GATE_UP
+    ev_src = ("HIP events around runs of %d back-to-back stage-%d launches on cold replicas, %d runs, "
+              "median per launch" % (R, st_gu, n_runs))
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_runs)]
     for i, e in enumerate(evs):
         x = xin[i % n_x]
         moe.layer_forward_stage(base, x, y, ws, moe.STAGE_ROUTER, routing=r)
         moe.layer_forward_stage(base, x, y, ws, moe.STAGE_ROUTE, routing=r)
+        if gemm:  # activation codes and tiles for stage 5
+            moe.layer_forward_stage(base, x, y, ws, moe.STAGE_GATE_UP, routing=r)
         torch.cuda._sleep(1000000)
         e[0].record()
         for W in reps:
-            moe.layer_forward_stage(W, x, y, ws, moe.STAGE_GATE_UP, routing=r)
+            moe.layer_forward_stage(W, x, y, ws, st_gu, routing=r)
         e[1].record()
         moe.layer_forward_stage(base, x, y, ws, moe.STAGE_DOWN_COMBINE, routing=r)
     torch.cuda.synchronize()
@@ -225,17 +231,24 @@ def main():
     sh_dn = synth.tensor_bytes(L.shared_fmt, D * Fs)
     router_b = D * L.n_expert * 4 + (L.n_expert * 4 if L.router_bias is not None else 0)
     step_bytes = router_b + nu * (gu_expert + dn_expert) + sh_gu + sh_dn + T * D * xb + T * D * 4
-    # stage 3 of the decode schedule (T <= 16) holds the routed experts only;
-    # the batched schedule's stage 3 also runs the shared expert
+    # the timed launch holds the routed experts' gate/up only: the decode
+    # kernel (T <= 16) or the grouped GEMM (stage 5); the other batched
+    # kernels' stage 3 also runs the shared expert
     small = T <= 16
-    gateup_bytes = nu * gu_expert + T * D * xb + T * k * F * 4
-    if not small:
-        gateup_bytes += sh_gu + T * Fs * 4
-    achieved = gateup_bytes / (gateup_ms * 1e-3) / 1e9
     if small:  # the decode gate/up kernel this layer takes
         kernel_name = "dec_k3_q2k4096_kernel" if L.gate_fmt == synth.Q2K and D == 4096 else "dec_k3_kernel"
+        gateup_bytes = nu * gu_expert + T * D * xb + T * k * F * 4
+    elif gemm:  # x codes (2 bytes per value) in, h out (bf16 or fp32)
+        kernel_name = "pf_gemm_kernel"
+        gateup_bytes = nu * gu_expert + T * D * 2 + T * k * F * xb
     else:
         kernel_name = "large_gateup_kernel"
+        gateup_bytes = nu * gu_expert + T * D * xb + T * k * F * 4 + sh_gu + T * Fs * 4
+    achieved = gateup_bytes / (gateup_ms * 1e-3) / 1e9
+    # bf16 rows: the routed gate/up is a dense contraction per expert at the
+    # ridge, priced against the dense bf16 matrix-core peak
+    gateup_flops = 2.0 * T * k * 2 * F * D
+    mfma_bound = gemm and mode == moe.BF16
     tokens_s = T / (ms_step * 1e-3)
     flops = 2.0 * T * (k * 3 * D * F + 3 * D * Fs)
 
@@ -283,6 +296,13 @@ def main():
         },
         "cpu_baseline": cpu,
     }
+    if mfma_bound:
+        tf = gateup_flops / (gateup_ms * 1e-3) / 1e12
+        line["roofline"].update({
+            "bound": "mfma", "achieved": round(tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tf / BF16_PEAK_TFLOPS, 4), "flops_per_launch": gateup_flops,
+            "hbm_gbps": round(achieved, 1),
+        })
     print(json.dumps(line), flush=True)
 
 
@@ -334,6 +354,8 @@ def run_stack(args, B):
                                    dev(L.down), dev(L.sh_gate), dev(L.sh_up), dev(L.sh_down), None, 1.0,
                                    codebook=cbd, gamma=dev(L.gamma)))
         del L
+        if (l + 1) % 8 == 0:
+            log("%d of %d layers resident (%.1f s)" % (l + 1, n_layer, time.time() - t0))
     torch.cuda.synchronize()
     log("%d layers generated and resident in %.1f s" % (n_layer, time.time() - t0))
     W0 = Ws[0]
@@ -417,7 +439,7 @@ def run_stack(args, B):
         cpu = {"value": round(B / (n_layer * per_layer), 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
                "sample": "%d pass(es) of layer 0 at %d token(s) in %.1f s, times 43 layers (nproc %d)" % (
                    done, B, el, os.cpu_count() or 0)}
-    kernel_name = "dec_k3_kernel"
+    kernel_name = "dec_k3_cb24096_kernel" if D == 4096 else "dec_k3_kernel"
     line = {
         "metric": METRIC,
         "value": round(tokens_s, 1),

@@ -129,9 +129,14 @@ int moe_route(const moe_layer_desc *desc, const void *x, int32_t T, int32_t x_ty
 /* Expert FFNs, shared expert and weighted combine for a routing produced by
  * moe_route on the same x ("Understanding Dwarf Star", 5.3.7 steps 2-5; 5.3.4).
  * y: [T][D] fp32.  flags: MOE_ACCUMULATE adds to y.
- * Numerics: x_type MOE_F32 computes in fp32 throughout; MOE_BF16 feeds bf16
- * activations and the exact integer codes of the weights to bf16 matrix
- * cores with fp32 accumulation and rounds the hidden activation h to bf16. */
+ * Numerics: x_type MOE_F32 keeps x, h and y in fp32; the products take the
+ * exact integer codes of the weights against activations coded as int16 per
+ * group of 16 values (few rows) or per row (many rows, on the matrix cores),
+ * accumulated exactly in int32 and scaled in fp32, and two calls give the
+ * same bits.  MOE_BF16 feeds bf16 activations and the exact integer codes of
+ * the weights to the matrix cores with fp32 accumulation, rounds the hidden
+ * activation h to bf16, and adds the routed down rows into y with atomics
+ * (the order of those additions varies between calls). */
 int moe_expert_ffn(const moe_layer_desc *desc, const void *x, int32_t T, int32_t x_type, const moe_routing *r,
                    float *y, uint32_t flags, void *ws, size_t ws_bytes, void *stream, char *err, size_t errlen);
 
@@ -149,7 +154,11 @@ int moe_layer_forward(const moe_layer_desc *desc, const void *x, int32_t T, int3
  *      gate/up)
  *   3  gate/up with SwiGLU
  *   4  down projection and the weighted combine into y (for a few rows, also
- *      the shared expert's down) */
+ *      the shared expert's down)
+ *   5  the routed gate/up kernel of stage 3 alone: on the grouped-GEMM path
+ *      (many rows, Q2K experts) it reuses the activation codes and tiles a
+ *      stage 3 call with the same x and routing left in the workspace;
+ *      elsewhere it equals stage 3.  For timing that kernel by itself. */
 int moe_layer_forward_stage(const moe_layer_desc *desc, const void *x, int32_t T, int32_t x_type, float *y,
                             uint32_t flags, const moe_routing *routing, int32_t stage, void *ws, size_t ws_bytes,
                             void *stream, char *err, size_t errlen);

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 F32, BF16, Q2K, Q8_0, CB2, Q4K = 0, 1, 2, 3, 4, 5
 ACCUMULATE = 1
-STAGE_ROUTER, STAGE_ROUTE, STAGE_GATE_UP, STAGE_DOWN_COMBINE = 1, 2, 3, 4
+STAGE_ROUTER, STAGE_ROUTE, STAGE_GATE_UP, STAGE_DOWN_COMBINE, STAGE_ROUTED_GATE_UP = 1, 2, 3, 4, 5
 STATUS = {0: "MOE_OK", -1: "MOE_EINVAL", -2: "MOE_EALIGN", -3: "MOE_EWORKSPACE", -4: "MOE_EUNSUPPORTED",
           -5: "MOE_EDEVICE"}
 

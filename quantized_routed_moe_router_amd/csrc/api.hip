@@ -97,13 +97,16 @@ RoutingPtrs from_ws(const Workspace &w) {
 // schedule; otherwise router logits, top-k + bucketing, gate/up, down.
 hipError_t forward(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r, float *y,
                    uint32_t flags, const Workspace &w, hipStream_t s, int stage) {
-    if (small_path_ok(d, T) && small_route_ok(d, T)) return launch_small(d, x, T, x_type, r, y, flags, w, s, stage, true);
+    // stage 5 (the routed gate/up kernel alone) differs from stage 3 on the
+    // grouped-GEMM path only
+    const int st3 = stage == 5 ? 3 : stage;
+    if (small_path_ok(d, T) && small_route_ok(d, T)) return launch_small(d, x, T, x_type, r, y, flags, w, s, st3, true);
     hipError_t e = hipSuccess;
     if (stage == 0 || stage == 1) e = launch_router_logits(d, x, T, x_type, w, s);
     if (e == hipSuccess && (stage == 0 || stage == 2)) e = launch_route_finish(d, T, r, w, s);
     if (e == hipSuccess && (stage == 0 || stage >= 3))
-        e = prefill_path_ok(d, T, x_type) ? launch_prefill(d, x, T, r, y, flags, w, s, stage)
-                                          : launch_ffn_large(d, x, T, x_type, r, y, flags, w, s, stage);
+        e = prefill_path_ok(d, T, x_type) ? launch_prefill(d, x, T, x_type, r, y, flags, w, s, stage)
+                                          : launch_ffn_large(d, x, T, x_type, r, y, flags, w, s, st3);
     return e;
 }
 
@@ -148,7 +151,7 @@ int moe_expert_ffn(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_
     Workspace w = workspace_layout(d, T, ws);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = small_path_ok(d, T)                ? launch_small(d, x, T, x_type, from_routing(r), y, flags, w, s, 0, false)
-                   : prefill_path_ok(d, T, x_type) ? launch_prefill(d, x, T, from_routing(r), y, flags, w, s, 0)
+                   : prefill_path_ok(d, T, x_type) ? launch_prefill(d, x, T, x_type, from_routing(r), y, flags, w, s, 0)
                                                    : launch_ffn_large(d, x, T, x_type, from_routing(r), y, flags, w, s, 0);
     return device_status(e, err, errlen);
 }
@@ -171,7 +174,7 @@ int moe_layer_forward(const moe_layer_desc *d, const void *x, int32_t T, int32_t
 int moe_layer_forward_stage(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, float *y,
                             uint32_t flags, const moe_routing *routing, int32_t stage, void *ws, size_t ws_bytes,
                             void *stream, char *err, size_t errlen) {
-    if (stage < 1 || stage > 4) return fail(err, errlen, MOE_EINVAL, "stage must be 1, 2, 3 or 4 (got %d)", stage);
+    if (stage < 1 || stage > 5) return fail(err, errlen, MOE_EINVAL, "stage must be 1 to 5 (got %d)", stage);
     int rc = check_call(d, x, T, x_type, ws, ws_bytes, err, errlen);
     if (rc) return rc;
     if (routing && (rc = check_routing(routing, err, errlen))) return rc;

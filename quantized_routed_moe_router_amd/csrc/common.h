@@ -437,6 +437,9 @@ MOE_DEV void prep_q2k(const float *x, XQ2K &p) {
 // Wave-cooperative preparation of ngroups (<= 4) groups: lane l holds the
 // value at position l % 16 of group l / 16; the records go to out[(l / 16) *
 // 10 ...].  All lanes of the wave must call it.
+// NAT: natural byte order instead (byte i % 4 of dword i / 4 holds value i),
+// the order of a codebook group's 8 values.
+template <bool NAT = false>
 MOE_DEV void prep16_wave(float v, uint32_t *out, int ngroups = 4) {
     const int lane = threadIdx.x & 63, pos = lane & 15;
     float m = fabsf(v), s = v;
@@ -448,12 +451,28 @@ MOE_DEV void prep16_wave(float v, uint32_t *out, int ngroups = 4) {
     const float S = m > 0.f ? kRec16Max / m : 0.f;
     int hi, lo;
     rec16_split(v, S, hi, lo);
-    // byte pos / 4 of dword pos % 4, gathered over the lanes of one residue
-    uint32_t A = (uint32_t)(hi & 0xFF) << (8 * (pos >> 2)), B = (uint32_t)(lo & 0xFF) << (8 * (pos >> 2));
-    A |= __shfl_xor(A, 4, kWave);
-    B |= __shfl_xor(B, 4, kWave);
-    A |= __shfl_xor(A, 8, kWave);
-    B |= __shfl_xor(B, 8, kWave);
+    uint32_t A, B;
+    if constexpr (NAT) {
+        // lanes 4j..4j+3 of the group gather dword j, which then moves to
+        // lane j (A) and lane 4 + j (B) of the group
+        A = (uint32_t)(hi & 0xFF) << (8 * (pos & 3));
+        B = (uint32_t)(lo & 0xFF) << (8 * (pos & 3));
+        A |= __shfl_xor(A, 1, kWave);
+        B |= __shfl_xor(B, 1, kWave);
+        A |= __shfl_xor(A, 2, kWave);
+        B |= __shfl_xor(B, 2, kWave);
+        const int src = (lane & ~15) + 4 * (pos & 3);
+        A = __shfl(A, src, kWave);
+        B = __shfl(B, src, kWave);
+    } else {
+        // byte pos / 4 of dword pos % 4, gathered over the lanes of one residue
+        A = (uint32_t)(hi & 0xFF) << (8 * (pos >> 2));
+        B = (uint32_t)(lo & 0xFF) << (8 * (pos >> 2));
+        A |= __shfl_xor(A, 4, kWave);
+        B |= __shfl_xor(B, 4, kWave);
+        A |= __shfl_xor(A, 8, kWave);
+        B |= __shfl_xor(B, 8, kWave);
+    }
     if ((lane >> 4) >= ngroups) return;
     uint32_t *rec = out + (lane >> 4) * kRec16Dwords;
     if (pos < 4) rec[pos] = A;
@@ -502,6 +521,47 @@ MOE_DEV float q2k_dot2(const Q2KChunk &c, const XQ2K &p) {
     group(std::integral_constant<int, 2>());
     group(std::integral_constant<int, 3>());
     return d * acc_q - dmin * acc_m;
+}
+
+// CB2 chunk against natural-order int16 activation records: per group of 16
+// values, the two codebook groups' signed int8 values (picked by byte
+// permutes from a table entry {values, negated values}: selector byte j is
+// j, or 4 + j when sign bit j is set) dotted with the hi and lo code halves,
+// sum = 256 A + B exact in int32 (|values| <= 127), scaled by the group's
+// 1/S; d * sum at the end.
+MOE_DEV uint32_t cb2_sel(uint32_t nib) { return 0x03020100u + (((nib * 0x00204081u) & 0x01010101u) << 2); }
+
+// bytewise negation of int8 values in [-127, 127]: (b ^ 0x7F) + 1 stays
+// below 0x100 in every byte, so no carry crosses a byte
+MOE_DEV uint32_t neg_bytes(uint32_t v) { return ((v ^ 0x7F7F7F7Fu) + 0x01010101u) ^ 0x80808080u; }
+
+MOE_DEV float cb2_dot_int(const CB2Chunk &c, const XQ2K &p, const u32x4 *tab) {
+    float acc = 0.f;
+    auto group = [&](auto G) {
+        constexpr int g = decltype(G)::value;
+        uint32_t w[4];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int q = 2 * g + hh;  // codebook group of the chunk
+            const uint32_t idx = ((q < 4 ? c.idx_lo : c.idx_hi) >> (8 * (q & 3))) & 0xFFu;
+            const uint32_t sg = ((q < 4 ? c.sg_lo : c.sg_hi) >> (8 * (q & 3))) & 0xFFu;
+            const u32x4 e = tab[idx];
+            w[2 * hh] = __builtin_amdgcn_perm(e[2], e[0], cb2_sel(sg & 15u));
+            w[2 * hh + 1] = __builtin_amdgcn_perm(e[3], e[1], cb2_sel(sg >> 4));
+        }
+        int A = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) A = sdot4(w[j], p.g[g].a[j], A);
+        int S = A << 8;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) S = sdot4(w[j], p.g[g].b[j], S);
+        acc = __builtin_fmaf((float)S, p.g[g].inv, acc);
+    };
+    group(std::integral_constant<int, 0>());
+    group(std::integral_constant<int, 1>());
+    group(std::integral_constant<int, 2>());
+    group(std::integral_constant<int, 3>());
+    return c.d * acc;
 }
 
 // scale S and 2^24/S for a set whose largest magnitude is m
@@ -742,6 +802,12 @@ bool small_path_ok(const moe_layer_desc *d, int32_t T);
 bool small_route_ok(const moe_layer_desc *d, int32_t T);
 hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
                         float *y, uint32_t flags, const Workspace &ws, hipStream_t s, int stage, bool route);
+// the shared expert's gate/up for any number of rows on the staged decode
+// kernel (Q8_0 shared expert at n_embd 4096): writes hs
+bool shared_gateup_staged_ok(const moe_layer_desc *d);
+hipError_t launch_shared_gateup_staged(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type,
+                                       const RoutingPtrs &r, float *y, uint32_t flags, const Workspace &ws,
+                                       hipStream_t s);
 // any number of rows: stage 3 = gate/up, 4 = down + combine, 0 = both
 hipError_t launch_ffn_large(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
                             float *y, uint32_t flags, const Workspace &ws, hipStream_t s, int stage);
@@ -749,10 +815,14 @@ hipError_t launch_ffn_large(const moe_layer_desc *d, const void *x, int32_t T, i
 hipError_t launch_ffn_large_shared(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type,
                                    const RoutingPtrs &r, float *y, uint32_t flags, const Workspace &ws, hipStream_t s,
                                    int stage);
-// many rows in bf16 mode with Q2K experts: MFMA grouped GEMMs
+// y = ys + sum_s w_s * ypart[pos] in slot order (+ y when accumulating)
+hipError_t launch_combine(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
+                          float *y, uint32_t flags, const Workspace &ws, hipStream_t s);
+// many rows with Q2K experts (bf16 rows, or fp32 rows beyond the decode
+// schedule): MFMA grouped GEMMs
 bool prefill_path_ok(const moe_layer_desc *d, int32_t T, int32_t x_type);
-hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, const RoutingPtrs &r, float *y,
-                          uint32_t flags, const Workspace &ws, hipStream_t s, int stage);
+hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
+                          float *y, uint32_t flags, const Workspace &ws, hipStream_t s, int stage);
 constexpr int kMaxHotlist = 16384;                  // entries one hot-list sort takes
 constexpr int64_t kHotCountMax = (int64_t)1 << 39;  // counts are clamped below this in the sort key
 hipError_t launch_count_selections(const int32_t *topk_idx, int32_t T, int32_t k, int32_t E, int32_t layer,

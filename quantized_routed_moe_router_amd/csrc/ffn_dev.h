@@ -35,6 +35,7 @@ struct FfnArgs {
     // rows ([T][D/16] records), x for Q8_0 rows ([T][D/64] records), h for the
     // routed Q2K down ([T*k][F/16] records)
     uint32_t *xp16, *xq8, *hp16;
+    int xp16_nat;       // x records in natural byte order (codebook gate/up)
     int n_prep_blocks;  // K1: x-preparing blocks
     int n_shgu_blocks;  // K2: shared gate/up blocks
     int shared_fmt;

@@ -106,7 +106,11 @@ __global__ void __launch_bounds__(256) dec_k1_kernel(FfnArgs a) {
     const int t = item / per_t, c = item % per_t;
     const int64_t i = (int64_t)t * a.D + 64 * c + lane;
     const float v = XT == MOE_BF16 ? bf16_bits_to_float(((const uint16_t *)a.x)[i]) : ((const float *)a.x)[i];
-    if (a.xp16) prep16_wave(v, a.xp16 + ((int64_t)t * (a.D / 16) + 4 * c) * kRec16Dwords);
+    if (a.xp16) {
+        uint32_t *out = a.xp16 + ((int64_t)t * (a.D / 16) + 4 * c) * kRec16Dwords;
+        if (a.xp16_nat) prep16_wave<true>(v, out);
+        else prep16_wave<false>(v, out);
+    }
     if (a.xq8) prep8_wave(v, a.xq8 + ((int64_t)t * (a.D / 64) + c) * kXQ8Dwords);
 }
 
@@ -433,6 +437,144 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
     }
 }
 
+// K3 for CB2 gate/up rows of 4096 weights ("Understanding Dwarf Star", 2.4:
+// per 256 weights an fp16 scale, 32 one-byte codebook indices of 8 values and
+// one sign bit per weight).  The schedule of the Q2K kernel above: all copies
+// issued at once, in the order [the raw codebook][records of the first token]
+// [gate rows 0-15][up rows 0-15], and the dot products of each 4-row group as
+// soon as it has landed.  Once the codebook has landed, each thread turns one
+// entry into {values, negated values} in a table; a group's signed values are
+// then two byte permutes, dotted as int8 against the token's int16 codes
+// (records in natural byte order, two int8 halves) by v_dot4.  12 copies of
+// 256 units: the last one's tail re-reads the final unit into spare LDS.
+constexpr int kK3CCbU = 128;                              // codebook: 256 entries x 8 bytes
+constexpr int kK3CXu = 640;                               // records of one token at n_embd 4096
+constexpr int kK3CHu = 264;                               // 4 rows of 4096 CB2 weights: 64 blocks of 66 bytes
+constexpr int kK3CUsed = kK3CCbU + kK3CXu + 8 * kK3CHu;  // 2880
+constexpr int kK3CCopies = (kK3CUsed + 255) / 256;        // 12 per lane
+constexpr int kK3CUnits = 256 * kK3CCopies;
+static_assert(kK3CHu * 16 == 4 * 16 * kCB2Bytes, "4 rows of 16 blocks");
+
+template <int END>
+MOE_DEV void k3c_wait() {
+    __builtin_amdgcn_sched_barrier(0);
+    vmem_wait_le<kK3CCopies - (END + 255) / 256>();
+    barrier_only();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int HG>
+MOE_DEV float k3c_group(const uint8_t *wb, int lr, int cidx, const XQ2K &xr, const u32x4 *tab) {
+    return cb2_dot_int(cb2_load(wb + 16 * (kK3CCbU + kK3CXu + kK3CHu * HG), (int64_t)lr * 4096 + 64 * cidx), xr, tab);
+}
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) dec_k3_cb24096_kernel(FfnArgs a) {
+    __shared__ __align__(16) u32x4 wbuf[kK3CUnits];
+    __shared__ u32x4 cbt[256];
+    __shared__ float part[4][32];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int gpe = a.F / 16, slot = blockIdx.x / gpe, g = blockIdx.x % gpe;
+    const SlotRec rec = uniform_slot(a.slots, slot);
+    if (rec.e < 0) return;  // uniform over the block
+    constexpr int RB = 16 * kCB2Bytes;  // bytes of one row
+    const int64_t goff = (int64_t)rec.e * a.gu_expert_bytes + (int64_t)16 * g * RB;
+    const uint8_t *gm = a.gate + goff, *um = a.up + goff;
+    {
+        const u32x4 *cs = (const u32x4 *)a.codebook;
+        const u32x4 *xs = (const u32x4 *)(a.xp16 + (int64_t)slot_token(rec, 0) * (4096 / 16) * kRec16Dwords);
+        const uint32_t lb = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(wbuf) + 1024 * wave);
+#pragma unroll
+        for (int i = 0; i < kK3CCopies; ++i) {
+            const int u = min(256 * i + tid, kK3CUsed - 1);
+            const void *src;
+            if (u < kK3CCbU) src = cs + u;
+            else if (u < kK3CCbU + kK3CXu) src = xs + (u - kK3CCbU);
+            else if (u < kK3CCbU + kK3CXu + 4 * kK3CHu) src = gm + 16 * (u - kK3CCbU - kK3CXu);
+            else src = um + 16 * (u - kK3CCbU - kK3CXu - 4 * kK3CHu);
+            dma16_m0(src, lb + 4096 * i);
+        }
+    }
+    const int c = lane & 15, lr = lane >> 4, cidx = 16 * wave + c;  // chunk of the row: 64 * cidx
+    const uint8_t *wb = (const uint8_t *)wbuf;
+    k3c_wait<kK3CCbU>();
+    {
+        const uint2 r = ((const uint2 *)wb)[tid];
+        cbt[tid] = u32x4{r.x, r.y, neg_bytes(r.x), neg_bytes(r.y)};
+    }
+    block_lds_sync();
+    XQ2K xr;
+    float v[8];
+    k3c_wait<kK3CCbU + kK3CXu>();
+    load_q2k_prep((const uint32_t *)(wb + 16 * kK3CCbU) + 40 * cidx, xr);
+    constexpr int X0 = kK3CCbU + kK3CXu;
+    k3c_wait<X0 + 1 * kK3CHu>();
+    v[0] = k3c_group<0>(wb, lr, cidx, xr, cbt);
+    pin_value(v[0]);
+    k3c_wait<X0 + 2 * kK3CHu>();
+    v[1] = k3c_group<1>(wb, lr, cidx, xr, cbt);
+    pin_value(v[1]);
+    k3c_wait<X0 + 3 * kK3CHu>();
+    v[2] = k3c_group<2>(wb, lr, cidx, xr, cbt);
+    pin_value(v[2]);
+    k3c_wait<X0 + 4 * kK3CHu>();
+    v[3] = k3c_group<3>(wb, lr, cidx, xr, cbt);
+    pin_value(v[3]);
+    k3c_wait<X0 + 5 * kK3CHu>();
+    v[4] = k3c_group<4>(wb, lr, cidx, xr, cbt);
+    pin_value(v[4]);
+    k3c_wait<X0 + 6 * kK3CHu>();
+    v[5] = k3c_group<5>(wb, lr, cidx, xr, cbt);
+    pin_value(v[5]);
+    k3c_wait<X0 + 7 * kK3CHu>();
+    v[6] = k3c_group<6>(wb, lr, cidx, xr, cbt);
+    pin_value(v[6]);
+    k3c_wait<X0 + 8 * kK3CHu>();
+    v[7] = k3c_group<7>(wb, lr, cidx, xr, cbt);
+    pin_value(v[7]);
+    for (int j = 0;;) {
+#pragma unroll
+        for (int hgrp = 0; hgrp < 8; ++hgrp) {
+            const float s = row16_sum(v[hgrp]);
+            if (c == 0) part[wave][2 * (4 * (hgrp & 3) + lr) + (hgrp >> 2)] = s;  // groups 0-3 gate, 4-7 up
+        }
+        block_lds_sync();
+        if (wave == 0) {
+            float hv = 0.f;
+            if (lane < 16) {
+                float gs = 0.f, us = 0.f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    gs += part[q][2 * lane];
+                    us += part[q][2 * lane + 1];
+                }
+                hv = swiglu_h(gs, us, a.x_bf16);
+                a.h[(int64_t)(rec.j0 + j) * a.F + 16 * g + lane] = hv;
+            }
+            if (a.hp16) prep16_wave(hv, a.hp16 + ((int64_t)(rec.j0 + j) * (a.F / 16) + g) * kRec16Dwords, 1);
+        }
+        if (++j >= rec.n) break;
+        block_lds_sync();  // part is rewritten for the next token
+        load_q2k_prep(a.xp16 + ((int64_t)slot_token(rec, j) * 256 + 4 * cidx) * kRec16Dwords, xr);
+        // one group at a time (the table reads of several would not fit)
+        v[0] = k3c_group<0>(wb, lr, cidx, xr, cbt);
+        pin_value(v[0]);
+        v[1] = k3c_group<1>(wb, lr, cidx, xr, cbt);
+        pin_value(v[1]);
+        v[2] = k3c_group<2>(wb, lr, cidx, xr, cbt);
+        pin_value(v[2]);
+        v[3] = k3c_group<3>(wb, lr, cidx, xr, cbt);
+        pin_value(v[3]);
+        v[4] = k3c_group<4>(wb, lr, cidx, xr, cbt);
+        pin_value(v[4]);
+        v[5] = k3c_group<5>(wb, lr, cidx, xr, cbt);
+        pin_value(v[5]);
+        v[6] = k3c_group<6>(wb, lr, cidx, xr, cbt);
+        pin_value(v[6]);
+        v[7] = k3c_group<7>(wb, lr, cidx, xr, cbt);
+        pin_value(v[7]);
+    }
+}
+
 // One block per 16 output rows, a wave per active slot in turn: the wave
 // copies the slot expert's 16 down rows into its own LDS area with aligned
 // 16-byte loads (no block barrier: every wave starts on its dots as soon as
@@ -714,6 +856,29 @@ FfnArgs make_ffn_args(const moe_layer_desc *d, const void *x, int32_t T, int32_t
     return a;
 }
 
+// The shared expert's gate/up for any number of fp32 or bf16 rows on the
+// staged K2 kernel (Q8_0 at n_embd 4096): the rows' Q8 records from K1's
+// preparing blocks, then one block per 8 shared rows, every token against
+// the staged rows.  Writes hs.
+bool shared_gateup_staged_ok(const moe_layer_desc *d) {
+    return d->n_ff_shared > 0 && d->shared_type == MOE_Q8_0 && d->n_embd == 4096 && d->n_ff_shared % 8 == 0;
+}
+
+hipError_t launch_shared_gateup_staged(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type,
+                                       const RoutingPtrs &r, float *y, uint32_t flags, const Workspace &ws,
+                                       hipStream_t s) {
+    FfnArgs a = make_ffn_args(d, x, T, x_type, r, y, flags, ws);
+    a.shared_fmt = MOE_Q8_0;
+    a.xq8 = ws.xq8;
+    a.n_router_blocks = 0;
+    a.build_slots = 0;
+    a.n_prep_blocks = (T * (a.D / 64) + 3) / 4;
+    if (x_type == MOE_BF16) dec_k1_kernel<MOE_BF16><<<a.n_prep_blocks, 256, 0, s>>>(a);
+    else dec_k1_kernel<MOE_F32><<<a.n_prep_blocks, 256, 0, s>>>(a);
+    dec_k2_q8sg4096_kernel<<<a.Fs / 8, 320, 0, s>>>(a, 0);
+    return hipGetLastError();
+}
+
 bool small_path_ok(const moe_layer_desc *d, int32_t T) {
     return T <= kMaxDecTokens && (int64_t)T * d->n_expert_used <= kMaxDecPairs && staged_fmt(d->gate_type) &&
            staged_fmt(d->down_type);
@@ -733,6 +898,11 @@ hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32
     a.nslots = (int)std::min<int64_t>((int64_t)T * a.k, a.E);
     a.build_slots = route ? 0 : 1;
     if (d->gate_type == MOE_Q2K) a.xp16 = ws.xp16;  // x records for the routed gate/up, written by K1
+    const bool cb4096 = d->gate_type == MOE_CB2 && a.D == 4096;
+    if (cb4096) {  // natural-order records for the codebook gate/up kernel
+        a.xp16 = ws.xp16;
+        a.xp16_nat = 1;
+    }
     if (d->down_type == MOE_Q2K) a.hp16 = ws.hp16;  // h records for the routed down, written by K3
     // a Q8_0 shared expert at n_embd 4096 takes the staged K2, on x records written by K1
     const bool sg_staged = has_sh && a.shared_fmt == MOE_Q8_0 && a.D == 4096 && a.Fs % 8 == 0;
@@ -756,7 +926,8 @@ hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32
         else with_fmt(a.shared_fmt, [&](auto S) { dec_k2_kernel<decltype(S)::value><<<k2, 256, 0, s>>>(a, route ? 1 : 0); });
     }
     if (stage == 0 || stage == 3) {
-        if (d->gate_type == MOE_CB2) dec_k3_kernel<MOE_CB2><<<k3, 256, 0, s>>>(a);
+        if (cb4096) dec_k3_cb24096_kernel<<<k3, 256, 0, s>>>(a);
+        else if (d->gate_type == MOE_CB2) dec_k3_kernel<MOE_CB2><<<k3, 256, 0, s>>>(a);
         else if (d->gate_type == MOE_Q4K) dec_k3_kernel<MOE_Q4K><<<k3, 256, 0, s>>>(a);
         else if (a.D == 4096) dec_k3_q2k4096_kernel<<<k3, 256, 0, s>>>(a);
         else dec_k3_kernel<MOE_Q2K><<<k3, 256, 0, s>>>(a);

@@ -42,7 +42,18 @@ __global__ void __launch_bounds__(256) large_down_kernel(FfnArgs a) {
     const int row0 = blockIdx.x * kLargeRows + wave * 4;
     load_codebook(a.codebook, cb_lds);
     if (row0 >= a.D) return;
-    if (shared) shared_down<SFMT>(a, row0, min(4, a.D - row0), cb_lds, lane);
+    if (shared) {
+        // blockIdx.z: a contiguous part of the token rows (the shared-only
+        // launch spreads its rows over more blocks this way)
+        const int tz = (a.T + (int)gridDim.z - 1) / (int)gridDim.z, t0 = (int)blockIdx.z * tz;
+        const int tn = min(a.T - t0, tz);
+        if (tn <= 0) return;
+        FfnArgs b = a;
+        b.T = tn;
+        b.hs = a.hs + (int64_t)t0 * a.Fs;
+        b.ys = a.ys + (int64_t)t0 * a.D;
+        shared_down<SFMT>(b, row0, min(4, a.D - row0), cb_lds, lane);
+    }
     else routed_down<DFMT>(a, a.active[s], row0, min(4, a.D - row0), cb_lds, lane, a.ypart + row0, a.D);
 }
 
@@ -83,13 +94,23 @@ hipError_t launch_ffn_large(const moe_layer_desc *d, const void *x, int32_t T, i
     return hipGetLastError();
 }
 
+// the gather of the per-pair down rows (ypart) in slot order, over the shared
+// output ys when there is a shared expert
+hipError_t launch_combine(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
+                          float *y, uint32_t flags, const Workspace &ws, hipStream_t s) {
+    FfnArgs a = make_ffn_args(d, x, T, x_type, r, y, flags, ws);
+    const int64_t n = (int64_t)T * a.D;
+    combine_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(a);
+    return hipGetLastError();
+}
+
 hipError_t launch_ffn_large_shared(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type,
                                    const RoutingPtrs &r, float *y, uint32_t flags, const Workspace &ws, hipStream_t s,
                                    int stage) {
     FfnArgs a = make_ffn_args(d, x, T, x_type, r, y, flags, ws);
     if (a.Fs <= 0) return hipSuccess;
     dim3 g1((a.Fs + kLargeRows - 1) / kLargeRows, 1);
-    dim3 g2((a.D + kLargeRows - 1) / kLargeRows, 1);
+    dim3 g2((a.D + kLargeRows - 1) / kLargeRows, 1, std::min(T, 8));  // down: up to 8 parts of the rows
     const int sf = d->shared_type;
     if (stage == 3)
         with_fmt(d->gate_type, [&](auto G) {

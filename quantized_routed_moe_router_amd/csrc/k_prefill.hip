@@ -68,7 +68,9 @@ struct PfArgs {
     int k;
     int D, F;
     uint16_t *hb;            // mode 0 output: h in bf16, [T*k][F] by bucket position
-    float *y;                // mode 1 output
+    float *hf;               // mode 0 output instead, when set: h in fp32 (fp32 mode)
+    float *y;                // mode 1 output: w * y_pair added into y by atomics
+    float *ypart;            // mode 1 output instead, when set: unweighted y_pair rows [T*k][D] by bucket position
 };
 
 // Global-to-LDS copies of 16 and 4 bytes per lane (lane l writes lds_wave +
@@ -167,20 +169,42 @@ MOE_DEV void pf_codes16(const float *v, float S, u32x4 &hi, u32x4 &lo) {
 // block per row, a thread per group of 16.  S = 32512 / max|row|; the group
 // sums are kept in code units (sum * S), so a whole product stays in code
 // units until the row's 1/S at the end.
-__global__ void __launch_bounds__(256) pf_prep_rows_kernel(const uint16_t *x, int n, uint8_t *xq, uint32_t *xs,
+// 16 consecutive values of a bf16 or fp32 row
+template <int XT>
+MOE_DEV void pf_load16(const void *x, int64_t i0, float *v) {
+    if constexpr (XT == MOE_BF16) {
+        const u32x4 *src = (const u32x4 *)((const uint16_t *)x + i0);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const u32x4 w = src[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[8 * i + 2 * j] = bf16_bits_to_float(w[j] & 0xFFFFu);
+                v[8 * i + 2 * j + 1] = bf16_bits_to_float(w[j] >> 16);
+            }
+        }
+    } else {
+        const f32x4 *src = (const f32x4 *)((const float *)x + i0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4 w = src[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[4 * i + j] = w[j];
+        }
+    }
+}
+
+template <int XT>
+__global__ void __launch_bounds__(256) pf_prep_rows_kernel(const void *x, int n, uint8_t *xq, uint32_t *xs,
                                                            float *xinv) {
     __shared__ float wmax[4];
     const int t = blockIdx.x, ng = n >> 4;
     float mt = 0.f;
     for (int g = threadIdx.x; g < ng; g += 256) {
-        const u32x4 *src = (const u32x4 *)(x + (int64_t)t * n + 16 * g);
+        float v[16];
+        pf_load16<XT>(x, (int64_t)t * n + 16 * g, v);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const u32x4 w = src[i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                mt = fmaxf(mt, fmaxf(fabsf(bf16_bits_to_float(w[j] & 0xFFFFu)), fabsf(bf16_bits_to_float(w[j] >> 16))));
-        }
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, fabsf(v[i]));
     }
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) mt = fmaxf(mt, __shfl_xor(mt, o, kWave));
@@ -192,16 +216,7 @@ __global__ void __launch_bounds__(256) pf_prep_rows_kernel(const uint16_t *x, in
     const int nkb = n >> 8;
     for (int g = threadIdx.x; g < ng; g += 256) {
         float v[16];
-        const u32x4 *src = (const u32x4 *)(x + (int64_t)t * n + 16 * g);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const u32x4 w = src[i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                v[8 * i + 2 * j] = bf16_bits_to_float(w[j] & 0xFFFFu);
-                v[8 * i + 2 * j + 1] = bf16_bits_to_float(w[j] >> 16);
-            }
-        }
+        pf_load16<XT>(x, (int64_t)t * n + 16 * g, v);
         const int kb = g >> 4, gi = g & 15;
         float sum = 0.f;
 #pragma unroll
@@ -318,7 +333,7 @@ __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
         const int pos = start + min(tid, cnt - 1);
         const int pair = a.perm[pos];
         row_tok[tid] = pair / a.k;
-        row_f[tid] = MODE == 0 ? a.ainv[pair / a.k] : a.ainv[pos] * a.topk_w[pair];
+        row_f[tid] = MODE == 0 ? a.ainv[pair / a.k] : a.ainv[pos] * (a.ypart ? 1.f : a.topk_w[pair]);
     }
     block_lds_sync();
 
@@ -522,7 +537,8 @@ __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
                         const float f = row_f[r];
                         const int col = wave * 64 + 32 * n + c;
                         const float hv = silu(tot[n][q][v] * f) * (U[r * 256 + col] * f);
-                        a.hb[(int64_t)(start + r) * a.F + o0 + col] = bf16_rne(hv);
+                        if (a.hf) a.hf[(int64_t)(start + r) * a.F + o0 + col] = hv;
+                        else a.hb[(int64_t)(start + r) * a.F + o0 + col] = bf16_rne(hv);
                     }
                 }
         }
@@ -535,9 +551,10 @@ __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int r = q * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-                    if (r < cnt)
-                        unsafeAtomicAdd(&a.y[(int64_t)row_tok[r] * a.D + o0 + wave * 64 + 32 * n + c],
-                                        row_f[r] * tot[n][q][v]);
+                    if (r >= cnt) continue;
+                    const int col = o0 + wave * 64 + 32 * n + c;
+                    if (a.ypart) a.ypart[(int64_t)(start + r) * a.D + col] = row_f[r] * tot[n][q][v];
+                    else unsafeAtomicAdd(&a.y[(int64_t)row_tok[r] * a.D + col], row_f[r] * tot[n][q][v]);
                 }
             }
     }
@@ -718,16 +735,24 @@ __global__ void __launch_bounds__(512) pf_sg_gemm_kernel(SgArgs a) {
     }
 }
 
+// bf16 rows at any count, and fp32 rows beyond the decode schedule (the caller
+// takes that first)
 bool prefill_path_ok(const moe_layer_desc *d, int32_t T, int32_t x_type) {
-    return x_type == MOE_BF16 && T > 0 && d->gate_type == MOE_Q2K && d->down_type == MOE_Q2K &&
+    return (x_type == MOE_BF16 || x_type == MOE_F32) && T > 0 && d->gate_type == MOE_Q2K && d->down_type == MOE_Q2K &&
            d->n_embd % 512 == 0 && d->n_ff_exp % 256 == 0 &&
            (d->n_ff_shared == 0 || (d->shared_type == MOE_Q8_0 && d->n_ff_shared % 128 == 0));
 }
 
 // stage 3: x codes, tiles, shared gate/up, routed gate/up; stage 4: h codes,
-// shared down, y init, routed down; 0: all
-hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, const RoutingPtrs &r, float *y,
-                          uint32_t flags, const Workspace &ws, hipStream_t s, int stage) {
+// shared down, y init, routed down; 0: all; 5: the routed gate/up GEMM alone.
+// bf16 mode: the shared expert as bf16 GEMMs, h in bf16, the routed down
+// added into y by atomics.  fp32 mode: the routed GEMMs take fp32 rows and
+// keep h in fp32, the shared expert runs on the batched kernels (hs, ys),
+// the routed down writes one row per pair and the gather adds them in slot
+// order, so that two runs give the same bits.
+hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
+                          float *y, uint32_t flags, const Workspace &ws, hipStream_t s, int stage) {
+    const bool f32 = x_type == MOE_F32;
     const int D = d->n_embd, F = d->n_ff_exp, k = d->n_expert_used, E = d->n_expert, Fs = d->n_ff_shared;
     const int ntmax = pf_max_tiles(T, k, E);
     static_assert(kPfM == kPfTileRows, "tile rows");
@@ -741,12 +766,20 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, con
     a.D = D;
     a.F = F;
     a.hb = ws.pf_hb;
+    a.hf = f32 ? ws.h : nullptr;
     a.y = y;
+    a.ypart = f32 ? ws.ypart : nullptr;
     a.expert_bytes = fmt_bytes(MOE_Q2K, (int64_t)F * D);
     if (stage == 0 || stage == 3) {
-        pf_prep_rows_kernel<<<T, 256, 0, s>>>((const uint16_t *)x, D, ws.pf_xq, ws.pf_xs, ws.pf_xinv);
+        if (f32) pf_prep_rows_kernel<MOE_F32><<<T, 256, 0, s>>>(x, D, ws.pf_xq, ws.pf_xs, ws.pf_xinv);
+        else pf_prep_rows_kernel<MOE_BF16><<<T, 256, 0, s>>>(x, D, ws.pf_xq, ws.pf_xs, ws.pf_xinv);
         pf_tiles_kernel<<<1, 64, 0, s>>>(r.active, r.n_active, r.count, r.offset, ws.pf_tiles, ws.pf_ntiles);
-        if (Fs > 0) {
+        if (Fs > 0 && f32) {
+            const hipError_t e = shared_gateup_staged_ok(d)
+                                     ? launch_shared_gateup_staged(d, x, T, x_type, r, y, flags, ws, s)
+                                     : launch_ffn_large_shared(d, x, T, x_type, r, y, flags, ws, s, 3);
+            if (e != hipSuccess) return e;
+        } else if (Fs > 0) {
             // shared weights split into bf16 halves, then the shared gate/up GEMM
             const int64_t nw = (int64_t)Fs * D, nb = nw / 32;
             uint16_t *hi = ws.pf_shw, *lo = ws.pf_shw + 3 * nw;
@@ -765,6 +798,8 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, con
             sg.hs = ws.pf_hsb;
             pf_sg_gemm_kernel<0><<<dim3(Fs / 128, (T + kSgM - 1) / kSgM), 512, 0, s>>>(sg);
         }
+    }
+    if (stage == 0 || stage == 3 || stage == 5) {  // 5: the routed gate/up GEMM alone, on stage 3's codes and tiles
         PfArgs g = a;
         g.w0 = (const uint8_t *)d->gate;
         g.w1 = (const uint8_t *)d->up;
@@ -775,7 +810,22 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, con
         pf_gemm_kernel<0><<<(unsigned)(((ntmax + 7) / 8) * 8 * (F / 256)), kPfThreads, 0, s>>>(g);
     }
     if (stage == 0 || stage == 4) {
-        pf_prep_rows_kernel<<<(unsigned)P, 256, 0, s>>>(ws.pf_hb, F, ws.pf_hq, ws.pf_hs, ws.pf_hinv);
+        if (f32) {
+            pf_prep_rows_kernel<MOE_F32><<<(unsigned)P, 256, 0, s>>>(ws.h, F, ws.pf_hq, ws.pf_hs, ws.pf_hinv);
+            if (Fs > 0) {
+                const hipError_t e = launch_ffn_large_shared(d, x, T, x_type, r, y, flags, ws, s, 4);
+                if (e != hipSuccess) return e;
+            }
+            PfArgs dn = a;
+            dn.w0 = dn.w1 = (const uint8_t *)d->down;
+            dn.n_in = F;
+            dn.aq = ws.pf_hq;
+            dn.as = ws.pf_hs;
+            dn.ainv = ws.pf_hinv;
+            pf_gemm_kernel<1><<<(unsigned)(((ntmax + 7) / 8) * 8 * (D / 512)), kPfThreads, 0, s>>>(dn);
+            return launch_combine(d, x, T, x_type, r, y, flags, ws, s);
+        }
+        pf_prep_rows_kernel<MOE_BF16><<<(unsigned)P, 256, 0, s>>>(ws.pf_hb, F, ws.pf_hq, ws.pf_hs, ws.pf_hinv);
         if (Fs > 0) {
             const int64_t nw = (int64_t)Fs * D;
             SgArgs sg{};

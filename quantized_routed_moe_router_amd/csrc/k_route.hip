@@ -53,15 +53,31 @@ MOE_DEV float router_x(const RouterX<XT> &v, int q) {
     }
 }
 
-template <int XT>
+// KS = 4 (fewer rows): the 4 waves of a block take quarters of the
+// reduction of one 16 x 16 tile instead, and wave 0 adds the four partial
+// sums in wave order (fixed, so the result does not vary between runs); the
+// blocks then map to tiles in order (n_ttx = token tiles, n_eq = expert tiles).
+template <int XT, int KS>
 __global__ void __launch_bounds__(256) router_mfma_kernel(const float *__restrict__ W, const float *__restrict__ bias,
                                                           const void *__restrict__ xin, int T, int D, int E,
                                                           double *__restrict__ logits, int n_ttx, int n_eq) {
+    __shared__ double red[KS == 4 ? 3 : 1][64][4];
     const int L = blockIdx.x, xcd = L & 7, j = L >> 3;
-    const int tt = xcd * n_ttx + j / n_eq, eq = j % n_eq;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int t0 = tt * 16, e0 = (eq * 4 + wave) * 16;
-    if (t0 >= T || e0 >= E) return;
+    int tt, e0, kbeg, kend;
+    if constexpr (KS == 1) {
+        tt = xcd * n_ttx + j / n_eq;
+        e0 = ((j % n_eq) * 4 + wave) * 16;
+        kbeg = 0;
+        kend = D;
+    } else {
+        tt = L / n_eq;
+        e0 = (L % n_eq) * 16;
+        kbeg = wave * (D / 4);
+        kend = kbeg + D / 4;
+    }
+    const int t0 = tt * 16;
+    if (t0 >= T || e0 >= E) return;  // uniform over the block when KS = 4
     const int row = lane & 15, kq = 4 * (lane >> 4);
     const int t = min(t0 + row, T - 1), e = min(e0 + row, E - 1);
     const void *xrow = XT == MOE_BF16 ? (const void *)((const uint16_t *)xin + (int64_t)t * D + kq)
@@ -88,12 +104,21 @@ __global__ void __launch_bounds__(256) router_mfma_kernel(const float *__restric
                 acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)router_x<XT>(xv[c], q), (double)wv[c][q], acc, 0,
                                                            0, 0);
     };
-    load(xa, wa, 0);
-    for (int k0 = 0; k0 < D; k0 += 128) {
+    load(xa, wa, kbeg);
+    for (int k0 = kbeg; k0 < kend; k0 += 128) {
         load(xb, wb, k0 + 64);
         mma(xa, wa);
-        load(xa, wa, min(k0 + 128, D - 64));  // the last step re-reads a slice: no branch, so the waits stay exact
+        load(xa, wa, min(k0 + 128, kend - 64));  // the last step re-reads a slice: no branch, so the waits stay exact
         mma(xb, wb);
+    }
+    if constexpr (KS == 4) {
+        if (wave > 0)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave - 1][lane][r] = acc[r];
+        __syncthreads();
+        if (wave > 0) return;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = ((acc[r] + red[0][lane][r]) + red[1][lane][r]) + red[2][lane][r];
     }
     const int ex = e0 + (lane & 15);
     if (ex >= E) return;
@@ -230,9 +255,11 @@ __global__ void __launch_bounds__(512) bucket_kernel(const int32_t *__restrict__
 
 // one block per expert row for few tokens, 16 x 16 tiles for many
 bool router_rows_ok(int T) { return T <= 16; }
-// the matrix-core router from 128 rows on (fewer rows leave most of the chip
-// idle with one wave per 16 x 16 tile); the k steps need D % 128 == 0
+// the matrix-core router: a wave per 16 x 16 tile from 128 rows on (the k
+// steps need D % 128 == 0); below that, for more rows than the one-block
+// router takes, four waves per tile (D % 512 == 0)
 bool router_mfma_ok(int T, int D) { return T >= 128 && D % 128 == 0; }
+bool router_mfma4_ok(int T, int D) { return T > 16 && D % 512 == 0; }
 
 hipError_t launch_router_logits(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type,
                                 const Workspace &ws, hipStream_t s) {
@@ -246,11 +273,19 @@ hipError_t launch_router_logits(const moe_layer_desc *d, const void *x, int32_t 
         const int n_tt = (T + 15) / 16, n_ttx = (n_tt + 7) / 8, n_eq = ((E + 15) / 16 + 3) / 4;
         const int grid = 8 * n_ttx * n_eq;
         if (x_type == MOE_BF16)
-            router_mfma_kernel<MOE_BF16><<<grid, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E, ws.logits,
-                                                               n_ttx, n_eq);
+            router_mfma_kernel<MOE_BF16, 1><<<grid, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E, ws.logits,
+                                                                  n_ttx, n_eq);
         else
-            router_mfma_kernel<MOE_F32><<<grid, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E, ws.logits,
-                                                              n_ttx, n_eq);
+            router_mfma_kernel<MOE_F32, 1><<<grid, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E, ws.logits,
+                                                                 n_ttx, n_eq);
+    } else if (router_mfma4_ok(T, D)) {
+        const int n_tt = (T + 15) / 16, n_et = (E + 15) / 16;
+        if (x_type == MOE_BF16)
+            router_mfma_kernel<MOE_BF16, 4><<<n_tt * n_et, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E,
+                                                                         ws.logits, n_tt, n_et);
+        else
+            router_mfma_kernel<MOE_F32, 4><<<n_tt * n_et, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E,
+                                                                        ws.logits, n_tt, n_et);
     } else {
         dim3 g((T + 15) / 16, (E + 15) / 16);
         if (x_type == MOE_BF16)

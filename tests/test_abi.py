@@ -105,7 +105,7 @@ def test_other_entry_points_validate():
                                    None, err, 256) == -1
     assert moe._lib.moe_layer_forward(ctypes.byref(d), 0x80000, 1, 0, None, 0, None, 0x90000, 1 << 30, None,
                                       err, 256) == -1
-    for stage in (0, 5):
+    for stage in (0, 6):
         assert moe._lib.moe_layer_forward_stage(ctypes.byref(d), 0x80000, 1, 0, 0x100000, 0, None, stage, 0x90000,
                                                 1 << 30, None, err, 256) == -1
 

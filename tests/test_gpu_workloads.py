@@ -138,6 +138,22 @@ def stack3():
     return layers, [gu.upload(L) for L in layers]
 
 
+@pytest.mark.parametrize("T", [3, 16])
+def test_cb2_full_width_layer(stack3, T):
+    # the codebook gate/up kernel at n_embd 4096 on its own, from a few tokens
+    # to the decode schedule's 16 (several tokens per expert of 16)
+    layers, Ws = stack3
+    L = layers[0]
+    x = synth.activations(120 + T, T, L.n_embd)
+    t = time.time()
+    y_ref, idx_ref, w_ref = oracle.moe_forward(L, x=x)
+    _log("cb2 layer T=%d: oracle %.1f s" % (T, time.time() - t))
+    y, r = gu.run_forward(Ws[0], gu.x_to_device(x=x))
+    gu.check_routing(r, idx_ref, w_ref, L.n_expert)
+    worst = gu.assert_close(y.cpu().numpy(), y_ref)
+    _log("cb2 layer T=%d: worst relative error %.3g" % (T, worst))
+
+
 @pytest.mark.parametrize("B", [1, 8])
 def test_stack_rmsnorm_residual_teacher_forced(stack3, B):
     # x <- x + MoE(RMSNorm(x)) layer by layer through the C ABI (rmsnorm, then

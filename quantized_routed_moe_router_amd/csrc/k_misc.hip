@@ -13,6 +13,7 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float *__restrict__ 
     int t = blockIdx.x;
     const float *xr = x + (int64_t)t * D;
     float ss = 0.f;
+#pragma unroll 4
     for (int i = threadIdx.x; i < D; i += 256) ss = __builtin_fmaf(xr[i], xr[i], ss);
     for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, kWave);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
@@ -23,9 +24,50 @@ __global__ void __launch_bounds__(256) rmsnorm_kernel(const float *__restrict__ 
     for (int i = threadIdx.x; i < D; i += 256) out[(int64_t)t * D + i] = gamma[i] * (xr[i] * inv);
 }
 
+// D = 1024 NV with 16-byte aligned rows: every load of a thread (NV x and NV
+// gamma, 16 bytes each) is issued before the first is used, and the values
+// stay in registers for the output, so the row costs one memory round trip
+// instead of one per element a thread holds.  A thread writes only the
+// elements it read, so out may be x.
+template <int NV>
+__global__ void __launch_bounds__(256) rmsnorm_vec_kernel(const float *__restrict__ x, const float *__restrict__ gamma,
+                                                          float eps, float *__restrict__ out) {
+    __shared__ float red[4];
+    constexpr int D = 1024 * NV;
+    const int t = blockIdx.x;
+    const f32x4 *xr = (const f32x4 *)(x + (int64_t)t * D), *gr = (const f32x4 *)gamma;
+    f32x4 v[NV], g[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] = xr[threadIdx.x + 256 * i];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) g[i] = gr[threadIdx.x + 256 * i];
+    float ss = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) ss = __builtin_fmaf(v[i][j], v[i][j], ss);
+    for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, kWave);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+    const float inv = 1.0f / sqrtf(tot / (float)D + eps);
+    f32x4 *orow = (f32x4 *)(out + (int64_t)t * D);
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        f32x4 r;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = g[i][j] * (v[i][j] * inv);
+        orow[threadIdx.x + 256 * i] = r;
+    }
+}
+
 hipError_t launch_rmsnorm(const float *x, const float *gamma, float eps, int32_t T, int32_t D, float *out,
                           hipStream_t s) {
-    rmsnorm_kernel<<<T, 256, 0, s>>>(x, gamma, eps, D, out);
+    const bool al = ((uintptr_t)x % 16 == 0) && ((uintptr_t)gamma % 16 == 0) && ((uintptr_t)out % 16 == 0);
+    if (al && D == 4096) rmsnorm_vec_kernel<4><<<T, 256, 0, s>>>(x, gamma, eps, out);
+    else if (al && D == 2048) rmsnorm_vec_kernel<2><<<T, 256, 0, s>>>(x, gamma, eps, out);
+    else if (al && D == 1024) rmsnorm_vec_kernel<1><<<T, 256, 0, s>>>(x, gamma, eps, out);
+    else rmsnorm_kernel<<<T, 256, 0, s>>>(x, gamma, eps, D, out);
     return hipGetLastError();
 }
 

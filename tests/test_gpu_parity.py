@@ -109,6 +109,29 @@ def test_cb2_gate_up_layer():
     _check_layer(L, 9, 73)
 
 
+def test_cb2_codebook_range_ends():
+    # the codebook gate/up kernel at n_embd 4096 with codebook values at the
+    # ends of the range it takes, [-127, 127] (its bytewise negation is
+    # carry-free there), and every block's indices redrawn over the four
+    # extreme entries so that they are used throughout; every block scale is
+    # set so that the weights keep the magnitude of N(0, 0.02) draws
+    cb = np.clip(synth.codebook(4).astype(np.int32) * 15, -127, 127).astype(np.int8)
+    cb[0] = [127, -127, 127, -127, 127, -127, 127, -127]
+    cb[1] = -127
+    cb[2] = 127
+    cb[3] = [0, 127, -127, 0, 1, -1, 126, -126]
+    L = synth.make_layer(130, 0, D=4096, E=8, k=2, F=128, Fs=0, gate_fmt=synth.CB2, cb=cb)
+    for i, name in enumerate(("gate", "up")):
+        g = np.ascontiguousarray(getattr(L, name)).copy()
+        blocks = g.reshape(-1, 66)
+        u = synth.uniform(131 + i, 0, synth.TAG_X, 0, blocks.shape[0] * 32)
+        blocks[:, 2:34] = (u * 4).astype(np.uint8).reshape(-1, 32)
+        blocks[:, 0:2] = np.array([1.5e-4], dtype=np.float16).view(np.uint8)
+        setattr(L, name, g)
+    worst, _, _ = _check_layer(L, 3, 133)
+    print("cb2 range ends: worst relative error %.3g" % worst)
+
+
 @pytest.mark.parametrize("E,k", [(1, 1), (6, 6), (16, 1)])
 def test_degenerate_routings(E, k):
     L = synth.make_layer(80 + E, 0, D=256, E=E, k=k, F=128, Fs=64)
@@ -226,10 +249,13 @@ def test_stages_equal_layer_forward(T):
     assert torch.equal(y, y2) and torch.equal(r.perm, r2.perm)
 
 
-def test_rmsnorm():
+@pytest.mark.parametrize("D", [4096, 1000])
+def test_rmsnorm(D):
+    # 4096: the vector kernel (16-byte loads held in registers); 1000: the
+    # general one
     import quantized_routed_moe_router_amd as moe
-    x = synth.activations(99, 8, 4096)
-    g = (0.9 + 0.2 * synth.uniform(99, 0, synth.TAG_GAMMA, 0, 4096)).astype(np.float32)
+    x = synth.activations(99, 8, D)
+    g = (0.9 + 0.2 * synth.uniform(99, 0, synth.TAG_GAMMA, 0, D)).astype(np.float32)
     ref = oracle.rmsnorm(x, g, 1e-6)
     xd, gd = gu.dev(x), gu.dev(g)
     out = torch.empty_like(xd)

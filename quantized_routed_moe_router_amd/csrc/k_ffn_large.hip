@@ -30,6 +30,31 @@ __global__ void __launch_bounds__(256) large_gateup_kernel(FfnArgs a) {
     else routed_gateup<GFMT>(a, a.active[s], row0, min(4, rows - row0), cb_lds, lane);
 }
 
+// Q8 records of rows of n fp32 values (one wave per 64 values), for the
+// shared expert's down: prepared once per call instead of in every lane of
+// every wave that dots a row with them.
+__global__ void __launch_bounds__(256) q8_rows_prep_kernel(const float *__restrict__ rows, int T, int n,
+                                                           uint32_t *__restrict__ out) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int item = blockIdx.x * 4 + wave, per_t = n / 64;
+    if (item >= T * per_t) return;  // uniform over the wave
+    const int t = item / per_t, c = item % per_t;
+    prep8_wave(rows[(int64_t)t * n + 64 * c + lane], out + ((int64_t)t * per_t + c) * kXQ8Dwords);
+}
+
+// The shared expert's down, rows [row0, row0 + nrows), every token, on the
+// Q8 records of hs in a.xq8 ([T][Fs / 64] records).
+MOE_DEV void shared_down_q8rec(const FfnArgs &a, int row0, int nrows, int lane) {
+    const RowPlan rp = row_plan(a.Fs, lane);
+    for (int t = 0; t < a.T; ++t) {
+        XQ8 xr;
+        load_q8_prep(a.xq8 + ((int64_t)t * (a.Fs / 64) + rp.c) * kXQ8Dwords, xr);
+        float *dst = a.ys + (int64_t)t * a.D + row0;
+        wave_rows<MOE_Q8_0, false>(a.sh_down, nullptr, a.Fs, row0, nrows, xr, nullptr, lane,
+                                   [&](int r, float s, float) { dst[r] = s; });
+    }
+}
+
 template <int DFMT, int SFMT>
 __global__ void __launch_bounds__(256) large_down_kernel(FfnArgs a) {
     __shared__ uint32_t cb_lds[512];
@@ -52,7 +77,12 @@ __global__ void __launch_bounds__(256) large_down_kernel(FfnArgs a) {
         b.T = tn;
         b.hs = a.hs + (int64_t)t0 * a.Fs;
         b.ys = a.ys + (int64_t)t0 * a.D;
-        shared_down<SFMT>(b, row0, min(4, a.D - row0), cb_lds, lane);
+        if (SFMT == MOE_Q8_0 && a.xq8) {
+            b.xq8 = a.xq8 + (int64_t)t0 * (a.Fs / 64) * kXQ8Dwords;
+            shared_down_q8rec(b, row0, min(4, a.D - row0), lane);
+        } else {
+            shared_down<SFMT>(b, row0, min(4, a.D - row0), cb_lds, lane);
+        }
     }
     else routed_down<DFMT>(a, a.active[s], row0, min(4, a.D - row0), cb_lds, lane, a.ypart + row0, a.D);
 }
@@ -116,10 +146,17 @@ hipError_t launch_ffn_large_shared(const moe_layer_desc *d, const void *x, int32
         with_fmt(d->gate_type, [&](auto G) {
             with_fmt(sf, [&](auto S) { large_gateup_kernel<decltype(G)::value, decltype(S)::value><<<g1, 256, 0, s>>>(a); });
         });
-    if (stage == 4)
+    if (stage == 4) {
+        // a Q8_0 down takes records of hs prepared once (the workspace's x
+        // records, [T][D / 64], are free again after the gate/up and hold them)
+        if (sf == MOE_Q8_0 && a.Fs % 64 == 0 && a.Fs <= a.D) {
+            a.xq8 = ws.xq8;
+            q8_rows_prep_kernel<<<(T * (a.Fs / 64) + 3) / 4, 256, 0, s>>>(ws.hs, T, a.Fs, ws.xq8);
+        }
         with_fmt(d->down_type, [&](auto DN) {
             with_fmt(sf, [&](auto S) { large_down_kernel<decltype(DN)::value, decltype(S)::value><<<g2, 256, 0, s>>>(a); });
         });
+    }
     return hipGetLastError();
 }
 

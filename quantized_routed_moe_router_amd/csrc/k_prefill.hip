@@ -567,32 +567,38 @@ __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulation): bf16 activations times
 // either half are exact products.
 
+// One thread per 8 weights (a quarter of a 34-byte block): its 8 codes and
+// the block's d come in as aligned dwords (the block starts at a 2-byte
+// boundary), and the 8 hi and 8 lo halves go out as one 16-byte store each.
 __global__ void __launch_bounds__(256) pf_q8_split_kernel(const uint8_t *src, int64_t nblocks, uint16_t *hi,
                                                           uint16_t *lo) {
-    const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x, b = q >> 2;
     if (b >= nblocks) return;
+    const int i0 = 8 * (int)(q & 3);
     const uint8_t *blk = src + b * kQ8Bytes;
-    const float d = half_bits_to_float((uint32_t)blk[0] | ((uint32_t)blk[1] << 8));
+    const uintptr_t ab = (uintptr_t)blk;
+    const uint32_t dw = *(const uint32_t *)(ab & ~(uintptr_t)3);
+    const float d = half_bits_to_float((ab & 2u) ? (dw >> 16) : (dw & 0xFFFFu));
+    uint32_t c[2];
+    load_8_at_even(blk + 2 + i0, c[0], c[1]);
+    uint32_t hw[4], lw[4];
 #pragma unroll
-    for (int i0 = 0; i0 < 32; i0 += 8) {
-        uint32_t hw[4], lw[4];
+    for (int j = 0; j < 8; j += 2) {
+        uint32_t hh = 0, ll = 0;
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-            uint32_t hh = 0, ll = 0;
-#pragma unroll
-            for (int z = 0; z < 2; ++z) {
-                const float w = d * (float)(int8_t)blk[2 + i0 + j + z];
-                const uint16_t wh = bf16_rne(w);
-                const uint16_t wl = bf16_rne(w - bf16_bits_to_float(wh));
-                hh |= (uint32_t)wh << (16 * z);
-                ll |= (uint32_t)wl << (16 * z);
-            }
-            hw[j / 2] = hh;
-            lw[j / 2] = ll;
+        for (int z = 0; z < 2; ++z) {
+            const int k = j + z;
+            const float w = d * (float)(int8_t)(c[k >> 2] >> (8 * (k & 3)));
+            const uint16_t wh = bf16_rne(w);
+            const uint16_t wl = bf16_rne(w - bf16_bits_to_float(wh));
+            hh |= (uint32_t)wh << (16 * z);
+            ll |= (uint32_t)wl << (16 * z);
         }
-        *(u32x4 *)(hi + b * 32 + i0) = u32x4{hw[0], hw[1], hw[2], hw[3]};
-        *(u32x4 *)(lo + b * 32 + i0) = u32x4{lw[0], lw[1], lw[2], lw[3]};
+        hw[j / 2] = hh;
+        lw[j / 2] = ll;
     }
+    *(u32x4 *)(hi + b * 32 + i0) = u32x4{hw[0], hw[1], hw[2], hw[3]};
+    *(u32x4 *)(lo + b * 32 + i0) = u32x4{lw[0], lw[1], lw[2], lw[3]};
 }
 
 constexpr int kSgM = 128;            // token rows per block (four 32-row subtiles)
@@ -783,7 +789,7 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int
             // shared weights split into bf16 halves, then the shared gate/up GEMM
             const int64_t nw = (int64_t)Fs * D, nb = nw / 32;
             uint16_t *hi = ws.pf_shw, *lo = ws.pf_shw + 3 * nw;
-            const unsigned g = (unsigned)((nb + 255) / 256);
+            const unsigned g = (unsigned)((4 * nb + 255) / 256);  // a thread per 8 weights
             pf_q8_split_kernel<<<g, 256, 0, s>>>((const uint8_t *)d->sh_gate, nb, hi, lo);
             pf_q8_split_kernel<<<g, 256, 0, s>>>((const uint8_t *)d->sh_up, nb, hi + nw, lo + nw);
             pf_q8_split_kernel<<<g, 256, 0, s>>>((const uint8_t *)d->sh_down, nb, hi + 2 * nw, lo + 2 * nw);

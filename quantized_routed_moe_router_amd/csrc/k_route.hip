@@ -169,6 +169,10 @@ __global__ void __launch_bounds__(1024) bucket_small_kernel(const int32_t *__res
 // expert; pass 2 walks the segment 64 pairs at a time and ranks equal experts
 // inside the wave with ballots, so the result is a pure function of topk_idx.
 constexpr int kBucketWaves = 8;
+// Pairs whose experts the bucketing block keeps in LDS between its two passes
+// (prefill at 2048 rows and top-6 is 12,288): the scatter pass then reads
+// them back from LDS instead of one dependent global round trip per 64 pairs.
+constexpr int kBucketKeyCache = 16384;
 
 __global__ void __launch_bounds__(512) bucket_kernel(const int32_t *__restrict__ topk_idx, int P, int E,
                                                      int32_t *__restrict__ count, int32_t *__restrict__ offset,
@@ -177,12 +181,18 @@ __global__ void __launch_bounds__(512) bucket_kernel(const int32_t *__restrict__
     __shared__ int32_t wc[kBucketWaves][kMaxExperts];
     __shared__ int32_t tot[kMaxExperts];
     __shared__ int32_t scan_tmp[kMaxExperts];
+    __shared__ int32_t keys[kBucketKeyCache];  // the experts of the pairs, when P fits
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     for (int i = tid; i < kBucketWaves * kMaxExperts; i += blockDim.x) (&wc[0][0])[i] = 0;
     __syncthreads();
     const int seg = ((P + kBucketWaves - 1) / kBucketWaves + 63) / 64 * 64;
     const int s0 = w * seg, s1 = min(P, s0 + seg);
-    for (int p = s0 + lane; p < s1; p += 64) atomicAdd(&wc[w][topk_idx[p]], 1);
+    const bool cached = P <= kBucketKeyCache;
+    for (int p = s0 + lane; p < s1; p += 64) {
+        const int e = topk_idx[p];
+        if (cached) keys[p] = e;  // a wave later reads back only the pairs it wrote
+        atomicAdd(&wc[w][e], 1);
+    }
     __syncthreads();
     for (int e = tid; e < E; e += blockDim.x) {  // exclusive prefix over waves
         int run = 0;
@@ -217,7 +227,7 @@ __global__ void __launch_bounds__(512) bucket_kernel(const int32_t *__restrict__
     for (int base = s0; base < s1; base += 64) {  // stable scatter
         int p = base + lane;
         bool valid = p < s1;
-        int key = valid ? topk_idx[p] : 0;
+        int key = valid ? (cached ? keys[p] : topk_idx[p]) : 0;
         uint64_t same = __ballot(valid);
         for (int b = 0; b < nbits; ++b) {
             uint64_t bal = __ballot(valid && ((key >> b) & 1));

@@ -250,12 +250,30 @@ __global__ void __launch_bounds__(320) dec_k2_q8sg4096_kernel(FfnArgs a, int do_
     sg_wait<kSgXu + 16 * kSgRu>();
     group(3);
     for (int t = 0;;) {
+        // the next token's records (several tokens): issued here and held in
+        // registers while this token's sums are reduced, instead of loaded
+        // after the barriers; the compiler barrier keeps the loads in front,
+        // and the barriers of the loop wait for LDS only
+        // (the pad dword is not loaded: a register whose load is in flight and
+        // whose value is never used gets reused, and that reuse waits for the load)
+        XQ8 xn;
+        const bool more = t + 1 < a.T;
+        if (more) {
+            const uint32_t *rec = a.xq8 + ((int64_t)(t + 1) * 64 + 16 * wave + c) * kXQ8Dwords;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) ((u32x4 *)&xn)[i] = *(const u32x4 *)(rec + 4 * i);
+            const uint3 tail = *(const uint3 *)(rec + 64);
+            xn.sx[0] = __uint_as_float(tail.x);
+            xn.sx[1] = __uint_as_float(tail.y);
+            xn.inv = __uint_as_float(tail.z);
+            xn.pad = 0.f;
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const float sv = row16_sum(v[q]);
             if (c == 0) part[wave][4 * q + r] = sv;  // [group][gate 2q, 2q+1, up 2q, 2q+1]
         }
-        __syncthreads();
+        block_lds_sync();
         if (tid < 8) {
             const int q = tid >> 1, j = tid & 1;
             float gs = 0.f, us = 0.f;
@@ -266,9 +284,10 @@ __global__ void __launch_bounds__(320) dec_k2_q8sg4096_kernel(FfnArgs a, int do_
             }
             a.hs[(int64_t)t * a.Fs + row0 + tid] = swiglu_h(gs, us, a.x_bf16);
         }
-        if (++t >= a.T) break;
-        __syncthreads();  // part is rewritten
-        load_q8_prep(a.xq8 + ((int64_t)t * 64 + 16 * wave + c) * kXQ8Dwords, xr);
+        if (!more) break;
+        ++t;
+        block_lds_sync();  // part is rewritten
+        xr = xn;
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = q8_dot2(q8_load(ab + 16 * (kSgXu + kSgRu * (4 * q + r)), 64 * c), xr);
     }

@@ -79,17 +79,21 @@ def test_bf16_small(T):
     _check_layer(L, T, 71, bf16=True)
 
 
+@pytest.mark.parametrize("bf16", [True, False])
 @pytest.mark.parametrize("D,F,E,k,T,Fs", [
     (512, 512, 8, 2, 150, 256),   # 1- and 2-subtile tiles with ragged rows
     (256, 256, 4, 2, 300, 0),     # several tiles per expert; one super-block column
     (1024, 256, 16, 6, 57, 128),
 ])
-def test_bf16_many_rows_matrix_cores(D, F, E, k, T, Fs):
-    # bf16 batches beyond the decode schedule run as grouped GEMMs on the
-    # matrix cores; outputs within tolerance of the oracle's bf16 mode
+def test_many_rows_matrix_cores(D, F, E, k, T, Fs, bf16):
+    # batches beyond the decode schedule run as grouped GEMMs on the matrix
+    # cores, bf16 rows (h in bf16, atomic combine) and fp32 rows (h in fp32,
+    # per-pair rows gathered in slot order); outputs within tolerance of the
+    # oracle in the same mode
     L = synth.make_layer(74 + T, 0, D=D, E=E, k=k, F=F, Fs=Fs)
-    worst, _, _ = _check_layer(L, T, 75 + T, bf16=True)
-    print("bf16 D=%d F=%d E=%d k=%d T=%d: worst relative error %.3g" % (D, F, E, k, T, worst))
+    worst, _, _ = _check_layer(L, T, 75 + T, bf16=bf16)
+    print("%s D=%d F=%d E=%d k=%d T=%d: worst relative error %.3g" % ("bf16" if bf16 else "fp32", D, F, E, k, T,
+                                                                        worst))
 
 
 def test_bf16_many_rows_accumulate():

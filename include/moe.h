@@ -97,7 +97,8 @@ typedef struct {
     const void *gate, *up;    /* [E][F][D] in gate_type / up_type blocks */
     const void *down;         /* [E][D][F] in down_type blocks */
     const void *sh_gate, *sh_up, *sh_down; /* [Fs][D], [Fs][D], [D][Fs] or NULL */
-    const int8_t *codebook;   /* [256][8] int8 when any format is MOE_CB2, else NULL */
+    const int8_t *codebook;   /* [256][8] int8 when any format is MOE_CB2, else NULL; entries in
+                                 [-127, 127] (the decode kernels negate them bytewise) */
 } moe_layer_desc;
 
 /* Routing of T token rows: caller-owned device arrays. */

@@ -374,23 +374,31 @@ __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
     const uint32_t lds_st[2] = {(uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(&st0)),
                                 (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(&st1))};
     const uint8_t *wbm_u = (const uint8_t *)wave_uniform(wbm);
-    auto issue = [&](int st, int kb) {
+    // A tile of at most 32 pairs (one row subtile) copies only code rows
+    // 0-31 (copies 0-16: waves take copies w and w + 8, wave 0 also copy 16)
+    // and their group sums (the first half): the other rows are never read.
+    auto issue = [&](auto nsub_c, int st, int kb) {
+        constexpr int NS = decltype(nsub_c)::value;
+        constexpr int kA = NS == 2 ? kAI - 1 : 2, kS = NS == 2 ? kSI : kSI / 2;
+        constexpr int kLast = NS == 2 ? kACopies - 1 : (kACopies - 1) / 2;  // wave 0's extra copy
         const uint8_t *ab = a.aq + kb * 512, *sb = (const uint8_t *)a.as + kb * 64, *wbk = wbm_u + kb * kQ2KBytes;
         const uint32_t L = lds_st[st];
 #pragma unroll
-        for (int i = 0; i < kAI - 1; ++i)
+        for (int i = 0; i < kA; ++i)
             pf_dma16u(ab, aoff[i], L + (uint32_t)offsetof(PfStage, a) + (uint32_t)((i * kPfWaves + wv) * 64 * 16));
-        if (wv == 0) pf_dma16u(ab, aoff[kAI - 1], L + (uint32_t)offsetof(PfStage, a) + (uint32_t)((kACopies - 1) * 64 * 16));
+        if (wv == 0) pf_dma16u(ab, aoff[kLast / kPfWaves], L + (uint32_t)offsetof(PfStage, a) + (uint32_t)(kLast * 64 * 16));
 #pragma unroll
-        for (int i = 0; i < kSI; ++i)
+        for (int i = 0; i < kS; ++i)
             pf_dma4u(sb, soff[i], L + (uint32_t)offsetof(PfStage, s) + (uint32_t)((i * kPfThreads + 64 * wv) * 4));
 #pragma unroll
         for (int j = 0; j < 5; ++j)
             pf_dma16u(wbk, boff[j], L + (uint32_t)offsetof(PfStage, b) + (uint32_t)((wv * kPfWaveRows * 5 + j * 64) * 16));
         pf_dma4u(wbk, ddoff, L + (uint32_t)offsetof(PfStage, dd) + (uint32_t)(wv * kPfWaveRows * 4));
     };
-    constexpr int kIssued = (kAI - 1) + kSI + 5 + 1;  // wave 0: one more
-    auto wait_stage = [&]() {
+    static_assert(kACopies == 33 && kAI == 5 && kSI == 2, "copy counts of the one-subtile issue");
+    auto wait_stage = [&](auto nsub_c) {
+        constexpr int NS = decltype(nsub_c)::value;
+        constexpr int kIssued = (NS == 2 ? (kAI - 1) + kSI : 2 + kSI / 2) + 5 + 1;  // wave 0: one more
         if (wave == 0) vmem_wait_at_most<kIssued + 1>();
         else vmem_wait_at_most<kIssued>();
     };
@@ -482,11 +490,11 @@ __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
         }
     };
 
-    issue(0, 0);
+    issue(nsub_c, 0, 0);
     for (int kb = 0; kb < nkb; kb += 2) {
         if (kb + 1 < nkb) {
-            issue(1, kb + 1);
-            wait_stage();
+            issue(nsub_c, 1, kb + 1);
+            wait_stage(nsub_c);
         } else {
             vmem_wait_at_most<0>();
         }
@@ -495,8 +503,8 @@ __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
         stage_barrier();
         if (kb + 1 >= nkb) break;
         if (kb + 2 < nkb) {
-            issue(0, kb + 2);
-            wait_stage();
+            issue(nsub_c, 0, kb + 2);
+            wait_stage(nsub_c);
         } else {
             vmem_wait_at_most<0>();
         }

@@ -253,6 +253,30 @@ def test_stages_equal_layer_forward(T):
     assert torch.equal(y, y2) and torch.equal(r.perm, r2.perm)
 
 
+@pytest.mark.parametrize("T,bf16", [(3, False), (40, False), (40, True)])
+def test_stage5_repeats_the_routed_gate_up(T, bf16):
+    # stage 5 runs the routed gate/up kernel alone on what stage 3 left in the
+    # workspace (the grouped GEMM's activation codes and tiles; elsewhere it is
+    # stage 3): stages 1, 2, 3, 5, 4 give the same y as one forward call
+    import quantized_routed_moe_router_amd as moe
+    L = synth.make_layer(105, 0, D=512, E=32, k=4, F=256, Fs=128)
+    xv = synth.activations(106, T, 512)
+    x = gu.x_to_device(x_bf16=synth.to_bf16_bits(xv)) if bf16 else gu.x_to_device(x=xv)
+    W = gu.upload(L)
+    mode = moe.BF16 if bf16 else moe.F32
+    ws = moe.alloc_workspace(W, T, mode)
+    r = moe.Routing(T, 4, 32)
+    y = torch.zeros((T, 512), dtype=torch.float32, device="cuda")
+    for st in (1, 2, 3, 5, 4):
+        moe.layer_forward_stage(W, x, y, ws, st, routing=r)
+    y2, _ = gu.run_forward(W, x)
+    torch.cuda.synchronize()
+    if bf16:  # the routed down adds into y with atomics in a varying order
+        gu.assert_close(y.cpu().numpy(), y2.cpu().numpy(), tol=1e-5)
+    else:
+        assert torch.equal(y, y2)
+
+
 @pytest.mark.parametrize("D", [4096, 1000])
 def test_rmsnorm(D):
     # 4096: the vector kernel (16-byte loads held in registers); 1000: the

@@ -47,12 +47,18 @@ MOE_DEV int sum_swz(int r) { return ((r >> 1) + (r >> 3)) & 3; }
 // after d, dmin) at b[5R..5R+4], d and dmin at dd[R].  The pad and the
 // swizzle put the 16-byte reads of 16 consecutive rows on distinct banks
 // (and of any 8 consecutive rows).
-struct PfStage {
-    u32x4 a[kPfAUnits];
-    uint32_t s[kPfSDwords];
-    u32x4 b[kPfBRows * 5];
-    uint32_t dd[kPfBRows];
+// W = 8: tiles of up to 64 pairs, 512 weight rows per stage; W = 4 (the
+// small variant, when no tile can exceed 32 pairs): 32 pairs, 256 weight
+// rows, 40 KB per stage, so that two blocks fit a compute unit.
+constexpr int pf_m(int W) { return W == 8 ? 64 : 32; }
+template <int W>
+struct PfStageT {
+    u32x4 a[pf_m(W) * kPfARow];
+    uint32_t s[pf_m(W) * 16];
+    u32x4 b[kPfWaveRows * W * 5];
+    uint32_t dd[kPfWaveRows * W];
 };
+typedef PfStageT<8> PfStage;
 
 struct PfArgs {
     const uint8_t *w0, *w1;  // gate and up (mode 0) or down (mode 1), expert-major Q2K
@@ -312,12 +318,16 @@ MOE_DEV void xcd_tile_map(int L, int nb, int &tile, int &col) {
 // 64w..64w+63, wave w >= 4 the same rows of up; writes h = silu(g) * u in
 // bf16.  Mode 1: a column block is 512 D-columns, wave w owns columns
 // 64w..64w+63; adds w * y_pair into y.
-template <int MODE>
-__global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
-    __shared__ PfStage st0, st1;
-    __shared__ int32_t row_tok[kPfM];
-    __shared__ float row_f[kPfM];
-    constexpr int kColRows = MODE == 0 ? kPfBRows / 2 : kPfBRows;  // output columns per block
+// (two waves per SIMD: for W = 4 that is two blocks per compute unit, which
+// also needs the registers of W = 8)
+template <int MODE, int W>
+__global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) pf_gemm_kernel(PfArgs a) {
+    typedef PfStageT<W> Stage;
+    constexpr int PM = pf_m(W), NT = 64 * W, BR = kPfWaveRows * W, AU = PM * kPfARow, SD = PM * 16;
+    __shared__ Stage st0, st1;
+    __shared__ int32_t row_tok[PM];
+    __shared__ float row_f[PM];
+    constexpr int kColRows = MODE == 0 ? BR / 2 : BR;  // output columns per block
     const int nb = (MODE == 0 ? a.F : a.D) / kColRows;
     int tile, colblk;
     xcd_tile_map(blockIdx.x, nb, tile, colblk);
@@ -329,7 +339,7 @@ __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
     const int o0 = colblk * kColRows;
     const int64_t rowbytes = (int64_t)nkb * kQ2KBytes;
 
-    if (tid < kPfM) {
+    if (tid < PM) {
         const int pos = start + min(tid, cnt - 1);
         const int pair = a.perm[pos];
         row_tok[tid] = pair / a.k;
@@ -341,25 +351,26 @@ __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
     // Code rows: 33 wave copies of 64 units; wave w takes copies w, w+8,
     // w+16, w+24 and wave 0 also copy 32; a pad unit loads a copy of unit 31.
     auto arow = [&](int r) { return MODE == 0 ? row_tok[r] : start + min(r, cnt - 1); };
-    constexpr int kACopies = kPfAUnits / 64, kAI = kACopies / kPfWaves + 1, kSI = kPfSDwords / kPfThreads;
-    static_assert(kACopies == 4 * kPfWaves + 1, "A copies");
+    // (W = 4: 1056 units, 16.5 copies; the last one is issued by lanes 0-31)
+    constexpr int kACopies = (AU + 63) / 64, kAI = kACopies / W + 1, kSI = SD / NT;
+    static_assert(kACopies == 4 * W + 1, "A copies");
     uint32_t aoff[kAI], soff[kSI];
 #pragma unroll
     for (int i = 0; i < kAI; ++i) {
-        const int L = min((i * kPfWaves + wave) * 64 + lane, kPfAUnits - 1), r = L / kPfARow, u = min(L % kPfARow, 31);
+        const int L = min((i * W + wave) * 64 + lane, AU - 1), r = L / kPfARow, u = min(L % kPfARow, 31);
         aoff[i] = (uint32_t)(arow(r) * nkb * 512 + u * 16);
     }
 #pragma unroll
     for (int i = 0; i < kSI; ++i) {
-        const int q = i * kPfThreads + tid, r = q >> 4;
+        const int q = i * NT + tid, r = q >> 4;
         const int unit = ((q >> 2) & 3) ^ sum_swz(r);
         soff[i] = (uint32_t)(arow(r) * nkb * 64 + unit * 16 + (q & 3) * 4);
     }
     // Weight rows: wave w copies its own 64 rows (5 units each = 5 copies of
     // 64 units) and their d, dmin (one copy); mode 0 waves 0-3 from gate,
     // 4-7 from up.
-    const int wrow0 = MODE == 0 ? (wave & 3) * kPfWaveRows : wave * kPfWaveRows;  // first row in its matrix block
-    const uint8_t *wbm = (MODE == 0 && wave >= 4 ? a.w1 : a.w0) + (int64_t)e * a.expert_bytes;
+    const int wrow0 = MODE == 0 ? (wave % (W / 2)) * kPfWaveRows : wave * kPfWaveRows;  // first row in its matrix block
+    const uint8_t *wbm = (MODE == 0 && wave >= W / 2 ? a.w1 : a.w0) + (int64_t)e * a.expert_bytes;
     uint32_t boff[5];
 #pragma unroll
     for (int j = 0; j < 5; ++j) {
@@ -378,32 +389,35 @@ __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
     // 0-31 (copies 0-16: waves take copies w and w + 8, wave 0 also copy 16)
     // and their group sums (the first half): the other rows are never read.
     auto issue = [&](auto nsub_c, int st, int kb) {
-        constexpr int NS = decltype(nsub_c)::value;
-        constexpr int kA = NS == 2 ? kAI - 1 : 2, kS = NS == 2 ? kSI : kSI / 2;
-        constexpr int kLast = NS == 2 ? kACopies - 1 : (kACopies - 1) / 2;  // wave 0's extra copy
+        constexpr bool FULL = decltype(nsub_c)::value == 2 || W == 4;  // the small variant's tile is 32 rows
+        constexpr int kA = FULL ? kAI - 1 : 2, kS = FULL ? kSI : kSI / 2;
+        constexpr int kLast = FULL ? kACopies - 1 : (kACopies - 1) / 2;  // wave 0's extra copy
         const uint8_t *ab = a.aq + kb * 512, *sb = (const uint8_t *)a.as + kb * 64, *wbk = wbm_u + kb * kQ2KBytes;
         const uint32_t L = lds_st[st];
 #pragma unroll
         for (int i = 0; i < kA; ++i)
-            pf_dma16u(ab, aoff[i], L + (uint32_t)offsetof(PfStage, a) + (uint32_t)((i * kPfWaves + wv) * 64 * 16));
-        if (wv == 0) pf_dma16u(ab, aoff[kLast / kPfWaves], L + (uint32_t)offsetof(PfStage, a) + (uint32_t)(kLast * 64 * 16));
+            pf_dma16u(ab, aoff[i], L + (uint32_t)offsetof(Stage, a) + (uint32_t)((i * W + wv) * 64 * 16));
+        if (wv == 0) {
+            if (W == 8 || lane < AU - 64 * kLast)  // W = 4: the half copy stays inside the array
+                pf_dma16u(ab, aoff[kLast / W], L + (uint32_t)offsetof(Stage, a) + (uint32_t)(kLast * 64 * 16));
+        }
 #pragma unroll
         for (int i = 0; i < kS; ++i)
-            pf_dma4u(sb, soff[i], L + (uint32_t)offsetof(PfStage, s) + (uint32_t)((i * kPfThreads + 64 * wv) * 4));
+            pf_dma4u(sb, soff[i], L + (uint32_t)offsetof(Stage, s) + (uint32_t)((i * NT + 64 * wv) * 4));
 #pragma unroll
         for (int j = 0; j < 5; ++j)
-            pf_dma16u(wbk, boff[j], L + (uint32_t)offsetof(PfStage, b) + (uint32_t)((wv * kPfWaveRows * 5 + j * 64) * 16));
-        pf_dma4u(wbk, ddoff, L + (uint32_t)offsetof(PfStage, dd) + (uint32_t)(wv * kPfWaveRows * 4));
+            pf_dma16u(wbk, boff[j], L + (uint32_t)offsetof(Stage, b) + (uint32_t)((wv * kPfWaveRows * 5 + j * 64) * 16));
+        pf_dma4u(wbk, ddoff, L + (uint32_t)offsetof(Stage, dd) + (uint32_t)(wv * kPfWaveRows * 4));
     };
-    static_assert(kACopies == 33 && kAI == 5 && kSI == 2, "copy counts of the one-subtile issue");
+    static_assert(kAI == 5 && kSI == 2, "copy counts of the one-subtile issue");
     auto wait_stage = [&](auto nsub_c) {
-        constexpr int NS = decltype(nsub_c)::value;
-        constexpr int kIssued = (NS == 2 ? (kAI - 1) + kSI : 2 + kSI / 2) + 5 + 1;  // wave 0: one more
+        constexpr bool FULL = decltype(nsub_c)::value == 2 || W == 4;
+        constexpr int kIssued = (FULL ? (kAI - 1) + kSI : 2 + kSI / 2) + 5 + 1;  // wave 0: one more
         if (wave == 0) vmem_wait_at_most<kIssued + 1>();
         else vmem_wait_at_most<kIssued>();
     };
 
-    const int nsub = cnt > 32 ? 2 : 1;
+    const int nsub = W == 8 && cnt > 32 ? 2 : 1;
     v16f tot[2][2];  // [column subtile][row subtile]
 #pragma unroll
     for (int n = 0; n < 2; ++n)
@@ -414,7 +428,7 @@ __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
 
     auto run = [&](auto nsub_c) {
     constexpr int NSUB = decltype(nsub_c)::value;
-    auto compute = [&](PfStage &S) {
+    auto compute = [&](Stage &S) {
         // unit 16*pass + 2p + h of row q*32 + c: constant offsets from abase
         const u32x4 *abase = &S.a[c * kPfARow + h];
 #pragma unroll
@@ -513,14 +527,18 @@ __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
         stage_barrier();
     }
     };
-    if (nsub == 2) run(std::integral_constant<int, 2>{});
-    else run(std::integral_constant<int, 1>{});
+    if constexpr (W == 8) {
+        if (nsub == 2) run(std::integral_constant<int, 2>{});
+        else run(std::integral_constant<int, 1>{});
+    } else {
+        run(std::integral_constant<int, 1>{});  // the launch guarantees tiles of at most 32 pairs
+    }
 
     if constexpr (MODE == 0) {
         // up waves hand their values to the gate waves of the same rows
-        float *U = (float *)&st0;  // [64 rows][256 columns]
-        static_assert(sizeof(PfStage) >= kPfM * 256 * sizeof(float), "exchange area");
-        if (wave >= 4) {
+        float *U = (float *)&st0;  // [PM rows][kColRows columns]
+        static_assert(sizeof(Stage) >= PM * kColRows * sizeof(float), "exchange area");
+        if (wave >= W / 2) {
 #pragma unroll
             for (int n = 0; n < 2; ++n)
 #pragma unroll
@@ -528,11 +546,12 @@ __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
                     if (q == 1 && nsub < 2) continue;
 #pragma unroll
                     for (int v = 0; v < 16; ++v)
-                        U[(q * 32 + 8 * (v >> 2) + 4 * h + (v & 3)) * 256 + (wave & 3) * 64 + 32 * n + c] = tot[n][q][v];
+                        U[(q * 32 + 8 * (v >> 2) + 4 * h + (v & 3)) * kColRows + (wave % (W / 2)) * 64 + 32 * n + c] =
+                            tot[n][q][v];
                 }
         }
         block_lds_sync();
-        if (wave < 4) {
+        if (wave < W / 2) {
 #pragma unroll
             for (int n = 0; n < 2; ++n)
 #pragma unroll
@@ -544,7 +563,7 @@ __global__ void __launch_bounds__(kPfThreads) pf_gemm_kernel(PfArgs a) {
                         if (r >= cnt) continue;
                         const float f = row_f[r];
                         const int col = wave * 64 + 32 * n + c;
-                        const float hv = silu(tot[n][q][v] * f) * (U[r * 256 + col] * f);
+                        const float hv = silu(tot[n][q][v] * f) * (U[r * kColRows + col] * f);
                         if (a.hf) a.hf[(int64_t)(start + r) * a.F + o0 + col] = hv;
                         else a.hb[(int64_t)(start + r) * a.F + o0 + col] = bf16_rne(hv);
                     }
@@ -770,6 +789,9 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int
     const int D = d->n_embd, F = d->n_ff_exp, k = d->n_expert_used, E = d->n_expert, Fs = d->n_ff_shared;
     const int ntmax = pf_max_tiles(T, k, E);
     static_assert(kPfM == kPfTileRows, "tile rows");
+    // no expert takes more pairs than there are rows, so with T <= 32 every
+    // tile fits the small variant's 32 rows
+    const bool small = T <= 32;
     const int64_t P = (int64_t)T * k;
     PfArgs a{};
     a.tiles = (const int4 *)ws.pf_tiles;
@@ -821,7 +843,8 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int
         g.aq = ws.pf_xq;
         g.as = ws.pf_xs;
         g.ainv = ws.pf_xinv;
-        pf_gemm_kernel<0><<<(unsigned)(((ntmax + 7) / 8) * 8 * (F / 256)), kPfThreads, 0, s>>>(g);
+        if (small) pf_gemm_kernel<0, 4><<<(unsigned)(((ntmax + 7) / 8) * 8 * (F / 128)), 256, 0, s>>>(g);
+        else pf_gemm_kernel<0, 8><<<(unsigned)(((ntmax + 7) / 8) * 8 * (F / 256)), 512, 0, s>>>(g);
     }
     if (stage == 0 || stage == 4) {
         if (f32) {
@@ -836,7 +859,8 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int
             dn.aq = ws.pf_hq;
             dn.as = ws.pf_hs;
             dn.ainv = ws.pf_hinv;
-            pf_gemm_kernel<1><<<(unsigned)(((ntmax + 7) / 8) * 8 * (D / 512)), kPfThreads, 0, s>>>(dn);
+            if (small) pf_gemm_kernel<1, 4><<<(unsigned)(((ntmax + 7) / 8) * 8 * (D / 256)), 256, 0, s>>>(dn);
+            else pf_gemm_kernel<1, 8><<<(unsigned)(((ntmax + 7) / 8) * 8 * (D / 512)), 512, 0, s>>>(dn);
             return launch_combine(d, x, T, x_type, r, y, flags, ws, s);
         }
         pf_prep_rows_kernel<MOE_BF16><<<(unsigned)P, 256, 0, s>>>(ws.pf_hb, F, ws.pf_hq, ws.pf_hs, ws.pf_hinv);
@@ -863,7 +887,8 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int
         dn.aq = ws.pf_hq;
         dn.as = ws.pf_hs;
         dn.ainv = ws.pf_hinv;
-        pf_gemm_kernel<1><<<(unsigned)(((ntmax + 7) / 8) * 8 * (D / 512)), kPfThreads, 0, s>>>(dn);
+        if (small) pf_gemm_kernel<1, 4><<<(unsigned)(((ntmax + 7) / 8) * 8 * (D / 256)), 256, 0, s>>>(dn);
+        else pf_gemm_kernel<1, 8><<<(unsigned)(((ntmax + 7) / 8) * 8 * (D / 512)), 512, 0, s>>>(dn);
     }
     return hipGetLastError();
 }

@@ -84,6 +84,8 @@ def test_bf16_small(T):
     (512, 512, 8, 2, 150, 256),   # 1- and 2-subtile tiles with ragged rows
     (256, 256, 4, 2, 300, 0),     # several tiles per expert; one super-block column
     (1024, 256, 16, 6, 57, 128),
+    (512, 256, 32, 4, 24, 128),   # at most 32 rows: the 4-wave variant, two blocks per compute unit
+    (512, 512, 4, 2, 32, 0),      # a bucket of all 32 rows
 ])
 def test_many_rows_matrix_cores(D, F, E, k, T, Fs, bf16):
     # batches beyond the decode schedule run as grouped GEMMs on the matrix

@@ -487,23 +487,6 @@ MOE_DEV void load_q2k_prep(const uint32_t *rec4, XQ2K &p) {
     for (int i = 0; i < 4 * kRec16Dwords / 4; ++i) dst[i] = *(const u32x4 *)(rec4 + 4 * i);
 }
 
-// the fields of a lane's records that the integer dot reads (a, b, inv), one
-// load per field: sx is left out (a register whose load is in flight and
-// whose value is never used gets reused, and the reuse waits for the load),
-// and no load straddles two records (such loads keep the records out of
-// registers)
-typedef uint32_t u32x4_a8 __attribute__((ext_vector_type(4), aligned(8)));
-MOE_DEV void load_q2k_prep_int(const uint32_t *rec4, XQ2K &p) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const uint32_t *r = rec4 + kRec16Dwords * g;
-        *(u32x4 *)p.g[g].a = *(const u32x4_a8 *)r;
-        *(u32x4 *)p.g[g].b = *(const u32x4_a8 *)(r + 4);
-        p.g[g].inv = __uint_as_float(r[9]);
-        p.g[g].sx = 0.f;
-    }
-}
-
 MOE_DEV int sdot4(uint32_t a, uint32_t b, int c) { return __builtin_amdgcn_sdot4((int)a, (int)b, c, false); }
 
 // sum_g inv_g * (d*sc_g*sum_i q_i c_i) - dmin * sum_g m_g * sx_g, the integer
@@ -579,35 +562,6 @@ MOE_DEV float cb2_dot_int(const CB2Chunk &c, const XQ2K &p, const u32x4 *tab) {
     group(std::integral_constant<int, 2>());
     group(std::integral_constant<int, 3>());
     return c.d * acc;
-}
-
-// Q8_0 chunk (two 34-byte blocks) against natural-order int16 activation
-// records: per group of 16 values the int8 codes (natural byte order) dotted
-// with the hi and lo code halves, 256 A + B exact in int32, scaled by the
-// group's 1/S, then each block's sum by its d.
-MOE_DEV float q8_dot_int(const Q8Chunk &c, const XQ2K &p) {
-    const float d0 = half_bits_to_float(c.w[0] & 0xFFFFu), d1 = half_bits_to_float(c.w[8] >> 16);
-    float s0 = 0.f, s1 = 0.f;
-    auto group = [&](auto G) {
-        constexpr int g = decltype(G)::value;
-        uint32_t q[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j)  // block 0's codes start at byte 2, block 1's at byte 36
-            q[j] = g < 2 ? __builtin_amdgcn_alignbyte(c.w[4 * g + j + 1], c.w[4 * g + j], 2) : c.w[9 + 4 * (g - 2) + j];
-        int A = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) A = sdot4(q[j], p.g[g].a[j], A);
-        int S = A << 8;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) S = sdot4(q[j], p.g[g].b[j], S);
-        if (g < 2) s0 = __builtin_fmaf((float)S, p.g[g].inv, s0);
-        else s1 = __builtin_fmaf((float)S, p.g[g].inv, s1);
-    };
-    group(std::integral_constant<int, 0>());
-    group(std::integral_constant<int, 1>());
-    group(std::integral_constant<int, 2>());
-    group(std::integral_constant<int, 3>());
-    return d0 * s0 + d1 * s1;
 }
 
 // scale S and 2^24/S for a set whose largest magnitude is m
@@ -773,6 +727,10 @@ struct Workspace {
     uint8_t *pf_hq;
     uint32_t *pf_hs;
     float *pf_hinv;       // [T*k]
+    // shared expert of many fp32 rows on the matrix cores: int16 codes of x
+    // (gate/up) or hs (down), [T][n/64][32 dwords], and each row's 1/S
+    uint32_t *sg_aq;
+    float *sg_ainv;       // [T]
     size_t bytes;
 };
 
@@ -825,6 +783,8 @@ __host__ inline Workspace workspace_layout(const moe_layer_desc *d, int32_t T, v
     w.pf_hq = (uint8_t *)take((size_t)P * (size_t)F * 2);
     w.pf_hs = (uint32_t *)take((size_t)P * (size_t)(F / 256 + 1) * 64);
     w.pf_hinv = (float *)take(sizeof(float) * (size_t)P);
+    w.sg_aq = (uint32_t *)take((size_t)T * (size_t)(D > Fs ? D : Fs) * 2);
+    w.sg_ainv = (float *)take(sizeof(float) * (size_t)T);
     w.bytes = off;
     return w;
 }
@@ -848,12 +808,11 @@ bool small_path_ok(const moe_layer_desc *d, int32_t T);
 bool small_route_ok(const moe_layer_desc *d, int32_t T);
 hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
                         float *y, uint32_t flags, const Workspace &ws, hipStream_t s, int stage, bool route);
-// the shared expert's gate/up for any number of rows on the staged decode
-// kernel (Q8_0 shared expert at n_embd 4096): writes hs
-bool shared_gateup_staged_ok(const moe_layer_desc *d);
-hipError_t launch_shared_gateup_staged(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type,
-                                       const RoutingPtrs &r, float *y, uint32_t flags, const Workspace &ws,
-                                       hipStream_t s);
+// the shared expert (Q8_0) of any number of fp32 rows as two int8 matrix-core
+// GEMMs: stage 3 writes hs, stage 4 ys
+bool shared_q8_mfma_ok(const moe_layer_desc *d);
+hipError_t launch_shared_q8_mfma(const moe_layer_desc *d, const float *x, int32_t T, const Workspace &ws,
+                                 hipStream_t s, int stage);
 // any number of rows: stage 3 = gate/up, 4 = down + combine, 0 = both
 hipError_t launch_ffn_large(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
                             float *y, uint32_t flags, const Workspace &ws, hipStream_t s, int stage);

@@ -176,10 +176,10 @@ constexpr int kSgRu = 1024 / 32 * kQ8Bytes / 16;  // 68 units: a row quarter
 constexpr int kSgCopies = 22;                 // 272 + 16 x 68 = 1360 units -> 22 copies of 64
 static_assert(kSgXu + 16 * kSgRu <= 64 * kSgCopies, "area");
 
-template <int END, int NC = kSgCopies>
+template <int END>
 MOE_DEV void sg_wait() {
     __builtin_amdgcn_sched_barrier(0);
-    vmem_wait_le<NC - (END + 63) / 64>();
+    vmem_wait_le<kSgCopies - (END + 63) / 64>();
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -187,11 +187,6 @@ MOE_DEV void sg_wait() {
 // token): a fifth wave of block 0 does, so that the grid is one block per
 // 8 shared rows and every block gets a compute unit of its own (the LDS
 // areas allow one block per unit).
-// INT (several token rows, no routing): the activations come as int16
-// records in natural byte order (a.xp16, 40 dwords per 64 values: 160 units
-// for a wave's quarter) and the dots are int8 codes against them
-// (q8_dot_int): two v_dot4 per 4 weights instead of four packed fp16 products.
-template <bool INT = false>
 __global__ void __launch_bounds__(320) dec_k2_q8sg4096_kernel(FfnArgs a, int do_route) {
     __shared__ __align__(16) u32x4 area[4][64 * kSgCopies];
     __shared__ float part[4][16];
@@ -219,23 +214,18 @@ __global__ void __launch_bounds__(320) dec_k2_q8sg4096_kernel(FfnArgs a, int do_
     }
     const int row0 = 8 * b;  // rows row0 .. row0 + 7 of gate and of up
     constexpr int RB = 4096 / 32 * kQ8Bytes;  // bytes of a row: 4352
-    constexpr int XU = INT ? 16 * 4 * kRec16Dwords / 4 : kSgXu;  // units of the first token's records
-    constexpr int NC = INT ? (XU + 16 * kSgRu + 63) / 64 : kSgCopies;
-    static_assert(NC <= kSgCopies, "area");
-    typedef typename std::conditional<INT, XQ2K, XQ8>::type Rec;
     {
-        const uint8_t *xs = INT ? (const uint8_t *)(a.xp16 + (int64_t)(16 * wave) * 4 * kRec16Dwords)
-                                : (const uint8_t *)(a.xq8 + (int64_t)(16 * wave) * kXQ8Dwords);  // token 0, quarter w
+        const uint8_t *xs = (const uint8_t *)(a.xq8 + (int64_t)(16 * wave) * kXQ8Dwords);  // token 0, quarter w
         const uint8_t *gm = a.sh_gate + (int64_t)row0 * RB + 1088 * wave, *um = a.sh_up + (int64_t)row0 * RB + 1088 * wave;
         const uint32_t lb = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(area[wave]));
 #pragma unroll
-        for (int i = 0; i < NC; ++i) {
+        for (int i = 0; i < kSgCopies; ++i) {
             const int u = 64 * i + lane;
             const uint8_t *src;
-            if (u < XU) {
+            if (u < kSgXu) {
                 src = xs + 16 * u;
             } else {
-                const int v = min(u - XU, 16 * kSgRu - 1), rw = v / kSgRu, o = v - rw * kSgRu;
+                const int v = min(u - kSgXu, 16 * kSgRu - 1), rw = v / kSgRu, o = v - rw * kSgRu;
                 const int q = rw >> 2, j = rw & 3;  // group q: gate 2q, 2q+1, up 2q, 2q+1
                 src = ((j & 2) ? um : gm) + (int64_t)(2 * q + (j & 1)) * RB + 16 * o;
             }
@@ -244,42 +234,31 @@ __global__ void __launch_bounds__(320) dec_k2_q8sg4096_kernel(FfnArgs a, int do_
     }
     const int r = lane >> 4, c = lane & 15;
     const uint8_t *ab = (const uint8_t *)area[wave];
-    Rec xr;
+    XQ8 xr;
     float v[4];
-    auto dot = [&](const Q8Chunk &ch, const Rec &x) {
-        if constexpr (INT) return q8_dot_int(ch, x);
-        else return q8_dot2(ch, x);
-    };
     auto group = [&](int q) {
-        if (q == 0) {
-            if constexpr (INT) load_q2k_prep_int((const uint32_t *)(ab + 160 * c), xr);
-            else load_q8_prep((const uint32_t *)(ab + 272 * c), xr);
-        }
-        v[q] = dot(q8_load(ab + 16 * (XU + kSgRu * (4 * q + r)), 64 * c), xr);
+        if (q == 0) load_q8_prep((const uint32_t *)(ab + 272 * c), xr);
+        v[q] = q8_dot2(q8_load(ab + 16 * (kSgXu + kSgRu * (4 * q + r)), 64 * c), xr);
         pin_value(v[q]);
     };
-    sg_wait<XU + 4 * kSgRu, NC>();
+    sg_wait<kSgXu + 4 * kSgRu>();
     group(0);
-    sg_wait<XU + 8 * kSgRu, NC>();
+    sg_wait<kSgXu + 8 * kSgRu>();
     group(1);
-    sg_wait<XU + 12 * kSgRu, NC>();
+    sg_wait<kSgXu + 12 * kSgRu>();
     group(2);
-    sg_wait<XU + 16 * kSgRu, NC>();
+    sg_wait<kSgXu + 16 * kSgRu>();
     group(3);
     for (int t = 0;;) {
         // the next token's records (several tokens): issued here and held in
         // registers while this token's sums are reduced, instead of loaded
-        // after the barriers, which wait for LDS only (the pad dword of a Q8
-        // record is not loaded: a register whose load is in flight and whose
-        // value is never used gets reused, and that reuse waits for the load)
-        Rec xn;
+        // after the barriers; the compiler barrier keeps the loads in front,
+        // and the barriers of the loop wait for LDS only
+        // (the pad dword is not loaded: a register whose load is in flight and
+        // whose value is never used gets reused, and that reuse waits for the load)
+        XQ8 xn;
         const bool more = t + 1 < a.T;
-        if constexpr (INT) {
-            // unconditional (the last token reads its own records again): a
-            // conditional load's registers are copied at the join, which waits
-            const int tn = more ? t + 1 : t;
-            load_q2k_prep_int(a.xp16 + ((int64_t)tn * 256 + 4 * (16 * wave + c)) * kRec16Dwords, xn);
-        } else if (more) {
+        if (more) {
             const uint32_t *rec = a.xq8 + ((int64_t)(t + 1) * 64 + 16 * wave + c) * kXQ8Dwords;
 #pragma unroll
             for (int i = 0; i < 16; ++i) ((u32x4 *)&xn)[i] = *(const u32x4 *)(rec + 4 * i);
@@ -310,7 +289,7 @@ __global__ void __launch_bounds__(320) dec_k2_q8sg4096_kernel(FfnArgs a, int do_
         block_lds_sync();  // part is rewritten
         xr = xn;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = dot(q8_load(ab + 16 * (XU + kSgRu * (4 * q + r)), 64 * c), xr);
+        for (int q = 0; q < 4; ++q) v[q] = q8_dot2(q8_load(ab + 16 * (kSgXu + kSgRu * (4 * q + r)), 64 * c), xr);
     }
 }
 
@@ -894,30 +873,6 @@ FfnArgs make_ffn_args(const moe_layer_desc *d, const void *x, int32_t T, int32_t
     a.logits = ws.logits;
     a.xp16 = a.xq8 = a.hp16 = nullptr;
     return a;
-}
-
-// The shared expert's gate/up for any number of fp32 or bf16 rows on the
-// staged K2 kernel (Q8_0 at n_embd 4096): the rows' int16 records in natural
-// byte order from K1's preparing blocks, then one block per 8 shared rows,
-// every token against the staged rows with integer dots.  Writes hs.
-bool shared_gateup_staged_ok(const moe_layer_desc *d) {
-    return d->n_ff_shared > 0 && d->shared_type == MOE_Q8_0 && d->n_embd == 4096 && d->n_ff_shared % 8 == 0;
-}
-
-hipError_t launch_shared_gateup_staged(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type,
-                                       const RoutingPtrs &r, float *y, uint32_t flags, const Workspace &ws,
-                                       hipStream_t s) {
-    FfnArgs a = make_ffn_args(d, x, T, x_type, r, y, flags, ws);
-    a.shared_fmt = MOE_Q8_0;
-    a.xp16 = ws.xp16;  // int16 records in natural byte order for the integer dots
-    a.xp16_nat = 1;
-    a.n_router_blocks = 0;
-    a.build_slots = 0;
-    a.n_prep_blocks = (T * (a.D / 64) + 3) / 4;
-    if (x_type == MOE_BF16) dec_k1_kernel<MOE_BF16><<<a.n_prep_blocks, 256, 0, s>>>(a);
-    else dec_k1_kernel<MOE_F32><<<a.n_prep_blocks, 256, 0, s>>>(a);
-    dec_k2_q8sg4096_kernel<true><<<a.Fs / 8, 320, 0, s>>>(a, 0);
-    return hipGetLastError();
 }
 
 bool small_path_ok(const moe_layer_desc *d, int32_t T) {

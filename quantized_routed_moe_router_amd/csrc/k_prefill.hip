@@ -811,9 +811,8 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int
         else pf_prep_rows_kernel<MOE_BF16><<<T, 256, 0, s>>>(x, D, ws.pf_xq, ws.pf_xs, ws.pf_xinv);
         pf_tiles_kernel<<<1, 64, 0, s>>>(r.active, r.n_active, r.count, r.offset, ws.pf_tiles, ws.pf_ntiles);
         if (Fs > 0 && f32) {
-            const hipError_t e = shared_gateup_staged_ok(d)
-                                     ? launch_shared_gateup_staged(d, x, T, x_type, r, y, flags, ws, s)
-                                     : launch_ffn_large_shared(d, x, T, x_type, r, y, flags, ws, s, 3);
+            const hipError_t e = shared_q8_mfma_ok(d) ? launch_shared_q8_mfma(d, (const float *)x, T, ws, s, 3)
+                                                      : launch_ffn_large_shared(d, x, T, x_type, r, y, flags, ws, s, 3);
             if (e != hipSuccess) return e;
         } else if (Fs > 0) {
             // shared weights split into bf16 halves, then the shared gate/up GEMM
@@ -850,7 +849,8 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int
         if (f32) {
             pf_prep_rows_kernel<MOE_F32><<<(unsigned)P, 256, 0, s>>>(ws.h, F, ws.pf_hq, ws.pf_hs, ws.pf_hinv);
             if (Fs > 0) {
-                const hipError_t e = launch_ffn_large_shared(d, x, T, x_type, r, y, flags, ws, s, 4);
+                const hipError_t e = shared_q8_mfma_ok(d) ? launch_shared_q8_mfma(d, nullptr, T, ws, s, 4)
+                                                          : launch_ffn_large_shared(d, x, T, x_type, r, y, flags, ws, s, 4);
                 if (e != hipSuccess) return e;
             }
             PfArgs dn = a;

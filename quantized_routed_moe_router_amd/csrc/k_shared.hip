@@ -1,0 +1,257 @@
+// k_shared.hip - the shared expert of a batch of fp32 token rows as two dense
+// Q8_0 GEMMs on the matrix cores ("Understanding Dwarf Star", 5.3.7 step 1:
+// the shared expert's SwiGLU FFN for every token; 2.8.2 the block-quantized
+// dot; the Q8_0 subsection: 32 int8 codes and one fp16 scale d per block).
+//
+// Per 32-weight block of a weight row and a token row:
+//   sum_k w_k x_k = d * sum_k q_k x_k ~= d * (sum_k q_k c_k) / S
+// with the token row's int16 codes c = rint(x*S), S = 32512 / max|row|, split
+// as c = 256*hi + lo.  The integer sum runs on v_mfma_i32_16x16x32_i8 (one
+// instruction per block and plane: K = 32 is exactly one Q8_0 block), exact in
+// int32; each lane owns one weight row (the output column) and so applies its
+// row's d to every product it holds, in fp32, once per block.
+//
+// Byte order: a pair of blocks (68 bytes, dword aligned in the row) holds the
+// codes of the even block at bytes 2..33 and of the odd block at bytes 36..67.
+// The odd block's 8 dwords are used as they are; the even block's are taken as
+// dwords 1..7 (codes 2..29) and one dword made of bytes 2, 3 and 32, 33 (codes
+// 0, 1, 30, 31).  The activation codes are written in that same order, so the
+// weights reach the matrix cores without any byte shuffling.
+#include "ffn_dev.h"
+
+namespace moe {
+
+typedef int sgq_v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kSgqWaves = 8;       // waves of a block: they split the reduction
+constexpr int kSgqRows = 16;       // weight rows of a block (the MFMA's columns)
+constexpr int kSgqTileTok = 16;    // token rows of an MFMA tile
+constexpr int kSgqTiles = 2;       // token tiles per pass
+constexpr int kSgqGroup = 4;       // block pairs a wave loads before it multiplies
+constexpr int kSgqPairDw = 32;     // dwords of a token row's codes for 64 values: hi 16, lo 16
+constexpr float kSgqCodeMax = 32512.f;
+
+// value index (0..63 within a block pair) of byte n of code dword m of the
+// pair in the order above: dwords 0-7 the even block, 8-15 the odd block
+__host__ __device__ inline int sgq_value_index(int m, int n) {
+    if (m < 7) return 4 * m + 2 + n;
+    if (m == 7) return n < 2 ? n : 28 + n;
+    return 32 + 4 * (m - 8) + n;
+}
+
+// The record of a token row for pair p: for each lane group g (0..3) four
+// dwords {even 2g, even 2g+1, odd 2g, odd 2g+1} of the hi plane, then the
+// same for the lo plane.  Position of code dword m in a plane:
+__host__ __device__ inline int sgq_plane_dword(int m) {
+    const int odd = m >= 8, mm = m & 7;
+    return 4 * (mm >> 1) + 2 * odd + (mm & 1);
+}
+
+// One block per token row: S from the row's largest magnitude, then a thread
+// per code dword pair (m, plane position) of every block pair.
+__global__ void __launch_bounds__(256) sgq_prep_kernel(const float *__restrict__ x, int n,
+                                                       uint32_t *__restrict__ rec, float *__restrict__ inv) {
+    __shared__ float wmax[4];
+    const int t = blockIdx.x;
+    const float *row = x + (int64_t)t * n;
+    float mt = 0.f;
+    for (int i = threadIdx.x; i < n; i += 256) mt = fmaxf(mt, fabsf(row[i]));
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) mt = fmaxf(mt, __shfl_xor(mt, o, kWave));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mt;
+    __syncthreads();
+    const float m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float S = m > 0.f ? kSgqCodeMax / m : 0.f;
+    if (threadIdx.x == 0) inv[t] = m / kSgqCodeMax;
+    const int np = n / 64;
+    uint32_t *out = rec + (int64_t)t * np * kSgqPairDw;
+    for (int i = threadIdx.x; i < np * 16; i += 256) {
+        const int p = i >> 4, md = i & 15;
+        uint32_t H = 0, L = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int c = (int)__builtin_rintf(row[64 * p + sgq_value_index(md, b)] * S);
+            const int hv = (c + 128) >> 8;
+            H |= (uint32_t)(hv & 0xFF) << (8 * b);
+            L |= (uint32_t)((c - 256 * hv) & 0xFF) << (8 * b);
+        }
+        out[p * kSgqPairDw + sgq_plane_dword(md)] = H;
+        out[p * kSgqPairDw + 16 + sgq_plane_dword(md)] = L;
+    }
+}
+
+struct SgqArgs {
+    const uint8_t *w0, *w1;  // MODE 0: gate and up rows [Fs][K]; MODE 1: down rows [D][K]
+    const uint32_t *aq;      // token records [T][K/64][32 dwords]
+    const float *ainv;       // 1/S of each token row
+    int T, K;
+    float *out;              // MODE 0: hs [T][Fs]; MODE 1: ys [T][D]
+    int ld;                  // row length of out
+};
+
+MOE_DEV uint2 sgq_load2(const uint8_t *p) {
+    uint2 v;
+    __builtin_memcpy(&v, __builtin_assume_aligned(p, 4), 8);
+    return v;
+}
+
+// MODE 0: block b owns gate rows 8b..8b+7 (columns 0-7) and the same up rows
+// (columns 8-15) and writes hs = silu(g) * u; MODE 1: down rows 16b..16b+15,
+// written to ys.  Wave w takes the block pairs w, w + 8, ...; the partial
+// sums meet in LDS and are added in wave order.
+template <int MODE>
+__global__ void __launch_bounds__(64 * kSgqWaves) sgq_gemm_kernel(SgqArgs a) {
+    __shared__ float red[kSgqWaves][kSgqTiles][4][64];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int j = lane & 15, g = lane >> 4;  // the lane's weight row (column) and k group
+    const int64_t rowbytes = (int64_t)(a.K / 32) * kQ8Bytes;
+    const uint8_t *wrow;
+    if (MODE == 0) wrow = (j < 8 ? a.w0 : a.w1) + (int64_t)(8 * blockIdx.x + (j & 7)) * rowbytes;
+    else wrow = a.w0 + (int64_t)(kSgqRows * blockIdx.x + j) * rowbytes;
+    const int np = a.K / 64;
+    for (int t0 = 0; t0 < a.T; t0 += kSgqTiles * kSgqTileTok) {
+        float tot[kSgqTiles][4];
+#pragma unroll
+        for (int i = 0; i < kSgqTiles; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) tot[i][r] = 0.f;
+        // the token rows this lane feeds to the A operand (row j of each tile)
+        const uint32_t *arow[kSgqTiles];
+        bool aok[kSgqTiles];
+#pragma unroll
+        for (int i = 0; i < kSgqTiles; ++i) {
+            const int t = t0 + kSgqTileTok * i + j;
+            aok[i] = t < a.T;
+            arow[i] = a.aq + (int64_t)(aok[i] ? t : 0) * np * kSgqPairDw + 4 * g;
+        }
+        // groups of kSgqGroup pairs: every load of a group is issued before
+        // its products, so that a wave has that many pairs in flight
+        for (int p0 = wave; p0 < np; p0 += kSgqGroup * kSgqWaves) {
+            uint2 e[kSgqGroup], o[kSgqGroup];
+            uint32_t w0[kSgqGroup], w8[kSgqGroup];
+            u32x4 hv[kSgqGroup][kSgqTiles], lv[kSgqGroup][kSgqTiles];
+#pragma unroll
+            for (int u = 0; u < kSgqGroup; ++u) {
+                const int p = p0 + u * kSgqWaves;
+                const bool pok = p < np;
+                const uint8_t *wp = wrow + (int64_t)(pok ? p : 0) * 2 * kQ8Bytes;
+                e[u] = sgq_load2(wp + 4 + 8 * g);
+                o[u] = sgq_load2(wp + 36 + 8 * g);
+                w0[u] = load_u32(wp);
+                w8[u] = load_u32(wp + 32);
+#pragma unroll
+                for (int i = 0; i < kSgqTiles; ++i) {
+                    hv[u][i] = lv[u][i] = u32x4{0u, 0u, 0u, 0u};
+                    if (aok[i] && pok) {
+                        hv[u][i] = *(const u32x4 *)(arow[i] + p * kSgqPairDw);
+                        lv[u][i] = *(const u32x4 *)(arow[i] + p * kSgqPairDw + 16);
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kSgqGroup; ++u) {
+                if (p0 + u * kSgqWaves >= np) break;  // uniform over the wave
+                uint2 ev = e[u];
+                if (g == 3) ev.y = __builtin_amdgcn_alignbyte(w8[u], w0[u], 2);  // codes 0, 1, 30, 31
+                const float d0 = half_bits_to_float(w0[u] & 0xFFFFu), d1 = half_bits_to_float(w8[u] >> 16);
+                long be, bo;
+                __builtin_memcpy(&be, &ev, 8);
+                __builtin_memcpy(&bo, &o[u], 8);
+#pragma unroll
+                for (int i = 0; i < kSgqTiles; ++i) {
+                    long he, ho, le, lo;
+                    const uint2 hve = {hv[u][i][0], hv[u][i][1]}, hvo = {hv[u][i][2], hv[u][i][3]};
+                    const uint2 lve = {lv[u][i][0], lv[u][i][1]}, lvo = {lv[u][i][2], lv[u][i][3]};
+                    __builtin_memcpy(&he, &hve, 8);
+                    __builtin_memcpy(&ho, &hvo, 8);
+                    __builtin_memcpy(&le, &lve, 8);
+                    __builtin_memcpy(&lo, &lvo, 8);
+                    const sgq_v4i z = {0, 0, 0, 0};
+                    sgq_v4i ce = __builtin_amdgcn_mfma_i32_16x16x32_i8(he, be, z, 0, 0, 0);
+                    sgq_v4i co = __builtin_amdgcn_mfma_i32_16x16x32_i8(ho, bo, z, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        ce[r] <<= 8;
+                        co[r] <<= 8;
+                    }
+                    ce = __builtin_amdgcn_mfma_i32_16x16x32_i8(le, be, ce, 0, 0, 0);
+                    co = __builtin_amdgcn_mfma_i32_16x16x32_i8(lo, bo, co, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        tot[i][r] = __builtin_fmaf(d0, (float)ce[r], tot[i][r]);
+                        tot[i][r] = __builtin_fmaf(d1, (float)co[r], tot[i][r]);
+                    }
+                }
+            }
+        }
+        // output element of register r: token 4g + r of the tile, column j
+#pragma unroll
+        for (int i = 0; i < kSgqTiles; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave][i][r][lane] = tot[i][r];
+        __syncthreads();
+        if (MODE == 0) {
+            // one output per thread: tile i, register r, k group g2, gate column c
+            const int tid = threadIdx.x;
+            if (tid < kSgqTiles * 4 * 4 * 8) {
+                const int i = tid >> 7, r = (tid >> 5) & 3, g2 = (tid >> 3) & 3, c = tid & 7;
+                const int t = t0 + kSgqTileTok * i + 4 * g2 + r;
+                float gs = 0.f, us = 0.f;
+#pragma unroll
+                for (int w = 0; w < kSgqWaves; ++w) {
+                    gs += red[w][i][r][16 * g2 + c];
+                    us += red[w][i][r][16 * g2 + 8 + c];
+                }
+                if (t < a.T) {
+                    const float s = a.ainv[t];
+                    a.out[(int64_t)t * a.ld + 8 * blockIdx.x + c] = swiglu_h(gs * s, us * s, 0);
+                }
+            }
+        } else {
+            for (int o = threadIdx.x; o < kSgqTiles * 4 * 64; o += 64 * kSgqWaves) {
+                const int i = o >> 8, r = (o >> 6) & 3, l = o & 63;
+                const int t = t0 + kSgqTileTok * i + 4 * (l >> 4) + r;
+                float s = 0.f;
+#pragma unroll
+                for (int w = 0; w < kSgqWaves; ++w) s += red[w][i][r][l];
+                if (t < a.T) a.out[(int64_t)t * a.ld + kSgqRows * blockIdx.x + (l & 15)] = s * a.ainv[t];
+            }
+        }
+        __syncthreads();  // red is rewritten by the next pass
+    }
+}
+
+bool shared_q8_mfma_ok(const moe_layer_desc *d) {
+    return d->n_ff_shared > 0 && d->shared_type == MOE_Q8_0 && d->n_embd % 64 == 0 && d->n_ff_shared % 64 == 0;
+}
+
+// stage 3: x codes, then the gate/up GEMM into hs; stage 4: hs codes, then
+// the down GEMM into ys.  The codes and scales sit in the workspace's sg_aq
+// and sg_ainv, rewritten by each stage.
+hipError_t launch_shared_q8_mfma(const moe_layer_desc *d, const float *x, int32_t T, const Workspace &ws,
+                                 hipStream_t s, int stage) {
+    const int D = d->n_embd, Fs = d->n_ff_shared;
+    SgqArgs a{};
+    a.T = T;
+    a.aq = ws.sg_aq;
+    a.ainv = ws.sg_ainv;
+    if (stage == 3) {
+        sgq_prep_kernel<<<T, 256, 0, s>>>(x, D, ws.sg_aq, ws.sg_ainv);
+        a.w0 = (const uint8_t *)d->sh_gate;
+        a.w1 = (const uint8_t *)d->sh_up;
+        a.K = D;
+        a.out = ws.hs;
+        a.ld = Fs;
+        sgq_gemm_kernel<0><<<Fs / 8, 64 * kSgqWaves, 0, s>>>(a);
+    } else {
+        sgq_prep_kernel<<<T, 256, 0, s>>>(ws.hs, Fs, ws.sg_aq, ws.sg_ainv);
+        a.w0 = a.w1 = (const uint8_t *)d->sh_down;
+        a.K = Fs;
+        a.out = ws.ys;
+        a.ld = D;
+        sgq_gemm_kernel<1><<<D / kSgqRows, 64 * kSgqWaves, 0, s>>>(a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

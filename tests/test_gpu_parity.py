@@ -98,6 +98,22 @@ def test_many_rows_matrix_cores(D, F, E, k, T, Fs, bf16):
                                                                         worst))
 
 
+def test_shared_expert_matrix_cores_full_width():
+    # the shared expert of fp32 rows as int8 matrix-core GEMMs at its full
+    # width (n_embd 4096, n_ff_shared 2048): a ragged second 16-row tile, a
+    # second pass over the rows, and an all-zero row (its scale is 0)
+    L = synth.make_layer(120, 0, D=4096, E=8, k=2, F=256, Fs=2048)
+    T = 35
+    x = synth.activations(121, T, 4096)
+    x[7] = 0.0
+    y_ref, idx_ref, w_ref = oracle.moe_forward(L, x=x)
+    W = gu.upload(L)
+    y, r = gu.run_forward(W, gu.x_to_device(x=x))
+    gu.check_routing(r, idx_ref, w_ref, L.n_expert)
+    worst = gu.assert_close(y.cpu().numpy(), y_ref)
+    print("fp32 shared expert at full width, T=%d: worst relative error %.3g" % (T, worst))
+
+
 def test_bf16_many_rows_accumulate():
     L = synth.make_layer(76, 0, D=512, E=8, k=2, F=512, Fs=256)
     x = synth.activations(77, 40, 512)

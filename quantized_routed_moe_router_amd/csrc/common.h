@@ -728,7 +728,8 @@ struct Workspace {
     uint32_t *pf_hs;
     float *pf_hinv;       // [T*k]
     // shared expert of many fp32 rows on the matrix cores: int16 codes of x
-    // (gate/up) or hs (down), [T][n/64][32 dwords], and each row's 1/S
+    // (gate/up; their 1/S is pf_xinv) or hs (down), [T][n/64][32 dwords],
+    // and hs rows' 1/S
     uint32_t *sg_aq;
     float *sg_ainv;       // [T]
     size_t bytes;
@@ -811,7 +812,7 @@ hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32
 // the shared expert (Q8_0) of any number of fp32 rows as two int8 matrix-core
 // GEMMs: stage 3 writes hs, stage 4 ys
 bool shared_q8_mfma_ok(const moe_layer_desc *d);
-hipError_t launch_shared_q8_mfma(const moe_layer_desc *d, const float *x, int32_t T, const Workspace &ws,
+hipError_t launch_shared_q8_mfma(const moe_layer_desc *d, int32_t T, const Workspace &ws, const float *ainv,
                                  hipStream_t s, int stage);
 // any number of rows: stage 3 = gate/up, 4 = down + combine, 0 = both
 hipError_t launch_ffn_large(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,

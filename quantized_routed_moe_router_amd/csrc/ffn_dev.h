@@ -508,6 +508,64 @@ inline void with_fmt(int f, Fn &&fn) {
     else fn(std::integral_constant<int, MOE_CB2>{});
 }
 
+// ---- int16 row codes for the shared expert's int8 matrix-core GEMMs ---------
+// A token row is coded as c = rint(v*S), S = 32512 / max|row|, c = 256*hi + lo,
+// per 64 values (a pair of Q8_0 blocks) as 32 dwords: for each lane group g
+// (0..3) four dwords {even 2g, even 2g+1, odd 2g, odd 2g+1} of the hi plane,
+// then the same for the lo plane.  Code dword m (0-7 the even block, 8-15 the
+// odd block) follows the byte order of the Q8_0 codes in the 68-byte pair:
+// the odd block's 8 aligned dwords, the even block's dwords 1..7 and one
+// dword of bytes 2, 3, 32, 33 (codes 0, 1, 30, 31).
+constexpr int kSgqPairDw = 32;
+constexpr float kSgqCodeMax = 32512.f;
+
+// value index (0..63 within the pair) of byte n of code dword m
+__host__ __device__ inline int sgq_value_index(int m, int n) {
+    if (m < 7) return 4 * m + 2 + n;
+    if (m == 7) return n < 2 ? n : 28 + n;
+    return 32 + 4 * (m - 8) + n;
+}
+
+// position of code dword m within a plane of the pair's record
+__host__ __device__ inline int sgq_plane_dword(int m) {
+    const int odd = m >= 8, mm = m & 7;
+    return 4 * (mm >> 1) + 2 * odd + (mm & 1);
+}
+
+// the records of one row of n fp32 values at scale S, a thread per code
+// dword of every pair (the whole block takes part)
+MOE_DEV void sgq_code_row(const float *row, int n, float S, uint32_t *out) {
+    const int np = n / 64;
+    for (int i = threadIdx.x; i < np * 16; i += blockDim.x) {
+        const int p = i >> 4, md = i & 15;
+        uint32_t H = 0, L = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int c = (int)__builtin_rintf(row[64 * p + sgq_value_index(md, b)] * S);
+            const int hv = (c + 128) >> 8;
+            H |= (uint32_t)(hv & 0xFF) << (8 * b);
+            L |= (uint32_t)((c - 256 * hv) & 0xFF) << (8 * b);
+        }
+        out[p * kSgqPairDw + sgq_plane_dword(md)] = H;
+        out[p * kSgqPairDw + 16 + sgq_plane_dword(md)] = L;
+    }
+}
+
+// S from the row's largest magnitude (a block of 256 threads), then its
+// records; inv = 1/S
+MOE_DEV void sgq_prep_row(const float *row, int n, uint32_t *rec, float *inv, float *wmax) {
+    float mt = 0.f;
+    for (int i = threadIdx.x; i < n; i += 256) mt = fmaxf(mt, fabsf(row[i]));
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) mt = fmaxf(mt, __shfl_xor(mt, o, kWave));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mt;
+    __syncthreads();
+    const float m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    const float S = m > 0.f ? kSgqCodeMax / m : 0.f;
+    if (threadIdx.x == 0) *inv = m / kSgqCodeMax;
+    sgq_code_row(row, n, S, rec);
+}
+
 FfnArgs make_ffn_args(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
                       float *y, uint32_t flags, const Workspace &ws);
 

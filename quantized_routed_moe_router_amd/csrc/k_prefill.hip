@@ -200,10 +200,28 @@ MOE_DEV void pf_load16(const void *x, int64_t i0, float *v) {
     }
 }
 
+// fp32 rows also feed the shared expert's int8 GEMMs (ffn_dev.h): sg_rec,
+// when set, takes each row's records at the same scale; blocks from nrows on
+// code the rows of rows2 (n2 values each, hs) for those GEMMs alone.
+struct PfPrepShared {
+    uint32_t *sg_rec;     // records of x's rows, or null
+    int nrows;            // blocks that code x (the rest code rows2)
+    const float *rows2;
+    int n2;
+    uint32_t *rec2;
+    float *inv2;
+};
+
 template <int XT>
 __global__ void __launch_bounds__(256) pf_prep_rows_kernel(const void *x, int n, uint8_t *xq, uint32_t *xs,
-                                                           float *xinv) {
+                                                           float *xinv, PfPrepShared extra) {
     __shared__ float wmax[4];
+    if ((int)blockIdx.x >= extra.nrows) {  // uniform over the block
+        const int r = (int)blockIdx.x - extra.nrows;
+        sgq_prep_row(extra.rows2 + (int64_t)r * extra.n2, extra.n2,
+                     extra.rec2 + (int64_t)r * (extra.n2 / 64) * kSgqPairDw, extra.inv2 + r, wmax);
+        return;
+    }
     const int t = blockIdx.x, ng = n >> 4;
     float mt = 0.f;
     for (int g = threadIdx.x; g < ng; g += 256) {
@@ -240,6 +258,9 @@ __global__ void __launch_bounds__(256) pf_prep_rows_kernel(const void *x, int n,
         sb[gi] = sh;
         sb[16 + gi] = sl;
     }
+    if constexpr (XT == MOE_F32)
+        if (extra.sg_rec)
+            sgq_code_row((const float *)x + (int64_t)t * n, n, S, extra.sg_rec + (int64_t)t * (n / 64) * kSgqPairDw);
 }
 
 // Tiles of at most 64 pairs over the active experts, ascending expert id:
@@ -793,6 +814,8 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int
     // tile fits the small variant's 32 rows
     const bool small = T <= 32;
     const int64_t P = (int64_t)T * k;
+    // fp32 rows with a Q8_0 shared expert: its two int8 matrix-core GEMMs
+    const bool sgq = f32 && Fs > 0 && shared_q8_mfma_ok(d);
     PfArgs a{};
     a.tiles = (const int4 *)ws.pf_tiles;
     a.n_tiles = ws.pf_ntiles;
@@ -807,12 +830,14 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int
     a.ypart = f32 ? ws.ypart : nullptr;
     a.expert_bytes = fmt_bytes(MOE_Q2K, (int64_t)F * D);
     if (stage == 0 || stage == 3) {
-        if (f32) pf_prep_rows_kernel<MOE_F32><<<T, 256, 0, s>>>(x, D, ws.pf_xq, ws.pf_xs, ws.pf_xinv);
-        else pf_prep_rows_kernel<MOE_BF16><<<T, 256, 0, s>>>(x, D, ws.pf_xq, ws.pf_xs, ws.pf_xinv);
+        // fp32 rows: the same launch codes x for the shared expert's int8 GEMMs
+        const PfPrepShared ex{sgq ? ws.sg_aq : nullptr, T, nullptr, 0, nullptr, nullptr};
+        if (f32) pf_prep_rows_kernel<MOE_F32><<<T, 256, 0, s>>>(x, D, ws.pf_xq, ws.pf_xs, ws.pf_xinv, ex);
+        else pf_prep_rows_kernel<MOE_BF16><<<T, 256, 0, s>>>(x, D, ws.pf_xq, ws.pf_xs, ws.pf_xinv, ex);
         pf_tiles_kernel<<<1, 64, 0, s>>>(r.active, r.n_active, r.count, r.offset, ws.pf_tiles, ws.pf_ntiles);
         if (Fs > 0 && f32) {
-            const hipError_t e = shared_q8_mfma_ok(d) ? launch_shared_q8_mfma(d, (const float *)x, T, ws, s, 3)
-                                                      : launch_ffn_large_shared(d, x, T, x_type, r, y, flags, ws, s, 3);
+            const hipError_t e = sgq ? launch_shared_q8_mfma(d, T, ws, ws.pf_xinv, s, 3)
+                                     : launch_ffn_large_shared(d, x, T, x_type, r, y, flags, ws, s, 3);
             if (e != hipSuccess) return e;
         } else if (Fs > 0) {
             // shared weights split into bf16 halves, then the shared gate/up GEMM
@@ -847,10 +872,13 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int
     }
     if (stage == 0 || stage == 4) {
         if (f32) {
-            pf_prep_rows_kernel<MOE_F32><<<(unsigned)P, 256, 0, s>>>(ws.h, F, ws.pf_hq, ws.pf_hs, ws.pf_hinv);
+            // blocks P.. of the same launch code hs for the shared expert's down
+            const PfPrepShared ex{nullptr, (int)P, ws.hs, Fs, ws.sg_aq, ws.sg_ainv};
+            pf_prep_rows_kernel<MOE_F32><<<(unsigned)(P + (sgq ? T : 0)), 256, 0, s>>>(ws.h, F, ws.pf_hq, ws.pf_hs,
+                                                                                       ws.pf_hinv, ex);
             if (Fs > 0) {
-                const hipError_t e = shared_q8_mfma_ok(d) ? launch_shared_q8_mfma(d, nullptr, T, ws, s, 4)
-                                                          : launch_ffn_large_shared(d, x, T, x_type, r, y, flags, ws, s, 4);
+                const hipError_t e = sgq ? launch_shared_q8_mfma(d, T, ws, ws.sg_ainv, s, 4)
+                                         : launch_ffn_large_shared(d, x, T, x_type, r, y, flags, ws, s, 4);
                 if (e != hipSuccess) return e;
             }
             PfArgs dn = a;
@@ -863,7 +891,8 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int
             else pf_gemm_kernel<1, 8><<<(unsigned)(((ntmax + 7) / 8) * 8 * (D / 512)), 512, 0, s>>>(dn);
             return launch_combine(d, x, T, x_type, r, y, flags, ws, s);
         }
-        pf_prep_rows_kernel<MOE_BF16><<<(unsigned)P, 256, 0, s>>>(ws.pf_hb, F, ws.pf_hq, ws.pf_hs, ws.pf_hinv);
+        pf_prep_rows_kernel<MOE_BF16><<<(unsigned)P, 256, 0, s>>>(ws.pf_hb, F, ws.pf_hq, ws.pf_hs, ws.pf_hinv,
+                                                                  PfPrepShared{nullptr, (int)P, nullptr, 0, nullptr, nullptr});
         if (Fs > 0) {
             const int64_t nw = (int64_t)Fs * D;
             SgArgs sg{};

@@ -15,8 +15,9 @@
 // codes of the even block at bytes 2..33 and of the odd block at bytes 36..67.
 // The odd block's 8 dwords are used as they are; the even block's are taken as
 // dwords 1..7 (codes 2..29) and one dword made of bytes 2, 3 and 32, 33 (codes
-// 0, 1, 30, 31).  The activation codes are written in that same order, so the
-// weights reach the matrix cores without any byte shuffling.
+// 0, 1, 30, 31).  The activation codes are written in that same order (the
+// record layout and writer are in ffn_dev.h; the many-row preparing kernel
+// fills them), so the weights reach the matrix cores without any shuffling.
 #include "ffn_dev.h"
 
 namespace moe {
@@ -28,58 +29,6 @@ constexpr int kSgqRows = 16;       // weight rows of a block (the MFMA's columns
 constexpr int kSgqTileTok = 16;    // token rows of an MFMA tile
 constexpr int kSgqTiles = 2;       // token tiles per pass
 constexpr int kSgqGroup = 4;       // block pairs a wave loads before it multiplies
-constexpr int kSgqPairDw = 32;     // dwords of a token row's codes for 64 values: hi 16, lo 16
-constexpr float kSgqCodeMax = 32512.f;
-
-// value index (0..63 within a block pair) of byte n of code dword m of the
-// pair in the order above: dwords 0-7 the even block, 8-15 the odd block
-__host__ __device__ inline int sgq_value_index(int m, int n) {
-    if (m < 7) return 4 * m + 2 + n;
-    if (m == 7) return n < 2 ? n : 28 + n;
-    return 32 + 4 * (m - 8) + n;
-}
-
-// The record of a token row for pair p: for each lane group g (0..3) four
-// dwords {even 2g, even 2g+1, odd 2g, odd 2g+1} of the hi plane, then the
-// same for the lo plane.  Position of code dword m in a plane:
-__host__ __device__ inline int sgq_plane_dword(int m) {
-    const int odd = m >= 8, mm = m & 7;
-    return 4 * (mm >> 1) + 2 * odd + (mm & 1);
-}
-
-// One block per token row: S from the row's largest magnitude, then a thread
-// per code dword pair (m, plane position) of every block pair.
-__global__ void __launch_bounds__(256) sgq_prep_kernel(const float *__restrict__ x, int n,
-                                                       uint32_t *__restrict__ rec, float *__restrict__ inv) {
-    __shared__ float wmax[4];
-    const int t = blockIdx.x;
-    const float *row = x + (int64_t)t * n;
-    float mt = 0.f;
-    for (int i = threadIdx.x; i < n; i += 256) mt = fmaxf(mt, fabsf(row[i]));
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) mt = fmaxf(mt, __shfl_xor(mt, o, kWave));
-    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mt;
-    __syncthreads();
-    const float m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
-    const float S = m > 0.f ? kSgqCodeMax / m : 0.f;
-    if (threadIdx.x == 0) inv[t] = m / kSgqCodeMax;
-    const int np = n / 64;
-    uint32_t *out = rec + (int64_t)t * np * kSgqPairDw;
-    for (int i = threadIdx.x; i < np * 16; i += 256) {
-        const int p = i >> 4, md = i & 15;
-        uint32_t H = 0, L = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int c = (int)__builtin_rintf(row[64 * p + sgq_value_index(md, b)] * S);
-            const int hv = (c + 128) >> 8;
-            H |= (uint32_t)(hv & 0xFF) << (8 * b);
-            L |= (uint32_t)((c - 256 * hv) & 0xFF) << (8 * b);
-        }
-        out[p * kSgqPairDw + sgq_plane_dword(md)] = H;
-        out[p * kSgqPairDw + 16 + sgq_plane_dword(md)] = L;
-    }
-}
-
 struct SgqArgs {
     const uint8_t *w0, *w1;  // MODE 0: gate and up rows [Fs][K]; MODE 1: down rows [D][K]
     const uint32_t *aq;      // token records [T][K/64][32 dwords]
@@ -225,18 +174,18 @@ bool shared_q8_mfma_ok(const moe_layer_desc *d) {
     return d->n_ff_shared > 0 && d->shared_type == MOE_Q8_0 && d->n_embd % 64 == 0 && d->n_ff_shared % 64 == 0;
 }
 
-// stage 3: x codes, then the gate/up GEMM into hs; stage 4: hs codes, then
-// the down GEMM into ys.  The codes and scales sit in the workspace's sg_aq
-// and sg_ainv, rewritten by each stage.
-hipError_t launch_shared_q8_mfma(const moe_layer_desc *d, const float *x, int32_t T, const Workspace &ws,
+// stage 3: the gate/up GEMM into hs, on x's records; stage 4: the down GEMM
+// into ys, on hs's records.  The records (sg_aq) and the rows' 1/S come from
+// the many-row preparing kernel (pf_prep_rows_kernel), which codes x for the
+// routed GEMMs at the same scale and hs in blocks of its own.
+hipError_t launch_shared_q8_mfma(const moe_layer_desc *d, int32_t T, const Workspace &ws, const float *ainv,
                                  hipStream_t s, int stage) {
     const int D = d->n_embd, Fs = d->n_ff_shared;
     SgqArgs a{};
     a.T = T;
     a.aq = ws.sg_aq;
-    a.ainv = ws.sg_ainv;
+    a.ainv = ainv;
     if (stage == 3) {
-        sgq_prep_kernel<<<T, 256, 0, s>>>(x, D, ws.sg_aq, ws.sg_ainv);
         a.w0 = (const uint8_t *)d->sh_gate;
         a.w1 = (const uint8_t *)d->sh_up;
         a.K = D;
@@ -244,7 +193,6 @@ hipError_t launch_shared_q8_mfma(const moe_layer_desc *d, const float *x, int32_
         a.ld = Fs;
         sgq_gemm_kernel<0><<<Fs / 8, 64 * kSgqWaves, 0, s>>>(a);
     } else {
-        sgq_prep_kernel<<<T, 256, 0, s>>>(ws.hs, Fs, ws.sg_aq, ws.sg_ainv);
         a.w0 = a.w1 = (const uint8_t *)d->sh_down;
         a.K = Fs;
         a.out = ws.ys;

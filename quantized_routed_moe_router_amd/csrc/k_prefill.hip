@@ -200,9 +200,34 @@ MOE_DEV void pf_load16(const void *x, int64_t i0, float *v) {
     }
 }
 
+// Tiles of at most 64 pairs over the active experts, ascending expert id:
+// one wave, 64 experts at a time, tile offsets by a prefix sum over lanes.
+MOE_DEV void pf_tiles_wave(const int32_t *active, const int32_t *n_active, const int32_t *count,
+                           const int32_t *offset, int4 *tiles, int32_t *n_tiles) {
+    const int lane = threadIdx.x & 63, n = n_active[0];
+    int base = 0;
+    for (int i0 = 0; i0 < n; i0 += 64) {
+        const int i = i0 + lane;
+        const int e = i < n ? active[i] : 0, c = i < n ? count[e] : 0, o = i < n ? offset[e] : 0;
+        const int nt = (c + kPfM - 1) / kPfM;
+        int incl = nt;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int v = __shfl_up(incl, d, kWave);
+            if (lane >= d) incl += v;
+        }
+        const int first = base + incl - nt;
+        for (int t = 0; t < nt; ++t) tiles[first + t] = make_int4(e, o + t * kPfM, min(kPfM, c - t * kPfM), 0);
+        base += __shfl(incl, 63, kWave);
+    }
+    if (lane == 0) n_tiles[0] = base;
+}
+
 // fp32 rows also feed the shared expert's int8 GEMMs (ffn_dev.h): sg_rec,
 // when set, takes each row's records at the same scale; blocks from nrows on
-// code the rows of rows2 (n2 values each, hs) for those GEMMs alone.
+// code the rows of rows2 (n2 values each, hs) for those GEMMs alone.  Block
+// tiles_block (when >= 0, after all of those) lays out the GEMM tiles
+// instead, with its first wave.
 struct PfPrepShared {
     uint32_t *sg_rec;     // records of x's rows, or null
     int nrows;            // blocks that code x (the rest code rows2)
@@ -210,12 +235,21 @@ struct PfPrepShared {
     int n2;
     uint32_t *rec2;
     float *inv2;
+    int tiles_block;
+    const int32_t *active, *n_active, *count, *offset;
+    int4 *tiles;
+    int32_t *n_tiles;
 };
 
 template <int XT>
 __global__ void __launch_bounds__(256) pf_prep_rows_kernel(const void *x, int n, uint8_t *xq, uint32_t *xs,
                                                            float *xinv, PfPrepShared extra) {
     __shared__ float wmax[4];
+    if ((int)blockIdx.x == extra.tiles_block) {
+        if (threadIdx.x < 64)
+            pf_tiles_wave(extra.active, extra.n_active, extra.count, extra.offset, extra.tiles, extra.n_tiles);
+        return;
+    }
     if ((int)blockIdx.x >= extra.nrows) {  // uniform over the block
         const int r = (int)blockIdx.x - extra.nrows;
         sgq_prep_row(extra.rows2 + (int64_t)r * extra.n2, extra.n2,
@@ -261,30 +295,6 @@ __global__ void __launch_bounds__(256) pf_prep_rows_kernel(const void *x, int n,
     if constexpr (XT == MOE_F32)
         if (extra.sg_rec)
             sgq_code_row((const float *)x + (int64_t)t * n, n, S, extra.sg_rec + (int64_t)t * (n / 64) * kSgqPairDw);
-}
-
-// Tiles of at most 64 pairs over the active experts, ascending expert id:
-// one wave, 64 experts at a time, tile offsets by a prefix sum over lanes.
-__global__ void __launch_bounds__(64) pf_tiles_kernel(const int32_t *active, const int32_t *n_active,
-                                                      const int32_t *count, const int32_t *offset, int4 *tiles,
-                                                      int32_t *n_tiles) {
-    const int lane = threadIdx.x, n = n_active[0];
-    int base = 0;
-    for (int i0 = 0; i0 < n; i0 += 64) {
-        const int i = i0 + lane;
-        const int e = i < n ? active[i] : 0, c = i < n ? count[e] : 0, o = i < n ? offset[e] : 0;
-        const int nt = (c + kPfM - 1) / kPfM;
-        int incl = nt;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            const int v = __shfl_up(incl, d, kWave);
-            if (lane >= d) incl += v;
-        }
-        const int first = base + incl - nt;
-        for (int t = 0; t < nt; ++t) tiles[first + t] = make_int4(e, o + t * kPfM, min(kPfM, c - t * kPfM), 0);
-        base += __shfl(incl, 63, kWave);
-    }
-    if (lane == 0) n_tiles[0] = base;
 }
 
 // y = ys (+ y when accumulating), or 0 / y without a shared expert: the
@@ -831,10 +841,11 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int
     a.expert_bytes = fmt_bytes(MOE_Q2K, (int64_t)F * D);
     if (stage == 0 || stage == 3) {
         // fp32 rows: the same launch codes x for the shared expert's int8 GEMMs
-        const PfPrepShared ex{sgq ? ws.sg_aq : nullptr, T, nullptr, 0, nullptr, nullptr};
-        if (f32) pf_prep_rows_kernel<MOE_F32><<<T, 256, 0, s>>>(x, D, ws.pf_xq, ws.pf_xs, ws.pf_xinv, ex);
-        else pf_prep_rows_kernel<MOE_BF16><<<T, 256, 0, s>>>(x, D, ws.pf_xq, ws.pf_xs, ws.pf_xinv, ex);
-        pf_tiles_kernel<<<1, 64, 0, s>>>(r.active, r.n_active, r.count, r.offset, ws.pf_tiles, ws.pf_ntiles);
+        // and one more block lays out the GEMM tiles from the routing
+        const PfPrepShared ex{sgq ? ws.sg_aq : nullptr, T, nullptr, 0, nullptr, nullptr, T,
+                              r.active, r.n_active, r.count, r.offset, (int4 *)ws.pf_tiles, ws.pf_ntiles};
+        if (f32) pf_prep_rows_kernel<MOE_F32><<<T + 1, 256, 0, s>>>(x, D, ws.pf_xq, ws.pf_xs, ws.pf_xinv, ex);
+        else pf_prep_rows_kernel<MOE_BF16><<<T + 1, 256, 0, s>>>(x, D, ws.pf_xq, ws.pf_xs, ws.pf_xinv, ex);
         if (Fs > 0 && f32) {
             const hipError_t e = sgq ? launch_shared_q8_mfma(d, T, ws, ws.pf_xinv, s, 3)
                                      : launch_ffn_large_shared(d, x, T, x_type, r, y, flags, ws, s, 3);
@@ -873,7 +884,8 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int
     if (stage == 0 || stage == 4) {
         if (f32) {
             // blocks P.. of the same launch code hs for the shared expert's down
-            const PfPrepShared ex{nullptr, (int)P, ws.hs, Fs, ws.sg_aq, ws.sg_ainv};
+            const PfPrepShared ex{nullptr, (int)P, ws.hs, Fs, ws.sg_aq, ws.sg_ainv, -1,
+                                  nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
             pf_prep_rows_kernel<MOE_F32><<<(unsigned)(P + (sgq ? T : 0)), 256, 0, s>>>(ws.h, F, ws.pf_hq, ws.pf_hs,
                                                                                        ws.pf_hinv, ex);
             if (Fs > 0) {
@@ -892,7 +904,9 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int
             return launch_combine(d, x, T, x_type, r, y, flags, ws, s);
         }
         pf_prep_rows_kernel<MOE_BF16><<<(unsigned)P, 256, 0, s>>>(ws.pf_hb, F, ws.pf_hq, ws.pf_hs, ws.pf_hinv,
-                                                                  PfPrepShared{nullptr, (int)P, nullptr, 0, nullptr, nullptr});
+                                                                  PfPrepShared{nullptr, (int)P, nullptr, 0, nullptr, nullptr, -1,
+                                                                               nullptr, nullptr, nullptr, nullptr, nullptr,
+                                                                               nullptr});
         if (Fs > 0) {
             const int64_t nw = (int64_t)Fs * D;
             SgArgs sg{};

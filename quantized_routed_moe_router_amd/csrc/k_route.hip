@@ -64,10 +64,13 @@ __global__ void __launch_bounds__(256) router_mfma_kernel(const float *__restric
     __shared__ double red[KS == 4 ? 3 : 1][64][4];
     const int L = blockIdx.x, xcd = L & 7, j = L >> 3;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // expert tiles per wave: with KS = 1 a wave takes two side by side, which
+    // share its activation loads and give two independent product chains
+    constexpr int NE = KS == 1 ? 2 : 1;
     int tt, e0, kbeg, kend;
     if constexpr (KS == 1) {
         tt = xcd * n_ttx + j / n_eq;
-        e0 = ((j % n_eq) * 4 + wave) * 16;
+        e0 = ((j % n_eq) * 4 + wave) * 16 * NE;
         kbeg = 0;
         kend = D;
     } else {
@@ -79,30 +82,38 @@ __global__ void __launch_bounds__(256) router_mfma_kernel(const float *__restric
     const int t0 = tt * 16;
     if (t0 >= T || e0 >= E) return;  // uniform over the block when KS = 4
     const int row = lane & 15, kq = 4 * (lane >> 4);
-    const int t = min(t0 + row, T - 1), e = min(e0 + row, E - 1);
+    const int t = min(t0 + row, T - 1);
     const void *xrow = XT == MOE_BF16 ? (const void *)((const uint16_t *)xin + (int64_t)t * D + kq)
                                       : (const void *)((const float *)xin + (int64_t)t * D + kq);
-    const float *wrow = W + (int64_t)e * D + kq;
-    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+    const float *wrow[NE];
+#pragma unroll
+    for (int n = 0; n < NE; ++n) wrow[n] = W + (int64_t)min(e0 + 16 * n + row, E - 1) * D + kq;
+    f64x4 acc[NE];
+#pragma unroll
+    for (int n = 0; n < NE; ++n) acc[n] = f64x4{0.0, 0.0, 0.0, 0.0};
     // 64 k per half step from two register sets: the loads of one set are in
     // flight while the other's products run (D is a multiple of 128 here)
     RouterX<XT> xa[4], xb[4];
-    f32x4 wa[4], wb[4];
-    auto load = [&](RouterX<XT> (&xv)[4], f32x4 (&wv)[4], int k) {
+    f32x4 wa[NE][4], wb[NE][4];
+    auto load = [&](RouterX<XT> (&xv)[4], f32x4 (&wv)[NE][4], int k) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             xv[c] = *(const RouterX<XT> *)((const char *)xrow + (int64_t)(k + 16 * c) * (XT == MOE_BF16 ? 2 : 4));
-            wv[c] = *(const f32x4 *)(wrow + k + 16 * c);
+#pragma unroll
+            for (int n = 0; n < NE; ++n) wv[n][c] = *(const f32x4 *)(wrow[n] + k + 16 * c);
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the products
     };
-    auto mma = [&](const RouterX<XT> (&xv)[4], const f32x4 (&wv)[4]) {
+    auto mma = [&](const RouterX<XT> (&xv)[4], const f32x4 (&wv)[NE][4]) {
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)router_x<XT>(xv[c], q), (double)wv[c][q], acc, 0,
-                                                           0, 0);
+            for (int q = 0; q < 4; ++q) {
+                const double xd = (double)router_x<XT>(xv[c], q);
+#pragma unroll
+                for (int n = 0; n < NE; ++n)
+                    acc[n] = __builtin_amdgcn_mfma_f64_16x16x4f64(xd, (double)wv[n][c][q], acc[n], 0, 0, 0);
+            }
     };
     load(xa, wa, kbeg);
     for (int k0 = kbeg; k0 < kend; k0 += 128) {
@@ -114,19 +125,23 @@ __global__ void __launch_bounds__(256) router_mfma_kernel(const float *__restric
     if constexpr (KS == 4) {
         if (wave > 0)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) red[wave - 1][lane][r] = acc[r];
+            for (int r = 0; r < 4; ++r) red[wave - 1][lane][r] = acc[0][r];
         __syncthreads();
         if (wave > 0) return;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = ((acc[r] + red[0][lane][r]) + red[1][lane][r]) + red[2][lane][r];
+        for (int r = 0; r < 4; ++r)
+            acc[0][r] = ((acc[0][r] + red[0][lane][r]) + red[1][lane][r]) + red[2][lane][r];
     }
-    const int ex = e0 + (lane & 15);
-    if (ex >= E) return;
-    const double b = bias ? (double)bias[ex] : 0.0;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int tok = t0 + (lane >> 4) + 4 * r;
-        if (tok < T) logits[(int64_t)tok * E + ex] = acc[r] + b;
+    for (int n = 0; n < NE; ++n) {
+        const int ex = e0 + 16 * n + (lane & 15);
+        if (ex >= E) continue;
+        const double b = bias ? (double)bias[ex] : 0.0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int tok = t0 + (lane >> 4) + 4 * r;
+            if (tok < T) logits[(int64_t)tok * E + ex] = acc[n][r] + b;
+        }
     }
 }
 
@@ -280,7 +295,7 @@ hipError_t launch_router_logits(const moe_layer_desc *d, const void *x, int32_t 
         else
             router_row_kernel<MOE_F32><<<E, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E, ws.logits);
     } else if (router_mfma_ok(T, D)) {
-        const int n_tt = (T + 15) / 16, n_ttx = (n_tt + 7) / 8, n_eq = ((E + 15) / 16 + 3) / 4;
+        const int n_tt = (T + 15) / 16, n_ttx = (n_tt + 7) / 8, n_eq = ((E + 15) / 16 + 7) / 8;  // 8 expert tiles a block
         const int grid = 8 * n_ttx * n_eq;
         if (x_type == MOE_BF16)
             router_mfma_kernel<MOE_BF16, 1><<<grid, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E, ws.logits,

@@ -168,7 +168,9 @@ int orc_logits(const orc_layer *L, const double *x, int32_t T, double *logits) {
     return 0;
 }
 
-static const double *orc_sort_keys;
+/* The comparator's keys, one pointer per calling thread, so that several
+ * threads may run the oracle at once on different rows. */
+static _Thread_local const double *orc_sort_keys;
 static int orc_cmp_desc(const void *a, const void *b) {
     int32_t i = *(const int32_t *)a, j = *(const int32_t *)b;
     double li = orc_sort_keys[i], lj = orc_sort_keys[j];
@@ -420,7 +422,7 @@ void orc_count_selections(const int32_t *topk_idx, int32_t T, int32_t k, int32_t
     }
 }
 
-static const int64_t *hot_counts;
+static _Thread_local const int64_t *hot_counts;
 static int64_t hot_key(int32_t i) {
     const int64_t c = hot_counts[i];
     return c < 0 ? 0 : (c >= ((int64_t)1 << 39) ? ((int64_t)1 << 39) - 1 : c);

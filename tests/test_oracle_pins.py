@@ -445,6 +445,62 @@ def test_rmsnorm_closed_form():
     assert np.allclose(oracle.rmsnorm(x, g), ref, rtol=1e-6)
 
 
+def _stack_numpy(layers, x, eps=1e-6):
+    """The stack written out in numpy float64 ("Understanding Dwarf Star" 5.2.1
+    and 5.6.2: each block normalizes its input, and the block's output is added
+    back to the un-normalized input): the normalized row is held in fp32 (the
+    block's input type), the block is the numpy dense definition above, and its
+    fp32 output is added to x in fp32."""
+    outs, cur = [], np.asarray(x, np.float32)
+    for L in layers:
+        xd = cur.astype(np.float64)
+        inv = 1.0 / np.sqrt(np.mean(xd * xd, axis=1, keepdims=True) + eps)
+        xn = (L.gamma.astype(np.float64) * xd * inv).astype(np.float32)
+        y = _dense_numpy(L, xn.astype(np.float64)).astype(np.float32)
+        cur = cur + y
+        outs.append(cur)
+    return outs
+
+
+@pytest.mark.parametrize("E,k", [(1, 1), (6, 2)])
+def test_stack_matches_numpy_composition(E, k):
+    # E = k = 1 makes each block a dense SwiGLU (plus the shared expert);
+    # E = 6, k = 2 routes.  At activations of 1e-3 the mean square equals
+    # eps, so a misplaced eps moves the result by sqrt(2); at 1 the norm
+    # scales each row by gamma, so a residual added to the normalized row
+    # instead of x moves it by up to 10%.
+    layers = [synth.make_layer(41, l, D=256, E=E, k=k, F=64, Fs=64, gamma=True) for l in range(3)]
+    for scale in (1.0, 1e-3):
+        x = (synth.activations(41, 3, 256) * scale).astype(np.float32)
+        got = oracle.stack_forward(layers, x)
+        ref = _stack_numpy(layers, x)
+        assert len(got) == 3
+        for a, b in zip(got, ref):
+            assert a.dtype == np.float32
+            # one fp32 ulp of the normalized row may differ (the sums run in
+            # another order) and moves outputs that cancel to near zero
+            assert np.allclose(a, b, rtol=1e-5, atol=1e-6 * np.abs(b).max())
+    # the layers differ (their own gamma and weights): repeating layer 0
+    # three times gives another result
+    x = synth.activations(41, 3, 256)
+    assert not np.allclose(oracle.stack_forward([layers[0]] * 3, x)[2], oracle.stack_forward(layers, x)[2],
+                           rtol=1e-4)
+
+
+def test_stack_with_zero_experts_passes_x_through():
+    # zero gate rows give silu(0) * u = 0, so every block adds exact zeros and
+    # each layer's output is its input, bit for bit
+    layers = []
+    for l in range(3):
+        L = synth.make_layer(42, l, D=256, E=8, k=2, F=64, Fs=64, gamma=True)
+        L.gate = np.zeros_like(L.gate)
+        L.sh_gate = np.zeros_like(L.sh_gate)
+        layers.append(L)
+    x = synth.activations(42, 4, 256)
+    for out in oracle.stack_forward(layers, x):
+        assert np.array_equal(out, x)
+
+
 def test_stack_teacher_forcing_is_consistent():
     cb = synth.codebook(4)
     layers = [synth.make_layer(40, l, D=256, E=8, k=2, F=64, Fs=64, gate_fmt=synth.CB2, down_fmt=synth.Q2K,
@@ -485,3 +541,18 @@ def test_hotlist_orders_by_hits_then_index():
     order, n_hot = oracle.hotlist(c)
     assert order.tolist() == sorted(range(c.size), key=lambda i: (-int(c[i]), i))
     assert n_hot == int((c > 0).sum())
+
+
+def test_oracle_is_thread_safe():
+    # the GPU parity tests evaluate the oracle's rows on a pool of threads;
+    # every thread must get what a serial call gives (the top-k sort keys are
+    # per thread)
+    import concurrent.futures
+    rng = np.random.default_rng(9)
+    lgs = [rng.normal(size=(64, 256)) for _ in range(16)]
+    serial = [oracle.topk(lg, 6) for lg in lgs]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=8) as ex:
+        for _ in range(4):
+            par = list(ex.map(lambda lg: oracle.topk(lg, 6), lgs))
+            for a, b in zip(serial, par):
+                assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

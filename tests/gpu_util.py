@@ -1,5 +1,9 @@
 """Helpers shared by the GPU tests: upload a synth.Layer, run the library,
-compare with the oracle at the stated tolerance."""
+compare with the oracle at the stated tolerance, and compute the oracle's
+output of many rows on the host cores."""
+import concurrent.futures
+import os
+
 import numpy as np
 import torch
 
@@ -70,3 +74,49 @@ def upload_bias(W, L):
     W2 = copy.copy(W)
     W2.router_bias = dev(L.router_bias)
     return W2
+
+
+def oracle_workers():
+    """Host threads for the oracle fan-out (at most 16, the CPU share of one GPU)."""
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def oracle_all_rows(L, x=None, x_bf16=None, workers=None):
+    """(y [T][D], topk_idx, topk_w) of every row from the oracle, with the rows
+    cut into chunks evaluated on a thread pool.  The oracle's C call releases
+    the interpreter lock, and a row's result does not depend on the other
+    rows of its call (batching is exact), so the chunks equal one call over
+    all rows."""
+    import oracle
+    src = x_bf16 if x_bf16 is not None else x
+    T = src.shape[0]
+    n = workers or oracle_workers()
+    # several chunks per worker so that an uneven chunk does not hold the pool
+    step = max(1, -(-T // (4 * n)))
+    cuts = [(a, min(T, a + step)) for a in range(0, T, step)]
+
+    def one(ab):
+        a, b = ab
+        kw = dict(x_bf16=x_bf16[a:b]) if x_bf16 is not None else dict(x=x[a:b])
+        return oracle.moe_forward(L, **kw)
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=n) as ex:
+        parts = list(ex.map(one, cuts))
+    return (np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]),
+            np.concatenate([p[2] for p in parts]))
+
+
+def oracle_stack(layers, x, teacher=None, workers=None):
+    """oracle.stack_forward with the rows evaluated one by one on a thread pool
+    (every step of a block is row by row, so the rows are independent)."""
+    import oracle
+    T = x.shape[0]
+    n = workers or oracle_workers()
+
+    def one(t):
+        tf = None if teacher is None else [tt[t:t + 1] for tt in teacher]
+        return oracle.stack_forward(layers, x[t:t + 1], teacher=tf)
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=n) as ex:
+        parts = list(ex.map(one, range(T)))
+    return [np.concatenate([p[l] for p in parts]) for l in range(len(layers))]

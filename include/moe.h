@@ -58,7 +58,9 @@
  *    property cache.
  *  - Limits: 1 <= k <= 16, k <= E <= 1024, D % 256 == 0, F % 64 == 0, the
  *    64-weight chunks of a row (n_in/64) a power of two up to 64 or a
- *    multiple of 64, weight and activation base addresses 16-byte aligned.
+ *    multiple of 64, weight and activation base addresses 16-byte aligned,
+ *    and T * D and T * k * F below 2^30 per call (MOE_EUNSUPPORTED beyond:
+ *    split the rows over several calls).
  */
 #ifndef MOE_H
 #define MOE_H
@@ -130,14 +132,15 @@ int moe_route(const moe_layer_desc *desc, const void *x, int32_t T, int32_t x_ty
 /* Expert FFNs, shared expert and weighted combine for a routing produced by
  * moe_route on the same x ("Understanding Dwarf Star", 5.3.7 steps 2-5; 5.3.4).
  * y: [T][D] fp32.  flags: MOE_ACCUMULATE adds to y.
- * Numerics: x_type MOE_F32 keeps x, h and y in fp32; the products take the
- * exact integer codes of the weights against activations coded as int16 per
- * group of 16 values (few rows) or per row (many rows, on the matrix cores),
- * accumulated exactly in int32 and scaled in fp32, and two calls give the
- * same bits.  MOE_BF16 feeds bf16 activations and the exact integer codes of
- * the weights to the matrix cores with fp32 accumulation, rounds the hidden
- * activation h to bf16, and adds the routed down rows into y with atomics
- * (the order of those additions varies between calls). */
+ * Numerics: in both modes the products take the exact integer codes of the
+ * weights against activations coded as int16 (c = rint(v * 32512 / max|v|))
+ * per group of 16 values (few rows) or per row (many rows, on the matrix
+ * cores), accumulated exactly in int32 and scaled in fp32.  x_type MOE_F32
+ * keeps x, h and y in fp32, and two calls give the same bits.  MOE_BF16
+ * takes bf16 x (coded per row like fp32 rows), rounds the hidden activation
+ * h to bf16 before it is coded for the down projection, and adds the routed
+ * down rows into y with atomics (the order of those additions varies between
+ * calls). */
 int moe_expert_ffn(const moe_layer_desc *desc, const void *x, int32_t T, int32_t x_type, const moe_routing *r,
                    float *y, uint32_t flags, void *ws, size_t ws_bytes, void *stream, char *err, size_t errlen);
 

@@ -152,6 +152,102 @@ def _xtype(x):
     raise TypeError("x must be float32 or bfloat16, got %s" % x.dtype)
 
 
+# Argument checks.  Every call checks its tensors here before anything reaches
+# the library, so a bad argument raises with nothing enqueued: shapes, dtypes
+# and contiguity first, then that every tensor lives on one CUDA device.
+
+def _tensor(name, t, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor, got %s" % (name, type(t).__name__))
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _one_cuda_device(**tensors):
+    devs = {n: t.device for n, t in tensors.items() if t is not None}
+    for n, d in devs.items():
+        if d.type != "cuda":
+            raise ValueError("%s must be on a CUDA device, got %s" % (n, d))
+    if len(set(devs.values())) > 1:
+        raise ValueError("tensors on different devices: %s" % ", ".join("%s=%s" % kv for kv in devs.items()))
+
+
+def _layer_tensors(layer):
+    # every device buffer the descriptor points at, checked for dtype and size
+    D, E, F, Fs = layer.n_embd, layer.n_expert, layer.n_ff_exp, layer.n_ff_shared
+    out = dict(router_w=_tensor("router_w", layer.router_w, torch.float32, (E, D)))
+    for n in ("gate", "up", "down"):
+        out[n] = _tensor(n, getattr(layer, n), torch.uint8)
+        if out[n].numel() != E * _block_bytes(layer.down_type if n == "down" else layer.gate_type, F * D):
+            raise ValueError("%s holds %d bytes, not the %d of %d experts" % (
+                n, out[n].numel(), E * _block_bytes(layer.down_type if n == "down" else layer.gate_type, F * D), E))
+    if Fs:
+        for n in ("sh_gate", "sh_up", "sh_down"):
+            t = getattr(layer, n)
+            if t is None:
+                raise ValueError("n_ff_shared > 0 needs %s" % n)
+            out[n] = _tensor(n, t, torch.uint8)
+            if out[n].numel() != _block_bytes(layer.shared_type, Fs * D):
+                raise ValueError("%s holds %d bytes, not %d" % (n, out[n].numel(),
+                                                                 _block_bytes(layer.shared_type, Fs * D)))
+    if layer.router_bias is not None:
+        out["router_bias"] = _tensor("router_bias", layer.router_bias, torch.float32, (E,))
+    if layer.codebook is not None:
+        out["codebook"] = _tensor("codebook", layer.codebook, (torch.int8, torch.uint8), (256, 8))
+    return out
+
+
+_BLOCK = {Q2K: (256, 84), Q8_0: (32, 34), CB2: (256, 66), Q4K: (256, 144)}
+
+
+def _block_bytes(fmt, n_weights):
+    if fmt not in _BLOCK:
+        raise ValueError("unknown block format %r" % (fmt,))
+    w, b = _BLOCK[fmt]
+    if n_weights % w:
+        raise ValueError("%d weights do not fill whole blocks of %d" % (n_weights, w))
+    return n_weights // w * b
+
+
+def _rows(layer, x):
+    _tensor("x", x, (torch.float32, torch.bfloat16))
+    if x.dim() != 2 or x.shape[1] != layer.n_embd:
+        raise ValueError("x must be [T][n_embd=%d], got %s" % (layer.n_embd, tuple(x.shape)))
+    return x.shape[0]
+
+
+def _routing_tensors(layer, routing, T):
+    if routing is None:
+        return {}
+    k, E = layer.n_expert_used, layer.n_expert
+    i32 = torch.int32
+    return dict(topk_idx=_tensor("routing.topk_idx", routing.topk_idx, i32, (T, k)),
+                topk_w=_tensor("routing.topk_w", routing.topk_w, torch.float32, (T, k)),
+                count=_tensor("routing.count", routing.count, i32, (E,)),
+                offset=_tensor("routing.offset", routing.offset, i32, (E + 1,)),
+                perm=_tensor("routing.perm", routing.perm, i32, (T * k,)),
+                pos=_tensor("routing.pos", routing.pos, i32, (T * k,)),
+                active=_tensor("routing.active", routing.active, i32, (E,)),
+                n_active=_tensor("routing.n_active", routing.n_active, i32, (1,)))
+
+
+def _check_call(layer, x, ws, y=None, routing=None, need_y=True):
+    T = _rows(layer, x)
+    rt = _routing_tensors(layer, routing, T)
+    if need_y:
+        _tensor("y", y, torch.float32, (T, layer.n_embd))
+    _tensor("ws", ws, torch.uint8)
+    if ws.dim() != 1:
+        raise ValueError("ws must be a 1-D uint8 tensor")
+    _one_cuda_device(x=x, y=y, ws=ws, **rt, **_layer_tensors(layer))
+    return T
+
+
 def workspace_size(layer, max_rows, x_type=F32):
     d = layer.desc()
     return int(_lib.moe_workspace_size(ctypes.byref(d), max_rows, x_type))
@@ -164,43 +260,51 @@ def alloc_workspace(layer, max_rows, x_type=F32, device="cuda"):
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def _rows(x):
-    if x.dim() != 2 or not x.is_contiguous():
-        raise ValueError("x must be a contiguous [T][D] tensor")
-    return x.shape[0]
-
-
 def route(layer, x, routing, ws, stream=None):
+    if routing is None:
+        raise ValueError("routing arrays are required")
+    T = _check_call(layer, x, ws, routing=routing, need_y=False)
     d, r, err = layer.desc(), routing.struct(), ctypes.create_string_buffer(512)
-    _check(_lib.moe_route(ctypes.byref(d), _ptr(x), _rows(x), _xtype(x), ctypes.byref(r), _ptr(ws), ws.numel(),
+    _check(_lib.moe_route(ctypes.byref(d), _ptr(x), T, _xtype(x), ctypes.byref(r), _ptr(ws), ws.numel(),
                           _stream(stream), err, 512), err)
 
 
 def expert_ffn(layer, x, routing, y, ws, accumulate=False, stream=None):
+    if routing is None:
+        raise ValueError("routing arrays are required")
+    T = _check_call(layer, x, ws, y=y, routing=routing)
     d, r, err = layer.desc(), routing.struct(), ctypes.create_string_buffer(512)
-    _check(_lib.moe_expert_ffn(ctypes.byref(d), _ptr(x), _rows(x), _xtype(x), ctypes.byref(r), _ptr(y),
+    _check(_lib.moe_expert_ffn(ctypes.byref(d), _ptr(x), T, _xtype(x), ctypes.byref(r), _ptr(y),
                                ACCUMULATE if accumulate else 0, _ptr(ws), ws.numel(), _stream(stream), err, 512),
            err)
 
 
 def layer_forward_stage(layer, x, y, ws, stage, routing=None, accumulate=False, stream=None):
+    T = _check_call(layer, x, ws, y=y, routing=routing)
     d, err = layer.desc(), ctypes.create_string_buffer(512)
     r = routing.struct() if routing is not None else None
-    _check(_lib.moe_layer_forward_stage(ctypes.byref(d), _ptr(x), _rows(x), _xtype(x), _ptr(y),
+    _check(_lib.moe_layer_forward_stage(ctypes.byref(d), _ptr(x), T, _xtype(x), _ptr(y),
                                         ACCUMULATE if accumulate else 0,
                                         ctypes.byref(r) if r is not None else None, stage, _ptr(ws), ws.numel(),
                                         _stream(stream), err, 512), err)
 
 
 def layer_forward(layer, x, y, ws, routing=None, accumulate=False, stream=None):
+    T = _check_call(layer, x, ws, y=y, routing=routing)
     d, err = layer.desc(), ctypes.create_string_buffer(512)
     r = routing.struct() if routing is not None else None
-    _check(_lib.moe_layer_forward(ctypes.byref(d), _ptr(x), _rows(x), _xtype(x), _ptr(y),
+    _check(_lib.moe_layer_forward(ctypes.byref(d), _ptr(x), T, _xtype(x), _ptr(y),
                                   ACCUMULATE if accumulate else 0, ctypes.byref(r) if r is not None else None,
                                   _ptr(ws), ws.numel(), _stream(stream), err, 512), err)
 
 
 def rmsnorm(x, gamma, out, eps=1e-6, stream=None):
+    _tensor("x", x, torch.float32)
+    if x.dim() != 2:
+        raise ValueError("x must be [T][D]")
+    _tensor("gamma", gamma, torch.float32, (x.shape[1],))
+    _tensor("out", out, torch.float32, tuple(x.shape))
+    _one_cuda_device(x=x, gamma=gamma, out=out)
     err = ctypes.create_string_buffer(512)
     _check(_lib.moe_rmsnorm(_ptr(x), _ptr(gamma), eps, x.shape[0], x.shape[1], _ptr(out), _stream(stream), err,
                             512), err)
@@ -208,8 +312,14 @@ def rmsnorm(x, gamma, out, eps=1e-6, stream=None):
 
 def count_selections(topk_idx, E, layer, counts, stream=None):
     """counts [n_layer*E] int64 (device) += selections of topk_idx [T][k] int32 in layer `layer`."""
-    assert topk_idx.dtype == torch.int32 and topk_idx.is_contiguous() and topk_idx.dim() == 2
-    assert counts.dtype == torch.int64 and counts.is_contiguous()
+    _tensor("topk_idx", topk_idx, torch.int32)
+    if topk_idx.dim() != 2:
+        raise ValueError("topk_idx must be [T][k]")
+    _tensor("counts", counts, torch.int64)
+    if counts.numel() < (layer + 1) * E:
+        raise ValueError("counts holds %d entries; layer %d of %d experts needs %d" % (
+            counts.numel(), layer, E, (layer + 1) * E))
+    _one_cuda_device(topk_idx=topk_idx, counts=counts)
     err = ctypes.create_string_buffer(512)
     _check(_lib.moe_count_selections(_ptr(topk_idx), topk_idx.shape[0], topk_idx.shape[1], E, layer, _ptr(counts),
                                      _stream(stream), err, 512), err)
@@ -217,13 +327,25 @@ def count_selections(topk_idx, E, layer, counts, stream=None):
 
 def hotlist(counts, order, n_hot, stream=None):
     """order [n] int32 <- entries by hits descending, ties by index; n_hot [1] int32 <- positive entries."""
-    assert counts.dtype == torch.int64 and counts.is_contiguous()
-    assert order.dtype == torch.int32 and n_hot.dtype == torch.int32 and order.numel() == counts.numel()
+    _tensor("counts", counts, torch.int64)
+    _tensor("order", order, torch.int32, (counts.numel(),))
+    _tensor("n_hot", n_hot, torch.int32, (1,))
+    _one_cuda_device(counts=counts, order=order, n_hot=n_hot)
     err = ctypes.create_string_buffer(512)
     _check(_lib.moe_hotlist(_ptr(counts), counts.numel(), _ptr(order), _ptr(n_hot), _stream(stream), err, 512), err)
 
 
 def dequant(fmt, src, n_weights, out, codebook=None, stream=None):
+    _tensor("src", src, torch.uint8)
+    if src.numel() < _block_bytes(fmt, n_weights):
+        raise ValueError("src holds %d bytes; %d weights need %d" % (src.numel(), n_weights,
+                                                                      _block_bytes(fmt, n_weights)))
+    _tensor("out", out, (torch.float32, torch.bfloat16))
+    if out.numel() < n_weights:
+        raise ValueError("out holds %d values; %d needed" % (out.numel(), n_weights))
+    if codebook is not None:
+        _tensor("codebook", codebook, (torch.int8, torch.uint8), (256, 8))
+    _one_cuda_device(src=src, out=out, codebook=codebook)
     err = ctypes.create_string_buffer(512)
     ot = BF16 if out.dtype == torch.bfloat16 else F32
     _check(_lib.moe_dequant(fmt, _ptr(src), n_weights, _ptr(codebook), ot, _ptr(out), _stream(stream), err, 512),

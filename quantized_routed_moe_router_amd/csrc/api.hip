@@ -68,7 +68,13 @@ int check_call(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type
     if (x_type != MOE_F32 && x_type != MOE_BF16)
         return fail(err, errlen, MOE_EUNSUPPORTED, "x_type must be MOE_F32 or MOE_BF16");
     if (T == 0) return MOE_OK;
-    if ((int64_t)T * d->n_expert_used > INT32_MAX / 2) return fail(err, errlen, MOE_EUNSUPPORTED, "T too large");
+    // The grouped GEMMs address the activation codes of x ([T][D]) and of h
+    // ([T*k][F]), 2 bytes per value, with 32-bit offsets from one base.
+    if ((int64_t)T * d->n_embd * 2 > INT32_MAX || (int64_t)T * d->n_expert_used * d->n_ff_exp * 2 > INT32_MAX)
+        return fail(err, errlen, MOE_EUNSUPPORTED,
+                    "T=%d rows is too many for one call: T*n_embd and T*k*n_ff_exp must stay below 2^30 "
+                    "(split the rows over several calls)",
+                    T);
     if (!x) return fail(err, errlen, MOE_EINVAL, "x is NULL");
     if (!aligned16(x)) return fail(err, errlen, MOE_EALIGN, "x must be 16-byte aligned");
     size_t need = ws_bytes_for(d, T);

@@ -1,5 +1,6 @@
-// k_prefill.hip - the routed experts of many token rows in bf16 mode as
-// grouped GEMMs on the matrix cores ("Understanding Dwarf Star", 5.3.7 steps
+// k_prefill.hip - the routed experts of many token rows (bf16 rows, and fp32
+// rows beyond the few-token decode kernels) as grouped GEMMs on the matrix
+// cores ("Understanding Dwarf Star", 5.3.7 steps
 // 3-5: each active expert's bucket of pairs runs gate/up, SwiGLU, down and a
 // weighted scatter into y; 2.8.2 the dequant-dot over 256-weight super-blocks;
 // the Q2_K subsection for w = d*sc*q - dmin*m).

@@ -84,6 +84,11 @@ def test_bad_calls_are_rejected():
     assert _call_route(d, ws_bytes=100)[0] == -3
     assert _call_route(d, ws=None)[0] == -3
     assert _call_route(d, x_type=3)[0] == -4
+    # the activation codes of x and h must stay addressable with 32-bit
+    # offsets: at n_embd 4096, k 6, FFN 2048 that is T*k*F*2 < 2^31
+    assert _call_route(d, T=87382)[0] == -4
+    assert _call_route(d, T=87381)[0] == -3  # accepted, then the 1 GiB workspace is short
+    assert _call_route(d, T=2 ** 31 - 1)[0] == -4
     # T = 0 is a valid no-op and touches nothing
     assert _call_route(d, T=0, x=None, ws=None, ws_bytes=0)[0] == 0
 
@@ -119,3 +124,107 @@ def test_hotlist_and_counts_validate_before_enqueue():
     assert moe._lib.moe_count_selections(None, 4, 0, 8, 0, None, None, err, 256) == -1
     assert moe._lib.moe_count_selections(None, 0, 6, 8, 0, None, None, err, 256) == 0  # T = 0
     assert moe._lib.moe_count_selections(None, 1, 6, 8, 0, None, None, err, 256) == -1  # pointers unset
+
+
+# The Python binding checks every tensor before the library is called
+# ("Understanding Dwarf Star" 3.7: validation fails early, nothing fails
+# silently).  The library is replaced by a stub that fails the test if any
+# entry point is reached.
+
+class _NoLibrary:
+    def __getattr__(self, name):
+        raise AssertionError("the library was called (%s) despite a bad argument" % name)
+
+
+def _cpu_layer(D=256, E=4, k=2, F=64, Fs=128):
+    import torch
+
+    import quantized_routed_moe_router_amd as moe
+    u8 = dict(dtype=torch.uint8)
+    return moe.LayerWeights(D, E, k, F, Fs, moe.Q2K, moe.Q2K, moe.Q2K, moe.Q8_0,
+                            router_w=torch.zeros(E, D), gate=torch.zeros(E * F * D // 256 * 84, **u8),
+                            up=torch.zeros(E * F * D // 256 * 84, **u8), down=torch.zeros(E * F * D // 256 * 84, **u8),
+                            sh_gate=torch.zeros(Fs * D // 32 * 34, **u8), sh_up=torch.zeros(Fs * D // 32 * 34, **u8),
+                            sh_down=torch.zeros(Fs * D // 32 * 34, **u8))
+
+
+def _bad_call(case):
+    import torch
+
+    import quantized_routed_moe_router_amd as moe
+    W = _cpu_layer()
+    T, D = 3, W.n_embd
+    x = torch.zeros(T, D)
+    y = torch.zeros(T, D)
+    ws = torch.zeros(1024, dtype=torch.uint8)
+    r = moe.Routing(T, W.n_expert_used, W.n_expert, device="cpu")
+    call = lambda: moe.layer_forward(W, x, y, ws, routing=r)
+    if case == "x_width":
+        x = torch.zeros(T, D + 256)
+    elif case == "x_dtype":
+        x = torch.zeros(T, D, dtype=torch.float64)
+    elif case == "x_strided":
+        x = torch.zeros(D, T).t()
+    elif case == "x_1d":
+        x = torch.zeros(T * D)
+    elif case == "y_dtype":
+        y = torch.zeros(T, D, dtype=torch.float64)
+    elif case == "y_shape":
+        y = torch.zeros(T + 1, D)
+    elif case == "y_strided":
+        y = torch.zeros(T, 2 * D)[:, ::2]
+    elif case == "y_missing":
+        y = None
+    elif case == "ws_dtype":
+        ws = torch.zeros(256, dtype=torch.int32)
+    elif case == "routing_rows":
+        r = moe.Routing(T + 1, W.n_expert_used, W.n_expert, device="cpu")
+    elif case == "routing_dtype":
+        r.topk_idx = r.topk_idx.long()
+    elif case == "gate_bytes":
+        W.gate = W.gate[:-84]
+    elif case == "router_shape":
+        W.router_w = torch.zeros(W.n_embd, W.n_expert)
+    elif case == "on_cpu":
+        pass  # every shape is right; the tensors are not on a GPU
+    elif case == "route_without_routing":
+        call = lambda: moe.route(W, x, None, ws)
+    elif case == "ffn_without_routing":
+        call = lambda: moe.expert_ffn(W, x, None, y, ws)
+    elif case == "rmsnorm_gamma":
+        call = lambda: moe.rmsnorm(x, torch.zeros(D - 1), y)
+    elif case == "rmsnorm_out":
+        call = lambda: moe.rmsnorm(x, torch.zeros(D), torch.zeros(T, D, dtype=torch.bfloat16))
+    elif case == "dequant_src":
+        call = lambda: moe.dequant(moe.Q2K, torch.zeros(83, dtype=torch.uint8), 256, torch.zeros(256))
+    elif case == "dequant_out":
+        call = lambda: moe.dequant(moe.Q2K, torch.zeros(84, dtype=torch.uint8), 256, torch.zeros(255))
+    elif case == "counts_small":
+        call = lambda: moe.count_selections(torch.zeros(2, 6, dtype=torch.int32), 256, 3,
+                                            torch.zeros(3 * 256, dtype=torch.int64))
+    elif case == "hotlist_order":
+        call = lambda: moe.hotlist(torch.zeros(10, dtype=torch.int64), torch.zeros(9, dtype=torch.int32),
+                                   torch.zeros(1, dtype=torch.int32))
+    else:
+        raise KeyError(case)
+    return call
+
+
+@pytest.mark.parametrize("case,exc,text", [
+    ("x_width", ValueError, "n_embd"), ("x_dtype", TypeError, "x must be"), ("x_strided", ValueError, "contiguous"),
+    ("x_1d", ValueError, "n_embd"), ("y_dtype", TypeError, "y must be"), ("y_shape", ValueError, "y must have"),
+    ("y_strided", ValueError, "contiguous"), ("y_missing", TypeError, "y must be a torch.Tensor"),
+    ("ws_dtype", TypeError, "ws must be"), ("routing_rows", ValueError, "routing.topk_idx"),
+    ("routing_dtype", TypeError, "routing.topk_idx"), ("gate_bytes", ValueError, "gate holds"),
+    ("router_shape", ValueError, "router_w"), ("on_cpu", ValueError, "CUDA device"),
+    ("route_without_routing", ValueError, "routing"), ("ffn_without_routing", ValueError, "routing"),
+    ("rmsnorm_gamma", ValueError, "gamma"), ("rmsnorm_out", TypeError, "out"), ("dequant_src", ValueError, "src"),
+    ("dequant_out", ValueError, "out"), ("counts_small", ValueError, "counts"),
+    ("hotlist_order", ValueError, "order"),
+])
+def test_binding_rejects_bad_tensors_before_the_library(monkeypatch, case, exc, text):
+    import quantized_routed_moe_router_amd as moe
+    call = _bad_call(case)
+    monkeypatch.setattr(moe, "_lib", _NoLibrary())
+    with pytest.raises(exc, match=text):
+        call()

@@ -35,18 +35,6 @@ static double orc_bf16(uint16_t b) {
     return (double)f;
 }
 
-/* Round to bf16 (nearest, ties to even) through fp32: the cast point of the
- * bf16 mode forms h in fp32 and stores it as bf16. */
-static double orc_round_bf16(double v) {
-    float f = (float)v;
-    uint32_t x;
-    memcpy(&x, &f, 4);
-    if ((x & 0x7FFFFFFFu) > 0x7F800000u) return v;
-    x = (x + 0x7FFFu + ((x >> 16) & 1u)) & 0xFFFF0000u;
-    memcpy(&f, &x, 4);
-    return (double)f;
-}
-
 /* silu(z) = z * sigmoid(z), the gate activation of SwiGLU ([UDS] 5.2.4). */
 static double orc_silu(double z) { return z / (1.0 + exp(-z)); }
 
@@ -238,9 +226,11 @@ int orc_bucket(const int32_t *idx, int32_t T, int32_t k, int32_t E, int32_t *cou
 /* ---- expert FFN ([UDS] 5.2.4, 5.3.7 step 4; [SPE] gate, up, down) --------- */
 
 /* y = W_down (silu(W_gate x) * (W_up x)); W_gate, W_up [F][D], W_down [D][F].
- * In bf16 mode h is rounded to bf16 before the down projection. */
+ * The mode only says how x was given: h is never rounded (the activations'
+ * cast to bf16 is the only cast point of the bf16 workload). */
 int orc_swiglu(int fmt_gu, int fmt_down, const uint8_t *gate, const uint8_t *up, const uint8_t *down,
                const int8_t *cb, int32_t D, int32_t F, int mode, const double *x, double *y) {
+    (void)mode;
     float *row = (float *)malloc(sizeof(float) * (size_t)(D > F ? D : F));
     double *h = (double *)malloc(sizeof(double) * (size_t)F);
     if (!row || !h) { free(row); free(h); return -1; }
@@ -251,7 +241,6 @@ int orc_swiglu(int fmt_gu, int fmt_down, const uint8_t *gate, const uint8_t *up,
         orc_dequant_range(fmt_gu, up, (int64_t)f * D, D, cb, row);
         for (int32_t k = 0; k < D; ++k) u += (double)row[k] * x[k];
         h[f] = orc_silu(g) * u;
-        if (mode == ORC_BF16) h[f] = orc_round_bf16(h[f]);
     }
     for (int32_t d = 0; d < D; ++d) {
         double s = 0.0;

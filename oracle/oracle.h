@@ -19,10 +19,10 @@
  *  [RDM]  antirez/ds4 README mirror: the --batched-session paragraph
  *         ("batching is exact").
  * Where the pages are silent the oracle takes the readings listed in the design doc
- * (block byte orders, tie order, fp64 logits, cast points in bf16 mode).
+ * (block byte orders, tie order, fp64 logits, the bf16 mode's one cast point).
  *
- * Everything here is computed in double precision unless a cast point of the
- * bf16 mode says otherwise.
+ * Everything here is computed in double precision; in bf16 mode the input x
+ * is given as bf16 values and nothing else is rounded.
  */
 #ifndef ORACLE_H
 #define ORACLE_H
@@ -60,8 +60,9 @@ int orc_topk(const double *logits, int32_t T, int32_t E, int32_t k, double route
 int orc_bucket(const int32_t *idx, int32_t T, int32_t k, int32_t E, int32_t *count, int32_t *offset,
                int32_t *perm, int32_t *pos, int32_t *active, int32_t *n_active);
 /* The block: y[t] = shared(x_t) + sum over chosen e of w_e * FFN_e(x_t).
- * mode ORC_F32: x_f32 used; ORC_BF16: x_bf16 (bf16 bits) used and the hidden
- * activations h are rounded to bf16 before the down projection.
+ * mode ORC_F32: x_f32 used; ORC_BF16: x_bf16 (bf16 bits) used; everything
+ * after the input is computed the same way in both modes (x's cast to bf16
+ * is the only cast point of the bf16 workload).
  * Rows listed in rows[0..n_rows) (NULL = all T) are computed; y is [T][D]
  * and only those rows are written.  idx/w (optional, [T][k]) receive the routing. */
 int orc_moe_forward(const orc_layer *L, int mode, const float *x_f32, const uint16_t *x_bf16, int32_t T,

@@ -380,13 +380,18 @@ def test_block_matches_numpy_definition():
 
 
 def test_bf16_mode_matches_numpy_definition():
+    # the bf16 workload casts the activations to bf16 and nothing else: the
+    # block on bf16 x is the numpy definition on x's bf16 values, and it is
+    # bit for bit the fp32 mode on those same values (bf16 -> fp32 is exact)
     L = synth.make_layer(33, 0, D=256, E=8, k=2, F=128, Fs=64)
     xb = synth.to_bf16_bits(synth.activations(33, 5, 256))
-    y, _, _ = oracle.moe_forward(L, x_bf16=xb)
+    y, idx, w = oracle.moe_forward(L, x_bf16=xb)
     xd = oracle.input_as_double(x_bf16=xb)
-    assert np.allclose(y, _dense_numpy(L, xd, bf16=True), rtol=1e-6, atol=1e-7)
-    # the h cast matters: without it the result moves
-    assert not np.allclose(y, _dense_numpy(L, xd, bf16=False), rtol=1e-7, atol=0)
+    assert np.allclose(y, _dense_numpy(L, xd), rtol=1e-6, atol=1e-7)
+    y32, idx32, w32 = oracle.moe_forward(L, x=xd.astype(np.float32))
+    assert np.array_equal(y, y32) and np.array_equal(idx, idx32) and np.array_equal(w, w32)
+    # rounding h to bf16 as well would move the result
+    assert not np.allclose(y, _dense_numpy(L, xd, bf16=True), rtol=1e-7, atol=0)
 
 
 @pytest.mark.parametrize("mode", ["f32", "bf16"])

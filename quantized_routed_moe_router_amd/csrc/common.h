@@ -721,9 +721,9 @@ struct Workspace {
     float *pf_xinv;       // [T]
     int4 *pf_tiles;       // {expert, first bucket position, rows, 0}
     int32_t *pf_ntiles;
-    uint16_t *pf_hb;      // [T*k][F] bf16 h by bucket position
     uint16_t *pf_shw;     // shared expert weights as bf16 hi (gate, up, down) then lo halves
-    uint16_t *pf_hsb;     // [T][Fs] bf16 shared h
+    uint16_t *pf_hsb;     // [T][Fs] shared h as a bf16 pair: hi = rne(h) here,
+    uint16_t *pf_hsb_lo;  //          lo = rne(h - hi) here
     uint8_t *pf_hq;
     uint32_t *pf_hs;
     float *pf_hinv;       // [T*k]
@@ -778,9 +778,9 @@ __host__ inline Workspace workspace_layout(const moe_layer_desc *d, int32_t T, v
     w.pf_xinv = (float *)take(sizeof(float) * (size_t)T);
     w.pf_tiles = (int4 *)take(sizeof(int4) * (size_t)pf_max_tiles(T, k, E));
     w.pf_ntiles = (int32_t *)take(sizeof(int32_t) * 4);
-    w.pf_hb = (uint16_t *)take((size_t)P * (size_t)F * 2);
     w.pf_shw = (uint16_t *)take((size_t)6 * (size_t)Fs * (size_t)D * 2);
     w.pf_hsb = (uint16_t *)take((size_t)T * (size_t)Fs * 2);
+    w.pf_hsb_lo = (uint16_t *)take((size_t)T * (size_t)Fs * 2);
     w.pf_hq = (uint8_t *)take((size_t)P * (size_t)F * 2);
     w.pf_hs = (uint32_t *)take((size_t)P * (size_t)(F / 256 + 1) * 64);
     w.pf_hinv = (float *)take(sizeof(float) * (size_t)P);

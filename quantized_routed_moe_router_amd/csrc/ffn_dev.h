@@ -425,10 +425,9 @@ MOE_DEV void wave_rows(const uint8_t *m0, const uint8_t *m1, int n_in, int row0,
     }
 }
 
-MOE_DEV float swiglu_h(float g, float u, int round_bf16) {
-    float hv = silu(g) * u;
-    return round_bf16 ? bf16_bits_to_float(float_to_bf16_bits(hv)) : hv;
-}
+// h = silu(g) * u in fp32, never rounded further (in bf16 mode only the
+// activations x were cast)
+MOE_DEV float swiglu_h(float g, float u) { return silu(g) * u; }
 
 // h rows for one routed expert e (rows [row0, row0+nrows) of its gate/up),
 // every token of its bucket, activations prepared in the lane.  The weight
@@ -447,7 +446,7 @@ MOE_DEV void routed_gateup(const FfnArgs &a, int e, int row0, int nrows, const u
         RawChunk<FMT>::prep(xf, xr);
         float *dst = a.h + (int64_t)(j0 + j) * a.F + row0;
         wave_rows<FMT, true>(g, u, a.D, row0, nrows, xr, cb, lane,
-                             [&](int r, float gs, float us) { dst[r] = swiglu_h(gs, us, a.x_bf16); });
+                             [&](int r, float gs, float us) { dst[r] = swiglu_h(gs, us); });
     }
 }
 
@@ -462,7 +461,7 @@ MOE_DEV void shared_gateup(const FfnArgs &a, int row0, int nrows, const uint32_t
         RawChunk<FMT>::prep(xf, xr);
         float *dst = a.hs + (int64_t)t * a.Fs + row0;
         wave_rows<FMT, true>(a.sh_gate, a.sh_up, a.D, row0, nrows, xr, cb, lane,
-                             [&](int r, float gs, float us) { dst[r] = swiglu_h(gs, us, a.x_bf16); });
+                             [&](int r, float gs, float us) { dst[r] = swiglu_h(gs, us); });
     }
 }
 

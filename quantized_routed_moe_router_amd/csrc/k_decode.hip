@@ -158,7 +158,7 @@ __global__ void __launch_bounds__(256) dec_k2_kernel(FfnArgs a, int do_route) {
         rows_dot_ch<F32Chunk<SFMT>, true, kShGuRows>(
             a.sh_gate, a.sh_up, a.D, 0, a.D, nrows, [&](int l) { return row0 + l; },
             [&](XF32 &xr) { load_x64(a.x, a.x_bf16, (int64_t)t * a.D + 64 * c, xr.x); }, cb_lds, lane, red[wave],
-            [&](int l, float gs, float us) { dst[l] = swiglu_h(gs, us, a.x_bf16); });
+            [&](int l, float gs, float us) { dst[l] = swiglu_h(gs, us); });
     }
 }
 
@@ -282,7 +282,7 @@ __global__ void __launch_bounds__(320) dec_k2_q8sg4096_kernel(FfnArgs a, int do_
                 gs += part[w][4 * q + j];
                 us += part[w][4 * q + 2 + j];
             }
-            a.hs[(int64_t)t * a.Fs + row0 + tid] = swiglu_h(gs, us, a.x_bf16);
+            a.hs[(int64_t)t * a.Fs + row0 + tid] = swiglu_h(gs, us);
         }
         if (!more) break;
         ++t;
@@ -345,7 +345,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
                     gs += part[rg * cs.P + q][2 * rl];
                     us += part[rg * cs.P + q][2 * rl + 1];
                 }
-                hv = swiglu_h(gs, us, a.x_bf16);
+                hv = swiglu_h(gs, us);
                 a.h[(int64_t)(rec.j0 + j) * a.F + 16 * g + lane] = hv;
             }
             if (a.hp16) prep16_wave(hv, a.hp16 + ((int64_t)(rec.j0 + j) * (a.F / 16) + g) * kRec16Dwords, 1);
@@ -442,7 +442,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
                     gs += part[q][2 * lane];
                     us += part[q][2 * lane + 1];
                 }
-                hv = swiglu_h(gs, us, a.x_bf16);
+                hv = swiglu_h(gs, us);
                 a.h[(int64_t)(rec.j0 + j) * a.F + 16 * g + lane] = hv;
             }
             if (a.hp16) prep16_wave(hv, a.hp16 + ((int64_t)(rec.j0 + j) * (a.F / 16) + g) * kRec16Dwords, 1);
@@ -566,7 +566,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
                     gs += part[q][2 * lane];
                     us += part[q][2 * lane + 1];
                 }
-                hv = swiglu_h(gs, us, a.x_bf16);
+                hv = swiglu_h(gs, us);
                 a.h[(int64_t)(rec.j0 + j) * a.F + 16 * g + lane] = hv;
             }
             if (a.hp16) prep16_wave(hv, a.hp16 + ((int64_t)(rec.j0 + j) * (a.F / 16) + g) * kRec16Dwords, 1);

@@ -29,13 +29,8 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kPfM = 64;                // pair rows per tile
-constexpr int kPfWaves = 8;
-constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfWaveRows = 64;         // weight rows per wave (two 32-column MFMA subtiles)
-constexpr int kPfBRows = kPfWaveRows * kPfWaves;  // weight rows staged per super-block column
 constexpr int kPfARow = 33;             // 16-byte units per code row in LDS: hi 16 + lo 16 + 1 pad
-constexpr int kPfAUnits = kPfM * kPfARow;
-constexpr int kPfSDwords = kPfM * 16;   // group sums: 8 dwords sH + 8 dwords sL per row
 constexpr float kPfCodeMax = 32512.f;   // |c| <= 32512 keeps hi in [-127, 127]
 
 // 4-unit rows (64 bytes): distinct banks for 8 and for 16 consecutive rows
@@ -74,8 +69,7 @@ struct PfArgs {
     const float *topk_w;
     int k;
     int D, F;
-    uint16_t *hb;            // mode 0 output: h in bf16, [T*k][F] by bucket position
-    float *hf;               // mode 0 output instead, when set: h in fp32 (fp32 mode)
+    float *hf;               // mode 0 output: h in fp32, [T*k][F] by bucket position
     float *y;                // mode 1 output: w * y_pair added into y by atomics
     float *ypart;            // mode 1 output instead, when set: unweighted y_pair rows [T*k][D] by bucket position
 };
@@ -172,8 +166,8 @@ MOE_DEV void pf_codes16(const float *v, float S, u32x4 &hi, u32x4 &lo) {
     }
 }
 
-// Activation codes of rows of n bf16 values (x for gate/up, h for down): one
-// block per row, a thread per group of 16.  S = 32512 / max|row|; the group
+// Activation codes of rows of n bf16 or fp32 values (x for gate/up, h for
+// down): one block per row, a thread per group of 16.  S = 32512 / max|row|; the group
 // sums are kept in code units (sum * S), so a whole product stays in code
 // units until the row's 1/S at the end.
 // 16 consecutive values of a bf16 or fp32 row
@@ -332,10 +326,6 @@ MOE_DEV void stage_barrier() {
     __asm__ volatile("" ::: "memory");
 }
 
-// Mode 0: a column block is 128 F-rows; wave w < 4 owns gate rows
-// 32w..32w+31, wave w >= 4 the same rows of up; writes h = silu(g) * u in
-// bf16.  Mode 1: a column block is 256 D-columns, wave w owns columns
-// 32w..32w+31; adds w * y_pair into y.
 // Linear block id -> (tile, column block), so that the column blocks of one
 // tile run on one XCD (blocks go round-robin to the 8 XCDs): its activation
 // rows are then fetched into that XCD's L2 once instead of into all of them.
@@ -348,8 +338,9 @@ MOE_DEV void xcd_tile_map(int L, int nb, int &tile, int &col) {
 
 // Mode 0: a column block is 256 F-rows; wave w < 4 owns gate rows
 // 64w..64w+63, wave w >= 4 the same rows of up; writes h = silu(g) * u in
-// bf16.  Mode 1: a column block is 512 D-columns, wave w owns columns
-// 64w..64w+63; adds w * y_pair into y.
+// fp32.  Mode 1: a column block is 512 D-columns, wave w owns columns
+// 64w..64w+63; adds w * y_pair into y (bf16 rows) or writes y_pair (fp32
+// rows).
 // (two waves per SIMD: for W = 4 that is two blocks per compute unit, which
 // also needs the registers of W = 8)
 template <int MODE, int W>
@@ -596,8 +587,7 @@ __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 
                         const float f = row_f[r];
                         const int col = wave * 64 + 32 * n + c;
                         const float hv = silu(tot[n][q][v] * f) * (U[r * kColRows + col] * f);
-                        if (a.hf) a.hf[(int64_t)(start + r) * a.F + o0 + col] = hv;
-                        else a.hb[(int64_t)(start + r) * a.F + o0 + col] = bf16_rne(hv);
+                        a.hf[(int64_t)(start + r) * a.F + o0 + col] = hv;
                     }
                 }
         }
@@ -664,28 +654,36 @@ constexpr int kSgM = 128;            // token rows per block (four 32-row subtil
 constexpr int kSgKc = 32;            // reduction columns per stage
 constexpr int kSgRowUnits = kSgKc * 2 / 16;   // 16-byte units per row per stage (4)
 
-struct SgStage {
+// LO: the activations come as a bf16 pair (hi, lo) too (mode 1: the shared
+// h, kept to fp32 precision)
+template <bool LO>
+struct SgStageT {
     u32x4 a[kSgM * kSgRowUnits];       // activation rows: unit u of row r at r*4 + (u ^ sum_swz(r))
+    u32x4 al[LO ? kSgM * kSgRowUnits : 1];  // their lo halves, same layout
     u32x4 bh[256 * kSgRowUnits];       // weight rows, hi halves, same swizzle
     u32x4 bl[256 * kSgRowUnits];       // lo halves
 };
 
 struct SgArgs {
-    const uint16_t *a;          // [T][K] bf16
+    const uint16_t *a;          // mode 0: x [T][K] bf16; mode 1: hs hi halves [T][K]
+    const uint16_t *a_lo;       // mode 1: hs lo halves [T][K]
     const uint16_t *wh, *wl;    // mode 0: gate rows then up rows [2*Fs][D]; mode 1: down [D][Fs]
     int T, K, Fs, D;
-    uint16_t *hs;               // mode 0 output [T][Fs] bf16
+    uint16_t *hs, *hs_lo;       // mode 0 output [T][Fs]: h = silu(g) * u as a bf16 pair hi + lo
     float *y;                   // mode 1 output [T][D]
     int accumulate;
 };
 
 MOE_DEV int sg_unit(int r, int u) { return r * kSgRowUnits + (u ^ sum_swz(r)); }
 
-// Mode 0: blockIdx.x = 128 F-rows (waves 0-3 gate, 4-7 up), writes bf16
-// h = silu(g) * u.  Mode 1: blockIdx.x = 256 D-columns, y = (y if
-// accumulating) + shared output.  blockIdx.y = 128 token rows.
+// Mode 0: blockIdx.x = 128 F-rows (waves 0-3 gate, 4-7 up), writes
+// h = silu(g) * u as a bf16 pair (hi + lo keeps h to about 2^-17).  Mode 1:
+// blockIdx.x = 256 D-columns, both halves of h against both halves of the
+// weights (hi*hi, hi*lo, lo*hi; lo*lo is below 2^-16 of the product), y =
+// (y if accumulating) + shared output.  blockIdx.y = 128 token rows.
 template <int MODE>
 __global__ void __launch_bounds__(512) pf_sg_gemm_kernel(SgArgs a) {
+    typedef SgStageT<MODE == 1> SgStage;
     __shared__ SgStage st0, st1;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, c = lane & 31, h = lane >> 5;
     const int m0 = blockIdx.y * kSgM;
@@ -697,7 +695,8 @@ __global__ void __launch_bounds__(512) pf_sg_gemm_kernel(SgArgs a) {
     // one 16-byte unit per thread for A (512 units), two for each weight half (1024 units)
     static_assert(kSgM * kSgRowUnits == 512 && 256 * kSgRowUnits == 1024, "stage shape");
     const int ar = tid >> 2;
-    const uint16_t *asrc = a.a + (int64_t)min(m0 + ar, a.T - 1) * a.K + 8 * ((tid & 3) ^ sum_swz(ar));
+    const int64_t aoff = (int64_t)min(m0 + ar, a.T - 1) * a.K + 8 * ((tid & 3) ^ sum_swz(ar));
+    const uint16_t *asrc = a.a + aoff, *asrc_lo = a.a_lo + aoff;
     int64_t boff[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -706,13 +705,14 @@ __global__ void __launch_bounds__(512) pf_sg_gemm_kernel(SgArgs a) {
     }
     auto issue = [&](SgStage &S, int kc) {
         pf_dma16(asrc + kc * kSgKc, &S.a[64 * wave]);
+        if constexpr (MODE == 1) pf_dma16(asrc_lo + kc * kSgKc, &S.al[64 * wave]);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             pf_dma16(a.wh + boff[i] + kc * kSgKc, &S.bh[i * 512 + 64 * wave]);
             pf_dma16(a.wl + boff[i] + kc * kSgKc, &S.bl[i * 512 + 64 * wave]);
         }
     };
-    constexpr int kIssued = 5;
+    constexpr int kIssued = MODE == 1 ? 6 : 5;
     v16f tot[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -734,6 +734,12 @@ __global__ void __launch_bounds__(512) pf_sg_gemm_kernel(SgArgs a) {
                 __builtin_memcpy(&av, &aw, 16);
                 tot[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bvh, tot[q], 0, 0, 0);
                 tot[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bvl, tot[q], 0, 0, 0);
+                if constexpr (MODE == 1) {
+                    const u32x4 alw = S.al[sg_unit(q * 32 + c, u)];
+                    v8bf avl;
+                    __builtin_memcpy(&avl, &alw, 16);
+                    tot[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(avl, bvh, tot[q], 0, 0, 0);
+                }
             }
         }
     };
@@ -782,7 +788,10 @@ __global__ void __launch_bounds__(512) pf_sg_gemm_kernel(SgArgs a) {
                         const int rl = qq * 32 + 8 * (v >> 2) + 4 * h + (v & 3), r = 64 * half + rl;
                         if (m0 + r >= a.T) continue;
                         const float hv = silu(tot[2 * half + qq][v]) * U[rl * 128 + wave * 32 + c];
-                        a.hs[(int64_t)(m0 + r) * a.Fs + blockIdx.x * 128 + wave * 32 + c] = bf16_rne(hv);
+                        const uint16_t hh = bf16_rne(hv);
+                        const int64_t o = (int64_t)(m0 + r) * a.Fs + blockIdx.x * 128 + wave * 32 + c;
+                        a.hs[o] = hh;
+                        a.hs_lo[o] = bf16_rne(hv - bf16_bits_to_float(hh));
                     }
             }
             block_lds_sync();
@@ -810,10 +819,11 @@ bool prefill_path_ok(const moe_layer_desc *d, int32_t T, int32_t x_type) {
 
 // stage 3: x codes, tiles, shared gate/up, routed gate/up; stage 4: h codes,
 // shared down, y init, routed down; 0: all; 5: the routed gate/up GEMM alone.
-// bf16 mode: the shared expert as bf16 GEMMs, h in bf16, the routed down
-// added into y by atomics.  fp32 mode: the routed GEMMs take fp32 rows and
-// keep h in fp32, the shared expert runs on the batched kernels (hs, ys),
-// the routed down writes one row per pair and the gather adds them in slot
+// In both modes the routed GEMMs keep h in fp32 and code it per row for the
+// down.  bf16 mode: the shared expert as bf16 GEMMs on exactly split
+// weights (h as a bf16 pair), the routed down added into y by atomics.  fp32
+// mode: the shared expert on its int8 GEMMs (or the batched kernels), the
+// routed down writes one row per pair and the gather adds them in slot
 // order, so that two runs give the same bits.
 hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
                           float *y, uint32_t flags, const Workspace &ws, hipStream_t s, int stage) {
@@ -835,8 +845,7 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int
     a.k = k;
     a.D = D;
     a.F = F;
-    a.hb = ws.pf_hb;
-    a.hf = f32 ? ws.h : nullptr;
+    a.hf = ws.h;
     a.y = y;
     a.ypart = f32 ? ws.ypart : nullptr;
     a.expert_bytes = fmt_bytes(MOE_Q2K, (int64_t)F * D);
@@ -868,6 +877,7 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int
             sg.Fs = Fs;
             sg.D = D;
             sg.hs = ws.pf_hsb;
+            sg.hs_lo = ws.pf_hsb_lo;
             pf_sg_gemm_kernel<0><<<dim3(Fs / 128, (T + kSgM - 1) / kSgM), 512, 0, s>>>(sg);
         }
     }
@@ -904,14 +914,15 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int
             else pf_gemm_kernel<1, 8><<<(unsigned)(((ntmax + 7) / 8) * 8 * (D / 512)), 512, 0, s>>>(dn);
             return launch_combine(d, x, T, x_type, r, y, flags, ws, s);
         }
-        pf_prep_rows_kernel<MOE_BF16><<<(unsigned)P, 256, 0, s>>>(ws.pf_hb, F, ws.pf_hq, ws.pf_hs, ws.pf_hinv,
-                                                                  PfPrepShared{nullptr, (int)P, nullptr, 0, nullptr, nullptr, -1,
-                                                                               nullptr, nullptr, nullptr, nullptr, nullptr,
-                                                                               nullptr});
+        pf_prep_rows_kernel<MOE_F32><<<(unsigned)P, 256, 0, s>>>(ws.h, F, ws.pf_hq, ws.pf_hs, ws.pf_hinv,
+                                                                 PfPrepShared{nullptr, (int)P, nullptr, 0, nullptr, nullptr, -1,
+                                                                              nullptr, nullptr, nullptr, nullptr, nullptr,
+                                                                              nullptr});
         if (Fs > 0) {
             const int64_t nw = (int64_t)Fs * D;
             SgArgs sg{};
             sg.a = ws.pf_hsb;
+            sg.a_lo = ws.pf_hsb_lo;
             sg.wh = ws.pf_shw + 2 * nw;
             sg.wl = ws.pf_shw + 5 * nw;
             sg.T = T;

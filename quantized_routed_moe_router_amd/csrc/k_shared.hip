@@ -153,7 +153,7 @@ __global__ void __launch_bounds__(64 * kSgqWaves) sgq_gemm_kernel(SgqArgs a) {
                 }
                 if (t < a.T) {
                     const float s = a.ainv[t];
-                    a.out[(int64_t)t * a.ld + 8 * blockIdx.x + c] = swiglu_h(gs * s, us * s, 0);
+                    a.out[(int64_t)t * a.ld + 8 * blockIdx.x + c] = swiglu_h(gs * s, us * s);
                 }
             }
         } else {

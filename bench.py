@@ -10,9 +10,15 @@ DeepSeek-V4-Flash-shaped layer (n_embd 4096, 256 routed experts, top-6, FFN
 width 2048, Q2K routed experts, Q8_0 shared expert, fp32 router), weights
 drawn from N(0, 0.02) and encoded, activations N(0, 1).
 
+The same run then measures the metric's prefill clause on the same resident
+layer: 2048 token rows of bf16 activations through the matrix-core grouped
+GEMMs, reported as the "prefill_2048" object of the line (its own tokens/s,
+MFMA roofline and CPU baseline).
+
 Cold-cache timing: step i runs on device replica i % R of the layer (R x
 2.14 GB, far above the 256 MB last-level cache) with token i % 64, so no
 step finds the previous steps' weights in cache and the routing varies.
+Steps are timed with HIP events on the stream that replays them.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -45,11 +51,19 @@ def parse():
                     choices=["decode_b1", "decode_b32", "prefill_2048", "stack43_b1", "stack43_b8", "hotlist_43x256",
                              "decode_b1_q4k"])
     ap.add_argument("--replicas", type=int, default=16)
+    ap.add_argument("--stack-layers", type=int, default=43,
+                    help="stack workloads: resident layers (43 = the whole stack; fewer for counter passes)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch every step eagerly (for counter profiling)")
     ap.add_argument("--copy-calib", type=float, default=0.0, metavar="MB",
                     help="only run 20 plain device copies of MB megabytes (scale reference for HBM counters)")
+    ap.add_argument("--read-stream", action="store_true",
+                    help="only measure the plain read-stream ceiling (moe_read_stream) at several sizes")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="decode_b1 only: skip the prefill_2048 measurement that the default run adds")
+    ap.add_argument("--prefill-cpu-seconds", type=float, default=10.0,
+                    help="budget of the oracle CPU baseline of the prefill_2048 measurement")
     return ap.parse_args()
 
 
@@ -75,6 +89,9 @@ def main():
     if args.copy_calib > 0:
         copy_calib(args.copy_calib)
         return
+    if args.read_stream:
+        read_stream(args)
+        return
 
     if args.workload.startswith("stack43"):
         run_stack(args, int(args.workload.split("_b")[1]))
@@ -83,10 +100,8 @@ def main():
         run_hotlist(args)
         return
 
-    import numpy as np
     import torch
 
-    import quantized_routed_moe_router_amd as moe
     import synth
 
     torch.cuda.set_device(0)
@@ -98,49 +113,99 @@ def main():
     else:
         L = synth.flash_layer()
     log("layer generated in %.1f s" % (time.time() - t0))
-    if args.workload in ("decode_b1", "decode_b1_q4k"):
+    reps = resident_replicas(L, max(1, args.replicas))
+    line = measure_layer(args, args.workload, L, reps, args.cpu_seconds)
+    line["context"] = PAGES_CONTEXT
+    if args.workload == "decode_b1" and not args.no_prefill:
+        # the metric's prefill clause, measured in the same run on the same
+        # resident layer: bf16 prefill of 2048 token rows on the matrix cores
+        pf = measure_layer(args, "prefill_2048", L, reps, args.prefill_cpu_seconds)
+        for key in ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "data"):
+            pf.pop(key, None)
+        line["prefill_2048"] = pf
+    print(json.dumps(line), flush=True)
+
+
+# The pages' own figure, for context only: the whole model (attention and all
+# 43 layers) on another machine ("DwarfStar Native Inference Engine",
+# performance table).
+PAGES_CONTEXT = {
+    "pages_generation_tokens_s": 39.35,
+    "pages_prefill_tokens_s": 790.18,
+    "pages_hardware": "MacBook Pro M5 Max 128 GB (Metal), whole DeepSeek-V4-Flash with attention, ctx 2048",
+    "note": "context only: another machine and the whole model, not this block alone",
+}
+
+
+def resident_replicas(L, R):
+    """R device copies of the layer (the bench rotates them so that every
+    step reads weights that are not in the 256 MB last-level cache)."""
+    import numpy as np
+    import torch
+
+    import quantized_routed_moe_router_amd as moe
+    dev = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    base = moe.LayerWeights(L.n_embd, L.n_expert, L.n_expert_used, L.n_ff_exp, L.n_ff_shared, L.gate_fmt,
+                            L.up_fmt, L.down_fmt, L.shared_fmt, dev(L.router_w), dev(L.gate), dev(L.up),
+                            dev(L.down), dev(L.sh_gate), dev(L.sh_up), dev(L.sh_down), None, L.route_scale)
+    reps = [base]
+    for _ in range(R - 1):
+        reps.append(moe.LayerWeights(**{f: (getattr(base, f).clone() if isinstance(getattr(base, f), torch.Tensor)
+                                            else getattr(base, f)) for f in base.__dataclass_fields__}))
+    torch.cuda.synchronize()
+    log("%d replicas resident (%.1f GB)" % (R, R * (base.gate.numel() * 3 + base.sh_gate.numel() * 3) / 1e9))
+    return reps
+
+
+def measure_layer(args, workload, L, reps, cpu_seconds):
+    """One workload on the resident replicas: K timed steps of one forward
+    each (graph replays, timed with HIP events on the stream), the per-call
+    spread, the dominant kernel's launch time, and the CPU oracle beside it."""
+    import copy
+
+    import numpy as np
+    import torch
+
+    import quantized_routed_moe_router_amd as moe
+    import synth
+
+    if workload in ("decode_b1", "decode_b1_q4k"):
         T, n_x = 1, 64
         x_all = synth.activations(1, n_x, L.n_embd)
         mode = moe.F32
-    elif args.workload == "decode_b32":
+        bias = None
+    elif workload == "decode_b32":
         T, n_x = 32, 8
         x_all = synth.activations(2, 32 * n_x, L.n_embd)
-        L.router_bias = synth.zipf_bias(2, L.n_expert)
+        bias = synth.zipf_bias(2, L.n_expert)
         mode = moe.F32
     else:
         T, n_x = 2048, 1
         x_all = synth.activations(3, 2048, L.n_embd)
         mode = moe.BF16
-
-    dev = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    base = moe.LayerWeights(L.n_embd, L.n_expert, L.n_expert_used, L.n_ff_exp, L.n_ff_shared, L.gate_fmt,
-                            L.up_fmt, L.down_fmt, L.shared_fmt, dev(L.router_w), dev(L.gate), dev(L.up),
-                            dev(L.down), dev(L.sh_gate), dev(L.sh_up), dev(L.sh_down), dev(L.router_bias),
-                            L.route_scale)
-    R = max(1, args.replicas)
-    reps = [base]
-    for _ in range(R - 1):
-        reps.append(moe.LayerWeights(**{f: (getattr(base, f).clone() if isinstance(getattr(base, f), torch.Tensor)
-                                            else getattr(base, f)) for f in base.__dataclass_fields__}))
+        bias = None
+    Lw = copy.copy(L)
+    Lw.router_bias = bias
+    if bias is not None:  # the same weights with the router bias attached
+        bd = torch.from_numpy(bias).cuda()
+        reps = [copy.copy(W) for W in reps]
+        for W in reps:
+            W.router_bias = bd
+    R = len(reps)
+    base = reps[0]
     if mode == moe.BF16:
         xs = torch.from_numpy(synth.to_bf16_bits(x_all).view(np.int16)).cuda().view(torch.bfloat16)
     else:
-        xs = dev(x_all)
+        xs = torch.from_numpy(np.ascontiguousarray(x_all)).cuda()
     xin = [xs[(i % n_x) * T:(i % n_x) * T + T] for i in range(n_x)]
     ws = moe.alloc_workspace(base, T, mode)
     r = moe.Routing(T, L.n_expert_used, L.n_expert)
     y = torch.zeros((T, L.n_embd), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
-    log("%d replicas resident (%.1f GB)" % (R, R * (base.gate.numel() * 3 + base.sh_gate.numel() * 3) / 1e9))
 
-    # The four stages of one forward.
+    # One forward of the block.
     def step(i):
-        W = reps[i % R]
-        x = xin[i % n_x]
-        moe.layer_forward_stage(W, x, y, ws, moe.STAGE_ROUTER, routing=r)
-        moe.layer_forward_stage(W, x, y, ws, moe.STAGE_ROUTE, routing=r)
-        moe.layer_forward_stage(W, x, y, ws, moe.STAGE_GATE_UP, routing=r)
-        moe.layer_forward_stage(W, x, y, ws, moe.STAGE_DOWN_COMBINE, routing=r)
+        moe.layer_forward(reps[i % R], xin[i % n_x], y, ws, routing=r)
 
     for i in range(args.warmup):
         step(i)
@@ -148,20 +213,25 @@ def main():
 
     # One graph holds R consecutive steps (one per replica).  Replaying it is
     # how a decode loop issues the block without per-kernel host overhead.
-    # --no-graph launches every step eagerly instead (counter profiling).
+    # The K steps are timed with HIP events on the replay stream (the host
+    # clock is kept beside them); --no-graph launches every step eagerly
+    # instead (counter profiling).
     K = args.steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    graphs, single = [], []
     if args.no_graph:
-        plan = []
         torch.cuda.synchronize()
         t_start = time.perf_counter()
+        ev0.record()
         for i in range(K):
             step(i)
+        ev1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_start
+        n_replays = 0
     else:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
-        graphs = []
         with torch.cuda.stream(side):
             for n in sorted({R, K % R} - {0}, reverse=True):
                 g = torch.cuda.CUDAGraph()
@@ -169,6 +239,11 @@ def main():
                     for i in range(n):
                         step(i)
                 graphs.append((n, g))
+            for i in range(R):  # one step per graph, for the per-call spread
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    step(i)
+                single.append(g)
         torch.cuda.current_stream().wait_stream(side)
         full = [g for n, g in graphs if n == R]
         rest = [g for n, g in graphs if n != R]
@@ -177,18 +252,36 @@ def main():
             g.replay()
         torch.cuda.synchronize()
         t_start = time.perf_counter()
+        ev0.record()
         for g in plan:
             g.replay()
+        ev1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_start
-    ms_step = 1000.0 * wall / K
+        n_replays = len(plan)
+    ms_step = ev0.elapsed_time(ev1) / K
+    # per-call spread: 64 single-step replays queued behind a spin kernel,
+    # an event between consecutive calls
+    spread = None
+    if single:
+        n_calls = 64
+        evc = [torch.cuda.Event(enable_timing=True) for _ in range(n_calls + 1)]
+        torch.cuda._sleep(2000000)
+        evc[0].record()
+        for j in range(n_calls):
+            single[j % R].replay()
+            evc[j + 1].record()
+        torch.cuda.synchronize()
+        per = np.array([evc[j].elapsed_time(evc[j + 1]) * 1000.0 for j in range(n_calls)])
+        spread = [round(float(np.percentile(per, q)), 2) for q in (10, 50, 90)]
+
     # The dominant kernel's launch time: HIP events on the launch stream
-    # around a run of R back-to-back stage-3 launches, one per weight replica
-    # (each reads cold weights), after stages 1-2 of one input; 8 such runs
-    # over different inputs.  Events inside a captured graph do not time, and
-    # a pair of events around a single launch also holds its dispatch
-    # latency, so the run is long and a bounded spin kernel ahead of it lets
-    # the host queue the whole run before the GPU reaches it.
+    # around a run of R back-to-back launches, one per weight replica (each
+    # reads cold weights), on the routing of one input; 8 such runs over
+    # different inputs.  Events inside a captured graph do not time, and a
+    # pair of events around a single launch also holds its dispatch latency,
+    # so the run is long and a bounded spin kernel ahead of it lets the host
+    # queue the whole run before the GPU reaches it.
     n_runs = 8
     # the grouped-GEMM path (many rows, Q2K experts): stage 5 is its routed
     # gate/up kernel alone; elsewhere stage 3 is the gate/up kernel
@@ -213,8 +306,8 @@ def main():
     times = [a.elapsed_time(b) / R for a, b in evs]
     gateup_ms = float(np.median(times))
     gateup_p10, gateup_p90 = float(np.percentile(times, 10)), float(np.percentile(times, 90))
-    log("timed %d steps in %.3f s (%d graph replays); gate/up avg %.2f us (%s)" % (
-        K, wall, len(plan), gateup_ms * 1e3, ev_src))
+    log("%s: timed %d steps, %.4f ms per step by HIP events (host clock %.4f ms, %d graph replays); "
+        "gate/up avg %.2f us (%s)" % (workload, K, ms_step, 1000.0 * wall / K, n_replays, gateup_ms * 1e3, ev_src))
 
     # routing of every distinct input, outside the timed region, for the byte counts
     n_unique = []
@@ -229,7 +322,7 @@ def main():
     dn_expert = synth.tensor_bytes(L.down_fmt, D * F)
     sh_gu = 2 * synth.tensor_bytes(L.shared_fmt, Fs * D)
     sh_dn = synth.tensor_bytes(L.shared_fmt, D * Fs)
-    router_b = D * L.n_expert * 4 + (L.n_expert * 4 if L.router_bias is not None else 0)
+    router_b = D * L.n_expert * 4 + (L.n_expert * 4 if bias is not None else 0)
     step_bytes = router_b + nu * (gu_expert + dn_expert) + sh_gu + sh_dn + T * D * xb + T * D * 4
     # the timed launch holds the routed experts' gate/up only: the decode
     # kernel (T <= 16) or the grouped GEMM (stage 5); the other batched
@@ -238,9 +331,9 @@ def main():
     if small:  # the decode gate/up kernel this layer takes
         kernel_name = "dec_k3_q2k4096_kernel" if L.gate_fmt == synth.Q2K and D == 4096 else "dec_k3_kernel"
         gateup_bytes = nu * gu_expert + T * D * xb + T * k * F * 4
-    elif gemm:  # x codes (2 bytes per value) in, h out (bf16 or fp32)
+    elif gemm:  # x codes (2 bytes per value) in, h out (fp32)
         kernel_name = "pf_gemm_kernel"
-        gateup_bytes = nu * gu_expert + T * D * 2 + T * k * F * xb
+        gateup_bytes = nu * gu_expert + T * D * 2 + T * k * F * 4
     else:
         kernel_name = "large_gateup_kernel"
         gateup_bytes = nu * gu_expert + T * D * xb + T * k * F * 4 + sh_gu + T * Fs * 4
@@ -254,7 +347,7 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(L, x_all, T, mode, args.cpu_seconds)
+        cpu = cpu_baseline(Lw, x_all, T, mode, cpu_seconds)
 
     line = {
         "metric": METRIC,
@@ -268,15 +361,22 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if mode == moe.BF16 else "f32",
+        "numerics": ("%s x, fp32 h and y; the exact integer codes of the weights against activations coded "
+                     "as int16 (per group of 16 values for a few rows, per row on the matrix cores), int32 "
+                     "sums scaled in fp32" % ("bf16" if mode == moe.BF16 else "fp32")),
         "data": "synthetic",
         "config": {
-            "workload": args.workload,
+            "workload": workload,
             "tokens_per_step": T,
             "n_embd": D, "n_expert": L.n_expert, "n_expert_used": k, "n_ff_exp": F, "n_ff_shared": Fs,
             "formats": "%s gate/up/down, Q8_0 shared, fp32 router" % ("Q4K" if L.gate_fmt == synth.Q4K else "Q2K"),
             "cache": "cold: %d device replicas rotated, %d distinct inputs" % (R, n_x),
             "launch": "hipGraph of %d steps, replayed" % R,
         },
+        "timing": "HIP events on the replay stream around the %d timed steps" % K,
+        "wall_ms_per_step": round(1000.0 * wall / K, 5),
+        "call_us_p10_p50_p90": spread,
+        "call_timing": "64 single-step graph replays queued back to back, an event between consecutive calls",
         "hbm_gbps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
         "algorithmic_bytes_per_step": int(step_bytes),
         "tflops": round(flops / (ms_step * 1e-3) / 1e12, 2),
@@ -288,7 +388,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(kernel_name, args.workload),
+            "traffic": measured_traffic(kernel_name, workload),
             "bytes_per_launch": int(gateup_bytes),
             "avg_launch_us": round(gateup_ms * 1e3, 3),
             "launch_us_p10_p90": [round(gateup_p10 * 1e3, 3), round(gateup_p90 * 1e3, 3)],
@@ -303,7 +403,70 @@ def main():
             "frac": round(tf / BF16_PEAK_TFLOPS, 4), "flops_per_launch": gateup_flops,
             "hbm_gbps": round(achieved, 1),
         })
-    print(json.dumps(line), flush=True)
+        line["mfma_pct_of_bf16_peak_whole_step"] = round(100.0 * flops / (ms_step * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                                                         2)
+    del ws, y, xs
+    torch.cuda.empty_cache()
+    return line
+
+
+def read_stream(args):
+    """The HBM bandwidth one launch of a plain read reaches (moe_read_stream),
+    at the sizes of this block's kernels and beyond: back-to-back launches
+    over rotating buffers (at least 1 GB in all, so no launch finds its data
+    in the 256 MB last-level cache), HIP events around each run of launches,
+    median per launch.  Also the cost of an almost empty launch."""
+    import numpy as np
+    import torch
+
+    import quantized_routed_moe_router_amd as moe
+    torch.cuda.set_device(0)
+    out = []
+    for mb in (4, 9, 18, 33, 80, 256, 1024):
+        nbytes = mb * (1 << 20)
+        nbuf = max(4, (1 << 30) // nbytes + 1)
+        bufs = [torch.ones(nbytes // 4, dtype=torch.float32, device="cuda") for _ in range(nbuf)]
+        blocks = max(1, min(4096, nbytes // 16 // (256 * 4)))
+        sink = torch.zeros(4 * blocks, dtype=torch.int32, device="cuda")
+        for bfr in bufs[:2]:
+            moe.read_stream(bfr, sink)
+        runs = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda._sleep(1000000)
+            a.record()
+            for bfr in bufs:
+                moe.read_stream(bfr, sink)
+            b.record()
+            torch.cuda.synchronize()
+            runs.append(a.elapsed_time(b) * 1000.0 / nbuf)
+        us = float(np.median(runs))
+        out.append({"mb": mb, "bytes": nbytes, "blocks": blocks, "us_per_launch": round(us, 3),
+                    "gbps": round(nbytes / (us * 1e-6) / 1e9, 1)})
+        log("read stream %5d MB: %.2f us per launch, %.0f GB/s" % (mb, us, out[-1]["gbps"]))
+        del bufs
+        torch.cuda.empty_cache()
+    # an almost empty launch (16 bytes, one workgroup), 256 of them captured
+    # in a graph and replayed, so that the host's launch rate plays no part
+    tiny = torch.ones(4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            for _ in range(256):
+                moe.read_stream(tiny, sink)
+    torch.cuda.current_stream().wait_stream(side)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    print(json.dumps({"read_stream": out, "empty_launch_us": round(a.elapsed_time(b) * 1000.0 / 256, 3),
+                      "peak_gbps": HBM_PEAK_GBS}), flush=True)
 
 
 def measured_traffic(kernel, workload):
@@ -339,7 +502,7 @@ def run_stack(args, B):
     import synth
 
     torch.cuda.set_device(0)
-    n_layer = 43
+    n_layer = max(1, min(43, args.stack_layers))
     cb = synth.codebook(4)
     cbd = torch.from_numpy(np.ascontiguousarray(cb)).cuda()
     dev = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
@@ -375,10 +538,13 @@ def run_stack(args, B):
         step()
     torch.cuda.synchronize()
     K = args.steps
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     if args.no_graph:
         t_start = time.perf_counter()
+        ev0.record()
         for _ in range(K):
             step()
+        ev1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_start
     else:
@@ -392,11 +558,13 @@ def run_stack(args, B):
         g.replay()
         torch.cuda.synchronize()
         t_start = time.perf_counter()
+        ev0.record()
         for _ in range(K):
             g.replay()
+        ev1.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_start
-    ms_step = 1000.0 * wall / K
+    ms_step = ev0.elapsed_time(ev1) / K
 
     # the dominant kernel (stage 3: routed gate/up, CB2): events around runs
     # of back-to-back stage-3 launches, one per layer (cold weights), on the
@@ -437,8 +605,8 @@ def run_stack(args, B):
                 break
         per_layer = el / done
         cpu = {"value": round(B / (n_layer * per_layer), 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-               "sample": "%d pass(es) of layer 0 at %d token(s) in %.1f s, times 43 layers (nproc %d)" % (
-                   done, B, el, os.cpu_count() or 0)}
+               "sample": "%d pass(es) of layer 0 at %d token(s) in %.1f s, times %d layers (nproc %d)" % (
+                   done, B, el, n_layer, os.cpu_count() or 0)}
     kernel_name = "dec_k3_cb24096_kernel" if D == 4096 else "dec_k3_kernel"
     line = {
         "metric": METRIC,
@@ -457,8 +625,10 @@ def run_stack(args, B):
             "workload": args.workload, "tokens_per_step": B, "n_layer": n_layer,
             "n_embd": D, "n_expert": W0.n_expert, "n_expert_used": W0.n_expert_used, "n_ff_exp": W0.n_ff_exp,
             "n_ff_shared": W0.n_ff_shared, "formats": "CB2 gate/up, Q2K down, Q8_0 shared, fp32 router",
-            "weights": "code-sampled per layer", "launch": "hipGraph of one 43-block step, replayed",
+            "weights": "code-sampled per layer", "launch": "hipGraph of one %d-block step, replayed" % n_layer,
         },
+        "timing": "HIP events on the replay stream around the %d timed steps" % K,
+        "wall_ms_per_step": round(1000.0 * wall / K, 5),
         "hbm_gbps": round(n_layer * layer_bytes / (ms_step * 1e-3) / 1e9, 1),
         "algorithmic_bytes_per_step": int(n_layer * layer_bytes),
         "unique_experts_layer0": nu,

@@ -205,6 +205,16 @@ int moe_rmsnorm(const float *x, const float *gamma, float eps, int32_t T, int32_
 int moe_dequant(int32_t type, const void *src, int64_t n_weights, const int8_t *codebook, int32_t out_type,
                 void *dst, void *stream, char *err, size_t errlen);
 
+/* A plain read of `bytes` (a multiple of 16) of device memory at src, every
+ * 16-byte unit once, by sink_words / 4 workgroups of 256 threads; sink
+ * (device, sink_words words, a multiple of 4) receives one XOR-fold per wave
+ * so that no read is dropped.  The bandwidth one launch of a pure stream
+ * reaches, beside the 8 TB/s HBM figure, for judging the kernels' rooflines
+ * (the measurement plan of the block: the achievable HBM bandwidth next to
+ * the specification).  bytes = 0 enqueues nothing. */
+int moe_read_stream(const void *src, int64_t bytes, uint32_t *sink, int32_t sink_words, void *stream, char *err,
+                    size_t errlen);
+
 /* Library version string (static storage). */
 const char *moe_version(void);
 

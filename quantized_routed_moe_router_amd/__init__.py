@@ -64,8 +64,9 @@ _lib.moe_dequant.argtypes = [_I32, _P, _I64, _P, _I32, _P, _P, ctypes.c_char_p, 
 _lib.moe_version.restype = ctypes.c_char_p
 _lib.moe_count_selections.argtypes = [_P, _I32, _I32, _I32, _I32, _P, _P, ctypes.c_char_p, _SZ]
 _lib.moe_hotlist.argtypes = [_P, _I32, _P, _P, _P, ctypes.c_char_p, _SZ]
+_lib.moe_read_stream.argtypes = [_P, _I64, _P, _I32, _P, ctypes.c_char_p, _SZ]
 for _f in ("moe_route", "moe_expert_ffn", "moe_layer_forward_stage", "moe_layer_forward", "moe_rmsnorm", "moe_dequant",
-           "moe_count_selections", "moe_hotlist"):
+           "moe_count_selections", "moe_hotlist", "moe_read_stream"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -350,3 +351,15 @@ def dequant(fmt, src, n_weights, out, codebook=None, stream=None):
     ot = BF16 if out.dtype == torch.bfloat16 else F32
     _check(_lib.moe_dequant(fmt, _ptr(src), n_weights, _ptr(codebook), ot, _ptr(out), _stream(stream), err, 512),
            err)
+
+
+def read_stream(src, sink, stream=None):
+    """One plain read of every byte of src (a contiguous device tensor whose
+    size is a multiple of 16 bytes); sink: int32 device tensor of 4*blocks words."""
+    _tensor("sink", sink, torch.int32)
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    nbytes = src.numel() * src.element_size()
+    _one_cuda_device(src=src, sink=sink)
+    err = ctypes.create_string_buffer(512)
+    _check(_lib.moe_read_stream(_ptr(src), nbytes, _ptr(sink), sink.numel(), _stream(stream), err, 512), err)

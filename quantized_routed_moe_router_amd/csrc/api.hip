@@ -237,6 +237,18 @@ int moe_dequant(int32_t type, const void *src, int64_t n, const int8_t *codebook
     return device_status(launch_dequant(type, src, n, codebook, out_type, dst, (hipStream_t)stream), err, errlen);
 }
 
+int moe_read_stream(const void *src, int64_t bytes, uint32_t *sink, int32_t sink_words, void *stream, char *err,
+                    size_t errlen) {
+    if (bytes < 0 || bytes % 16) return fail(err, errlen, MOE_EINVAL, "bytes must be a multiple of 16 (got %lld)",
+                                             (long long)bytes);
+    if (sink_words < 4 || sink_words % 4)
+        return fail(err, errlen, MOE_EINVAL, "sink_words must be a positive multiple of 4 (got %d)", sink_words);
+    if (bytes == 0) return MOE_OK;
+    if (!src || !sink) return fail(err, errlen, MOE_EINVAL, "src and sink must be set");
+    if (!aligned16(src)) return fail(err, errlen, MOE_EALIGN, "src must be 16-byte aligned");
+    return device_status(launch_read_stream(src, bytes, sink, sink_words / 4, (hipStream_t)stream), err, errlen);
+}
+
 const char *moe_version(void) { return "moe-gfx950 0.1"; }
 
 }  // extern "C"

@@ -838,5 +838,6 @@ hipError_t launch_rmsnorm(const float *x, const float *gamma, float eps, int32_t
                           hipStream_t s);
 hipError_t launch_dequant(int32_t type, const void *src, int64_t n, const int8_t *cb, int32_t out_type, void *dst,
                           hipStream_t s);
+hipError_t launch_read_stream(const void *src, int64_t bytes, uint32_t *sink, int32_t blocks, hipStream_t s);
 
 }  // namespace moe

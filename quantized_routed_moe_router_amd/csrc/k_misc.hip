@@ -1,6 +1,7 @@
 // k_misc.hip - RMSNorm before each block ("Understanding Dwarf Star", 5.2.1
-// norm + residual, 5.6.2 step 1) and the dequantization test hook
-// ("Understanding Dwarf Star", 2.8.2 steps 1-3).
+// norm + residual, 5.6.2 step 1), the dequantization test hook
+// ("Understanding Dwarf Star", 2.8.2 steps 1-3), and a plain read stream
+// that measures the HBM bandwidth one launch can reach.
 #include "common.h"
 
 namespace moe {
@@ -112,6 +113,33 @@ hipError_t launch_dequant(int32_t type, const void *src, int64_t n, const int8_t
     int64_t units = type == MOE_Q8_0 ? n / 32 : n / 64;
     dequant_kernel<<<(unsigned)((units + 255) / 256), 256, 0, s>>>(type, (const uint8_t *)src, units, cb,
                                                                  out_type == MOE_BF16, dst);
+    return hipGetLastError();
+}
+
+// Plain read stream: every 16-byte unit of src read once (four loads in
+// flight per thread, the grid striding over the buffer), folded by XOR into
+// one word per wave so that no load can be dropped.  sink: gridDim.x * 4
+// words.
+__global__ void __launch_bounds__(256) read_stream_kernel(const u32x4 *__restrict__ src, int64_t n16,
+                                                          uint32_t *__restrict__ sink) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    uint32_t acc = 0;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (; i + 3 * stride < n16; i += 4 * stride) {
+        const u32x4 a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+        acc ^= a[0] ^ a[1] ^ a[2] ^ a[3] ^ b[0] ^ b[1] ^ b[2] ^ b[3] ^ c[0] ^ c[1] ^ c[2] ^ c[3] ^ d[0] ^ d[1] ^
+               d[2] ^ d[3];
+    }
+    for (; i < n16; i += stride) {
+        const u32x4 a = src[i];
+        acc ^= a[0] ^ a[1] ^ a[2] ^ a[3];
+    }
+    for (int o = 32; o > 0; o >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, o, kWave);
+    if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = acc;
+}
+
+hipError_t launch_read_stream(const void *src, int64_t bytes, uint32_t *sink, int32_t blocks, hipStream_t s) {
+    read_stream_kernel<<<blocks, 256, 0, s>>>((const u32x4 *)src, bytes / 16, sink);
     return hipGetLastError();
 }
 

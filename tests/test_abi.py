@@ -23,7 +23,8 @@ def test_exports_every_declared_symbol():
     import quantized_routed_moe_router_amd as moe
     names = _declared()
     assert {"moe_route", "moe_expert_ffn", "moe_layer_forward", "moe_layer_forward_stage", "moe_workspace_size",
-            "moe_rmsnorm", "moe_dequant", "moe_version", "moe_count_selections", "moe_hotlist"} <= names
+            "moe_rmsnorm", "moe_dequant", "moe_version", "moe_count_selections", "moe_hotlist",
+            "moe_read_stream"} <= names
     for n in names:
         assert hasattr(moe._lib, n), n
     assert moe.version().startswith("moe-gfx950")
@@ -228,3 +229,12 @@ def test_binding_rejects_bad_tensors_before_the_library(monkeypatch, case, exc, 
     monkeypatch.setattr(moe, "_lib", _NoLibrary())
     with pytest.raises(exc, match=text):
         call()
+
+
+def test_read_stream_validates():
+    import quantized_routed_moe_router_amd as moe
+    err = ctypes.create_string_buffer(256)
+    assert moe._lib.moe_read_stream(0x1000, 24, 0x2000, 4, None, err, 256) == -1      # not a multiple of 16
+    assert moe._lib.moe_read_stream(0x1000, 32, 0x2000, 6, None, err, 256) == -1      # sink not a multiple of 4
+    assert moe._lib.moe_read_stream(0x1008, 32, 0x2000, 4, None, err, 256) == -2      # misaligned
+    assert moe._lib.moe_read_stream(None, 0, None, 4, None, err, 256) == 0            # nothing to read

@@ -69,10 +69,13 @@ def test_decode_small_batches(flash, T, zipf):
     _run(wl, W)
 
 
-@pytest.mark.parametrize("E,k,Fs,accumulate", [(16, 4, 0, False), (12, 6, 2048, True), (8, 1, 2048, False)])
+@pytest.mark.parametrize("E,k,Fs,accumulate", [(16, 4, 0, False), (12, 6, 2048, True), (8, 1, 2048, False),
+                                                (6, 6, 0, True), (40, 3, 2048, False)])
 def test_one_token_full_width(E, k, Fs, accumulate):
     # one token through full-width experts (n_embd 4096, FFN 2048) with fewer
-    # slots than waves, with and without the shared expert, and adding into y
+    # slots than waves, with and without the shared expert, and adding into
+    # y; two calls on one workspace and the four stages one by one give the
+    # same bits, routing arrays included.
     import torch
 
     import quantized_routed_moe_router_amd as moe
@@ -80,11 +83,26 @@ def test_one_token_full_width(E, k, Fs, accumulate):
     x = synth.activations(8, 1, 4096)
     y0 = synth.activations(9, 1, 4096) if accumulate else np.zeros((1, 4096), np.float32)
     W = gu.upload(L)
-    y = gu.dev(y0)
+    xd = gu.dev(x)
+    _log("one token E=%d k=%d Fs=%d accumulate=%s on the GPU" % (E, k, Fs, accumulate))
     ws = moe.alloc_workspace(W, 1)
-    moe.layer_forward(W, gu.dev(x), y, ws, accumulate=accumulate)
+    outs = []
+    for rep in range(2):  # the second call reuses the workspace (and its barrier counter)
+        y = gu.dev(y0)
+        r = moe.Routing(1, k, E)
+        moe.layer_forward(W, xd, y, ws, routing=r, accumulate=accumulate)
+        outs.append((y, r))
+    ys = gu.dev(y0)
+    rs = moe.Routing(1, k, E)
+    for st in (1, 2, 3, 4):
+        moe.layer_forward_stage(W, xd, ys, ws, st, routing=rs, accumulate=accumulate)
+    torch.cuda.synchronize()
+    for y, r in outs:
+        assert torch.equal(y, ys)
+        for name in ("topk_idx", "topk_w", "count", "offset", "perm", "pos", "active", "n_active"):
+            assert torch.equal(getattr(r, name), getattr(rs, name)), name
     y_ref, _, _ = oracle.moe_forward(L, x=x)
-    worst = gu.assert_close(y.cpu().numpy(), y_ref + y0)
+    worst = gu.assert_close(outs[0][0].cpu().numpy(), y_ref + y0)
     _log("one token E=%d k=%d Fs=%d: worst relative error %.3g" % (E, k, Fs, worst))
 
 

@@ -167,6 +167,22 @@ int moe_layer_forward_stage(const moe_layer_desc *desc, const void *x, int32_t T
                             uint32_t flags, const moe_routing *routing, int32_t stage, void *ws, size_t ws_bytes,
                             void *stream, char *err, size_t errlen);
 
+/* moe_layer_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation): the buffers live in a static scratch of
+ * 8 MiB per device (a file-scope device array, held until the process ends),
+ * so the call allocates nothing.  It takes the few-row schedule only: T <= 16
+ * and T*k <= 256 with Q2K, CB2 or Q4K routed experts (MOE_EUNSUPPORTED
+ * otherwise), and shapes whose buffers fit the scratch (MOE_EWORKSPACE
+ * otherwise; the DeepSeek-V4-Flash shape needs about 3.6 MB at 16 rows).
+ * The stream's device must be current.  Every call on one GPU shares that
+ * GPU's scratch, so calls that overlap on one GPU (other streams, other
+ * threads) race; nothing in the scratch needs to start at zero.  Arguments,
+ * errors and results as moe_layer_forward (the same kernels, so the same
+ * bits). */
+int moe_layer_forward_noalloc(const moe_layer_desc *desc, const void *x, int32_t T, int32_t x_type, float *y,
+                              uint32_t flags, const moe_routing *routing, void *stream, char *err, size_t errlen);
+
 /* Expert selection counts for the hot list ("The sparsity that pays for
  * everything else in DwarfStar", "Some experts run far more often than
  * others": a run counts expert selections per {layer, expert} and merges

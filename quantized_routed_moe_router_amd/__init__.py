@@ -65,8 +65,10 @@ _lib.moe_version.restype = ctypes.c_char_p
 _lib.moe_count_selections.argtypes = [_P, _I32, _I32, _I32, _I32, _P, _P, ctypes.c_char_p, _SZ]
 _lib.moe_hotlist.argtypes = [_P, _I32, _P, _P, _P, ctypes.c_char_p, _SZ]
 _lib.moe_read_stream.argtypes = [_P, _I64, _P, _I32, _P, ctypes.c_char_p, _SZ]
+_lib.moe_layer_forward_noalloc.argtypes = [ctypes.POINTER(LayerDesc), _P, _I32, _I32, _P, ctypes.c_uint32,
+                                           ctypes.POINTER(RoutingStruct), _P, ctypes.c_char_p, _SZ]
 for _f in ("moe_route", "moe_expert_ffn", "moe_layer_forward_stage", "moe_layer_forward", "moe_rmsnorm", "moe_dequant",
-           "moe_count_selections", "moe_hotlist", "moe_read_stream"):
+           "moe_count_selections", "moe_hotlist", "moe_read_stream", "moe_layer_forward_noalloc"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -297,6 +299,22 @@ def layer_forward(layer, x, y, ws, routing=None, accumulate=False, stream=None):
     _check(_lib.moe_layer_forward(ctypes.byref(d), _ptr(x), T, _xtype(x), _ptr(y),
                                   ACCUMULATE if accumulate else 0, ctypes.byref(r) if r is not None else None,
                                   _ptr(ws), ws.numel(), _stream(stream), err, 512), err)
+
+
+def layer_forward_noalloc(layer, x, y, routing=None, accumulate=False, stream=None):
+    """layer_forward on the library's static per-device scratch (no workspace,
+    no allocation); few rows only (see include/moe.h)."""
+    T = _rows(layer, x)
+    rt = _routing_tensors(layer, routing, T)
+    _tensor("y", y, torch.float32, (T, layer.n_embd))
+    _one_cuda_device(x=x, y=y, **rt, **_layer_tensors(layer))
+    d, err = layer.desc(), ctypes.create_string_buffer(512)
+    r = routing.struct() if routing is not None else None
+    with torch.cuda.device(x.device):  # the scratch is looked up on the current device
+        _check(_lib.moe_layer_forward_noalloc(ctypes.byref(d), _ptr(x), T, _xtype(x), _ptr(y),
+                                              ACCUMULATE if accumulate else 0,
+                                              ctypes.byref(r) if r is not None else None, _stream(stream), err, 512),
+               err)
 
 
 def rmsnorm(x, gamma, out, eps=1e-6, stream=None):

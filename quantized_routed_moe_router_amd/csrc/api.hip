@@ -3,10 +3,15 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 
 #include "common.h"
 
 using namespace moe;
+
+// The static scratch of moe_layer_forward_noalloc (see below).
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -121,6 +126,40 @@ int device_status(hipError_t e, char *err, size_t errlen) {
     return fail(err, errlen, MOE_EDEVICE, "HIP: %s", hipGetErrorString(e));
 }
 
+// ---- scratch of the entry point that allocates nothing -----------------------
+// A file-scope device array: every GPU the library runs on holds its own copy
+// until the process ends.  Host code never uses the array's name as an
+// address: its device address comes from hipGetSymbolAddress, once per
+// device, with that device current.
+constexpr int kMaxDevices = 64;
+
+std::mutex scratch_mu;
+void *scratch_addr[kMaxDevices];
+
+int scratch_of_current_device(void **out, char *err, size_t errlen) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return device_status(e, err, errlen);
+    if (dev < 0 || dev >= kMaxDevices) return fail(err, errlen, MOE_EDEVICE, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return device_status(e, err, errlen);
+        if (!p) return fail(err, errlen, MOE_EDEVICE, "no device address for the scratch array");
+        scratch_addr[dev] = p;
+    }
+    *out = scratch_addr[dev];
+    return MOE_OK;
+}
+
+// Bytes of workspace the few-row schedule reads and writes: it uses only the
+// buffers laid out before the many-row ones.
+size_t few_row_ws_bytes(const moe_layer_desc *d, int32_t T) {
+    char *const base = (char *)(uintptr_t)4096;  // any aligned address: only offsets are taken
+    return (size_t)((char *)workspace_layout(d, T, base).pf_xq - base);
+}
+
 }  // namespace
 
 extern "C" {
@@ -191,6 +230,34 @@ int moe_layer_forward_stage(const moe_layer_desc *d, const void *x, int32_t T, i
     Workspace w = workspace_layout(d, T, ws);
     RoutingPtrs r = routing ? from_routing(routing) : from_ws(w);
     return device_status(forward(d, x, T, x_type, r, y, flags, w, (hipStream_t)stream, stage), err, errlen);
+}
+
+int moe_layer_forward_noalloc(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, float *y,
+                              uint32_t flags, const moe_routing *routing, void *stream, char *err, size_t errlen) {
+    int rc = check_desc(d, err, errlen);
+    if (rc) return rc;
+    if (T < 0) return fail(err, errlen, MOE_EINVAL, "T must be >= 0 (T=%d)", T);
+    if (x_type != MOE_F32 && x_type != MOE_BF16)
+        return fail(err, errlen, MOE_EUNSUPPORTED, "x_type must be MOE_F32 or MOE_BF16");
+    if (routing && (rc = check_routing(routing, err, errlen))) return rc;
+    if (flags & ~(uint32_t)MOE_ACCUMULATE) return fail(err, errlen, MOE_EINVAL, "unknown flags 0x%x", flags);
+    if (T == 0) return MOE_OK;
+    if (!(small_path_ok(d, T) && small_route_ok(d, T)))
+        return fail(err, errlen, MOE_EUNSUPPORTED,
+                    "the entry point without allocation takes the few-row schedule only: T <= 16, T*k <= 256, "
+                    "Q2K, CB2 or Q4K experts (T=%d k=%d)",
+                    T, d->n_expert_used);
+    const size_t need = few_row_ws_bytes(d, T);
+    if (need > kScratchBytes)
+        return fail(err, errlen, MOE_EWORKSPACE, "%zu bytes of scratch needed, the static scratch holds %zu", need,
+                    kScratchBytes);
+    if (!x || !y) return fail(err, errlen, MOE_EINVAL, "x and y must be set");
+    if (!aligned16(x) || !aligned16(y)) return fail(err, errlen, MOE_EALIGN, "x and y must be 16-byte aligned");
+    void *ws = nullptr;
+    if ((rc = scratch_of_current_device(&ws, err, errlen))) return rc;
+    Workspace w = workspace_layout(d, T, ws);
+    RoutingPtrs r = routing ? from_routing(routing) : from_ws(w);
+    return device_status(forward(d, x, T, x_type, r, y, flags, w, (hipStream_t)stream, 0), err, errlen);
 }
 
 int moe_count_selections(const int32_t *topk_idx, int32_t T, int32_t k, int32_t E, int32_t layer, int64_t *counts,

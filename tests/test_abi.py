@@ -238,3 +238,20 @@ def test_read_stream_validates():
     assert moe._lib.moe_read_stream(0x1000, 32, 0x2000, 6, None, err, 256) == -1      # sink not a multiple of 4
     assert moe._lib.moe_read_stream(0x1008, 32, 0x2000, 4, None, err, 256) == -2      # misaligned
     assert moe._lib.moe_read_stream(None, 0, None, 4, None, err, 256) == 0            # nothing to read
+
+
+def test_noalloc_entry_point_validates_before_touching_the_device():
+    # the entry point without a workspace takes the few-row schedule only and
+    # rejects shapes whose buffers exceed its static scratch, before any HIP call
+    import quantized_routed_moe_router_amd as moe
+    err = ctypes.create_string_buffer(256)
+    f = moe._lib.moe_layer_forward_noalloc
+    d = _desc()
+    assert f(ctypes.byref(d), 0x80000, 17, 0, 0x100000, 0, None, None, err, 256) == -4  # beyond 16 rows
+    assert b"few-row" in err.value
+    big = _desc(n_expert=1024, n_expert_used=16, n_ff_exp=4096)  # 16 rows need more than the scratch
+    assert f(ctypes.byref(big), 0x80000, 16, 0, 0x100000, 0, None, None, err, 256) == -3
+    assert b"scratch" in err.value
+    assert f(ctypes.byref(d), None, 0, 0, None, 0, None, None, err, 256) == 0  # T = 0: nothing to do
+    assert f(ctypes.byref(d), 0x80008, 1, 0, 0x100000, 0, None, None, err, 256) == -2
+    assert f(ctypes.byref(d), 0x80000, 1, 0, 0x100000, 4, None, None, err, 256) == -1  # unknown flag

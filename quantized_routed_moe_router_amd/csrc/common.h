@@ -623,6 +623,38 @@ MOE_DEV void prep8_wave(float v, uint32_t *rec) {
     }
 }
 
+// The same records, four chunks per wave at once: row q (16 lanes) of the
+// wave takes one chunk, lane m of the row its values 4m..4m+3 in v.  The
+// bits are prep8_wave's: the maximum does not depend on order, and each
+// 32-value sum is the same tree of pairwise block sums (2, 4, 8, 16, 32
+// values, each lane's own block first; fp32 addition is commutative), here
+// in registers and DPP moves within the row instead of cross-lane shuffles.
+template <int CTRL>
+MOE_DEV float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+MOE_DEV void prep8_rows(f32x4 v, uint32_t *rec) {
+    const int m = threadIdx.x & 15;
+    float mx = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    float s = (v[0] + v[1]) + (v[2] + v[3]);
+    mx = fmaxf(mx, dpp_f32<0xB1>(mx));  // quad_perm [1,0,3,2]: lane m ^ 1
+    s += dpp_f32<0xB1>(s);
+    mx = fmaxf(mx, dpp_f32<0x4E>(mx));  // quad_perm [2,3,0,1]: lane m ^ 2
+    s += dpp_f32<0x4E>(s);
+    mx = fmaxf(mx, dpp_f32<0x141>(mx));  // row_half_mirror: lane 7 - m of its 8
+    s += dpp_f32<0x141>(s);
+    mx = fmaxf(mx, dpp_f32<0x140>(mx));  // row_mirror: lane 15 - m
+    float inv;
+    const float S = group_scale(mx, inv);
+    uint32_t h0, l0, h1, l1;
+    split2(v[0] * S, v[1] * S, h0, l0);
+    split2(v[2] * S, v[3] * S, h1, l1);
+    *(uint2 *)(rec + 2 * m) = uint2{h0, h1};
+    *(uint2 *)(rec + 32 + 2 * m) = uint2{l0, l1};
+    if ((m & 7) == 0) rec[64 + (m >> 3)] = __float_as_uint(s);
+    if (m == 0) *(uint2 *)(rec + 66) = uint2{__float_as_uint(inv), 0u};
+}
+
 MOE_DEV void load_q8_prep(const uint32_t *rec, XQ8 &p) {
     u32x4 *dst = (u32x4 *)&p;
 #pragma unroll

@@ -43,6 +43,7 @@ struct FfnArgs {
     SlotRec *slots;
     int nslots;
     int build_slots;  // K1 writes the records from a given routing
+    int k3_topk;      // one token: each routed gate/up block selects the top-k itself (no K2)
 };
 
 // Load the lane's 64 activations at element offset off of x (fp32 or bf16).

@@ -293,6 +293,170 @@ __global__ void __launch_bounds__(320) dec_k2_q8sg4096_kernel(FfnArgs a, int do_
     }
 }
 
+// K1 for one fp32 token at n_embd 4096 when the routed gate/up kernel selects
+// the top-k itself (no K2): block b computes router logit b and, with a
+// Q8_0 shared expert, 8 rows of the shared gate and of up -> hs, so the
+// latency-bound router rows run under the shared expert's weight stream.
+// Wave w works on column quarter w throughout.  It copies into its own LDS
+// area, in this order: x's quarter, router row b's quarter, then the shared
+// rows as the K2 kernel above lays them out.  From x in LDS it forms the
+// Q8_0 records of its 16 chunks (prep8_rows, the bits of K1's prep8_wave)
+// in the place the K2 kernel copies them to, and (blocks 0-15) chunk
+// 16 w + b's record for the routed Q2K or codebook rows.  The logit is
+// summed exactly as router_row_block sums it (lane l: 16 consecutive
+// columns of the quarter in ascending order in fp64, then the lanes by a
+// fixed butterfly, then the quarters in wave order), so both schedules give
+// the same logits.
+constexpr int kT1Xu = 256;                         // units of a 1024-value fp32 quarter
+constexpr int kT1WeightCopies = 16 * kSgRu / 64;   // 17
+constexpr int kT1Units = kSgXu + 16 * kSgRu + 2 * kT1Xu;  // records, rows, x, router: 1872
+static_assert(16 * kSgRu == 64 * kT1WeightCopies, "whole copies of the shared rows");
+
+template <int N>  // at most N of the wave's copies outstanding
+MOE_DEV void t1_wait() {
+    __builtin_amdgcn_sched_barrier(0);
+    vmem_wait_le<N>();
+    __builtin_amdgcn_sched_barrier(0);
+}
+template <int END>  // shared-row units [0, END) of the wave's area (after the records) have landed
+MOE_DEV void t1_wait_rows() {
+    t1_wait<kT1WeightCopies - (END + 63) / 64>();
+}
+
+__global__ void __launch_bounds__(256) dec_k1_t1_kernel(FfnArgs a) {
+    __shared__ __align__(16) u32x4 area[4][kT1Units];
+    __shared__ double rpart[4];
+    __shared__ float part[4][16];
+    const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const bool router = b < a.E, shared = b < a.Fs / 8;  // uniform over the block
+    u32x4 *my = area[wave];
+    float *xq = (float *)(my + kSgXu + 16 * kSgRu);  // x, columns 1024 w ..
+    float *rq = xq + 1024;                          // router row b, the same columns
+    const int row0 = 8 * b;
+    constexpr int RB = 4096 / 32 * kQ8Bytes;  // bytes of a shared row: 4352
+    {
+        const uint8_t *xs = (const uint8_t *)a.x + 4096 * wave;
+        const uint8_t *rs = (const uint8_t *)(a.router_w + (int64_t)min(b, a.E - 1) * 4096) + 4096 * wave;
+        const uint32_t lx = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(xq));
+        const uint32_t lr = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(rq));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16_m0(xs + 16 * (64 * i + lane), lx + 1024 * i);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16_m0(rs + 16 * (64 * i + lane), lr + 1024 * i);
+        if (shared) {
+            const uint8_t *gm = a.sh_gate + (int64_t)row0 * RB + 1088 * wave;
+            const uint8_t *um = a.sh_up + (int64_t)row0 * RB + 1088 * wave;
+            const uint32_t lb = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(my + kSgXu));
+#pragma unroll
+            for (int i = 0; i < kT1WeightCopies; ++i) {
+                const int v = 64 * i + lane, rw = v / kSgRu, o = v - rw * kSgRu;
+                const int q = rw >> 2, j = rw & 3;  // group q: gate 2q, 2q+1, up 2q, 2q+1
+                dma16_m0(((j & 2) ? um : gm) + (int64_t)(2 * q + (j & 1)) * RB + 16 * o, lb + 1024 * i);
+            }
+        }
+    }
+    // x's quarter has landed
+    if (shared) t1_wait<4 + kT1WeightCopies>();
+    else t1_wait<4>();
+    // Q8_0 records of the quarter's 16 chunks, four at a time
+    if (shared) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int c = 4 * r4 + (lane >> 4);
+            prep8_rows(*(const f32x4 *)(xq + 64 * c + 4 * (lane & 15)), (uint32_t *)(my + 17 * c));
+        }
+    }
+    // router row b's quarter has landed
+    if (shared) t1_wait<kT1WeightCopies>();
+    else t1_wait<0>();
+    if (router) {
+        double acc = 0.0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4 xv = *(const f32x4 *)(xq + 16 * lane + 4 * i), wv = *(const f32x4 *)(rq + 16 * lane + 4 * i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc = __builtin_fma((double)xv[j], (double)wv[j], acc);
+        }
+        acc = seg_sum_f64(acc, kWave);
+        if (lane == 0) rpart[wave] = acc;
+    }
+    // the routed rows' record of chunk 16 w + b (global stores: issued only
+    // once every copy of the wave has landed, as vmcnt counts them too)
+    auto routed_record = [&]() {
+        if (a.xp16 && b < 16) {
+            uint32_t *out = a.xp16 + (int64_t)4 * (16 * wave + b) * kRec16Dwords;
+            if (a.xp16_nat) prep16_wave<true>(xq[64 * b + lane], out);
+            else prep16_wave<false>(xq[64 * b + lane], out);
+        }
+    };
+    if (!shared) {
+        routed_record();
+        __syncthreads();
+        if (router && tid == 0)
+            a.logits[b] = (((rpart[0] + rpart[1]) + rpart[2]) + rpart[3]) + (a.router_bias ? (double)a.router_bias[b] : 0.0);
+        return;
+    }
+    const int r = lane >> 4, c = lane & 15;
+    const uint8_t *ab = (const uint8_t *)my;
+    XQ8 xr;
+    float v[4];
+    auto group = [&](int q) {
+        if (q == 0) load_q8_prep((const uint32_t *)(ab + 272 * c), xr);
+        v[q] = q8_dot2(q8_load(ab + 16 * (kSgXu + kSgRu * (4 * q + r)), 64 * c), xr);
+        pin_value(v[q]);
+    };
+    t1_wait_rows<4 * kSgRu>();
+    group(0);
+    t1_wait_rows<8 * kSgRu>();
+    group(1);
+    t1_wait_rows<12 * kSgRu>();
+    group(2);
+    t1_wait_rows<16 * kSgRu>();
+    group(3);
+    routed_record();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float sv = row16_sum(v[q]);
+        if (c == 0) part[wave][4 * q + r] = sv;  // [group][gate 2q, 2q+1, up 2q, 2q+1]
+    }
+    block_lds_sync();
+    if (router && tid == 0)
+        a.logits[b] = (((rpart[0] + rpart[1]) + rpart[2]) + rpart[3]) + (a.router_bias ? (double)a.router_bias[b] : 0.0);
+    if (tid < 8) {
+        const int q = tid >> 1, j = tid & 1;
+        float gs = 0.f, us = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            gs += part[w][4 * q + j];
+            us += part[w][4 * q + 2 + j];
+        }
+        a.hs[row0 + tid] = swiglu_h(gs, us);
+    }
+}
+
+// The slot record of a routed gate/up block.  With k3_topk (one token, no
+// K2) every wave selects the top-k from the router logits itself, so the
+// slot's expert is wave-uniform without a barrier: slot s is the expert of
+// rank s among the k (bucket position s, token 0), as the bucketing orders
+// them.  Wave 0 of block 0 also writes the routing and the slot records the
+// down kernel reads.
+MOE_DEV SlotRec k3_slot(const FfnArgs &a, int slot) {
+    if (!a.k3_topk) return uniform_slot(a.slots, slot);
+    const bool writer = blockIdx.x == 0 && threadIdx.x < kWave;  // uniform over the wave
+    const int my_e = select_topk(a.logits, a.E, a.k, a.route_scale, writer ? a.w_topk_idx : nullptr,
+                                 writer ? a.w_topk_w : nullptr);
+    if (writer)
+        bucket_one_token(my_e, a.k, a.E, a.w_count, a.w_offset, a.w_perm, a.w_pos, a.w_active, a.w_n_active,
+                         a.slots, a.nslots);
+    const int lane = threadIdx.x & 63;
+    int rank = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) rank += q < a.k && __builtin_amdgcn_readlane(my_e, q) < my_e;
+    const uint64_t hit = __ballot(lane < a.k && rank == slot);
+    const int e = hit ? __builtin_amdgcn_readlane(my_e, (int)__builtin_ctzll(hit)) : -1;
+    return make_slot(e, slot, 1, 0, 0);
+}
+
 // One block per (active slot, group g of 16 rows of the expert's gate and up):
 // the 16 rows of both are staged in LDS, wave w takes column part w % P of
 // the rows of row group w / P; the parts of a row are added in LDS in column
@@ -310,7 +474,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     if constexpr (GFMT == MOE_CB2) load_codebook(a.codebook, cb_lds);
     const int gpe = a.F / 16, slot = blockIdx.x / gpe, g = blockIdx.x % gpe;
-    const SlotRec rec = uniform_slot(a.slots, slot);
+    const SlotRec rec = k3_slot(a, slot);
     if (rec.e < 0) return;  // uniform over the block
     const int U = (int)fmt_bytes(GFMT, (int64_t)16 * a.D) / 16;  // 16 rows in 16-byte units
     const int64_t goff = (int64_t)rec.e * a.gu_expert_bytes + fmt_bytes(GFMT, (int64_t)16 * g * a.D);
@@ -389,16 +553,28 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
     __shared__ float part[4][32];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int gpe = a.F / 16, slot = blockIdx.x / gpe, g = blockIdx.x % gpe;
-    const SlotRec rec = uniform_slot(a.slots, slot);
-    if (rec.e < 0) return;  // uniform over the block
+    const uint32_t lb = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(wbuf) + 1024 * wave);
+    constexpr int kPre = kK3PXu / 256;  // copies 0-1 hold records only
+    // one token (k3_topk): its records do not depend on the slot, so their
+    // first copies go out before the selection
+    const int first = a.k3_topk ? kPre : 0;
+    if (a.k3_topk) {
+#pragma unroll
+        for (int i = 0; i < kPre; ++i) dma16_m0((const u32x4 *)a.xp16 + 256 * i + tid, lb + 4096 * i);
+    }
+    const SlotRec rec = k3_slot(a, slot);
+    if (rec.e < 0) {  // uniform over the block
+        vmem_wait_all();
+        return;
+    }
     constexpr int RB = 16 * kQ2KBytes;  // bytes of one row
     const int64_t goff = (int64_t)rec.e * a.gu_expert_bytes + (int64_t)16 * g * RB;
     const uint8_t *gm = a.gate + goff, *um = a.up + goff;
     {
         const u32x4 *xs = (const u32x4 *)(a.xp16 + (int64_t)slot_token(rec, 0) * (4096 / 16) * kRec16Dwords);
-        const uint32_t lb = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(wbuf) + 1024 * wave);
 #pragma unroll
         for (int i = 0; i < kK3PCopies; ++i) {
+            if (i < first) continue;
             const int u = 256 * i + tid;
             const void *src;
             if (u < kK3PXu) src = xs + u;
@@ -493,17 +669,33 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
     __shared__ float part[4][32];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int gpe = a.F / 16, slot = blockIdx.x / gpe, g = blockIdx.x % gpe;
-    const SlotRec rec = uniform_slot(a.slots, slot);
-    if (rec.e < 0) return;  // uniform over the block
+    const uint32_t lb = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(wbuf) + 1024 * wave);
+    const u32x4 *cs = (const u32x4 *)a.codebook;
+    constexpr int kPre = (kK3CCbU + kK3CXu) / 256;  // copies 0-2 hold the codebook and records only
+    static_assert((kK3CCbU + kK3CXu) % 256 == 0, "whole copies before the rows");
+    // one token (k3_topk): the codebook and the token's records do not
+    // depend on the slot, so their copies go out before the selection
+    const int first = a.k3_topk ? kPre : 0;
+    if (a.k3_topk) {
+#pragma unroll
+        for (int i = 0; i < kPre; ++i) {
+            const int u = 256 * i + tid;
+            dma16_m0(u < kK3CCbU ? cs + u : (const u32x4 *)a.xp16 + (u - kK3CCbU), lb + 4096 * i);
+        }
+    }
+    const SlotRec rec = k3_slot(a, slot);
+    if (rec.e < 0) {  // uniform over the block
+        vmem_wait_all();
+        return;
+    }
     constexpr int RB = 16 * kCB2Bytes;  // bytes of one row
     const int64_t goff = (int64_t)rec.e * a.gu_expert_bytes + (int64_t)16 * g * RB;
     const uint8_t *gm = a.gate + goff, *um = a.up + goff;
     {
-        const u32x4 *cs = (const u32x4 *)a.codebook;
         const u32x4 *xs = (const u32x4 *)(a.xp16 + (int64_t)slot_token(rec, 0) * (4096 / 16) * kRec16Dwords);
-        const uint32_t lb = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(wbuf) + 1024 * wave);
 #pragma unroll
         for (int i = 0; i < kK3CCopies; ++i) {
+            if (i < first) continue;
             const int u = min(256 * i + tid, kK3CUsed - 1);
             const void *src;
             if (u < kK3CCbU) src = cs + u;
@@ -872,6 +1064,7 @@ FfnArgs make_ffn_args(const moe_layer_desc *d, const void *x, int32_t T, int32_t
     a.route_scale = d->route_scale;
     a.logits = ws.logits;
     a.xp16 = a.xq8 = a.hp16 = nullptr;
+    a.k3_topk = 0;
     return a;
 }
 
@@ -903,14 +1096,24 @@ hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32
     // a Q8_0 shared expert at n_embd 4096 takes the staged K2, on x records written by K1
     const bool sg_staged = has_sh && a.shared_fmt == MOE_Q8_0 && a.D == 4096 && a.Fs % 8 == 0;
     if (sg_staged) a.xq8 = ws.xq8;
+    // one fp32 token at n_embd 4096 with a Q8_0 shared expert (or none): K1
+    // also runs the shared gate/up and the routed gate/up blocks select the
+    // top-k themselves, so there is no K2
+    const bool t1 = route && T == 1 && x_type == MOE_F32 && a.D == 4096 && (!has_sh || sg_staged);
+    if (t1) {
+        a.k3_topk = 1;
+        a.xq8 = nullptr;
+    }
     a.n_prep_blocks = a.xp16 || a.xq8 ? (T * (a.D / 64) + 3) / 4 : 0;
     a.n_shgu_blocks = has_sh ? (a.Fs + 4 * kShGuRows - 1) / (4 * kShGuRows) : 0;
-    const int k1 = a.build_slots + a.n_router_blocks + a.n_prep_blocks;
-    const int k2 = (route ? 1 : 0) + a.n_shgu_blocks;
+    const int k1 = t1 ? std::max(std::max(a.E, has_sh ? a.Fs / 8 : 0), 16)
+                      : a.build_slots + a.n_router_blocks + a.n_prep_blocks;
+    const int k2 = t1 ? 0 : (route ? 1 : 0) + a.n_shgu_blocks;
     const int k3 = a.nslots * (a.F / 16);
     if ((stage == 0 || stage == 1) && k1 > 0)
     {
-        if (x_type == MOE_BF16) dec_k1_kernel<MOE_BF16><<<k1, 256, 0, s>>>(a);
+        if (t1) dec_k1_t1_kernel<<<k1, 256, 0, s>>>(a);
+        else if (x_type == MOE_BF16) dec_k1_kernel<MOE_BF16><<<k1, 256, 0, s>>>(a);
         else dec_k1_kernel<MOE_F32><<<k1, 256, 0, s>>>(a);
     }
     if ((stage == 0 || stage == 2) && k2 > 0)

@@ -179,7 +179,8 @@ MOE_DEV int wave_min_i32(int v) {
 // the lanes offering it; only the lane that supplied the winner rescans its
 // candidates.  Lane s keeps slot s; then w_s = route_scale * exp(l_s - l_0) /
 // sum_j exp(l_j - l_0) in fp64, the exponentials computed by lanes 0..k-1 at
-// once.  Returns the lane's slot expert (lanes < k).
+// once.  Writes idx_out[s], w_out[s] unless idx_out is null; returns the
+// lane's slot expert (lanes < k).
 template <int PER>
 MOE_DEV int select_topk_per(const double *lg, int E, int k, float route_scale, int32_t *idx_out, float *w_out) {
     const int lane = threadIdx.x & 63;
@@ -223,6 +224,7 @@ MOE_DEV int select_topk_per(const double *lg, int E, int k, float route_scale, i
             my_e = we;
         }
     }
+    if (!idx_out) return my_e;  // the selection only (uniform over the wave)
     const double mx = __shfl(my_v, 0, kWave);  // slot 0 holds the largest logit
     const double ex = lane < k ? exp(my_v - mx) : 0.0;
     double den = ex;

@@ -435,26 +435,28 @@ __global__ void __launch_bounds__(256) dec_k1_t1_kernel(FfnArgs a) {
 }
 
 // The slot record of a routed gate/up block.  With k3_topk (one token, no
-// K2) every wave selects the top-k from the router logits itself, so the
-// slot's expert is wave-uniform without a barrier: slot s is the expert of
-// rank s among the k (bucket position s, token 0), as the bucketing orders
-// them.  Wave 0 of block 0 also writes the routing and the slot records the
-// down kernel reads.
-MOE_DEV SlotRec k3_slot(const FfnArgs &a, int slot) {
-    if (!a.k3_topk) return uniform_slot(a.slots, slot);
-    const bool writer = blockIdx.x == 0 && threadIdx.x < kWave;  // uniform over the wave
-    const int my_e = select_topk(a.logits, a.E, a.k, a.route_scale, writer ? a.w_topk_idx : nullptr,
-                                 writer ? a.w_topk_w : nullptr);
-    if (writer)
-        bucket_one_token(my_e, a.k, a.E, a.w_count, a.w_offset, a.w_perm, a.w_pos, a.w_active, a.w_n_active,
-                         a.slots, a.nslots);
-    const int lane = threadIdx.x & 63;
+// K2) every wave runs the selection from the router logits, so the slot's
+// expert is wave-uniform without a barrier: slot s is the expert of rank s
+// among the k (bucket position s, token 0), as the bucketing orders them.
+// The slot's first block (g = 0) stores the record for the down kernel, at
+// once, before its weight copies go out (a store issued after them could
+// be counted in their place by the copy waits).  The down kernel writes the
+// rest of the routing.
+MOE_DEV int rank_among_k(int my_e, int k) {  // lanes < k: my_e's rank among the k distinct experts
     int rank = 0;
 #pragma unroll
-    for (int q = 0; q < 16; ++q) rank += q < a.k && __builtin_amdgcn_readlane(my_e, q) < my_e;
+    for (int q = 0; q < 16; ++q) rank += q < k && __builtin_amdgcn_readlane(my_e, q) < my_e;
+    return rank;
+}
+MOE_DEV SlotRec k3_slot(const FfnArgs &a, int slot, int g) {
+    if (!a.k3_topk) return uniform_slot(a.slots, slot);
+    const int my_e = select_topk(a.logits, a.E, a.k, a.route_scale, nullptr, nullptr);
+    const int lane = threadIdx.x & 63, rank = rank_among_k(my_e, a.k);
     const uint64_t hit = __ballot(lane < a.k && rank == slot);
     const int e = hit ? __builtin_amdgcn_readlane(my_e, (int)__builtin_ctzll(hit)) : -1;
-    return make_slot(e, slot, 1, 0, 0);
+    const SlotRec rec = make_slot(e, slot, 1, 0, 0);
+    if (g == 0 && threadIdx.x == 0) a.slots[slot] = rec;
+    return rec;
 }
 
 // One block per (active slot, group g of 16 rows of the expert's gate and up):
@@ -474,8 +476,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     if constexpr (GFMT == MOE_CB2) load_codebook(a.codebook, cb_lds);
     const int gpe = a.F / 16, slot = blockIdx.x / gpe, g = blockIdx.x % gpe;
-    const SlotRec rec = k3_slot(a, slot);
-    if (rec.e < 0) return;  // uniform over the block
+    const SlotRec rec = k3_slot(a, slot, g);
+    if ((uint32_t)rec.e >= (uint32_t)a.E) return;  // an empty slot (uniform over the block)
     const int U = (int)fmt_bytes(GFMT, (int64_t)16 * a.D) / 16;  // 16 rows in 16-byte units
     const int64_t goff = (int64_t)rec.e * a.gu_expert_bytes + fmt_bytes(GFMT, (int64_t)16 * g * a.D);
     const u32x4 *sg = (const u32x4 *)(a.gate + goff), *su = (const u32x4 *)(a.up + goff);
@@ -562,8 +564,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
 #pragma unroll
         for (int i = 0; i < kPre; ++i) dma16_m0((const u32x4 *)a.xp16 + 256 * i + tid, lb + 4096 * i);
     }
-    const SlotRec rec = k3_slot(a, slot);
-    if (rec.e < 0) {  // uniform over the block
+    const SlotRec rec = k3_slot(a, slot, g);
+    if ((uint32_t)rec.e >= (uint32_t)a.E) {  // an empty slot (uniform over the block)
         vmem_wait_all();
         return;
     }
@@ -683,8 +685,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
             dma16_m0(u < kK3CCbU ? cs + u : (const u32x4 *)a.xp16 + (u - kK3CCbU), lb + 4096 * i);
         }
     }
-    const SlotRec rec = k3_slot(a, slot);
-    if (rec.e < 0) {  // uniform over the block
+    const SlotRec rec = k3_slot(a, slot, g);
+    if ((uint32_t)rec.e >= (uint32_t)a.E) {  // an empty slot (uniform over the block)
         vmem_wait_all();
         return;
     }
@@ -831,7 +833,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) dec_k4_kernel(FfnArgs a) {
     const uint8_t *ws = (const uint8_t *)wstage[wave];
     for (int u = wave; u < a.nslots; u += kDecWaves) {
         const SlotRec rec = uniform_slot(a.slots, u);
-        if (rec.e < 0) continue;
+        if ((uint32_t)rec.e >= (uint32_t)a.E) continue;
         const uint8_t *m = a.down + (int64_t)rec.e * a.down_expert_bytes;
         for (int r0 = 0; r0 < kDecRows; r0 += rb) {
             const int nunits = (int)(fmt_bytes(DFMT, (int64_t)rb * a.F) / 16);
@@ -901,23 +903,42 @@ MOE_DEV float sum32(float v) {  // over lanes [32 r, 32 r + 32)
     return v + __shfl_xor(v, 16, kWave);
 }
 
-__global__ void __launch_bounds__(512) dec_k4_t1_kernel(FfnArgs a) {
+// With k3_topk (no K2) a ninth wave selects the top-k again from the logits
+// while the others stream, for the combine's weights and bucket positions;
+// block 0's also writes the routing (top-k, weights and bucketing).
+__global__ void __launch_bounds__(576) dec_k4_t1_kernel(FfnArgs a) {
     __shared__ __align__(16) u32x4 sarea[6][64 * kK4T1SlotCopies];
     __shared__ __align__(16) u32x4 harea[2][64 * kK4T1ShCopies];
     __shared__ float part[6][kDecRows];
     __shared__ float ysl[kDecRows];
     __shared__ float wl[6];
     __shared__ int32_t posl[6];
+    __shared__ int32_t sidx[6];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int row0 = blockIdx.x * kDecRows, k = a.k;
     const int r = lane >> 5, c = lane & 31;  // row parity, 64-weight chunk of the row
-    if (tid < k) {
+    if (wave == 8) {
+        if (a.k3_topk) {
+            const bool out = blockIdx.x == 0;
+            const int my_e = select_topk(a.logits, a.E, k, a.route_scale, sidx, wl);
+            const int rank = rank_among_k(my_e, k);
+            if (lane < k) posl[lane] = rank;
+            if (out) {
+                if (lane < k) {
+                    a.w_topk_idx[lane] = my_e;
+                    a.w_topk_w[lane] = wl[lane];
+                }
+                bucket_one_token(my_e, k, a.E, a.w_count, a.w_offset, a.w_perm, a.w_pos, a.w_active, a.w_n_active,
+                                 nullptr, 0);
+            }
+        }
+    } else if (!a.k3_topk && tid < k) {
         wl[tid] = a.topk_w[tid];
         posl[tid] = a.pos[tid];
     }
     if (wave < 6) {
         const SlotRec rec = wave < k ? uniform_slot(a.slots, wave) : make_slot(-1, 0, 0, 0, 0);
-        if (rec.e >= 0) {
+        if ((uint32_t)rec.e < (uint32_t)a.E) {
             constexpr int RB = 8 * kQ2KBytes;  // bytes of a row
             const uint8_t *hrow = (const uint8_t *)(a.hp16 + (int64_t)rec.j0 * (2048 / 16) * kRec16Dwords);
             const uint8_t *rows = a.down + (int64_t)rec.e * a.down_expert_bytes + (int64_t)row0 * RB;
@@ -965,7 +986,7 @@ __global__ void __launch_bounds__(512) dec_k4_t1_kernel(FfnArgs a) {
                 if (c == 0) part[rec.j0][4 * (q >> 1) + 2 * (q & 1) + r] = sv;
             }
         }
-    } else if (a.Fs > 0) {
+    } else if (wave < 8 && a.Fs > 0) {
         const int h = wave - 6;  // rows row0 + 8 h .. + 8
         constexpr int SB = 2048 / 32 * kQ8Bytes;  // bytes of a row
         const uint8_t *hsb = (const uint8_t *)a.hs;
@@ -1096,10 +1117,14 @@ hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32
     // a Q8_0 shared expert at n_embd 4096 takes the staged K2, on x records written by K1
     const bool sg_staged = has_sh && a.shared_fmt == MOE_Q8_0 && a.D == 4096 && a.Fs % 8 == 0;
     if (sg_staged) a.xq8 = ws.xq8;
-    // one fp32 token at n_embd 4096 with a Q8_0 shared expert (or none): K1
-    // also runs the shared gate/up and the routed gate/up blocks select the
-    // top-k themselves, so there is no K2
-    const bool t1 = route && T == 1 && x_type == MOE_F32 && a.D == 4096 && (!has_sh || sg_staged);
+    // the one-token down kernel
+    const bool k4t1 = T == 1 && d->down_type == MOE_Q2K && a.F == 2048 && a.k <= 6 && a.D % kDecRows == 0 &&
+                      (a.Fs == 0 || (a.Fs == 2048 && a.shared_fmt == MOE_Q8_0));
+    // one fp32 token at n_embd 4096 with a Q8_0 shared expert (or none) and
+    // the one-token down kernel: K1 also runs the shared gate/up, the routed
+    // gate/up blocks select the top-k themselves and the down kernel writes
+    // the routing, so there is no K2
+    const bool t1 = route && k4t1 && x_type == MOE_F32 && a.D == 4096 && (!has_sh || sg_staged);
     if (t1) {
         a.k3_topk = 1;
         a.xq8 = nullptr;
@@ -1132,9 +1157,7 @@ hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32
         else dec_k3_kernel<MOE_Q2K><<<k3, 256, 0, s>>>(a);
     }
     if (stage == 0 || stage == 4) {
-        const bool t1 = T == 1 && d->down_type == MOE_Q2K && a.F == 2048 && a.k <= 6 && a.D % kDecRows == 0 &&
-                        (a.Fs == 0 || (a.Fs == 2048 && a.shared_fmt == MOE_Q8_0));
-        if (t1) dec_k4_t1_kernel<<<a.D / kDecRows, 64 * kDecWaves, 0, s>>>(a);
+        if (k4t1) dec_k4_t1_kernel<<<a.D / kDecRows, 64 * (kDecWaves + 1), 0, s>>>(a);
         else with_fmt(a.shared_fmt, [&](auto S) {
             constexpr int SF = decltype(S)::value;
             if (d->down_type == MOE_CB2) dec_k4_kernel<MOE_CB2, SF><<<a.D / kDecRows, 64 * kDecWaves, 0, s>>>(a);

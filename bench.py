@@ -494,7 +494,8 @@ def measured_traffic(kernel, workload):
 def run_stack(args, B):
     """The 43-block stack x <- x + MoE(RMSNorm(x)) at B token rows: every
     layer resident (code-sampled weights of the stack's formats and shapes),
-    one step = the 43 blocks, captured once in a graph and replayed."""
+    one step = the 43 blocks (moe_block_forward each), captured once in a
+    graph and replayed."""
     import numpy as np
     import torch
 
@@ -529,10 +530,9 @@ def run_stack(args, B):
     ws = moe.alloc_workspace(W0, B)
     r = moe.Routing(B, W0.n_expert_used, W0.n_expert)
 
-    def step():
+    def step():  # one moe_block_forward per block: x <- x + MoE(RMSNorm(x))
         for W in Ws:
-            moe.rmsnorm(x, W.gamma, xn, 1e-6)
-            moe.layer_forward(W, xn, x, ws, routing=r, accumulate=True)
+            moe.block_forward(W, x, ws, eps=1e-6, routing=r)
 
     for _ in range(args.warmup):
         step()
@@ -625,7 +625,8 @@ def run_stack(args, B):
             "workload": args.workload, "tokens_per_step": B, "n_layer": n_layer,
             "n_embd": D, "n_expert": W0.n_expert, "n_expert_used": W0.n_expert_used, "n_ff_exp": W0.n_ff_exp,
             "n_ff_shared": W0.n_ff_shared, "formats": "CB2 gate/up, Q2K down, Q8_0 shared, fp32 router",
-            "weights": "code-sampled per layer", "launch": "hipGraph of one %d-block step, replayed" % n_layer,
+            "weights": "code-sampled per layer",
+            "launch": "hipGraph of one %d-block step (moe_block_forward per block), replayed" % n_layer,
         },
         "timing": "HIP events on the replay stream around the %d timed steps" % K,
         "wall_ms_per_step": round(1000.0 * wall / K, 5),
@@ -642,8 +643,8 @@ def run_stack(args, B):
             "traffic": measured_traffic(kernel_name, args.workload),
             "bytes_per_launch": int(gateup_bytes),
             "avg_launch_us": round(gu_ms * 1e3, 3),
-            "timing": "HIP events around runs of 43 back-to-back stage-3 launches (one per layer), %d runs, "
-                      "median per launch" % n_runs,
+            "timing": "HIP events around runs of %d back-to-back stage-3 launches (one per layer), %d runs, "
+                      "median per launch" % (n_layer, n_runs),
         },
         "cpu_baseline": cpu,
     }

@@ -137,10 +137,9 @@ int moe_route(const moe_layer_desc *desc, const void *x, int32_t T, int32_t x_ty
  * per group of 16 values (few rows) or per row (many rows, on the matrix
  * cores), accumulated exactly in int32 and scaled in fp32.  x_type MOE_F32
  * keeps x, h and y in fp32, and two calls give the same bits.  MOE_BF16
- * takes bf16 x (coded per row like fp32 rows), rounds the hidden activation
- * h to bf16 before it is coded for the down projection, and adds the routed
- * down rows into y with atomics (the order of those additions varies between
- * calls). */
+ * takes bf16 x (coded per row like fp32 rows); h stays fp32 and is coded
+ * per row for the down projection, and the routed down rows are added into y
+ * with atomics (the order of those additions varies between calls). */
 int moe_expert_ffn(const moe_layer_desc *desc, const void *x, int32_t T, int32_t x_type, const moe_routing *r,
                    float *y, uint32_t flags, void *ws, size_t ws_bytes, void *stream, char *err, size_t errlen);
 
@@ -166,6 +165,20 @@ int moe_layer_forward(const moe_layer_desc *desc, const void *x, int32_t T, int3
 int moe_layer_forward_stage(const moe_layer_desc *desc, const void *x, int32_t T, int32_t x_type, float *y,
                             uint32_t flags, const moe_routing *routing, int32_t stage, void *ws, size_t ws_bytes,
                             void *stream, char *err, size_t errlen);
+
+/* One block of the stack ("Understanding Dwarf Star", 5.6.2: the layers
+ * applied in turn, each normalising its input first; 5.2.1 RMSNorm):
+ * x <- x + MoE(RMSNorm(x) * gamma), in place on the residual stream.
+ * x: [T][D] fp32, read and then overwritten; gamma: [D] fp32, 16-byte
+ * aligned; eps >= 0.  The normalised rows have the bits of moe_rmsnorm and
+ * the MoE output those of moe_layer_forward on them with MOE_ACCUMULATE.  One
+ * token with Q2K or codebook gate/up rows runs in three launches (the first
+ * normalises x itself, the last adds into x); otherwise moe_rmsnorm into the
+ * workspace, then moe_layer_forward.  routing may be NULL.  Workspace from
+ * moe_workspace_size (which covers the normalised rows). */
+int moe_block_forward(const moe_layer_desc *desc, const float *gamma, float eps, float *x, int32_t T,
+                      const moe_routing *routing, void *ws, size_t ws_bytes, void *stream, char *err,
+                      size_t errlen);
 
 /* moe_layer_forward without a workspace argument, for callers that cannot
  * allocate device memory (code under graph capture, tight serving loops,

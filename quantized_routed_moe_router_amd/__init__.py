@@ -65,10 +65,13 @@ _lib.moe_version.restype = ctypes.c_char_p
 _lib.moe_count_selections.argtypes = [_P, _I32, _I32, _I32, _I32, _P, _P, ctypes.c_char_p, _SZ]
 _lib.moe_hotlist.argtypes = [_P, _I32, _P, _P, _P, ctypes.c_char_p, _SZ]
 _lib.moe_read_stream.argtypes = [_P, _I64, _P, _I32, _P, ctypes.c_char_p, _SZ]
+_lib.moe_block_forward.argtypes = [ctypes.POINTER(LayerDesc), _P, ctypes.c_float, _P, _I32,
+                                   ctypes.POINTER(RoutingStruct), _P, _SZ, _P, ctypes.c_char_p, _SZ]
 _lib.moe_layer_forward_noalloc.argtypes = [ctypes.POINTER(LayerDesc), _P, _I32, _I32, _P, ctypes.c_uint32,
                                            ctypes.POINTER(RoutingStruct), _P, ctypes.c_char_p, _SZ]
 for _f in ("moe_route", "moe_expert_ffn", "moe_layer_forward_stage", "moe_layer_forward", "moe_rmsnorm", "moe_dequant",
-           "moe_count_selections", "moe_hotlist", "moe_read_stream", "moe_layer_forward_noalloc"):
+           "moe_count_selections", "moe_hotlist", "moe_read_stream", "moe_layer_forward_noalloc",
+           "moe_block_forward"):
     getattr(_lib, _f).restype = ctypes.c_int
 
 
@@ -299,6 +302,21 @@ def layer_forward(layer, x, y, ws, routing=None, accumulate=False, stream=None):
     _check(_lib.moe_layer_forward(ctypes.byref(d), _ptr(x), T, _xtype(x), _ptr(y),
                                   ACCUMULATE if accumulate else 0, ctypes.byref(r) if r is not None else None,
                                   _ptr(ws), ws.numel(), _stream(stream), err, 512), err)
+
+
+def block_forward(layer, x, ws, gamma=None, eps=1e-6, routing=None, stream=None):
+    """x <- x + MoE(RMSNorm(x) * gamma) in place on fp32 x [T][n_embd]
+    (gamma defaults to the layer's)."""
+    gamma = layer.gamma if gamma is None else gamma
+    _tensor("x", x, torch.float32)
+    T = _check_call(layer, x, ws, routing=routing, need_y=False)
+    _tensor("gamma", gamma, torch.float32, (layer.n_embd,))
+    _one_cuda_device(x=x, gamma=gamma)
+    d, err = layer.desc(), ctypes.create_string_buffer(512)
+    r = routing.struct() if routing is not None else None
+    _check(_lib.moe_block_forward(ctypes.byref(d), _ptr(gamma), eps, _ptr(x), T,
+                                  ctypes.byref(r) if r is not None else None, _ptr(ws), ws.numel(), _stream(stream),
+                                  err, 512), err)
 
 
 def layer_forward_noalloc(layer, x, y, routing=None, accumulate=False, stream=None):

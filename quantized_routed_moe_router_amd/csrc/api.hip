@@ -260,6 +260,28 @@ int moe_layer_forward_noalloc(const moe_layer_desc *d, const void *x, int32_t T,
     return device_status(forward(d, x, T, x_type, r, y, flags, w, (hipStream_t)stream, 0), err, errlen);
 }
 
+int moe_block_forward(const moe_layer_desc *d, const float *gamma, float eps, float *x, int32_t T,
+                      const moe_routing *routing, void *ws, size_t ws_bytes, void *stream, char *err, size_t errlen) {
+    int rc = check_call(d, x, T, MOE_F32, ws, ws_bytes, err, errlen);
+    if (rc) return rc;
+    if (routing && (rc = check_routing(routing, err, errlen))) return rc;
+    if (!(eps >= 0.f)) return fail(err, errlen, MOE_EINVAL, "eps must be >= 0");
+    if (T == 0) return MOE_OK;
+    if (!gamma) return fail(err, errlen, MOE_EINVAL, "gamma is NULL");
+    if (!aligned16(gamma)) return fail(err, errlen, MOE_EALIGN, "gamma must be 16-byte aligned");
+    Workspace w = workspace_layout(d, T, ws);
+    RoutingPtrs r = routing ? from_routing(routing) : from_ws(w);
+    hipStream_t s = (hipStream_t)stream;
+    // one token with Q2K or codebook gate/up rows: the first kernel normalises
+    // x itself and the last adds the block's output into x
+    if (t1_schedule_ok(d, T, MOE_F32) && (d->gate_type == MOE_Q2K || d->gate_type == MOE_CB2))
+        return device_status(launch_small(d, x, T, MOE_F32, r, x, MOE_ACCUMULATE, w, s, 0, true, gamma, eps), err,
+                             errlen);
+    hipError_t e = launch_rmsnorm(x, gamma, eps, T, d->n_embd, w.xn, s);
+    if (e == hipSuccess) e = forward(d, w.xn, T, MOE_F32, r, x, MOE_ACCUMULATE, w, s, 0);
+    return device_status(e, err, errlen);
+}
+
 int moe_count_selections(const int32_t *topk_idx, int32_t T, int32_t k, int32_t E, int32_t layer, int64_t *counts,
                          void *stream, char *err, size_t errlen) {
     if (T < 0 || k < 1 || E < 1 || layer < 0)

@@ -764,6 +764,7 @@ struct Workspace {
     // and hs rows' 1/S
     uint32_t *sg_aq;
     float *sg_ainv;       // [T]
+    float *xn;            // [T][D] normalised rows of moe_block_forward (when not fused)
     size_t bytes;
 };
 
@@ -818,6 +819,7 @@ __host__ inline Workspace workspace_layout(const moe_layer_desc *d, int32_t T, v
     w.pf_hinv = (float *)take(sizeof(float) * (size_t)P);
     w.sg_aq = (uint32_t *)take((size_t)T * (size_t)(D > Fs ? D : Fs) * 2);
     w.sg_ainv = (float *)take(sizeof(float) * (size_t)T);
+    w.xn = (float *)take(sizeof(float) * (size_t)T * (size_t)D);
     w.bytes = off;
     return w;
 }
@@ -840,7 +842,11 @@ hipError_t launch_route(const moe_layer_desc *d, const void *x, int32_t T, int32
 bool small_path_ok(const moe_layer_desc *d, int32_t T);
 bool small_route_ok(const moe_layer_desc *d, int32_t T);
 hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
-                        float *y, uint32_t flags, const Workspace &ws, hipStream_t s, int stage, bool route);
+                        float *y, uint32_t flags, const Workspace &ws, hipStream_t s, int stage, bool route,
+                        const float *gamma = nullptr, float eps = 0.f);
+// one fp32 token on the schedule without K2; with a gamma (Q2K or codebook
+// gate/up rows) K1 also normalises x
+bool t1_schedule_ok(const moe_layer_desc *d, int32_t T, int32_t x_type);
 // the shared expert (Q8_0) of any number of fp32 rows as two int8 matrix-core
 // GEMMs: stage 3 writes hs, stage 4 ys
 bool shared_q8_mfma_ok(const moe_layer_desc *d);

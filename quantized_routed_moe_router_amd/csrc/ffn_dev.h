@@ -44,6 +44,9 @@ struct FfnArgs {
     int nslots;
     int build_slots;  // K1 writes the records from a given routing
     int k3_topk;      // one token: each routed gate/up block selects the top-k itself (no K2)
+    // one token: K1 normalises x first (x <- gamma * x / rms(x)) when set
+    const float *norm_gamma;
+    float norm_eps;
 };
 
 // Load the lane's 64 activations at element offset off of x (fp32 or bf16).

@@ -323,15 +323,18 @@ MOE_DEV void t1_wait_rows() {
     t1_wait<kT1WeightCopies - (END + 63) / 64>();
 }
 
+template <bool NORM>
 __global__ void __launch_bounds__(256) dec_k1_t1_kernel(FfnArgs a) {
-    __shared__ __align__(16) u32x4 area[4][kT1Units];
+    __shared__ __align__(16) u32x4 area[4][kT1Units + (NORM ? kT1Xu : 0)];
     __shared__ double rpart[4];
     __shared__ float part[4][16];
+    __shared__ float red[4];
     const int b = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const bool router = b < a.E, shared = b < a.Fs / 8;  // uniform over the block
     u32x4 *my = area[wave];
     float *xq = (float *)(my + kSgXu + 16 * kSgRu);  // x, columns 1024 w ..
     float *rq = xq + 1024;                          // router row b, the same columns
+    float *gq = xq + 2048;                          // NORM: gamma, the same columns
     const int row0 = 8 * b;
     constexpr int RB = 4096 / 32 * kQ8Bytes;  // bytes of a shared row: 4352
     {
@@ -341,6 +344,12 @@ __global__ void __launch_bounds__(256) dec_k1_t1_kernel(FfnArgs a) {
         const uint32_t lr = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(rq));
 #pragma unroll
         for (int i = 0; i < 4; ++i) dma16_m0(xs + 16 * (64 * i + lane), lx + 1024 * i);
+        if constexpr (NORM) {
+            const uint8_t *gs = (const uint8_t *)a.norm_gamma + 4096 * wave;
+            const uint32_t lg = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(gq));
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dma16_m0(gs + 16 * (64 * i + lane), lg + 1024 * i);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) dma16_m0(rs + 16 * (64 * i + lane), lr + 1024 * i);
         if (shared) {
@@ -355,9 +364,36 @@ __global__ void __launch_bounds__(256) dec_k1_t1_kernel(FfnArgs a) {
             }
         }
     }
-    // x's quarter has landed
+    // x's quarter (and gamma's) has landed
     if (shared) t1_wait<4 + kT1WeightCopies>();
     else t1_wait<4>();
+    if constexpr (NORM) {
+        // x <- gamma * (x / sqrt(mean(x^2) + eps)) in LDS, with the bits of
+        // rmsnorm_vec_kernel<4>: thread t sums the squares of its float4s
+        // t + 256 i (i = 0..3, one in each quarter) in that order, the lanes
+        // by the same butterfly, the waves as (0 + 1) + (2 + 3)
+        block_lds_sync();  // every wave's quarter has landed
+        float ss = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4 v = *(const f32x4 *)((const float *)(area[i] + kSgXu + 16 * kSgRu) + 4 * tid);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ss = __builtin_fmaf(v[j], v[j], ss);
+        }
+        for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, kWave);
+        if (lane == 0) red[wave] = ss;
+        block_lds_sync();  // also: every read of x for the squares is done
+        const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+        const float inv = 1.0f / sqrtf(tot / 4096.f + a.norm_eps);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f32x4 v = *(f32x4 *)(xq + 16 * lane + 4 * i);
+            const f32x4 g = *(const f32x4 *)(gq + 16 * lane + 4 * i);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = g[j] * (v[j] * inv);
+            *(f32x4 *)(xq + 16 * lane + 4 * i) = v;
+        }
+    }
     // Q8_0 records of the quarter's 16 chunks, four at a time
     if (shared) {
 #pragma unroll
@@ -1086,6 +1122,8 @@ FfnArgs make_ffn_args(const moe_layer_desc *d, const void *x, int32_t T, int32_t
     a.logits = ws.logits;
     a.xp16 = a.xq8 = a.hp16 = nullptr;
     a.k3_topk = 0;
+    a.norm_gamma = nullptr;
+    a.norm_eps = 0.f;
     return a;
 }
 
@@ -1098,8 +1136,21 @@ bool small_route_ok(const moe_layer_desc *d, int32_t T) { return route_small_ok(
 
 // stage 0 = all; 1..4 = K1..K4.  route: also compute the routing (K1's router
 // blocks and K2's block 0); otherwise the routing in r is given.
+// The one-token schedule without K2 (the routed gate/up blocks select the
+// top-k, the down kernel writes the routing), when it applies.
+bool t1_schedule_ok(const moe_layer_desc *d, int32_t T, int32_t x_type) {
+    const bool has_sh = d->n_ff_shared > 0;
+    const bool sg_staged = has_sh && d->shared_type == MOE_Q8_0 && d->n_embd == 4096 && d->n_ff_shared % 8 == 0;
+    const bool k4t1 = T == 1 && d->down_type == MOE_Q2K && d->n_ff_exp == 2048 && d->n_expert_used <= 6 &&
+                      d->n_embd % kDecRows == 0 &&
+                      (d->n_ff_shared == 0 || (d->n_ff_shared == 2048 && d->shared_type == MOE_Q8_0));
+    return small_path_ok(d, T) && small_route_ok(d, T) && k4t1 && x_type == MOE_F32 && d->n_embd == 4096 &&
+           (!has_sh || sg_staged);
+}
+
 hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
-                        float *y, uint32_t flags, const Workspace &ws, hipStream_t s, int stage, bool route) {
+                        float *y, uint32_t flags, const Workspace &ws, hipStream_t s, int stage, bool route,
+                        const float *gamma, float eps) {
     FfnArgs a = make_ffn_args(d, x, T, x_type, r, y, flags, ws);
     const bool has_sh = a.Fs > 0;
     a.shared_fmt = has_sh ? d->shared_type : MOE_Q8_0;
@@ -1125,9 +1176,12 @@ hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32
     // gate/up blocks select the top-k themselves and the down kernel writes
     // the routing, so there is no K2
     const bool t1 = route && k4t1 && x_type == MOE_F32 && a.D == 4096 && (!has_sh || sg_staged);
+    if (gamma && !(t1 && (d->gate_type == MOE_Q2K || d->gate_type == MOE_CB2))) return hipErrorInvalidValue;
     if (t1) {
         a.k3_topk = 1;
         a.xq8 = nullptr;
+        a.norm_gamma = gamma;
+        a.norm_eps = eps;
     }
     a.n_prep_blocks = a.xp16 || a.xq8 ? (T * (a.D / 64) + 3) / 4 : 0;
     a.n_shgu_blocks = has_sh ? (a.Fs + 4 * kShGuRows - 1) / (4 * kShGuRows) : 0;
@@ -1137,7 +1191,8 @@ hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32
     const int k3 = a.nslots * (a.F / 16);
     if ((stage == 0 || stage == 1) && k1 > 0)
     {
-        if (t1) dec_k1_t1_kernel<<<k1, 256, 0, s>>>(a);
+        if (t1 && gamma) dec_k1_t1_kernel<true><<<k1, 256, 0, s>>>(a);
+        else if (t1) dec_k1_t1_kernel<false><<<k1, 256, 0, s>>>(a);
         else if (x_type == MOE_BF16) dec_k1_kernel<MOE_BF16><<<k1, 256, 0, s>>>(a);
         else dec_k1_kernel<MOE_F32><<<k1, 256, 0, s>>>(a);
     }

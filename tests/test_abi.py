@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol():
     names = _declared()
     assert {"moe_route", "moe_expert_ffn", "moe_layer_forward", "moe_layer_forward_stage", "moe_workspace_size",
             "moe_rmsnorm", "moe_dequant", "moe_version", "moe_count_selections", "moe_hotlist",
-            "moe_read_stream"} <= names
+            "moe_read_stream", "moe_block_forward"} <= names
     for n in names:
         assert hasattr(moe._lib, n), n
     assert moe.version().startswith("moe-gfx950")
@@ -255,3 +255,16 @@ def test_noalloc_entry_point_validates_before_touching_the_device():
     assert f(ctypes.byref(d), None, 0, 0, None, 0, None, None, err, 256) == 0  # T = 0: nothing to do
     assert f(ctypes.byref(d), 0x80008, 1, 0, 0x100000, 0, None, None, err, 256) == -2
     assert f(ctypes.byref(d), 0x80000, 1, 0, 0x100000, 4, None, None, err, 256) == -1  # unknown flag
+
+
+def test_block_forward_validates():
+    import quantized_routed_moe_router_amd as moe
+    err = ctypes.create_string_buffer(256)
+    f = moe._lib.moe_block_forward
+    d = _desc()
+    ws, n = 0x200000, 1 << 30
+    assert f(ctypes.byref(d), None, 1e-6, 0x100000, 1, None, ws, n, None, err, 256) == -1  # no gamma
+    assert f(ctypes.byref(d), 0x80008, 1e-6, 0x100000, 1, None, ws, n, None, err, 256) == -2  # misaligned gamma
+    assert f(ctypes.byref(d), 0x80000, -1.0, 0x100000, 1, None, ws, n, None, err, 256) == -1  # eps < 0
+    assert f(ctypes.byref(d), 0x80000, 1e-6, 0x100000, 1, None, ws, 16, None, err, 256) == -3  # workspace
+    assert f(ctypes.byref(d), None, 1e-6, None, 0, None, ws, n, None, err, 256) == 0  # T = 0

@@ -177,9 +177,10 @@ def test_cb2_full_width_layer(stack3, T):
     _log("cb2 layer T=%d: worst relative error %.3g" % (T, worst))
 
 
-def _stack_on_gpu(Ws, x):
-    # x <- x + MoE(RMSNorm(x)) layer by layer through the C ABI (rmsnorm, then
-    # layer_forward accumulating into x); returns every layer's output
+def _stack_on_gpu(Ws, x, block=False):
+    # x <- x + MoE(RMSNorm(x)) layer by layer through the C ABI: rmsnorm, then
+    # layer_forward accumulating into x, or (block) block_forward; returns
+    # every layer's output
     import torch
 
     import quantized_routed_moe_router_amd as moe
@@ -188,8 +189,11 @@ def _stack_on_gpu(Ws, x):
     ws = moe.alloc_workspace(Ws[0], x.shape[0])
     outs = []
     for W in Ws:
-        moe.rmsnorm(xd, W.gamma, xn, 1e-6)
-        moe.layer_forward(W, xn, xd, ws, accumulate=True)
+        if block:
+            moe.block_forward(W, xd, ws)
+        else:
+            moe.rmsnorm(xd, W.gamma, xn, 1e-6)
+            moe.layer_forward(W, xn, xd, ws, accumulate=True)
         outs.append(xd.cpu().numpy().copy())
     return outs
 
@@ -234,6 +238,20 @@ def stack4_flash():
 def test_stack_flash_shape_teacher_forced(stack4_flash, B):
     layers, Ws = stack4_flash
     _check_stack(layers, Ws, B, "stack of 256-expert blocks")
+
+
+@pytest.mark.parametrize("B", [1, 8])
+def test_block_forward_is_rmsnorm_then_layer_forward(stack4_flash, B):
+    # block_forward (at one token: RMSNorm inside the first kernel, the
+    # residual added by the last) gives the bits of rmsnorm followed by
+    # layer_forward accumulating into x, layer after layer
+    layers, Ws = stack4_flash
+    x = synth.stack43(B=B).x
+    composed = _stack_on_gpu(Ws, x)
+    fused = _stack_on_gpu(Ws, x, block=True)
+    for l in range(len(layers)):
+        assert np.array_equal(fused[l].view(np.uint32), composed[l].view(np.uint32)), "layer %d" % l
+    _log("block_forward B=%d: %d layers bitwise equal to rmsnorm + layer_forward" % (B, len(layers)))
 
 
 def test_cb2_flash_shape_many_rows(stack4_flash):

@@ -74,15 +74,18 @@ MOE_DEV float byte_to_float(uint32_t v) {
 
 // 8 bytes starting at a 2-byte aligned address, assembled from aligned dwords.
 MOE_DEV void load_8_at_even(const uint8_t *p, uint32_t &lo, uint32_t &hi) {
-    uintptr_t a = (uintptr_t)p;
-    const uint32_t *q = (const uint32_t *)(a & ~(uintptr_t)3);
-    uint32_t s = (uint32_t)(a & 3u);  // 0 or 2
-    uint32_t w0 = q[0], w1 = q[1];
+    // aligned dwords from p rounded down to 4 bytes (a third one only when p
+    // is 2 bytes into a dword), then a byte shift; the address is formed by
+    // pointer arithmetic on p so that the compiler keeps its address space
+    // (an LDS pointer stays an LDS read instead of a flat one)
+    const uint32_t s = (uint32_t)((uintptr_t)p & 3u);  // 0 or 2
+    const uint32_t *q = (const uint32_t *)(p - s);
+    const uint32_t w0 = q[0], w1 = q[1];
     if (s == 0) {
         lo = w0;
         hi = w1;
     } else {
-        uint32_t w2 = q[2];
+        const uint32_t w2 = q[2];
         lo = __builtin_amdgcn_alignbyte(w1, w0, s);
         hi = __builtin_amdgcn_alignbyte(w2, w1, s);
     }
@@ -269,9 +272,9 @@ MOE_DEV CB2Chunk cb2_load(const uint8_t *base, int64_t i0) {
     CB2Chunk c;
     load_8_at_even(blk + 2 + 8 * sub, c.idx_lo, c.idx_hi);
     load_8_at_even(blk + 34 + 8 * sub, c.sg_lo, c.sg_hi);
-    uintptr_t a = (uintptr_t)blk;
-    uint32_t w = *(const uint32_t *)(a & ~(uintptr_t)3);
-    c.d = half_bits_to_float((a & 2u) ? (w >> 16) : w);
+    const uint32_t s2 = (uint32_t)((uintptr_t)blk & 2u);  // the block starts 0 or 2 bytes into a dword
+    const uint32_t w = *(const uint32_t *)(blk - s2);
+    c.d = half_bits_to_float(s2 ? (w >> 16) : w);
     return c;
 }
 

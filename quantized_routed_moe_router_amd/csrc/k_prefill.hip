@@ -625,9 +625,9 @@ __global__ void __launch_bounds__(256) pf_q8_split_kernel(const uint8_t *src, in
     if (b >= nblocks) return;
     const int i0 = 8 * (int)(q & 3);
     const uint8_t *blk = src + b * kQ8Bytes;
-    const uintptr_t ab = (uintptr_t)blk;
-    const uint32_t dw = *(const uint32_t *)(ab & ~(uintptr_t)3);
-    const float d = half_bits_to_float((ab & 2u) ? (dw >> 16) : (dw & 0xFFFFu));
+    const uint32_t s2 = (uint32_t)((uintptr_t)blk & 2u);  // the block starts 0 or 2 bytes into a dword
+    const uint32_t dw = *(const uint32_t *)(blk - s2);
+    const float d = half_bits_to_float(s2 ? (dw >> 16) : (dw & 0xFFFFu));
     uint32_t c[2];
     load_8_at_even(blk + 2 + i0, c[0], c[1]);
     uint32_t hw[4], lw[4];

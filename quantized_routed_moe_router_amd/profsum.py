@@ -1,6 +1,7 @@
 """Condense rocprofv3 CSV output into a short Markdown summary.
 
     python -m quantized_routed_moe_router_amd.profsum DIR [--match NAME ...]
+    python -m quantized_routed_moe_router_amd.profsum DIR --by-grid NAME
 
 DIR is a rocprofv3 output directory written with ``--output-format csv``.
 Every ``*kernel_stats.csv`` found under it (from ``--kernel-trace --stats``)
@@ -64,6 +65,23 @@ def counters(path, match):
     for k in sorted(acc, key=lambda k: -len(disp[k])):
         n = len(disp[k])
         out.append("| %s | %d | " % (_short(k), n) + " | ".join("%.6g" % (acc[k][c] / n) for c in names) + " |")
+    return out
+
+
+def grid_table(path, name):
+    """Durations of one kernel's dispatches grouped by grid size (workgroups)."""
+    groups = collections.defaultdict(list)
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            if name not in r["Kernel_Name"]:
+                continue
+            wg = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]) // max(
+                1, int(r["Workgroup_Size_X"]) * int(r["Workgroup_Size_Y"]) * int(r["Workgroup_Size_Z"]))
+            groups[wg].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = ["| workgroups | dispatches | avg us | min us | max us |", "|---:|---:|---:|---:|---:|"]
+    for wg in sorted(groups):
+        v = groups[wg]
+        out.append("| %d | %d | %.2f | %.2f | %.2f |" % (wg, len(v), sum(v) / len(v), min(v), max(v)))
     return out
 
 
@@ -142,6 +160,8 @@ def main(argv=None):
     ap.add_argument("--copy-write")
     ap.add_argument("--copy-bytes", type=float)
     ap.add_argument("--algorithmic-bytes", type=int, default=0)
+    ap.add_argument("--by-grid", metavar="KERNEL",
+                    help="durations of the kernel's dispatches grouped by workgroup count (from the kernel trace)")
     a = ap.parse_args(argv)
     if a.hbm:
         if not (a.fetch and a.write and a.copy_fetch and a.copy_write and a.copy_bytes):
@@ -150,6 +170,12 @@ def main(argv=None):
     if not a.dir:
         ap.error("a rocprofv3 output directory is needed")
     found = False
+    if a.by_grid:
+        for p in sorted(glob.glob(os.path.join(a.dir, "**", "*kernel_trace.csv"), recursive=True)):
+            found = True
+            print("dispatches of %s by grid size (%s):\n" % (a.by_grid, os.path.basename(p)))
+            print("\n".join(grid_table(p, a.by_grid)) + "\n")
+        return 0 if found else 1
     for p in sorted(glob.glob(os.path.join(a.dir, "**", "*kernel_stats.csv"), recursive=True)):
         found = True
         print("kernel durations (%s):\n" % os.path.basename(p))

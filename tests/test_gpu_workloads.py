@@ -142,6 +142,35 @@ def test_one_token_stages_and_repeats_are_bitwise_equal(flash):
     gu.assert_close(y.cpu().numpy(), y_ref)
 
 
+@pytest.mark.parametrize("T", [1, 3])
+def test_exact_ties_across_waves_at_full_width(flash, T):
+    # eight experts with the same router row and bias in every quarter of the
+    # 256 (the one-token gate/up blocks select with their 4 waves, one quarter
+    # each): the tied logits are the largest, so the top-6 are the six lowest
+    # of the eight indices, and the cut falls inside the tie
+    import copy
+
+    import quantized_routed_moe_router_amd as moe
+    L, W = flash
+    tied = [5, 40, 64, 100, 129, 190, 200, 255]
+    L2 = copy.copy(L)
+    R = L.router_w.copy()
+    for e in tied[1:]:
+        R[e] = R[tied[0]]
+    bias = np.zeros(L.n_expert, np.float32)
+    bias[tied] = 40.0
+    L2.router_w, L2.router_bias = R, bias
+    W2 = copy.copy(W)
+    W2.router_w, W2.router_bias = gu.dev(R), gu.dev(bias)
+    x = synth.activations(30 + T, T, L.n_embd)
+    y, r = gu.run_forward(W2, gu.x_to_device(x=x))
+    y_ref, idx_ref, w_ref = gu.oracle_all_rows(L2, x=x)
+    assert np.all(idx_ref == tied[:6])
+    gu.check_routing(r, idx_ref, w_ref, L.n_expert)
+    worst = gu.assert_close(y.cpu().numpy(), y_ref)
+    _log("ties across waves T=%d: worst relative error %.3g" % (T, worst))
+
+
 def test_prefill_2048(flash):
     L, W = flash
     _run(synth.prefill_2048(L), W)

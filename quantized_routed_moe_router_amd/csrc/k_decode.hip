@@ -64,6 +64,19 @@ MOE_DEV void lane_prep(const uint32_t *rec, const void *src, int src_bf16, int64
     }
 }
 
+// A slot record as the decode kernels use it: wave-uniform, and empty (e =
+// -1) unless its fields fit the call (expert in [0, E), 1..16 entries inside
+// [0, T*k), tokens below T), so that a record that does not belong to this
+// call can give a wrong result but never an address outside the buffers.
+MOE_DEV SlotRec checked_slot(const FfnArgs &a, int s) {
+    SlotRec r = uniform_slot(a.slots, s);
+    bool ok = (uint32_t)r.e < (uint32_t)a.E && r.n >= 1 && r.n <= kMaxDecTokens && r.j0 >= 0 &&
+              r.j0 + r.n <= a.T * a.k;
+    for (int j = 0; ok && j < r.n; ++j) ok = slot_token(r, j) < a.T;
+    if (!ok) r = make_slot(-1, 0, 0, 0, 0);
+    return r;
+}
+
 // Per-slot records from a routing given by the caller (no routing in K1/K2).
 MOE_DEV void build_slot_records(const FfnArgs &a) {
     const int na = a.n_active[0];
@@ -485,7 +498,7 @@ MOE_DEV int rank_among_k(int my_e, int k) {  // lanes < k: my_e's rank among the
     return rank;
 }
 MOE_DEV SlotRec k3_slot(const FfnArgs &a, int slot, int g) {
-    if (!a.k3_topk) return uniform_slot(a.slots, slot);
+    if (!a.k3_topk) return checked_slot(a, slot);
     const int my_e = select_topk(a.logits, a.E, a.k, a.route_scale, nullptr, nullptr);
     const int lane = threadIdx.x & 63, rank = rank_among_k(my_e, a.k);
     const uint64_t hit = __ballot(lane < a.k && rank == slot);
@@ -868,7 +881,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) dec_k4_kernel(FfnArgs a) {
     const int c = lane % (a.F >> 6);
     const uint8_t *ws = (const uint8_t *)wstage[wave];
     for (int u = wave; u < a.nslots; u += kDecWaves) {
-        const SlotRec rec = uniform_slot(a.slots, u);
+        const SlotRec rec = checked_slot(a, u);
         if ((uint32_t)rec.e >= (uint32_t)a.E) continue;
         const uint8_t *m = a.down + (int64_t)rec.e * a.down_expert_bytes;
         for (int r0 = 0; r0 < kDecRows; r0 += rb) {
@@ -973,7 +986,7 @@ __global__ void __launch_bounds__(576) dec_k4_t1_kernel(FfnArgs a) {
         posl[tid] = a.pos[tid];
     }
     if (wave < 6) {
-        const SlotRec rec = wave < k ? uniform_slot(a.slots, wave) : make_slot(-1, 0, 0, 0, 0);
+        const SlotRec rec = wave < k ? checked_slot(a, wave) : make_slot(-1, 0, 0, 0, 0);
         if ((uint32_t)rec.e < (uint32_t)a.E) {
             constexpr int RB = 8 * kQ2KBytes;  // bytes of a row
             const uint8_t *hrow = (const uint8_t *)(a.hp16 + (int64_t)rec.j0 * (2048 / 16) * kRec16Dwords);

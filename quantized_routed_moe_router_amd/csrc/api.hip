@@ -104,6 +104,68 @@ RoutingPtrs from_ws(const Workspace &w) {
     return RoutingPtrs{w.topk_idx, w.topk_w, w.count, w.offset, w.perm, w.pos, w.active, w.n_active};
 }
 
+// ---- a second stream for the bf16 rows' shared expert ------------------------
+// The shared expert needs only x, so on the many-row bf16 path it runs on a
+// stream of its own beside the router, the bucketing and the routed gate/up
+// GEMM; the routed down, which adds into the y that the shared down writes,
+// waits for it.  One stream and two events per device, made on first use
+// (not while the caller's stream is being captured: that call runs the
+// shared expert in line).  The lock is held from the fork to the join's wait,
+// so that the join event a call waits on is the one it recorded.
+constexpr int kMaxSideDevices = 64;
+
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+
+std::mutex side_mu;
+SideStream side_of[kMaxSideDevices];
+
+// nullptr: run in line (no device, capture before first use, or no stream)
+SideStream *side_stream_locked(hipStream_t main) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSideDevices) return nullptr;
+    SideStream &ss = side_of[dev];
+    if (ss.s && ss.fork && ss.join) return &ss;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(main, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+    if (!ss.s && hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess) ss.s = nullptr;
+    if (!ss.fork && hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess) ss.fork = nullptr;
+    if (!ss.join && hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) ss.join = nullptr;
+    return ss.s && ss.fork && ss.join ? &ss : nullptr;
+}
+
+// The many-row bf16 block with the shared expert on the side stream; route:
+// the router and the bucketing run first (stage 0), else r is given.
+hipError_t prefill_bf16_overlapped(const moe_layer_desc *d, const void *x, int32_t T, const RoutingPtrs &r, float *y,
+                                   uint32_t flags, const Workspace &w, hipStream_t s, bool route, bool *done) {
+    *done = false;
+    std::lock_guard<std::mutex> lock(side_mu);
+    SideStream *ss = side_stream_locked(s);
+    if (!ss) return hipSuccess;
+    hipError_t e = hipEventRecord(ss->fork, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ss->s, ss->fork, 0);
+    if (e != hipSuccess) return e;
+    *done = true;
+    hipError_t es = launch_prefill_shared_bf16(d, x, T, y, flags, w, ss->s);
+    const hipError_t ej = hipEventRecord(ss->join, ss->s);
+    if (es == hipSuccess) es = ej;
+    if (es != hipSuccess) {
+        (void)hipStreamWaitEvent(s, ss->join, 0);  // the caller's stream still joins what was enqueued
+        return es;
+    }
+    if (route) e = launch_router_logits(d, x, T, MOE_BF16, w, s);
+    if (route && e == hipSuccess) e = launch_route_finish(d, T, r, w, s);
+    if (e == hipSuccess) return launch_prefill(d, x, T, MOE_BF16, r, y, flags, w, s, 0, ss->join);
+    (void)hipStreamWaitEvent(s, ss->join, 0);
+    return e;
+}
+
+bool overlap_shared(const moe_layer_desc *d, int32_t T, int32_t x_type) {
+    return x_type == MOE_BF16 && d->n_ff_shared > 0 && prefill_path_ok(d, T, x_type);
+}
+
 // The whole block (stage 0) or one of its four stages.  Few rows: the decode
 // schedule; otherwise router logits, top-k + bucketing, gate/up, down.
 hipError_t forward(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r, float *y,
@@ -113,6 +175,11 @@ hipError_t forward(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_
     const int st3 = stage == 5 ? 3 : stage;
     if (small_path_ok(d, T) && small_route_ok(d, T)) return launch_small(d, x, T, x_type, r, y, flags, w, s, st3, true);
     hipError_t e = hipSuccess;
+    if (stage == 0 && overlap_shared(d, T, x_type)) {
+        bool done = false;
+        e = prefill_bf16_overlapped(d, x, T, r, y, flags, w, s, true, &done);
+        if (done || e != hipSuccess) return e;
+    }
     if (stage == 0 || stage == 1) e = launch_router_logits(d, x, T, x_type, w, s);
     if (e == hipSuccess && (stage == 0 || stage == 2)) e = launch_route_finish(d, T, r, w, s);
     if (e == hipSuccess && (stage == 0 || stage >= 3))
@@ -195,6 +262,11 @@ int moe_expert_ffn(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_
     if (!aligned16(y)) return fail(err, errlen, MOE_EALIGN, "y must be 16-byte aligned");
     Workspace w = workspace_layout(d, T, ws);
     hipStream_t s = (hipStream_t)stream;
+    if (!small_path_ok(d, T) && overlap_shared(d, T, x_type)) {
+        bool done = false;
+        const hipError_t e = prefill_bf16_overlapped(d, x, T, from_routing(r), y, flags, w, s, false, &done);
+        if (done || e != hipSuccess) return device_status(e, err, errlen);
+    }
     hipError_t e = small_path_ok(d, T)                ? launch_small(d, x, T, x_type, from_routing(r), y, flags, w, s, 0, false)
                    : prefill_path_ok(d, T, x_type) ? launch_prefill(d, x, T, x_type, from_routing(r), y, flags, w, s, 0)
                                                    : launch_ffn_large(d, x, T, x_type, from_routing(r), y, flags, w, s, 0);

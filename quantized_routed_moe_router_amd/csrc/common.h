@@ -868,8 +868,17 @@ hipError_t launch_combine(const moe_layer_desc *d, const void *x, int32_t T, int
 // many rows with Q2K experts (bf16 rows, or fp32 rows beyond the decode
 // schedule): MFMA grouped GEMMs
 bool prefill_path_ok(const moe_layer_desc *d, int32_t T, int32_t x_type);
+// shared_done: bf16 rows whose shared expert runs on another stream
+// (launch_prefill_shared_bf16): the shared launches are left out here, and
+// the routed down (which adds into the y that the shared down writes) waits
+// for this event.
 hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
-                          float *y, uint32_t flags, const Workspace &ws, hipStream_t s, int stage);
+                          float *y, uint32_t flags, const Workspace &ws, hipStream_t s, int stage,
+                          hipEvent_t shared_done = nullptr);
+// bf16 rows: the shared expert alone (its Q8_0 weights split into bf16
+// halves, gate/up -> hs, down -> y = ys (+ y)); it needs only x.
+hipError_t launch_prefill_shared_bf16(const moe_layer_desc *d, const void *x, int32_t T, float *y, uint32_t flags,
+                                      const Workspace &ws, hipStream_t s);
 constexpr int kMaxHotlist = 16384;                  // entries one hot-list sort takes
 constexpr int64_t kHotCountMax = (int64_t)1 << 39;  // counts are clamped below this in the sort key
 hipError_t launch_count_selections(const int32_t *topk_idx, int32_t T, int32_t k, int32_t E, int32_t layer,

@@ -825,8 +825,45 @@ bool prefill_path_ok(const moe_layer_desc *d, int32_t T, int32_t x_type) {
 // mode: the shared expert on its int8 GEMMs (or the batched kernels), the
 // routed down writes one row per pair and the gather adds them in slot
 // order, so that two runs give the same bits.
+hipError_t launch_prefill_shared_bf16(const moe_layer_desc *d, const void *x, int32_t T, float *y, uint32_t flags,
+                                      const Workspace &ws, hipStream_t s) {
+    const int D = d->n_embd, Fs = d->n_ff_shared;
+    const int64_t nw = (int64_t)Fs * D, nb = nw / 32;
+    uint16_t *hi = ws.pf_shw, *lo = ws.pf_shw + 3 * nw;
+    const unsigned g = (unsigned)((4 * nb + 255) / 256);  // a thread per 8 weights
+    pf_q8_split_kernel<<<g, 256, 0, s>>>((const uint8_t *)d->sh_gate, nb, hi, lo);
+    pf_q8_split_kernel<<<g, 256, 0, s>>>((const uint8_t *)d->sh_up, nb, hi + nw, lo + nw);
+    pf_q8_split_kernel<<<g, 256, 0, s>>>((const uint8_t *)d->sh_down, nb, hi + 2 * nw, lo + 2 * nw);
+    SgArgs sg{};
+    sg.a = (const uint16_t *)x;
+    sg.wh = hi;
+    sg.wl = lo;
+    sg.T = T;
+    sg.K = D;
+    sg.Fs = Fs;
+    sg.D = D;
+    sg.hs = ws.pf_hsb;
+    sg.hs_lo = ws.pf_hsb_lo;
+    pf_sg_gemm_kernel<0><<<dim3(Fs / 128, (T + kSgM - 1) / kSgM), 512, 0, s>>>(sg);
+    SgArgs dn{};
+    dn.a = ws.pf_hsb;
+    dn.a_lo = ws.pf_hsb_lo;
+    dn.wh = ws.pf_shw + 2 * nw;
+    dn.wl = ws.pf_shw + 5 * nw;
+    dn.T = T;
+    dn.K = Fs;
+    dn.Fs = Fs;
+    dn.D = D;
+    dn.y = y;
+    dn.accumulate = (flags & MOE_ACCUMULATE) ? 1 : 0;
+    pf_sg_gemm_kernel<1><<<dim3(D / 256, (T + kSgM - 1) / kSgM), 512, 0, s>>>(dn);
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
-                          float *y, uint32_t flags, const Workspace &ws, hipStream_t s, int stage) {
+                          float *y, uint32_t flags, const Workspace &ws, hipStream_t s, int stage,
+                          hipEvent_t shared_done) {
+    const bool apart = shared_done != nullptr && x_type == MOE_BF16;  // the shared expert runs elsewhere
     const bool f32 = x_type == MOE_F32;
     const int D = d->n_embd, F = d->n_ff_exp, k = d->n_expert_used, E = d->n_expert, Fs = d->n_ff_shared;
     const int ntmax = pf_max_tiles(T, k, E);
@@ -860,7 +897,7 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int
             const hipError_t e = sgq ? launch_shared_q8_mfma(d, T, ws, ws.pf_xinv, s, 3)
                                      : launch_ffn_large_shared(d, x, T, x_type, r, y, flags, ws, s, 3);
             if (e != hipSuccess) return e;
-        } else if (Fs > 0) {
+        } else if (Fs > 0 && !apart) {
             // shared weights split into bf16 halves, then the shared gate/up GEMM
             const int64_t nw = (int64_t)Fs * D, nb = nw / 32;
             uint16_t *hi = ws.pf_shw, *lo = ws.pf_shw + 3 * nw;
@@ -918,7 +955,10 @@ hipError_t launch_prefill(const moe_layer_desc *d, const void *x, int32_t T, int
                                                                  PfPrepShared{nullptr, (int)P, nullptr, 0, nullptr, nullptr, -1,
                                                                               nullptr, nullptr, nullptr, nullptr, nullptr,
                                                                               nullptr});
-        if (Fs > 0) {
+        if (apart) {
+            const hipError_t e = hipStreamWaitEvent(s, shared_done, 0);  // y holds the shared expert's rows
+            if (e != hipSuccess) return e;
+        } else if (Fs > 0) {
             const int64_t nw = (int64_t)Fs * D;
             SgArgs sg{};
             sg.a = ws.pf_hsb;

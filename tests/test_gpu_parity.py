@@ -344,6 +344,52 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
 
 
+def test_bf16_shared_expert_beside_the_routed_path():
+    # bf16 rows on the matrix-core path run the shared expert on a second
+    # stream that the routed down waits for: eager (the layer, and route then
+    # expert_ffn, both plain and accumulating into y) and the layer captured
+    # into a HIP graph, whose fork and join are captured too, replayed with
+    # eager work between the replays, all against the oracle
+    import quantized_routed_moe_router_amd as moe
+    T = 40
+    L = synth.make_layer(110, 0, D=512, E=16, k=4, F=512, Fs=256)
+    x = synth.activations(111, T, 512)
+    xb = synth.to_bf16_bits(x)
+    y_ref, idx_ref, w_ref = oracle.moe_forward(L, x_bf16=xb)
+    W = gu.upload(L)
+    xd = gu.x_to_device(x_bf16=xb)
+    ws = moe.alloc_workspace(W, T, moe.BF16)
+    r = moe.Routing(T, 4, 16)
+    y = torch.zeros((T, 512), dtype=torch.float32, device="cuda")
+    moe.layer_forward(W, xd, y, ws, routing=r)
+    torch.cuda.synchronize()
+    gu.check_routing(r, idx_ref, w_ref, L.n_expert)
+    gu.assert_close(y.cpu().numpy(), y_ref)
+    y2 = torch.full((T, 512), 0.25, dtype=torch.float32, device="cuda")
+    moe.expert_ffn(W, xd, r, y2, ws, accumulate=True)
+    y3 = torch.zeros_like(y2)
+    moe.expert_ffn(W, xd, r, y3, ws)
+    torch.cuda.synchronize()
+    gu.assert_close(y2.cpu().numpy(), y_ref + np.float32(0.25))
+    gu.assert_close(y3.cpu().numpy(), y_ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            moe.layer_forward(W, xd, y, ws, routing=r)
+    torch.cuda.current_stream().wait_stream(side)
+    xo = gu.x_to_device(x_bf16=synth.to_bf16_bits(synth.activations(112, T, 512)))
+    for rep in range(3):
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        gu.assert_close(y.cpu().numpy(), y_ref, what="y, replay %d" % rep)
+        yo = torch.zeros_like(y)
+        moe.layer_forward(W, xo, yo, ws)  # other eager work on the same workspace
+        torch.cuda.synchronize()
+
+
 def test_selection_counts_and_hotlist_bit_exact():
     # counts per {layer, expert} merged over 43 layers of routings (one from a
     # real forward, with out-of-range entries mixed in elsewhere), then hot

@@ -238,6 +238,9 @@ size_t moe_workspace_size(const moe_layer_desc *d, int32_t max_rows, int32_t x_t
     size_t b = ws_bytes_for(d, max_rows);
     b = std::max(b, ws_bytes_for(d, std::min<int32_t>(max_rows, 4)));
     b = std::max(b, ws_bytes_for(d, std::min<int32_t>(max_rows, 64)));
+    // the largest row count whose router writes partial sums
+    const int32_t split_top = std::min<int32_t>(127, kRouteMidPairs / d->n_expert_used);
+    b = std::max(b, ws_bytes_for(d, std::min<int32_t>(max_rows, split_top)));
     return b;
 }
 

@@ -773,6 +773,18 @@ struct Workspace {
 
 constexpr int kPfTileRows = 64;  // pair rows per tile of the many-row bf16 path
 
+// Routing of 17 to 127 rows with at most kRouteMidPairs pairs (the pairs
+// are then sorted in one block) and at most 256 experts: the fp64 router
+// splits the reduction over router_parts blocks per 16 x 16 tile (128
+// columns a wave), whose partial sums the top-k selection adds as it reads
+// them.  1: the router writes the logits themselves.
+constexpr int kRouteMidPairs = 1024;
+constexpr int kMaxRouterParts = 8;
+__host__ __device__ inline int router_parts(int32_t T, int D, int k, int E) {
+    if (T <= 16 || T >= 128 || D % 512 || (int64_t)T * k > kRouteMidPairs || E > 256) return 1;
+    return D / 512 < kMaxRouterParts ? D / 512 : kMaxRouterParts;
+}
+
 // tiles of at most kPfTileRows pairs over the active experts
 __host__ inline int pf_max_tiles(int32_t T, int k, int E) {
     const int64_t P = (int64_t)T * k;
@@ -792,7 +804,7 @@ __host__ inline Workspace workspace_layout(const moe_layer_desc *d, int32_t T, v
         off = align_up(off + n, 256);
         return b ? (void *)(b + at) : nullptr;
     };
-    w.logits = (double *)take(sizeof(double) * (size_t)T * (size_t)E);
+    w.logits = (double *)take(sizeof(double) * (size_t)T * (size_t)E * (size_t)router_parts(T, D, k, E));
     w.topk_idx = (int32_t *)take(sizeof(int32_t) * (size_t)P);
     w.topk_w = (float *)take(sizeof(float) * (size_t)P);
     w.count = (int32_t *)take(sizeof(int32_t) * (size_t)E);

@@ -56,11 +56,15 @@ MOE_DEV float router_x(const RouterX<XT> &v, int q) {
 // KS = 4 (fewer rows): the 4 waves of a block take quarters of the
 // reduction of one 16 x 16 tile instead, and wave 0 adds the four partial
 // sums in wave order (fixed, so the result does not vary between runs); the
-// blocks then map to tiles in order (n_ttx = token tiles, n_eq = expert tiles).
+// blocks then map to tiles in order (n_ttx = token tiles, n_eq = expert
+// tiles).  nparts > 1: nparts blocks per tile take consecutive slices of the
+// reduction, and block b of a tile writes its sum, without the bias, to
+// partial row set b (logits + b*T*E); the selection adds them in order.
 template <int XT, int KS>
 __global__ void __launch_bounds__(256) router_mfma_kernel(const float *__restrict__ W, const float *__restrict__ bias,
                                                           const void *__restrict__ xin, int T, int D, int E,
-                                                          double *__restrict__ logits, int n_ttx, int n_eq) {
+                                                          double *__restrict__ logits, int n_ttx, int n_eq,
+                                                          int nparts) {
     __shared__ double red[KS == 4 ? 3 : 1][64][4];
     const int L = blockIdx.x, xcd = L & 7, j = L >> 3;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -74,10 +78,15 @@ __global__ void __launch_bounds__(256) router_mfma_kernel(const float *__restric
         kbeg = 0;
         kend = D;
     } else {
-        tt = L / n_eq;
-        e0 = (L % n_eq) * 16;
-        kbeg = wave * (D / 4);
-        kend = kbeg + D / 4;
+        const int tile = L / nparts, part = L % nparts, kw = D / (4 * nparts);
+        tt = tile / n_eq;
+        e0 = (tile % n_eq) * 16;
+        kbeg = (part * 4 + wave) * kw;
+        kend = kbeg + kw;
+        if (nparts > 1) {
+            logits += (int64_t)part * T * E;
+            bias = nullptr;
+        }
     }
     const int t0 = tt * 16;
     if (t0 >= T || e0 >= E) return;  // uniform over the block when KS = 4
@@ -158,24 +167,112 @@ __global__ void __launch_bounds__(256) route_finish_small_kernel(const double *_
                        nullptr, 0);
 }
 
-// One wave per token: top-k of its logit row.
-__global__ void __launch_bounds__(256) router_topk_kernel(const double *__restrict__ logits, int T, int E, int k,
+// One wave per token: top-k of its logit row.  PARTS: the row is the sum of
+// nparts partial row sets (the split router's, T*E apart) in order, then the
+// bias; the eight reads of a logit are issued at once (past nparts they
+// re-read set 0 and add 0).
+template <int PER, bool PARTS>
+__global__ void __launch_bounds__(256) router_topk_kernel(const double *__restrict__ logits, int nparts,
+                                                          const float *__restrict__ bias, int T, int E, int k,
                                                           float route_scale, int32_t *__restrict__ topk_idx,
                                                           float *__restrict__ topk_w) {
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    select_topk(logits + (int64_t)t * E, E, k, route_scale, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
+    const double *lt = logits + (int64_t)t * E;
+    const int64_t stride = (int64_t)T * E;
+    auto logit = [&](int e) {
+        if constexpr (!PARTS) {
+            return lt[e];
+        } else {
+            double pv[kMaxRouterParts];
+#pragma unroll
+            for (int b = 0; b < kMaxRouterParts; ++b) pv[b] = lt[min(b, nparts - 1) * stride + e];
+            const double be = bias ? (double)bias[e] : 0.0;
+            double v = pv[0];
+#pragma unroll
+            for (int b = 1; b < kMaxRouterParts; ++b) v += b < nparts ? pv[b] : 0.0;
+            return v + be;
+        }
+    };
+    select_topk_load<PER>(logit, E, k, route_scale, topk_idx + (int64_t)t * k, topk_w + (int64_t)t * k);
 }
 
-__global__ void __launch_bounds__(1024) bucket_small_kernel(const int32_t *__restrict__ topk_idx, int P, int E,
-                                                            int32_t *__restrict__ count, int32_t *__restrict__ offset,
-                                                            int32_t *__restrict__ perm, int32_t *__restrict__ pos,
-                                                            int32_t *__restrict__ active,
-                                                            int32_t *__restrict__ n_active) {
-    __shared__ int32_t sidx[1024];
-    for (int p = threadIdx.x; p < P; p += blockDim.x) sidx[p] = topk_idx[p];
+// Stable counting sort of up to 1024 pairs by expert in one block of 16
+// waves, in LDS.  Wave w holds pairs 64w..64w+63; ballots over the expert's
+// bits rank equal experts inside the wave (the lower pair id first); a
+// prefix over the waves per expert, then one scan over the experts of
+// (count | active flag << 16), gives each expert's offset and place in the
+// active list, and each pair's slot is offset + earlier waves' count + rank.
+// The result is a pure function of topk_idx: the same arrays as the other
+// sorts.
+constexpr int kMidWaves = 16;
+constexpr int kMidPairs = 64 * kMidWaves;
+static_assert(kMidPairs == kRouteMidPairs, "pairs of the one-block sort");
+
+__global__ void __launch_bounds__(1024) bucket_mid_kernel(const int32_t *__restrict__ topk_idx, int P, int E,
+                                                          int32_t *__restrict__ count, int32_t *__restrict__ offset,
+                                                          int32_t *__restrict__ perm, int32_t *__restrict__ pos,
+                                                          int32_t *__restrict__ active,
+                                                          int32_t *__restrict__ n_active) {
+    __shared__ int32_t wc[kMidWaves][kMaxExperts];  // per (wave, expert): count, then first slot
+    __shared__ int32_t wsum[kMidWaves];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const bool valid = tid < P;
+    const int key = valid ? topk_idx[tid] : 0;
+    for (int w = 0; w < kMidWaves; ++w)
+        if (tid < E) wc[w][tid] = 0;  // blockDim.x = kMaxExperts >= E
+    uint64_t same = __ballot(valid);
+    const int nbits = 32 - __clz(max(E - 1, 1));
+    for (int b = 0; b < nbits; ++b) {
+        const uint64_t bal = __ballot(valid && ((key >> b) & 1));
+        same &= ((key >> b) & 1) ? bal : ~bal;
+    }
+    const int rank = __popcll(same & ((1ull << lane) - 1ull));
     __syncthreads();
-    bucket_small(sidx, P, E, 1, count, offset, perm, pos, active, n_active, nullptr, 0);
+    if (valid && rank == 0) wc[wave][key] = __popcll(same);
+    __syncthreads();
+
+    const int e = tid;
+    int tot = 0;
+    if (e < E) {
+        for (int w = 0; w < kMidWaves; ++w) {
+            const int c = wc[w][e];
+            wc[w][e] = tot;
+            tot += c;
+        }
+    }
+    const int packed = tot | ((tot > 0 ? 1 : 0) << 16);  // both sums stay below 2^16
+    int incl = packed;
+    for (int o = 1; o < 64; o <<= 1) {
+        const int v = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += v;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+    for (int w = 0; w < kMidWaves; ++w) {
+        const int v = wsum[w];
+        before += w < wave ? v : 0;
+        all += v;
+    }
+    const int excl = before + incl - packed, first = excl & 0xFFFF, na = all >> 16;
+    if (e < E) {
+        count[e] = tot;
+        offset[e] = first;
+        for (int w = 0; w < kMidWaves; ++w) wc[w][e] += first;
+        if (tot > 0) active[excl >> 16] = e;  // below na
+        if (e >= na) active[e] = -1;
+    }
+    if (tid == 0) {
+        n_active[0] = na;
+        offset[E] = P;
+    }
+    __syncthreads();
+    if (valid) {
+        const int slot = wc[wave][key] + rank;
+        perm[slot] = tid;
+        pos[tid] = slot;
+    }
 }
 
 // Stable counting sort of the P = T*k pairs by expert, one block of 8 waves.
@@ -299,18 +396,19 @@ hipError_t launch_router_logits(const moe_layer_desc *d, const void *x, int32_t 
         const int grid = 8 * n_ttx * n_eq;
         if (x_type == MOE_BF16)
             router_mfma_kernel<MOE_BF16, 1><<<grid, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E, ws.logits,
-                                                                  n_ttx, n_eq);
+                                                                  n_ttx, n_eq, 1);
         else
             router_mfma_kernel<MOE_F32, 1><<<grid, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E, ws.logits,
-                                                                 n_ttx, n_eq);
+                                                                 n_ttx, n_eq, 1);
     } else if (router_mfma4_ok(T, D)) {
-        const int n_tt = (T + 15) / 16, n_et = (E + 15) / 16;
+        const int n_tt = (T + 15) / 16, n_et = (E + 15) / 16, np = router_parts(T, D, d->n_expert_used, E);
+        const unsigned grid = (unsigned)(n_tt * n_et * np);
         if (x_type == MOE_BF16)
-            router_mfma_kernel<MOE_BF16, 4><<<n_tt * n_et, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E,
-                                                                         ws.logits, n_tt, n_et);
+            router_mfma_kernel<MOE_BF16, 4><<<grid, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E,
+                                                                  ws.logits, n_tt, n_et, np);
         else
-            router_mfma_kernel<MOE_F32, 4><<<n_tt * n_et, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E,
-                                                                        ws.logits, n_tt, n_et);
+            router_mfma_kernel<MOE_F32, 4><<<grid, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E,
+                                                                 ws.logits, n_tt, n_et, np);
     } else {
         dim3 g((T + 15) / 16, (E + 15) / 16);
         if (x_type == MOE_BF16)
@@ -329,10 +427,25 @@ hipError_t launch_route_finish(const moe_layer_desc *d, int32_t T, const Routing
                                                      r.count, r.offset, r.perm, r.pos, r.active, r.n_active);
         return hipGetLastError();
     }
-    router_topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(ws.logits, T, E, k, d->route_scale, r.topk_idx, r.topk_w);
-    if (P <= 1024)
-        bucket_small_kernel<<<1, 1024, 0, s>>>(r.topk_idx, P, E, r.count, r.offset, r.perm, r.pos, r.active,
-                                               r.n_active);
+    const int np = router_parts(T, d->n_embd, k, E);
+    auto topk = [&](auto kern) {
+        kern<<<(T + 3) / 4, 256, 0, s>>>(ws.logits, np, d->router_bias, T, E, k, d->route_scale, r.topk_idx,
+                                         r.topk_w);
+    };
+    if (np > 1) {  // E <= 256 here
+        if (E <= 64) topk(router_topk_kernel<1, true>);
+        else if (E <= 128) topk(router_topk_kernel<2, true>);
+        else topk(router_topk_kernel<4, true>);
+    } else {
+        if (E <= 64) topk(router_topk_kernel<1, false>);
+        else if (E <= 128) topk(router_topk_kernel<2, false>);
+        else if (E <= 256) topk(router_topk_kernel<4, false>);
+        else if (E <= 512) topk(router_topk_kernel<8, false>);
+        else topk(router_topk_kernel<16, false>);
+    }
+    if (P <= kMidPairs)
+        bucket_mid_kernel<<<1, kMaxExperts, 0, s>>>(r.topk_idx, P, E, r.count, r.offset, r.perm, r.pos, r.active,
+                                                    r.n_active);
     else
         bucket_kernel<<<1, 512, 0, s>>>(r.topk_idx, P, E, r.count, r.offset, r.perm, r.pos, r.active, r.n_active);
     return hipGetLastError();

@@ -181,8 +181,9 @@ MOE_DEV int wave_min_i32(int v) {
 // sum_j exp(l_j - l_0) in fp64, the exponentials computed by lanes 0..k-1 at
 // once.  Writes idx_out[s], w_out[s] unless idx_out is null; returns the
 // lane's slot expert (lanes < k).
-template <int PER>
-MOE_DEV int select_topk_per(const double *lg, int E, int k, float route_scale, int32_t *idx_out, float *w_out) {
+// (select_topk_load: the same with logit(e) from a loader, e < E.)
+template <int PER, class Load>
+MOE_DEV int select_topk_load(Load logit, int E, int k, float route_scale, int32_t *idx_out, float *w_out) {
     const int lane = threadIdx.x & 63;
     constexpr int NONE = 0x7FFFFFFF;
     double v[PER];
@@ -190,7 +191,7 @@ MOE_DEV int select_topk_per(const double *lg, int E, int k, float route_scale, i
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int e = lane + 64 * i;
-        v[i] = lg[min(e, E - 1)];
+        v[i] = logit(min(e, E - 1));
         if (e < E) avail |= 1u << i;
     }
     double bv = -__builtin_inf();
@@ -234,6 +235,11 @@ MOE_DEV int select_topk_per(const double *lg, int E, int k, float route_scale, i
         w_out[lane] = (float)((double)route_scale * ex / den);
     }
     return my_e;
+}
+
+template <int PER>
+MOE_DEV int select_topk_per(const double *lg, int E, int k, float route_scale, int32_t *idx_out, float *w_out) {
+    return select_topk_load<PER>([&](int e) { return lg[e]; }, E, k, route_scale, idx_out, w_out);
 }
 
 MOE_DEV int select_topk(const double *lg, int E, int k, float route_scale, int32_t *idx_out, float *w_out) {

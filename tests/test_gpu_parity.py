@@ -197,6 +197,32 @@ def test_route_many_rows_matrix_cores(T, bf16):
     gu.check_routing(r, idx_ref, w_ref, L.n_expert)
 
 
+@pytest.mark.parametrize("T,E,k,D", [(17, 1024, 1, 512), (170, 64, 6, 512), (256, 8, 4, 512), (64, 512, 16, 512),
+                                     (33, 300, 3, 512), (171, 64, 6, 512), (33, 256, 6, 4096), (100, 64, 8, 2048),
+                                     (17, 16, 2, 1024), (127, 200, 8, 4096)])
+def test_route_one_block_sort_bounds(T, E, k, D):
+    # 17 to 1024 pairs: one block selects every row's top k and sorts the
+    # pairs (16 waves of 64 pairs): the largest expert count (ten key bits),
+    # exactly 1024 pairs with every expert active, the largest k, an expert
+    # count that is no power of two, one pair over the bound (the many-pair
+    # sort instead), and below 128 rows with n_embd 1024 to 4096 the router's
+    # reduction split over 2, 4 and 8 blocks whose partial sums the selection
+    # adds (ragged token and expert tiles at 127 rows and 200 experts)
+    import quantized_routed_moe_router_amd as moe
+    L = synth.make_layer(130 + T, 0, D=D, E=E, k=k, F=64, Fs=0)
+    L.router_bias = synth.zipf_bias(131, E)
+    x = synth.activations(132 + T, T, D)
+    idx_ref, w_ref, gap = oracle.route(L, x=x)
+    W = gu.upload(L)
+    ws = moe.alloc_workspace(W, T)
+    r = moe.Routing(T, k, E)
+    moe.route(W, gu.x_to_device(x=x), r, ws)
+    torch.cuda.synchronize()
+    print("route T=%d E=%d k=%d: %d active, smallest k/k+1 gap %.3g" % (T, E, k, int(r.n_active.cpu()[0]),
+                                                                        float(np.min(gap))))
+    gu.check_routing(r, idx_ref, w_ref, E)
+
+
 def test_route_scale_and_accumulate():
     L = synth.make_layer(92, 0, D=512, E=32, k=4, F=256, Fs=128)
     L.route_scale = 1.5

@@ -347,7 +347,7 @@ template <int MODE, int W>
 __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2))) pf_gemm_kernel(PfArgs a) {
     typedef PfStageT<W> Stage;
     constexpr int PM = pf_m(W), NT = 64 * W, BR = kPfWaveRows * W, AU = PM * kPfARow, SD = PM * 16;
-    __shared__ Stage st0, st1;
+    __shared__ Stage stg[2];
     __shared__ int32_t row_tok[PM];
     __shared__ float row_f[PM];
     constexpr int kColRows = MODE == 0 ? BR / 2 : BR;  // output columns per block
@@ -405,8 +405,8 @@ __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 
     // uniform (scalar) DMA operands: stage LDS addresses, this wave's
     // destinations within a stage, the weight base of this wave's rows
     const int wv = __builtin_amdgcn_readfirstlane(wave);
-    const uint32_t lds_st[2] = {(uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(&st0)),
-                                (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(&st1))};
+    const uint32_t lds_st[2] = {(uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(&stg[0])),
+                                (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(&stg[1]))};
     const uint8_t *wbm_u = (const uint8_t *)wave_uniform(wbm);
     // A tile of at most 32 pairs (one row subtile) copies only code rows
     // 0-31 (copies 0-16: waves take copies w and w + 8, wave 0 also copy 16)
@@ -528,26 +528,44 @@ __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 
     };
 
     issue(nsub_c, 0, 0);
-    for (int kb = 0; kb < nkb; kb += 2) {
-        if (kb + 1 < nkb) {
-            issue(nsub_c, 1, kb + 1);
-            wait_stage(nsub_c);
-        } else {
+    if constexpr (W == 8) {
+        // One barrier per step: past it every wave's copies of step kb are
+        // in LDS and every wave has finished step kb - 1, whose stage then
+        // takes the copies of step kb + 1 while step kb computes.  (With
+        // many pairs the compute, not the copies, sets the pace, and the
+        // second barrier of the scheme below cost about 7%.)
+        for (int kb = 0; kb < nkb; ++kb) {
             vmem_wait_at_most<0>();
+            stage_barrier();
+            if (kb + 1 < nkb) issue(nsub_c, (kb + 1) & 1, kb + 1);
+            compute(stg[kb & 1]);
         }
-        stage_barrier();
-        compute(st0);
-        stage_barrier();
-        if (kb + 1 >= nkb) break;
-        if (kb + 2 < nkb) {
-            issue(nsub_c, 0, kb + 2);
-            wait_stage(nsub_c);
-        } else {
-            vmem_wait_at_most<0>();
+        stage_barrier();  // the stages are free again
+    } else {
+        // Few pairs: the copies set the pace, so those of step kb + 1 are
+        // issued before the wait for step kb, which needs a second barrier
+        // (every wave done with the stage they overwrite).
+        for (int kb = 0; kb < nkb; kb += 2) {
+            if (kb + 1 < nkb) {
+                issue(nsub_c, 1, kb + 1);
+                wait_stage(nsub_c);
+            } else {
+                vmem_wait_at_most<0>();
+            }
+            stage_barrier();
+            compute(stg[0]);
+            stage_barrier();
+            if (kb + 1 >= nkb) break;
+            if (kb + 2 < nkb) {
+                issue(nsub_c, 0, kb + 2);
+                wait_stage(nsub_c);
+            } else {
+                vmem_wait_at_most<0>();
+            }
+            stage_barrier();
+            compute(stg[1]);
+            stage_barrier();
         }
-        stage_barrier();
-        compute(st1);
-        stage_barrier();
     }
     };
     if constexpr (W == 8) {
@@ -559,7 +577,7 @@ __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 
 
     if constexpr (MODE == 0) {
         // up waves hand their values to the gate waves of the same rows
-        float *U = (float *)&st0;  // [PM rows][kColRows columns]
+        float *U = (float *)&stg[0];  // [PM rows][kColRows columns]
         static_assert(sizeof(Stage) >= PM * kColRows * sizeof(float), "exchange area");
         if (wave >= W / 2) {
 #pragma unroll
@@ -684,7 +702,7 @@ MOE_DEV int sg_unit(int r, int u) { return r * kSgRowUnits + (u ^ sum_swz(r)); }
 template <int MODE>
 __global__ void __launch_bounds__(512) pf_sg_gemm_kernel(SgArgs a) {
     typedef SgStageT<MODE == 1> SgStage;
-    __shared__ SgStage st0, st1;
+    __shared__ SgStage stg[2];
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, c = lane & 31, h = lane >> 5;
     const int m0 = blockIdx.y * kSgM;
     const int nkc = a.K / kSgKc;
@@ -712,7 +730,6 @@ __global__ void __launch_bounds__(512) pf_sg_gemm_kernel(SgArgs a) {
             pf_dma16(a.wl + boff[i] + kc * kSgKc, &S.bl[i * 512 + 64 * wave]);
         }
     };
-    constexpr int kIssued = MODE == 1 ? 6 : 5;
     v16f tot[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -743,31 +760,20 @@ __global__ void __launch_bounds__(512) pf_sg_gemm_kernel(SgArgs a) {
             }
         }
     };
-    issue(st0, 0);
-    for (int kc = 0; kc < nkc; kc += 2) {
-        if (kc + 1 < nkc) {
-            issue(st1, kc + 1);
-            vmem_wait_at_most<kIssued>();
-        } else {
-            vmem_wait_at_most<0>();
-        }
+    // one barrier per step, as in the routed GEMM of many pairs: past it
+    // every wave's copies of chunk kc are in LDS and every wave has finished
+    // chunk kc - 1, whose stage then takes chunk kc + 1
+    issue(stg[0], 0);
+    for (int kc = 0; kc < nkc; ++kc) {
+        vmem_wait_at_most<0>();
         stage_barrier();
-        compute(st0);
-        stage_barrier();
-        if (kc + 1 >= nkc) break;
-        if (kc + 2 < nkc) {
-            issue(st0, kc + 2);
-            vmem_wait_at_most<kIssued>();
-        } else {
-            vmem_wait_at_most<0>();
-        }
-        stage_barrier();
-        compute(st1);
-        stage_barrier();
+        if (kc + 1 < nkc) issue(stg[(kc + 1) & 1], kc + 1);
+        compute(stg[kc & 1]);
     }
+    stage_barrier();  // the stages are free again
     if constexpr (MODE == 0) {
         // up waves hand their values to the gate waves, 64 rows at a time
-        float *U = (float *)&st0;  // [64 rows][128 columns], 32 KB of the 40 KB stage
+        float *U = (float *)&stg[0];  // [64 rows][128 columns], 32 KB of the 40 KB stage
         static_assert(sizeof(SgStage) >= 64 * 128 * sizeof(float), "exchange area");
 #pragma unroll
         for (int half = 0; half < 2; ++half) {

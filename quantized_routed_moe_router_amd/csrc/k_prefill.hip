@@ -6,10 +6,12 @@
 // the Q2_K subsection for w = d*sc*q - dmin*m).
 //
 // A tile is up to 64 pairs of one expert (two 32-row MFMA subtiles).  A block
-// of 8 waves streams one 256-weight super-block column of 256 weight rows
-// (gate and up, or down) per step through two LDS stages filled by
-// global-to-LDS DMA; each wave owns 32 weight rows for both subtiles.  Per
-// super-block column:
+// of 8 waves streams one 256-weight super-block column of 512 weight rows
+// (256 F-rows of gate and of up, or 512 down columns) per step through two
+// LDS stages filled by global-to-LDS DMA; each wave owns 64 weight rows (two
+// 32-row subtiles) against both pair subtiles, and each activation read from
+// LDS feeds both of its row subtiles.  (The small variant: 4 waves, tiles of
+// up to 32 pairs.)  Per super-block column:
 //   sum_k w_k a_k = d * sum_k (sc*q)_k a_k - sum_g (dmin*m_g) * (sum_{k in g} a_k)
 // The first sum runs on v_mfma_i32_32x32x32_i8: the codes sc*q (0..45) are
 // exact int8 and the activations are int16 codes c = rint(a*S) split as
@@ -454,24 +456,26 @@ __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 
     auto compute = [&](Stage &S) {
         // unit 16*pass + 2p + h of row q*32 + c: constant offsets from abase
         const u32x4 *abase = &S.a[c * kPfARow + h];
+        // both row subtiles' codes first, so that each activation read
+        // feeds the two of them
+        v4i bq[2][8];
+        uint32_t bmh[2][4], bml[2][4];
+        float dsc[2];
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
-            // keep the two column subtiles apart in the schedule (registers)
-            __builtin_amdgcn_sched_barrier(0);
             const int R = wave * kPfWaveRows + 32 * n + c;
-            v4i bq[8];
-            uint32_t bmh[4], bml[4];
             const uint8_t *rb = (const uint8_t *)&S.b[R * 5];
             const uint2 sm = *(const uint2 *)(rb + 8 * h);
             const u32x4 q0 = *(const u32x4 *)(rb + 16 + 32 * h), q1 = *(const u32x4 *)(rb + 32 + 32 * h);
             const uint32_t dd = S.dd[R];
-            const float dsc = half_bits_to_float(dd), dmin = half_bits_to_float(dd >> 16);
+            dsc[n] = half_bits_to_float(dd);
+            const float dmin = half_bits_to_float(dd >> 16);
 #pragma unroll
             for (int p = 0; p < 8; ++p) {
                 const uint32_t Q = p < 4 ? q0[p] : q1[p - 4];
                 const uint32_t sc = ((p < 4 ? sm.x : sm.y) >> (8 * (p & 3))) & 15u;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) bq[p][j] = (int)mul_bytes((Q >> (2 * j)) & 0x03030303u, sc);
+                for (int j = 0; j < 4; ++j) bq[n][p][j] = (int)mul_bytes((Q >> (2 * j)) & 0x03030303u, sc);
             }
             // -dmin * m_g of the lane's 8 groups, exactly as bf16 hi + lo
             const uint32_t mA = (sm.x >> 4) & 0x0F0F0F0Fu, mB = (sm.y >> 4) & 0x0F0F0F0Fu;
@@ -481,45 +485,53 @@ __global__ void __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 
                 const float c0 = -dmin * (float)((mw >> (16 * (i & 1))) & 0xFFu);
                 const float c1 = -dmin * (float)((mw >> (16 * (i & 1) + 8)) & 0xFFu);
                 const uint32_t hw = bf16x2_rne(c0, c1);
-                bmh[i] = hw;
-                bml[i] = bf16x2_rne(c0 - __uint_as_float(hw << 16), c1 - __uint_as_float(hw & 0xFFFF0000u));
+                bmh[n][i] = hw;
+                bml[n][i] = bf16x2_rne(c0 - __uint_as_float(hw << 16), c1 - __uint_as_float(hw & 0xFFFF0000u));
             }
-            // two independent accumulation chains, one per row subtile
-            v16i acc[2];
+        }
+        v16i acc[2][2];  // [row subtile][pair subtile]
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
 #pragma unroll
             for (int q = 0; q < 2; ++q)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) acc[q][v] = 0;
+                for (int v = 0; v < 16; ++v) acc[n][q][v] = 0;
 #pragma unroll
-            for (int pass = 0; pass < 2; ++pass) {
-                if (pass == 1) {
+        for (int pass = 0; pass < 2; ++pass) {
+            if (pass == 1) {
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
 #pragma unroll
                     for (int q = 0; q < NSUB; ++q)
 #pragma unroll
-                        for (int v = 0; v < 16; ++v) acc[q][v] <<= 8;
-                }
+                        for (int v = 0; v < 16; ++v) acc[n][q][v] <<= 8;
+            }
 #pragma unroll
-                for (int p = 0; p < 8; ++p) {
+            for (int p = 0; p < 8; ++p) {
 #pragma unroll
-                    for (int q = 0; q < NSUB; ++q) {
-                        const u32x4 av = abase[32 * kPfARow * q + 16 * pass + 2 * p];
-                        v4i ai;
-                        __builtin_memcpy(&ai, &av, 16);
-                        acc[q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ai, bq[p], acc[q], 0, 0, 0);
-                    }
+                for (int q = 0; q < NSUB; ++q) {
+                    const u32x4 av = abase[32 * kPfARow * q + 16 * pass + 2 * p];
+                    v4i ai;
+                    __builtin_memcpy(&ai, &av, 16);
+#pragma unroll
+                    for (int n = 0; n < 2; ++n)
+                        acc[n][q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ai, bq[n][p], acc[n][q], 0, 0, 0);
                 }
             }
-            const v8bf ch = as_v8bf(bmh), cl = as_v8bf(bml);
+        }
 #pragma unroll
-            for (int q = 0; q < NSUB; ++q) {
+        for (int q = 0; q < NSUB; ++q) {
+            const int row = q * 32 + c, sw = sum_swz(row);
+            const u32x4 shu = *(const u32x4 *)&S.s[4 * (row * 4 + (h ^ sw))];
+            const u32x4 slu = *(const u32x4 *)&S.s[4 * (row * 4 + ((2 + h) ^ sw))];
+            v8bf sh, sl;
+            __builtin_memcpy(&sh, &shu, 16);
+            __builtin_memcpy(&sl, &slu, 16);
 #pragma unroll
-                for (int v = 0; v < 16; ++v) tot[n][q][v] = __builtin_fmaf((float)acc[q][v], dsc, tot[n][q][v]);
-                const int row = q * 32 + c, sw = sum_swz(row);
-                const u32x4 shu = *(const u32x4 *)&S.s[4 * (row * 4 + (h ^ sw))];
-                const u32x4 slu = *(const u32x4 *)&S.s[4 * (row * 4 + ((2 + h) ^ sw))];
-                v8bf sh, sl;
-                __builtin_memcpy(&sh, &shu, 16);
-                __builtin_memcpy(&sl, &slu, 16);
+            for (int n = 0; n < 2; ++n) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) tot[n][q][v] = __builtin_fmaf((float)acc[n][q][v], dsc[n], tot[n][q][v]);
+                const v8bf ch = as_v8bf(bmh[n]), cl = as_v8bf(bml[n]);
                 tot[n][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sh, ch, tot[n][q], 0, 0, 0);
                 tot[n][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sl, ch, tot[n][q], 0, 0, 0);
                 tot[n][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sh, cl, tot[n][q], 0, 0, 0);

@@ -183,7 +183,9 @@ __global__ void __launch_bounds__(256) dec_k2_kernel(FfnArgs a, int do_route) {
 // up 2q, 2q+1] for q = 0..3), and starts on each group once it has landed.
 // Lane (r, c) dots row r of a group with chunk c of the quarter (packed fp16
 // products of the int8 codes with the hi/lo split activations); the 16 lanes
-// of a row are added by DPP, the quarters in LDS.
+// of a row are added by DPP, the quarters in LDS after the last token (the
+// waves run through the tokens without waiting for each other, each loading
+// the next token's records while it sums the current one's).
 constexpr int kSgXu = 16 * kXQ8Dwords / 4;   // 272 units: 16 chunk records
 constexpr int kSgRu = 1024 / 32 * kQ8Bytes / 16;  // 68 units: a row quarter
 constexpr int kSgCopies = 22;                 // 272 + 16 x 68 = 1360 units -> 22 copies of 64
@@ -202,7 +204,7 @@ MOE_DEV void sg_wait() {
 // areas allow one block per unit).
 __global__ void __launch_bounds__(320) dec_k2_q8sg4096_kernel(FfnArgs a, int do_route) {
     __shared__ __align__(16) u32x4 area[4][64 * kSgCopies];
-    __shared__ float part[4][16];
+    __shared__ float part[kMaxDecTokens][4][16];
     int b = blockIdx.x;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     if (do_route == 1) {
@@ -213,16 +215,13 @@ __global__ void __launch_bounds__(320) dec_k2_q8sg4096_kernel(FfnArgs a, int do_
         }
         b -= 1;
     }
-    if (wave == 4) {  // joins the block's barriers below: one per token, one between tokens
+    if (wave == 4) {  // joins the block's one barrier below
         if (do_route == 2 && b == 0) {
             const int my_e = select_topk(a.logits, a.E, a.k, a.route_scale, a.w_topk_idx, a.w_topk_w);
             bucket_one_token(my_e, a.k, a.E, a.w_count, a.w_offset, a.w_perm, a.w_pos, a.w_active, a.w_n_active,
                              a.slots, a.nslots);
         }
-        for (int t = 0; t < a.T; ++t) {
-            __syncthreads();
-            if (t + 1 < a.T) __syncthreads();
-        }
+        block_lds_sync();
         return;
     }
     const int row0 = 8 * b;  // rows row0 .. row0 + 7 of gate and of up
@@ -264,9 +263,7 @@ __global__ void __launch_bounds__(320) dec_k2_q8sg4096_kernel(FfnArgs a, int do_
     group(3);
     for (int t = 0;;) {
         // the next token's records (several tokens): issued here and held in
-        // registers while this token's sums are reduced, instead of loaded
-        // after the barriers; the compiler barrier keeps the loads in front,
-        // and the barriers of the loop wait for LDS only
+        // registers while this token's sums are written
         // (the pad dword is not loaded: a register whose load is in flight and
         // whose value is never used gets reused, and that reuse waits for the load)
         XQ8 xn;
@@ -284,25 +281,24 @@ __global__ void __launch_bounds__(320) dec_k2_q8sg4096_kernel(FfnArgs a, int do_
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const float sv = row16_sum(v[q]);
-            if (c == 0) part[wave][4 * q + r] = sv;  // [group][gate 2q, 2q+1, up 2q, 2q+1]
-        }
-        block_lds_sync();
-        if (tid < 8) {
-            const int q = tid >> 1, j = tid & 1;
-            float gs = 0.f, us = 0.f;
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                gs += part[w][4 * q + j];
-                us += part[w][4 * q + 2 + j];
-            }
-            a.hs[(int64_t)t * a.Fs + row0 + tid] = swiglu_h(gs, us);
+            if (c == 0) part[t][wave][4 * q + r] = sv;  // [group][gate 2q, 2q+1, up 2q, 2q+1]
         }
         if (!more) break;
         ++t;
-        block_lds_sync();  // part is rewritten
         xr = xn;
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = q8_dot2(q8_load(ab + 16 * (kSgXu + kSgRu * (4 * q + r)), 64 * c), xr);
+    }
+    block_lds_sync();
+    for (int o = tid; o < 8 * a.T; o += 256) {  // token o / 8, row o % 8
+        const int t = o >> 3, i = o & 7, q = i >> 1, j = i & 1;
+        float gs = 0.f, us = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            gs += part[t][w][4 * q + j];
+            us += part[t][w][4 * q + 2 + j];
+        }
+        a.hs[(int64_t)t * a.Fs + row0 + i] = swiglu_h(gs, us);
     }
 }
 

@@ -839,6 +839,15 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
 // its own rows have landed), then dots them with the prepared h of every
 // token of its bucket, into part[bucket position].  Then the combine adds,
 // per output, the shared expert's term and the k routed terms in slot order.
+// A Q8_0 shared down of width 2048 runs on the fp32 matrix cores
+// (v_mfma_f32_16x16x4f32, tokens x rows): wave w takes columns [256 w,
+// 256 w + 256) of the block's 16 rows for every token at once; lane l (token
+// and row l % 16, quarter l / 16 of the wave's columns) holds 64 consecutive
+// values of its token's hs and its row's weights d*q (exact in fp32), and
+// instruction i takes value i of each quarter, so every product enters the
+// sum once.  The waves' partial sums meet in LDS and the combine adds them
+// in wave order.  Other shared formats and widths: the rows are dotted per
+// token with the routed rows' VALU helpers.
 template <int DFMT, int SFMT>
 __global__ void __launch_bounds__(64 * kDecWaves) dec_k4_kernel(FfnArgs a) {
     static_assert(staged_fmt(DFMT), "staged formats only");
@@ -850,14 +859,46 @@ __global__ void __launch_bounds__(64 * kDecWaves) dec_k4_kernel(FfnArgs a) {
     __shared__ float ysl[kMaxDecTokens][kDecRows];
     __shared__ float wl[kMaxDecPairs];
     __shared__ int32_t posl[kMaxDecPairs];
+    constexpr bool kShQ8 = SFMT == MOE_Q8_0;
+    __shared__ float shp[kShQ8 ? kDecWaves : 1][kMaxDecTokens][kDecRows];  // matrix-core partial sums
     if constexpr (DFMT == MOE_CB2 || SFMT == MOE_CB2) load_codebook(a.codebook, cb_lds);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int row0 = blockIdx.x * kDecRows;
+    const bool sh_mfma = kShQ8 && a.Fs == 256 * kDecWaves;
+    auto shared_down_mfma = [&]() {
+        const int tq = lane & 15, kq = lane >> 4;
+        const int k0 = 256 * wave + 64 * kq;
+        const f32x4 *hp = (const f32x4 *)(a.hs + (int64_t)min(tq, a.T - 1) * a.Fs + k0);
+        f32x4 hv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) hv[i] = hp[i];
+        // two Q8_0 blocks (68 bytes): d, 32 codes, d, 32 codes
+        const uint8_t *wp = a.sh_down + (int64_t)(row0 + tq) * (a.Fs / 32 * kQ8Bytes) + (k0 / 32) * kQ8Bytes;
+        uint32_t wd[17];
+#pragma unroll
+        for (int j = 0; j < 17; ++j) wd[j] = load_u32(wp + 4 * j);
+        const float d0 = half_bits_to_float(wd[0] & 0xFFFFu), d1 = half_bits_to_float(wd[8] >> 16);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 64; ++i) {
+            const int B = i < 32 ? 2 + i : 4 + i;  // byte of code i
+            const int q = (int)(int8_t)(wd[B >> 2] >> (8 * (B & 3)));
+            const float w = (i < 32 ? d0 : d1) * (float)q;
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(hv[i >> 2][i & 3], w, acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) shp[kShQ8 ? wave : 0][4 * kq + j][tq] = acc[j];  // [token][row]
+    };
     // The shared expert's down for rows row0 + 2 wave, +1 and every token
     // (fp32 activations hs), into ysl.  A wave with a routed slot runs it
     // while the copies of its first slot's rows are in flight.
     bool sh_pending = a.Fs > 0;
     auto shared_down = [&]() {
+        sh_pending = false;
+        if (sh_mfma) {
+            shared_down_mfma();
+            return;
+        }
         const int r0 = row0 + kShDownRowsK4 * wave, c = lane % (a.Fs >> 6);
         for (int t = 0; t < a.T; ++t)
             rows_dot_ch<F32Chunk<SFMT>, false, 1>(
@@ -908,7 +949,13 @@ __global__ void __launch_bounds__(64 * kDecWaves) dec_k4_kernel(FfnArgs a) {
     for (int i = tid; i < a.T * kDecRows; i += blockDim.x) {
         const int t = i / kDecRows, r = i % kDecRows;
         const int64_t o = (int64_t)t * a.D + row0 + r;
-        float acc = a.Fs > 0 ? ysl[t][r] : 0.f;
+        float acc = 0.f;
+        if (sh_mfma) {
+#pragma unroll
+            for (int w = 0; w < kDecWaves; ++w) acc += shp[kShQ8 ? w : 0][t][r];
+        } else if (a.Fs > 0) {
+            acc = ysl[t][r];
+        }
         for (int s = 0; s < a.k; ++s) {
             const int p = t * a.k + s;
             acc = __builtin_fmaf(wl[p], part[posl[p]][r], acc);

@@ -302,6 +302,67 @@ __global__ void __launch_bounds__(320) dec_k2_q8sg4096_kernel(FfnArgs a, int do_
     }
 }
 
+// K2 with a Q8_0 shared expert at n_embd 4096 and 2 to 16 tokens: the
+// shared gate/up on the fp32 matrix cores (v_mfma_f32_16x16x4f32, tokens x
+// rows), every token at once.  Block b (after the routing block, when
+// routing) takes gate rows 8b..8b+7 (columns 0-7) and the same up rows
+// (columns 8-15); wave w takes input columns [512 w, 512 w + 512).  Lane l
+// (token and row l % 16, quarter l / 16 of the wave's columns) holds 128
+// consecutive values of its token's x and of its row's weights d*q (exact in
+// fp32); instruction i takes value i of each quarter, so every product
+// enters the sum once.  The waves' partial sums meet in LDS and are added in
+// wave order, then h = silu(g) * u.
+constexpr int kSgmWaves = 8;
+__global__ void __launch_bounds__(64 * kSgmWaves) dec_k2_q8sg_mfma_kernel(FfnArgs a, int route) {
+    __shared__ float shp[kSgmWaves][16][16];  // [wave][token][gate 0-7, up 8-15]
+    int b = blockIdx.x;
+    if (route) {
+        if (b == 0) {
+            route_finish_block(a.logits, a.T, a.E, a.k, a.route_scale, a.w_topk_idx, a.w_topk_w, a.w_count,
+                               a.w_offset, a.w_perm, a.w_pos, a.w_active, a.w_n_active, a.slots, a.nslots);
+            return;
+        }
+        b -= 1;
+    }
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, n = lane & 15, kq = lane >> 4;
+    const int row0 = 8 * b;
+    constexpr int RB = 4096 / 32 * kQ8Bytes;  // bytes of a row: 4352
+    const int k0 = 512 * wave + 128 * kq;    // the lane's 128 columns: 4 Q8_0 blocks
+    float xs[128];
+    load_x64(a.x, a.x_bf16, (int64_t)min(n, a.T - 1) * 4096 + k0, xs);
+    load_x64(a.x, a.x_bf16, (int64_t)min(n, a.T - 1) * 4096 + k0 + 64, xs + 64);
+    const uint8_t *wp = (n < 8 ? a.sh_gate : a.sh_up) + (int64_t)(row0 + (n & 7)) * RB + (k0 / 32) * kQ8Bytes;
+    uint32_t wd[34];
+#pragma unroll
+    for (int j = 0; j < 34; ++j) wd[j] = load_u32(wp + 4 * j);
+    float dq[4];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+        const int B = kQ8Bytes * blk;  // d of block blk (fp16, 2-byte aligned)
+        dq[blk] = half_bits_to_float((wd[B >> 2] >> (8 * (B & 3))) & 0xFFFFu);
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 128; ++i) {
+        const int B = kQ8Bytes * (i >> 5) + 2 + (i & 31);  // byte of code i
+        const int q = (int)(int8_t)(wd[B >> 2] >> (8 * (B & 3)));
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xs[i], dq[i >> 5] * (float)q, acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) shp[wave][4 * kq + j][n] = acc[j];
+    block_lds_sync();
+    if (tid < 8 * a.T) {  // token tid / 8, row tid % 8
+        const int t = tid >> 3, i = tid & 7;
+        float gs = 0.f, us = 0.f;
+#pragma unroll
+        for (int w = 0; w < kSgmWaves; ++w) {
+            gs += shp[w][t][i];
+            us += shp[w][t][8 + i];
+        }
+        a.hs[(int64_t)t * a.Fs + row0 + i] = swiglu_h(gs, us);
+    }
+}
+
 // K1 for one fp32 token at n_embd 4096 when the routed gate/up kernel selects
 // the top-k itself (no K2): block b computes router logit b and, with a
 // Q8_0 shared expert, 8 rows of the shared gate and of up -> hs, so the
@@ -1221,9 +1282,10 @@ hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32
         a.xp16_nat = 1;
     }
     if (d->down_type == MOE_Q2K) a.hp16 = ws.hp16;  // h records for the routed down, written by K3
-    // a Q8_0 shared expert at n_embd 4096 takes the staged K2, on x records written by K1
+    // a Q8_0 shared expert at n_embd 4096 takes the staged K2: at one token on
+    // x records written by K1, at several on the matrix cores from x itself
     const bool sg_staged = has_sh && a.shared_fmt == MOE_Q8_0 && a.D == 4096 && a.Fs % 8 == 0;
-    if (sg_staged) a.xq8 = ws.xq8;
+    if (sg_staged && T == 1) a.xq8 = ws.xq8;
     // the one-token down kernel
     const bool k4t1 = T == 1 && d->down_type == MOE_Q2K && a.F == 2048 && a.k <= 6 && a.D % kDecRows == 0 &&
                       (a.Fs == 0 || (a.Fs == 2048 && a.shared_fmt == MOE_Q8_0));
@@ -1254,7 +1316,9 @@ hipError_t launch_small(const moe_layer_desc *d, const void *x, int32_t T, int32
     }
     if ((stage == 0 || stage == 2) && k2 > 0)
     {
-        if (sg_staged) {
+        if (sg_staged && T >= 2) {
+            dec_k2_q8sg_mfma_kernel<<<(route ? 1 : 0) + a.Fs / 8, 64 * kSgmWaves, 0, s>>>(a, route ? 1 : 0);
+        } else if (sg_staged) {
             const int mode = !route ? 0 : (T == 1 && a.k <= 16 ? 2 : 1);
             dec_k2_q8sg4096_kernel<<<(mode == 1 ? 1 : 0) + a.Fs / 8, 320, 0, s>>>(a, mode);
         }

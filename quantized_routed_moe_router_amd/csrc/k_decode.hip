@@ -907,8 +907,8 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))
 // values of its token's hs and its row's weights d*q (exact in fp32), and
 // instruction i takes value i of each quarter, so every product enters the
 // sum once.  The waves' partial sums meet in LDS and the combine adds them
-// in wave order.  Other shared formats and widths: the rows are dotted per
-// token with the routed rows' VALU helpers.
+// in wave order.  One token, other shared formats and widths: the rows are
+// dotted per token with the routed rows' VALU helpers.
 template <int DFMT, int SFMT>
 __global__ void __launch_bounds__(64 * kDecWaves) dec_k4_kernel(FfnArgs a) {
     static_assert(staged_fmt(DFMT), "staged formats only");
@@ -925,7 +925,7 @@ __global__ void __launch_bounds__(64 * kDecWaves) dec_k4_kernel(FfnArgs a) {
     if constexpr (DFMT == MOE_CB2 || SFMT == MOE_CB2) load_codebook(a.codebook, cb_lds);
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int row0 = blockIdx.x * kDecRows;
-    const bool sh_mfma = kShQ8 && a.Fs == 256 * kDecWaves;
+    const bool sh_mfma = kShQ8 && a.Fs == 256 * kDecWaves && a.T >= 2;  // one token: the VALU pass is shorter
     auto shared_down_mfma = [&]() {
         const int tq = lane & 15, kq = lane >> 4;
         const int k0 = 256 * wave + 64 * kq;

@@ -255,7 +255,15 @@ __global__ void __launch_bounds__(256) pf_prep_rows_kernel(const void *x, int n,
     }
     const int t = blockIdx.x, ng = n >> 4;
     float mt = 0.f;
-    for (int g = threadIdx.x; g < ng; g += 256) {
+    // rows of up to 4096 values: a thread's one group stays in registers
+    // between the two passes (longer rows read theirs again)
+    float v0[16];
+    if (ng <= 256 && (int)threadIdx.x < ng) {
+        pf_load16<XT>(x, (int64_t)t * n + 16 * threadIdx.x, v0);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, fabsf(v0[i]));
+    }
+    for (int g = threadIdx.x; ng > 256 && g < ng; g += 256) {
         float v[16];
         pf_load16<XT>(x, (int64_t)t * n + 16 * g, v);
 #pragma unroll
@@ -271,7 +279,12 @@ __global__ void __launch_bounds__(256) pf_prep_rows_kernel(const void *x, int n,
     const int nkb = n >> 8;
     for (int g = threadIdx.x; g < ng; g += 256) {
         float v[16];
-        pf_load16<XT>(x, (int64_t)t * n + 16 * g, v);
+        if (ng <= 256) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) v[i] = v0[i];
+        } else {
+            pf_load16<XT>(x, (int64_t)t * n + 16 * g, v);
+        }
         const int kb = g >> 4, gi = g & 15;
         float sum = 0.f;
 #pragma unroll

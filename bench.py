@@ -10,10 +10,12 @@ DeepSeek-V4-Flash-shaped layer (n_embd 4096, 256 routed experts, top-6, FFN
 width 2048, Q2K routed experts, Q8_0 shared expert, fp32 router), weights
 drawn from N(0, 0.02) and encoded, activations N(0, 1).
 
-The same run then measures the metric's prefill clause on the same resident
-layer: 2048 token rows of bf16 activations through the matrix-core grouped
-GEMMs, reported as the "prefill_2048" object of the line (its own tokens/s,
-MFMA roofline and CPU baseline).
+The same run then measures the other workloads of the metric, each as an
+object of the line with its own tokens/s, roofline and CPU baseline:
+"prefill_2048" (2048 bf16 token rows through the matrix-core grouped GEMMs)
+and "decode_b32" (32 fp32 rows, Zipf-skewed routing) on the same resident
+layer, then "stack43_b1" and "stack43_b8" (the 43-block stack, every layer
+resident, one and eight token rows).  --clauses picks them.
 
 Cold-cache timing: step i runs on device replica i % R of the layer (R x
 2.14 GB, far above the 256 MB last-level cache) with token i % 64, so no
@@ -38,6 +40,10 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, published
 
 
+# the workloads the default run measures after decode_b1, in this order
+CLAUSES = ("prefill_2048", "decode_b32", "stack43_b1", "stack43_b8")
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -60,10 +66,11 @@ def parse():
                     help="only run 20 plain device copies of MB megabytes (scale reference for HBM counters)")
     ap.add_argument("--read-stream", action="store_true",
                     help="only measure the plain read-stream ceiling (moe_read_stream) at several sizes")
-    ap.add_argument("--no-prefill", action="store_true",
-                    help="decode_b1 only: skip the prefill_2048 measurement that the default run adds")
+    ap.add_argument("--clauses", default=",".join(CLAUSES),
+                    help="decode_b1 only: the other workloads the run adds to the line (comma list, empty for none)")
+    ap.add_argument("--no-prefill", action="store_true", help="decode_b1 only: the same as --clauses ''")
     ap.add_argument("--prefill-cpu-seconds", type=float, default=10.0,
-                    help="budget of the oracle CPU baseline of the prefill_2048 measurement")
+                    help="budget of the oracle CPU baseline of each added workload")
     return ap.parse_args()
 
 
@@ -94,7 +101,10 @@ def main():
         return
 
     if args.workload.startswith("stack43"):
-        run_stack(args, int(args.workload.split("_b")[1]))
+        B = int(args.workload.split("_b")[1])
+        st = make_stack(args.stack_layers)
+        print(json.dumps(measure_stack(st, B, args.steps, args.warmup, args.no_graph,
+                                       None if args.no_cpu else args.cpu_seconds)), flush=True)
         return
     if args.workload == "hotlist_43x256":
         run_hotlist(args)
@@ -116,13 +126,32 @@ def main():
     reps = resident_replicas(L, max(1, args.replicas))
     line = measure_layer(args, args.workload, L, reps, args.cpu_seconds)
     line["context"] = PAGES_CONTEXT
-    if args.workload == "decode_b1" and not args.no_prefill:
-        # the metric's prefill clause, measured in the same run on the same
-        # resident layer: bf16 prefill of 2048 token rows on the matrix cores
-        pf = measure_layer(args, "prefill_2048", L, reps, args.prefill_cpu_seconds)
-        for key in ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "data"):
-            pf.pop(key, None)
-        line["prefill_2048"] = pf
+    clauses = [] if args.no_prefill or args.workload != "decode_b1" else [c for c in args.clauses.split(",") if c]
+    for c in clauses:
+        if c not in CLAUSES:
+            sys.exit("unknown clause %r (one of %s)" % (c, ", ".join(CLAUSES)))
+
+    def add(name, sub):
+        for key in ("metric", "n_gpus", "higher_is_better", "scaling", "vs_baseline", "data", "context"):
+            sub.pop(key, None)
+        line[name] = sub
+        log("%s: %.1f tokens/s, %.4f ms per step" % (name, sub["value"], sub["ms_per_step"]))
+
+    # the metric's other workloads, measured in the same run: the batched
+    # ones on the same resident layer, then the stack on layers of its own
+    for c in clauses:
+        if not c.startswith("stack43"):
+            add(c, measure_layer(args, c, L, reps, args.prefill_cpu_seconds))
+    if any(c.startswith("stack43") for c in clauses):
+        del reps
+        import torch
+        torch.cuda.empty_cache()
+        st = make_stack(43)
+        for c in clauses:
+            if c.startswith("stack43"):
+                B = int(c.split("_b")[1])
+                add(c, measure_stack(st, B, 256 if B == 1 else 64, 20 if B == 1 else 8, False,
+                                     None if args.no_cpu else args.prefill_cpu_seconds / 2))
     print(json.dumps(line), flush=True)
 
 
@@ -491,11 +520,10 @@ def measured_traffic(kernel, workload):
     return vals["bytes"]
 
 
-def run_stack(args, B):
-    """The 43-block stack x <- x + MoE(RMSNorm(x)) at B token rows: every
-    layer resident (code-sampled weights of the stack's formats and shapes),
-    one step = the 43 blocks (moe_block_forward each), captured once in a
-    graph and replayed."""
+def make_stack(n_layer):
+    """The 43-block stack's layers, resident: code-sampled weights of the
+    stack's formats and shapes per layer (n_layer of them, 43 = the whole
+    stack), and layer 0 on the host for the CPU baseline."""
     import numpy as np
     import torch
 
@@ -503,7 +531,7 @@ def run_stack(args, B):
     import synth
 
     torch.cuda.set_device(0)
-    n_layer = max(1, min(43, args.stack_layers))
+    n_layer = max(1, min(43, n_layer))
     cb = synth.codebook(4)
     cbd = torch.from_numpy(np.ascontiguousarray(cb)).cuda()
     dev = lambda a: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
@@ -522,10 +550,26 @@ def run_stack(args, B):
             log("%d of %d layers resident (%.1f s)" % (l + 1, n_layer, time.time() - t0))
     torch.cuda.synchronize()
     log("%d layers generated and resident in %.1f s" % (n_layer, time.time() - t0))
+    return Ws, host0
+
+
+def measure_stack(st, B, K, warmup, no_graph, cpu_seconds):
+    """The 43-block stack x <- x + MoE(RMSNorm(x)) at B token rows on the
+    resident layers st: one step = the blocks in order (moe_block_forward
+    each), captured once in a graph and replayed; K timed steps after
+    `warmup`; the CPU oracle for cpu_seconds (None: skipped)."""
+    import numpy as np
+    import torch
+
+    import quantized_routed_moe_router_amd as moe
+    import synth
+
+    Ws, host0 = st
+    n_layer = len(Ws)
     W0 = Ws[0]
     D = W0.n_embd
     x0 = synth.stack43(B=B).x
-    x = dev(x0)
+    x = torch.from_numpy(np.ascontiguousarray(x0)).cuda()
     xn = torch.empty_like(x)
     ws = moe.alloc_workspace(W0, B)
     r = moe.Routing(B, W0.n_expert_used, W0.n_expert)
@@ -534,12 +578,11 @@ def run_stack(args, B):
         for W in Ws:
             moe.block_forward(W, x, ws, eps=1e-6, routing=r)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    K = args.steps
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    if args.no_graph:
+    if no_graph:
         t_start = time.perf_counter()
         ev0.record()
         for _ in range(K):
@@ -594,14 +637,14 @@ def run_stack(args, B):
     log("timed %d steps in %.3f s; gate/up %.2f us per launch" % (K, wall, gu_ms * 1e3))
 
     cpu = None
-    if not args.no_cpu:
+    if cpu_seconds is not None:
         import oracle
         t_start, done = time.perf_counter(), 0
         while True:
             oracle.stack_forward([host0], x0)
             done += 1
             el = time.perf_counter() - t_start
-            if el >= args.cpu_seconds:
+            if el >= cpu_seconds:
                 break
         per_layer = el / done
         cpu = {"value": round(B / (n_layer * per_layer), 4), "unit": "tokens/s", "cores": 1, "kind": "oracle",
@@ -614,7 +657,7 @@ def run_stack(args, B):
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -622,7 +665,7 @@ def run_stack(args, B):
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": args.workload, "tokens_per_step": B, "n_layer": n_layer,
+            "workload": "stack43_b%d" % B, "tokens_per_step": B, "n_layer": n_layer,
             "n_embd": D, "n_expert": W0.n_expert, "n_expert_used": W0.n_expert_used, "n_ff_exp": W0.n_ff_exp,
             "n_ff_shared": W0.n_ff_shared, "formats": "CB2 gate/up, Q2K down, Q8_0 shared, fp32 router",
             "weights": "code-sampled per layer",
@@ -640,7 +683,7 @@ def run_stack(args, B):
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(kernel_name, args.workload),
+            "traffic": measured_traffic(kernel_name, "stack43_b%d" % B),
             "bytes_per_launch": int(gateup_bytes),
             "avg_launch_us": round(gu_ms * 1e3, 3),
             "timing": "HIP events around runs of %d back-to-back stage-3 launches (one per layer), %d runs, "
@@ -648,7 +691,9 @@ def run_stack(args, B):
         },
         "cpu_baseline": cpu,
     }
-    print(json.dumps(line), flush=True)
+    del ws, x, xn
+    torch.cuda.empty_cache()
+    return line
 
 
 def run_hotlist(args):

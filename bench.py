@@ -574,9 +574,16 @@ def measure_stack(st, B, K, warmup, no_graph, cpu_seconds):
     ws = moe.alloc_workspace(W0, B)
     r = moe.Routing(B, W0.n_expert_used, W0.n_expert)
 
+    # eager runs (counter profiling) keep each block's number of active
+    # experts, so that the gate/up kernel's bytes per launch can be averaged
+    # over exactly the launches the counters see
+    seen = [] if no_graph else None
+
     def step():  # one moe_block_forward per block: x <- x + MoE(RMSNorm(x))
         for W in Ws:
             moe.block_forward(W, x, ws, eps=1e-6, routing=r)
+            if seen is not None:
+                seen.append(r.n_active.clone())
 
     for _ in range(warmup):
         step()
@@ -627,6 +634,9 @@ def measure_stack(st, B, K, warmup, no_graph, cpu_seconds):
     times = [a.elapsed_time(b) / n_layer for a, b in evs]
     gu_ms = float(np.median(times))
     nu = float(r.n_active.item())
+    launch_nu = None
+    if seen:  # every block of the warm-up and timed steps, then the timing runs on layer 0's routing
+        launch_nu = (float(torch.cat(seen).double().sum().item()) + nu * n_runs * n_layer) / (len(seen) + n_runs * n_layer)
     gu_expert = 2 * synth.tensor_bytes(synth.CB2, W0.n_ff_exp * D)
     dn_expert = synth.tensor_bytes(synth.Q2K, D * W0.n_ff_exp)
     sh = 3 * synth.tensor_bytes(synth.Q8_0, W0.n_ff_shared * D)
@@ -676,6 +686,7 @@ def measure_stack(st, B, K, warmup, no_graph, cpu_seconds):
         "hbm_gbps": round(n_layer * layer_bytes / (ms_step * 1e-3) / 1e9, 1),
         "algorithmic_bytes_per_step": int(n_layer * layer_bytes),
         "unique_experts_layer0": nu,
+        "unique_experts_per_gate_up_launch": launch_nu,
         "roofline": {
             "kernel": kernel_name,
             "bound": "hbm",

@@ -285,6 +285,7 @@ constexpr int kBucketWaves = 8;
 // (prefill at 2048 rows and top-6 is 12,288): the scatter pass then reads
 // them back from LDS instead of one dependent global round trip per 64 pairs.
 constexpr int kBucketKeyCache = 16384;
+static_assert(kBucketKeyCache % (kBucketWaves * 64) == 0, "whole keys per lane");
 
 __global__ void __launch_bounds__(512) bucket_kernel(const int32_t *__restrict__ topk_idx, int P, int E,
                                                      int32_t *__restrict__ count, int32_t *__restrict__ offset,
@@ -300,10 +301,25 @@ __global__ void __launch_bounds__(512) bucket_kernel(const int32_t *__restrict__
     const int seg = ((P + kBucketWaves - 1) / kBucketWaves + 63) / 64 * 64;
     const int s0 = w * seg, s1 = min(P, s0 + seg);
     const bool cached = P <= kBucketKeyCache;
-    for (int p = s0 + lane; p < s1; p += 64) {
-        const int e = topk_idx[p];
-        if (cached) keys[p] = e;  // a wave later reads back only the pairs it wrote
-        atomicAdd(&wc[w][e], 1);
+    if (cached) {
+        // every key of the lane's share in flight at once (at most
+        // kBucketKeyCache / (kBucketWaves * 64) = 32), then the counts
+        constexpr int kPer = kBucketKeyCache / (kBucketWaves * 64);
+        int kv[kPer];
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            const int p = s0 + lane + 64 * i;
+            kv[i] = p < s1 ? topk_idx[p] : -1;
+        }
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+            if (kv[i] >= 0) {
+                keys[s0 + lane + 64 * i] = kv[i];  // a wave later reads back only the pairs it wrote
+                atomicAdd(&wc[w][kv[i]], 1);
+            }
+        }
+    } else {
+        for (int p = s0 + lane; p < s1; p += 64) atomicAdd(&wc[w][topk_idx[p]], 1);
     }
     __syncthreads();
     for (int e = tid; e < E; e += blockDim.x) {  // exclusive prefix over waves
@@ -318,7 +334,7 @@ __global__ void __launch_bounds__(512) bucket_kernel(const int32_t *__restrict__
     __syncthreads();
     for (int e = tid; e < kMaxExperts; e += blockDim.x) scan_tmp[e] = e < E ? tot[e] : 0;
     __syncthreads();
-    for (int o = 1; o < kMaxExperts; o <<= 1) {  // inclusive scan over experts
+    for (int o = 1; o < E; o <<= 1) {  // inclusive scan over experts (entries from E on stay 0)
         int a0 = tid, a1 = tid + 512;
         int v0 = scan_tmp[a0] + (a0 >= o ? scan_tmp[a0 - o] : 0);
         int v1 = scan_tmp[a1] + (a1 >= o ? scan_tmp[a1 - o] : 0);
@@ -358,7 +374,7 @@ __global__ void __launch_bounds__(512) bucket_kernel(const int32_t *__restrict__
     __syncthreads();
     for (int e = tid; e < kMaxExperts; e += blockDim.x) scan_tmp[e] = (e < E && tot[e] > 0) ? 1 : 0;
     __syncthreads();
-    for (int o = 1; o < kMaxExperts; o <<= 1) {
+    for (int o = 1; o < E; o <<= 1) {
         int a0 = tid, a1 = tid + 512;
         int v0 = scan_tmp[a0] + (a0 >= o ? scan_tmp[a0 - o] : 0);
         int v1 = scan_tmp[a1] + (a1 >= o ? scan_tmp[a1 - o] : 0);
@@ -367,7 +383,7 @@ __global__ void __launch_bounds__(512) bucket_kernel(const int32_t *__restrict__
         scan_tmp[a1] = v1;
         __syncthreads();
     }
-    const int na = scan_tmp[kMaxExperts - 1];
+    const int na = scan_tmp[E - 1];
     for (int e = tid; e < E; e += blockDim.x) active[e] = -1;
     __syncthreads();
     for (int e = tid; e < E; e += blockDim.x)

@@ -54,8 +54,15 @@
  *  - Return 0 (MOE_OK) or a negative moe_status; err (host, may be NULL)
  *    receives a NUL-terminated message of at most errlen bytes.
  *  - T = 0 is valid and enqueues nothing.
- *  - Reentrant: no global mutable state beyond a lazily filled per-device
- *    property cache.
+ *  - Reentrant.  Global state: a lazily filled per-device property cache,
+ *    and per device one second stream of the library's (default priority,
+ *    made on first use) with two events.  On the many-row bf16 path
+ *    (moe_layer_forward, moe_expert_ffn) the shared expert runs on that
+ *    stream, forked from `stream` and joined back into it by the events, so
+ *    every result is still ordered on `stream` (under graph capture the fork
+ *    and the join are captured as edges; a call made while `stream` is being
+ *    captured before that stream exists runs the shared expert in line).
+ *    Host threads that call on one device take turns over the fork and join.
  *  - Limits: 1 <= k <= 16, k <= E <= 1024, D % 256 == 0, F % 64 == 0, the
  *    64-weight chunks of a row (n_in/64) a power of two up to 64 or a
  *    multiple of 64, weight and activation base addresses 16-byte aligned,

@@ -156,7 +156,7 @@ hipError_t prefill_bf16_overlapped(const moe_layer_desc *d, const void *x, int32
         return es;
     }
     if (route) e = launch_router_logits(d, x, T, MOE_BF16, w, s);
-    if (route && e == hipSuccess) e = launch_route_finish(d, T, r, w, s);
+    if (route && e == hipSuccess) e = launch_route_finish(d, x, T, MOE_BF16, r, w, s);
     if (e == hipSuccess) return launch_prefill(d, x, T, MOE_BF16, r, y, flags, w, s, 0, ss->join);
     (void)hipStreamWaitEvent(s, ss->join, 0);
     return e;
@@ -181,7 +181,7 @@ hipError_t forward(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_
         if (done || e != hipSuccess) return e;
     }
     if (stage == 0 || stage == 1) e = launch_router_logits(d, x, T, x_type, w, s);
-    if (e == hipSuccess && (stage == 0 || stage == 2)) e = launch_route_finish(d, T, r, w, s);
+    if (e == hipSuccess && (stage == 0 || stage == 2)) e = launch_route_finish(d, x, T, x_type, r, w, s);
     if (e == hipSuccess && (stage == 0 || stage >= 3))
         e = prefill_path_ok(d, T, x_type) ? launch_prefill(d, x, T, x_type, r, y, flags, w, s, stage)
                                           : launch_ffn_large(d, x, T, x_type, r, y, flags, w, s, st3);

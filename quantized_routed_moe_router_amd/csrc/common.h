@@ -35,6 +35,13 @@ __host__ __device__ inline int64_t fmt_bytes(int fmt, int64_t n) {
 
 // ---- scalar conversions ---------------------------------------------------
 
+// two floats -> a bf16 pair (lo in the low half), each rounded to nearest even
+MOE_DEV uint32_t bf16x2_rne(float lo, float hi) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){lo, hi}, b2));
+}
+
 MOE_DEV float half_bits_to_float(uint32_t bits) {
     _Float16 h = __builtin_bit_cast(_Float16, (uint16_t)(bits & 0xFFFFu));
     return (float)h;
@@ -768,10 +775,15 @@ struct Workspace {
     uint32_t *sg_aq;
     float *sg_ainv;       // [T]
     float *xn;            // [T][D] normalised rows of moe_block_forward (when not fused)
+    // the two-pass router of many bf16 rows: per D slice, the logit sums of
+    // pass 1 [kRtSplitMax][T][E] and the experts' sums of w^2 [kRtSplitMax][E]
+    float *rt_part;
+    float *rt_wn;
     size_t bytes;
 };
 
 constexpr int kPfTileRows = 64;  // pair rows per tile of the many-row bf16 path
+constexpr int kRtSplitMax = 16;  // D slices of the two-pass router's first pass
 
 // Routing of 17 to 127 rows with at most kRouteMidPairs pairs (the pairs
 // are then sorted in one block) and at most 256 experts: the fp64 router
@@ -835,6 +847,9 @@ __host__ inline Workspace workspace_layout(const moe_layer_desc *d, int32_t T, v
     w.sg_aq = (uint32_t *)take((size_t)T * (size_t)(D > Fs ? D : Fs) * 2);
     w.sg_ainv = (float *)take(sizeof(float) * (size_t)T);
     w.xn = (float *)take(sizeof(float) * (size_t)T * (size_t)D);
+    const bool rt = T >= 128;  // the two-pass router may run (bf16 rows)
+    w.rt_part = (float *)take(rt ? sizeof(float) * kRtSplitMax * (size_t)T * (size_t)E : 0);
+    w.rt_wn = (float *)take(rt ? sizeof(float) * kRtSplitMax * (size_t)E : 0);
     w.bytes = off;
     return w;
 }
@@ -849,8 +864,10 @@ struct RoutingPtrs {
 
 hipError_t launch_router_logits(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type,
                                  const Workspace &ws, hipStream_t s);
-hipError_t launch_route_finish(const moe_layer_desc *d, int32_t T, const RoutingPtrs &r, const Workspace &ws,
-                               hipStream_t s);
+// x, x_type: the rows the logits came from (the two-pass router of many bf16
+// rows computes the candidates' logits again from them)
+hipError_t launch_route_finish(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type,
+                               const RoutingPtrs &r, const Workspace &ws, hipStream_t s);
 hipError_t launch_route(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type, const RoutingPtrs &r,
                         const Workspace &ws, hipStream_t s);
 // decode schedule (few rows): stage 0 = all, 1..4 = its four kernels

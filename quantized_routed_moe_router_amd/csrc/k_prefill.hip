@@ -144,11 +144,6 @@ MOE_DEV void vmem_wait_at_most() {
 // are finite)
 MOE_DEV uint16_t bf16_rne(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
-MOE_DEV uint32_t bf16x2_rne(float lo, float hi) {
-    typedef float f2 __attribute__((ext_vector_type(2)));
-    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){lo, hi}, b2));
-}
 
 // 16 activations -> t-ordered int8 halves (byte 4j+n of the unit holds value
 // 4n+j, the order the code dwords of a Q2K group take after >> 2j & 0x03030303)

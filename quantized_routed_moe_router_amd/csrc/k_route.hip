@@ -391,6 +391,276 @@ __global__ void __launch_bounds__(512) bucket_kernel(const int32_t *__restrict__
     if (tid == 0) n_active[0] = na;
 }
 
+// ---- many bf16 rows: the router in two passes ---------------------------------
+// The selection must be that of the fp64 router ("Understanding Dwarf Star",
+// 5.3.2: fp32 router weights, the top k by logit, then the softmax over them).
+// Pass 1 (router_bf16x3_kernel) bounds every logit cheaply on the bf16 matrix
+// cores: x is exact in bf16 and each fp32 weight is split into three bf16
+// parts w = w1 + w2 + w3 (8 + 8 + 8 significant bits), so every product is
+// exact and only the fp32 accumulation rounds.  A block takes 128 tokens x 128
+// experts over one of kRtSplit slices of D; wave w owns experts 32w..32w+31
+// against the 4 token subtiles (v_mfma_f32_32x32x16_bf16, three per subtile
+// and 16-wide step of k); lane (c, h) loads 8 consecutive values of token row
+// c and of expert row c per step, the layout both operands share.  It also
+// writes each slice's sum of w^2 per expert.
+// Pass 2 (router_refine_kernel, a wave per token) adds the slices per logit and bounds its
+// error by eps_e = C |x| |w_e| (Cauchy-Schwarz; C covers the 3 D / kRtSplit
+// fp32 roundings of a slice's sum, truncating or not, with a factor 2 to
+// spare).  An expert whose upper bound stays below the k-th largest lower
+// bound has k experts strictly above it, so only the others can be in the top
+// k.  Their logits are computed again exactly as the fp64 router does (exact
+// products of bf16 x and fp32 w, fp64 sums plus the bias), and the top k and
+// the weights come from those, with the usual order (logit desc, index asc).
+constexpr int kRtSplit = kRtSplitMax;       // D slices of pass 1
+constexpr int kRtTok = 128, kRtExp = 128;   // block tile of pass 1
+
+bool router_split_ok(int T, int D, int E, int x_type) {
+    return x_type == MOE_BF16 && T >= 128 && (D == 1024 || D == 2048 || D == 4096) && E <= 256;
+}
+
+template <int STEPS>  // 16-wide steps of k per slice: D / (16 kRtSplit), a multiple of 4
+__global__ void __launch_bounds__(256) router_bf16x3_kernel(const float *__restrict__ W, const uint16_t *__restrict__ x,
+                                                            int T, int D, int E, float *__restrict__ part,
+                                                            float *__restrict__ wn) {
+    typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+    typedef float v16f __attribute__((ext_vector_type(16)));
+    const int tt = blockIdx.x, et = blockIdx.y, sl = blockIdx.z;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, c = lane & 31, h = lane >> 5;
+    // Columns of step j for lane half h: 64 (j / 4) + 32 h + 8 (j % 4) + 0..7
+    // (a permutation of k that both operands share), so that over 4 steps a
+    // lane reads 32 consecutive values of its row: whole cache lines instead
+    // of 32-byte pieces of 32 rows per step.
+    const int k0 = sl * (16 * STEPS) + 32 * h;
+    const int eo = et * kRtExp + 32 * wave + c;  // the lane's expert column
+    const float *wr = W + (int64_t)min(eo, E - 1) * D + k0;
+    const uint16_t *xr[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) xr[m] = x + (int64_t)min(tt * kRtTok + 32 * m + c, T - 1) * D + k0;
+    v16f acc[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[m][v] = 0.f;
+    float ss = 0.f;
+    // a ring of 4 steps' operands: step s of a group of 4 reads buffer s,
+    // which then takes step s of the next group
+    f32x4 wa[4][2];
+    u32x4 xa[4][4];
+    auto load = [&](int g, int s) {
+        const int o = 64 * g + 8 * s;
+        wa[s][0] = *(const f32x4 *)(wr + o);
+        wa[s][1] = *(const f32x4 *)(wr + o + 4);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) xa[s][m] = *(const u32x4 *)(xr[m] + o);
+    };
+#pragma unroll
+    for (int s = 0; s < 4; ++s) load(0, s);
+    constexpr int G = STEPS / 4;
+#pragma unroll 1
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const float wv[8] = {wa[s][0][0], wa[s][0][1], wa[s][0][2], wa[s][0][3],
+                                 wa[s][1][0], wa[s][1][1], wa[s][1][2], wa[s][1][3]};
+            u32x4 xs[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) xs[m] = xa[s][m];
+            if (g + 1 < G) load(g + 1, s);
+            __builtin_amdgcn_sched_barrier(0);  // the loads go out here, not next to their use
+            uint32_t p1[4], p2[4], p3[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float a = wv[2 * i], bb = wv[2 * i + 1];
+                ss = __builtin_fmaf(a, a, ss);
+                ss = __builtin_fmaf(bb, bb, ss);
+                p1[i] = bf16x2_rne(a, bb);
+                const float ra = a - __uint_as_float(p1[i] << 16), rb = bb - __uint_as_float(p1[i] & 0xFFFF0000u);
+                p2[i] = bf16x2_rne(ra, rb);
+                const float qa = ra - __uint_as_float(p2[i] << 16), qb = rb - __uint_as_float(p2[i] & 0xFFFF0000u);
+                p3[i] = bf16x2_rne(qa, qb);
+            }
+            v8bf w1, w2, w3;
+            __builtin_memcpy(&w1, p1, 16);
+            __builtin_memcpy(&w2, p2, 16);
+            __builtin_memcpy(&w3, p3, 16);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                v8bf a;
+                __builtin_memcpy(&a, &xs[m], 16);
+                acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w1, acc[m], 0, 0, 0);
+                acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w2, acc[m], 0, 0, 0);
+                acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w3, acc[m], 0, 0, 0);
+            }
+        }
+    }
+    // lane (c, h): expert column c, token rows 8 (v / 4) + 4 h + v % 4 of each subtile
+    if (eo < E) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int t = tt * kRtTok + 32 * m + 8 * (v >> 2) + 4 * h + (v & 3);
+                if (t < T) part[((int64_t)sl * T + t) * E + eo] = acc[m][v];
+            }
+    }
+    ss += __shfl_xor(ss, 32, kWave);  // the two halves of each 16-wide step
+    if (tt == 0 && h == 0 && eo < E) wn[sl * E + eo] = ss;
+}
+
+// Pass 2: a wave per token (4 per block); lane l holds the token's V = D / 64
+// columns from V l, as bf16 pairs.
+template <int PER, int V>
+__global__ void __launch_bounds__(256) router_refine_kernel(const float *__restrict__ W, const float *__restrict__ bias,
+                                                            const uint16_t *__restrict__ x,
+                                                            const float *__restrict__ part,
+                                                            const float *__restrict__ wn, int T, int D, int E, int k,
+                                                            float route_scale, int32_t *__restrict__ idx_out,
+                                                            float *__restrict__ w_out) {
+    __shared__ int32_t cand_e[4][256];
+    __shared__ double cand_v[4][256];
+    __shared__ int32_t by_rank[4][256];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, t = blockIdx.x * 4 + wave;
+    if (t >= T) return;  // the whole wave: no block barrier below
+    const int q0 = V * lane;
+    uint32_t xp[V / 2];
+#pragma unroll
+    for (int g = 0; g < V / 8; ++g) {
+        const u32x4 u = *(const u32x4 *)(x + (int64_t)t * D + q0 + 8 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xp[4 * g + i] = u[i];
+    }
+    double sq = 0.0;
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i) {
+        const double a = (double)__uint_as_float(xp[i] << 16), b = (double)__uint_as_float(xp[i] & 0xFFFF0000u);
+        sq = __builtin_fma(a, a, sq);
+        sq = __builtin_fma(b, b, sq);
+    }
+    const double nx = sqrt(seg_sum_f64(sq, kWave)) * (1.0 + 0x1p-40);
+    // bounds of the lane's experts l + 64 i
+    const double C = 2.0 * 2.0 * 3.0 * (double)(D / kRtSplit) * 0x1p-24;
+    double lb[PER], ub[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E) {
+            double a = 0.0, n2 = 0.0;
+#pragma unroll
+            for (int sl = 0; sl < kRtSplit; ++sl) {
+                a += (double)part[((int64_t)sl * T + t) * E + e];
+                n2 += (double)wn[sl * E + e];
+            }
+            // the fp32 sums of squares round too: 1 + 2^-10 covers them
+            const double eps = C * nx * sqrt(n2 * (1.0 + 0x1p-10)) + 0x1p-100;
+            if (bias) a += (double)bias[e];
+            lb[i] = a - eps;
+            ub[i] = a + eps;
+        } else {
+            lb[i] = ub[i] = -__builtin_inf();
+        }
+    }
+    // L: the k-th largest lower bound (k rounds of the wave maximum, one
+    // lane's copy taken out per round)
+    double L = -__builtin_inf();
+    {
+        uint32_t taken = 0;
+        for (int r = 0; r < k; ++r) {
+            double best = -__builtin_inf();
+            int bi = -1;
+#pragma unroll
+            for (int i = 0; i < PER; ++i)
+                if (!((taken >> i) & 1u) && lb[i] > best) {
+                    best = lb[i];
+                    bi = i;
+                }
+            const double m = wave_max_f64(best);
+            const uint64_t has = __ballot(bi >= 0 && best == m);
+            if (has && lane == (int)__builtin_ctzll(has)) taken |= 1u << bi;
+            L = m;
+        }
+    }
+    // the candidates (cnt >= k: every expert whose lower bound reaches L)
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const bool cnd = lane + 64 * i < E && ub[i] >= L;
+        const uint64_t m = __ballot(cnd);
+        if (cnd) cand_e[wave][cnt + __popcll(m & ((1ull << lane) - 1ull))] = lane + 64 * i;
+        cnt += __popcll(m);
+    }
+    __builtin_amdgcn_wave_barrier();
+    // their logits again, exactly: fp64 sums of exact products in column
+    // order within the lane, then the fixed butterfly over the lanes
+    // Each row in two halves of the lane's columns; the loads of the next two
+    // halves are in flight under each half's products.
+    constexpr int H = V / 8;  // f32x4 per half
+    const float *wb = W + q0;
+    auto load_half = [&](int j, f32x4 (&buf)[H]) {
+        const float *wr = wb + (int64_t)cand_e[wave][j >> 1] * D + (j & 1) * (V / 2);
+#pragma unroll
+        for (int g = 0; g < H; ++g) buf[g] = *(const f32x4 *)(wr + 4 * g);
+    };
+    double acc = 0.0;
+    auto half = [&](int j, const f32x4 (&buf)[H]) {
+        if (!(j & 1)) acc = 0.0;
+#pragma unroll
+        for (int g = 0; g < H; ++g) {
+            const int i = (j & 1) * (V / 4) + 2 * g;  // the pair index of the half's values
+            const uint32_t p0 = xp[i], p1 = xp[i + 1];
+            acc = __builtin_fma((double)__uint_as_float(p0 << 16), (double)buf[g][0], acc);
+            acc = __builtin_fma((double)__uint_as_float(p0 & 0xFFFF0000u), (double)buf[g][1], acc);
+            acc = __builtin_fma((double)__uint_as_float(p1 << 16), (double)buf[g][2], acc);
+            acc = __builtin_fma((double)__uint_as_float(p1 & 0xFFFF0000u), (double)buf[g][3], acc);
+        }
+        if (j & 1) {
+            double v = seg_sum_f64(acc, kWave);
+            if (bias) v += (double)bias[cand_e[wave][j >> 1]];
+            if (lane == 0) cand_v[wave][j >> 1] = v;
+        }
+    };
+    f32x4 ra[H], rb[H], rc[H];  // three halves: two in flight under the products of the third
+    const int nh = 2 * cnt;       // even: both halves of every row
+    load_half(0, ra);
+    load_half(1, rb);
+    for (int j = 0; j < nh; j += 3) {
+        if (j + 2 < nh) load_half(j + 2, rc);
+        half(j, ra);
+        if (j + 1 >= nh) break;
+        if (j + 3 < nh) load_half(j + 3, ra);
+        half(j + 1, rb);
+        if (j + 2 >= nh) break;
+        if (j + 4 < nh) load_half(j + 4, rb);
+        half(j + 2, rc);
+    }
+    __builtin_amdgcn_wave_barrier();
+    // ranks among the candidates (logit descending, then expert ascending)
+    for (int c = lane; c < cnt; c += kWave) {
+        const double v = cand_v[wave][c];
+        const int e = cand_e[wave][c];
+        int rank = 0;
+        for (int o = 0; o < cnt; ++o) rank += before(cand_v[wave][o], cand_e[wave][o], v, e);
+        by_rank[wave][rank] = c;
+    }
+    __builtin_amdgcn_wave_barrier();
+    // slot s = rank s; w_s = route_scale exp(l_s - l_0) / sum_j exp(l_j - l_0)
+    // in fp64, as the other selections compute it
+    double my_v = 0.0;
+    int my_e = 0;
+    if (lane < k) {
+        const int c = by_rank[wave][lane];
+        my_v = cand_v[wave][c];
+        my_e = cand_e[wave][c];
+    }
+    const double mx = __shfl(my_v, 0, kWave);
+    const double ex = lane < k ? exp(my_v - mx) : 0.0;
+    double den = ex;
+    for (int o = 1; o < 64; o <<= 1) den += __shfl_xor(den, o, kWave);
+    if (lane < k) {
+        idx_out[(int64_t)t * k + lane] = my_e;
+        w_out[(int64_t)t * k + lane] = (float)((double)route_scale * ex / den);
+    }
+}
+
 // one block per expert row for few tokens, 16 x 16 tiles for many
 bool router_rows_ok(int T) { return T <= 16; }
 // the matrix-core router: a wave per 16 x 16 tile from 128 rows on (the k
@@ -402,6 +672,15 @@ bool router_mfma4_ok(int T, int D) { return T > 16 && D % 512 == 0; }
 hipError_t launch_router_logits(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type,
                                 const Workspace &ws, hipStream_t s) {
     const int D = d->n_embd, E = d->n_expert;
+    if (router_split_ok(T, D, E, x_type)) {
+        const dim3 g((unsigned)((T + kRtTok - 1) / kRtTok), (unsigned)((E + kRtExp - 1) / kRtExp), kRtSplit);
+        auto go = [&](auto kern) { kern<<<g, 256, 0, s>>>(d->router_w, (const uint16_t *)x, T, D, E, ws.rt_part, ws.rt_wn); };
+        static_assert((1024 / (16 * kRtSplit)) % 4 == 0, "whole groups of 4 steps");
+        if (D == 1024) go(router_bf16x3_kernel<1024 / (16 * kRtSplit)>);
+        else if (D == 2048) go(router_bf16x3_kernel<2048 / (16 * kRtSplit)>);
+        else go(router_bf16x3_kernel<4096 / (16 * kRtSplit)>);
+        return hipGetLastError();
+    }
     if (router_rows_ok(T)) {
         if (x_type == MOE_BF16)
             router_row_kernel<MOE_BF16><<<E, 256, 0, s>>>(d->router_w, d->router_bias, x, T, D, E, ws.logits);
@@ -435,9 +714,34 @@ hipError_t launch_router_logits(const moe_layer_desc *d, const void *x, int32_t 
     return hipGetLastError();
 }
 
-hipError_t launch_route_finish(const moe_layer_desc *d, int32_t T, const RoutingPtrs &r, const Workspace &ws,
-                               hipStream_t s) {
+template <int PER>
+static void launch_refine(const moe_layer_desc *d, const void *x, int32_t T, const RoutingPtrs &r,
+                          const Workspace &ws, hipStream_t s) {
+    const int D = d->n_embd;
+    auto go = [&](auto kern) {
+        kern<<<(T + 3) / 4, 256, 0, s>>>(d->router_w, d->router_bias, (const uint16_t *)x, ws.rt_part, ws.rt_wn, T, D,
+                                         d->n_expert, d->n_expert_used, d->route_scale, r.topk_idx, r.topk_w);
+    };
+    if (D == 1024) go(router_refine_kernel<PER, 16>);
+    else if (D == 2048) go(router_refine_kernel<PER, 32>);
+    else go(router_refine_kernel<PER, 64>);
+}
+
+hipError_t launch_route_finish(const moe_layer_desc *d, const void *x, int32_t T, int32_t x_type,
+                               const RoutingPtrs &r, const Workspace &ws, hipStream_t s) {
     const int E = d->n_expert, k = d->n_expert_used, P = T * k;
+    if (router_split_ok(T, d->n_embd, E, x_type)) {
+        if (E <= 64) launch_refine<1>(d, x, T, r, ws, s);
+        else if (E <= 128) launch_refine<2>(d, x, T, r, ws, s);
+        else launch_refine<4>(d, x, T, r, ws, s);
+        if (P <= kMidPairs)
+            bucket_mid_kernel<<<1, kMaxExperts, 0, s>>>(r.topk_idx, P, E, r.count, r.offset, r.perm, r.pos, r.active,
+                                                        r.n_active);
+        else
+            bucket_kernel<<<1, 512, 0, s>>>(r.topk_idx, P, E, r.count, r.offset, r.perm, r.pos, r.active,
+                                            r.n_active);
+        return hipGetLastError();
+    }
     if (route_small_ok(T, E, k)) {
         route_finish_small_kernel<<<1, 256, 0, s>>>(ws.logits, T, E, k, d->route_scale, r.topk_idx, r.topk_w,
                                                      r.count, r.offset, r.perm, r.pos, r.active, r.n_active);
@@ -471,7 +775,7 @@ hipError_t launch_route(const moe_layer_desc *d, const void *x, int32_t T, int32
                         const Workspace &ws, hipStream_t s) {
     hipError_t e = launch_router_logits(d, x, T, x_type, ws, s);
     if (e != hipSuccess) return e;
-    return launch_route_finish(d, T, r, ws, s);
+    return launch_route_finish(d, x, T, x_type, r, ws, s);
 }
 
 }  // namespace moe

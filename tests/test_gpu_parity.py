@@ -197,6 +197,46 @@ def test_route_many_rows_matrix_cores(T, bf16):
     gu.check_routing(r, idx_ref, w_ref, L.n_expert)
 
 
+@pytest.mark.parametrize("T,E,k,D,bias", [(128, 256, 6, 4096, False), (203, 40, 6, 1024, True),
+                                          (300, 200, 8, 2048, True), (160, 256, 6, 1024, False),
+                                          (129, 64, 1, 4096, True)])
+def test_route_two_pass_bf16(T, E, k, D, bias):
+    # 128 or more bf16 rows: the logits are first bounded on the bf16 matrix
+    # cores (three-part weights, fp32 sums), then the experts that can still
+    # reach the top k are computed again exactly.  Exact ties (four copies of
+    # one enlarged router row, so they reach the top k often), a near tie (a
+    # fifth copy with one weight changed in its last bit), ragged token and
+    # expert tiles, k = 1 and 8, a Zipf bias: indices and bucketing bit-exact
+    # against the fp64 oracle, weights within tolerance
+    import quantized_routed_moe_router_amd as moe
+    L = synth.make_layer(120 + T, 0, D=D, E=E, k=k, F=256, Fs=0)
+    rw = np.array(L.router_w, dtype=np.float32).reshape(E, D)
+    base = E // 3
+    rw[base] *= np.float32(3.0)
+    for e in (base + 1, base + 2, E - 1):
+        rw[e] = rw[base]
+    near = rw[base].copy()
+    near[D // 2] = np.nextafter(near[D // 2], np.float32(np.inf))
+    rw[base + 3] = near
+    L.router_w = rw.reshape(np.shape(L.router_w))
+    if bias:
+        L.router_bias = synth.zipf_bias(121 + T, E)
+    x = synth.activations(122 + T, T, D)
+    xb = synth.to_bf16_bits(x)
+    idx_ref, w_ref, gap = oracle.route(L, x_bf16=xb)
+    n_tied = int(np.sum(np.isin(idx_ref, [base, base + 1, base + 2, base + 3, E - 1])))
+    print("two-pass route T=%d E=%d D=%d: %d selections among the tied rows, smallest k/k+1 gap %.3g"
+          % (T, E, D, n_tied, float(np.min(gap))))
+    assert n_tied > 0
+    W = gu.upload(L)
+    xd = gu.x_to_device(x_bf16=xb)
+    ws = moe.alloc_workspace(W, T, moe.BF16)
+    r = moe.Routing(T, k, E)
+    moe.route(W, xd, r, ws)
+    torch.cuda.synchronize()
+    gu.check_routing(r, idx_ref, w_ref, E)
+
+
 @pytest.mark.parametrize("T,E,k,D", [(17, 1024, 1, 512), (170, 64, 6, 512), (256, 8, 4, 512), (64, 512, 16, 512),
                                      (33, 300, 3, 512), (171, 64, 6, 512), (33, 256, 6, 4096), (100, 64, 8, 2048),
                                      (17, 16, 2, 1024), (127, 200, 8, 4096)])

@@ -132,7 +132,10 @@ size_t moe_workspace_size(const moe_layer_desc *desc, int32_t max_rows, int32_t 
  * 5.3.7 step 1 and the sparse indexing of step 2).
  * x: [T][D] fp32 (x_type MOE_F32) or bf16 (MOE_BF16).  out: every array set.
  * The logits are accumulated in fp64 so that the selected indices do not
- * depend on the summation order. */
+ * depend on the summation order.  From 128 bf16 rows on (n_embd 1024, 2048
+ * or 4096, at most 256 experts) they are first bounded on the bf16 matrix
+ * cores, and only the experts whose bound can still reach the top k are
+ * summed in fp64: the indices and weights are those of the fp64 sums. */
 int moe_route(const moe_layer_desc *desc, const void *x, int32_t T, int32_t x_type, const moe_routing *out,
               void *ws, size_t ws_bytes, void *stream, char *err, size_t errlen);
 

@@ -3,6 +3,7 @@
 // 5.3.7 step 1 and the sparse indexing of step 2).
 #include <type_traits>
 
+#include "ffn_dev.h"
 #include "route_dev.h"
 
 namespace moe {
@@ -418,59 +419,77 @@ bool router_split_ok(int T, int D, int E, int x_type) {
     return x_type == MOE_BF16 && T >= 128 && (D == 1024 || D == 2048 || D == 4096) && E <= 256;
 }
 
-template <int STEPS>  // 16-wide steps of k per slice: D / (16 kRtSplit), a multiple of 4
+// Pass 1 in groups of 64 columns (4 steps of 16): the block's 128 token rows
+// of a group are copied into LDS once for its 4 waves (global-to-LDS DMA,
+// two stages, the next group's copies in flight under this group's
+// products), and each lane loads its expert row's 32 columns of the group
+// (one 128-byte line) into registers, also a group ahead.  Columns of step s
+// for lane half h: 32 h + 8 s + 0..7 of the group (a permutation of k that
+// both operands share).  LDS unit j (16 bytes) of token row r holds the
+// row's columns 8 (j ^ (r & 7)) .. + 7, so that the 32 rows one read spans
+// fall on different banks.
+constexpr int kRtGroupUnits = kRtTok * 8;  // 16-byte units of one group's token rows: 1024
+template <int G>  // groups of 64 columns per slice: D / (64 kRtSplit)
 __global__ void __launch_bounds__(256) router_bf16x3_kernel(const float *__restrict__ W, const uint16_t *__restrict__ x,
                                                             int T, int D, int E, float *__restrict__ part,
                                                             float *__restrict__ wn) {
     typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
     typedef float v16f __attribute__((ext_vector_type(16)));
+    __shared__ __align__(16) u32x4 xs[2][kRtGroupUnits];
     const int tt = blockIdx.x, et = blockIdx.y, sl = blockIdx.z;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, c = lane & 31, h = lane >> 5;
-    // Columns of step j for lane half h: 64 (j / 4) + 32 h + 8 (j % 4) + 0..7
-    // (a permutation of k that both operands share), so that over 4 steps a
-    // lane reads 32 consecutive values of its row: whole cache lines instead
-    // of 32-byte pieces of 32 rows per step.
-    const int k0 = sl * (16 * STEPS) + 32 * h;
+    const int kb = sl * (64 * G);  // the slice's first column
     const int eo = et * kRtExp + 32 * wave + c;  // the lane's expert column
-    const float *wr = W + (int64_t)min(eo, E - 1) * D + k0;
-    const uint16_t *xr[4];
+    const float *wr = W + (int64_t)min(eo, E - 1) * D + kb + 32 * h;
+    // the DMA sources of the lane's 4 units per group (copy i: units 256 i + 64 wave + lane)
+    const uint16_t *xsrc[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) xr[m] = x + (int64_t)min(tt * kRtTok + 32 * m + c, T - 1) * D + k0;
+    for (int i = 0; i < 4; ++i) {
+        const int p = 256 * i + 64 * wave + lane, r = p >> 3, j = p & 7;
+        xsrc[i] = x + (int64_t)min(tt * kRtTok + r, T - 1) * D + kb + 8 * (j ^ (r & 7));
+    }
+    const uint32_t lbase = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr(&xs[0][0])) + 1024u * (uint32_t)wave;
+    auto issue = [&](int g) {  // 4 copies per wave
+        const uint32_t st = lbase + (uint32_t)((g & 1) * kRtGroupUnits * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dma16_m0(xsrc[i] + 64 * g, st + 4096u * (uint32_t)i);
+    };
+    f32x4 wg[2][8];  // the lane's 32 columns of the group, two groups
+    auto load_w = [&](int g, int b) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) wg[b][q] = *(const f32x4 *)(wr + 64 * g + 4 * q);
+        // issued here, in this order after the copies: the copy waits below count them
+        __asm__ volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    };
     v16f acc[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[m][v] = 0.f;
     float ss = 0.f;
-    // a ring of 4 steps' operands: step s of a group of 4 reads buffer s,
-    // which then takes step s of the next group
-    f32x4 wa[4][2];
-    u32x4 xa[4][4];
-    auto load = [&](int g, int s) {
-        const int o = 64 * g + 8 * s;
-        wa[s][0] = *(const f32x4 *)(wr + o);
-        wa[s][1] = *(const f32x4 *)(wr + o + 4);
+    issue(0);
+    load_w(0, 0);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) xa[s][m] = *(const u32x4 *)(xr[m] + o);
-    };
-#pragma unroll
-    for (int s = 0; s < 4; ++s) load(0, s);
-    constexpr int G = STEPS / 4;
-#pragma unroll 1
     for (int g = 0; g < G; ++g) {
+        const int b = g & 1;
+        if (g + 1 < G) {
+            issue(g + 1);
+            load_w(g + 1, b ^ 1);
+            // group g's copies have landed: after them this wave issued its
+            // 8 row loads of group g, then 4 copies and 8 loads of group g + 1
+            vmem_wait_le<20>();
+        } else {
+            vmem_wait_le<8>();  // after them: the 8 row loads of group g
+        }
+        barrier_only();  // every wave's copies of group g are in LDS
+        const u32x4 *st = &xs[b][0];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const float wv[8] = {wa[s][0][0], wa[s][0][1], wa[s][0][2], wa[s][0][3],
-                                 wa[s][1][0], wa[s][1][1], wa[s][1][2], wa[s][1][3]};
-            u32x4 xs[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) xs[m] = xa[s][m];
-            if (g + 1 < G) load(g + 1, s);
-            __builtin_amdgcn_sched_barrier(0);  // the loads go out here, not next to their use
             uint32_t p1[4], p2[4], p3[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float a = wv[2 * i], bb = wv[2 * i + 1];
+                const float a = wg[b][2 * s + (i >> 1)][2 * (i & 1)], bb = wg[b][2 * s + (i >> 1)][2 * (i & 1) + 1];
                 ss = __builtin_fmaf(a, a, ss);
                 ss = __builtin_fmaf(bb, bb, ss);
                 p1[i] = bf16x2_rne(a, bb);
@@ -485,13 +504,16 @@ __global__ void __launch_bounds__(256) router_bf16x3_kernel(const float *__restr
             __builtin_memcpy(&w3, p3, 16);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
+                const int r = 32 * m + c;
+                const u32x4 av = st[r * 8 + ((4 * h + s) ^ (r & 7))];
                 v8bf a;
-                __builtin_memcpy(&a, &xs[m], 16);
+                __builtin_memcpy(&a, &av, 16);
                 acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w1, acc[m], 0, 0, 0);
                 acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w2, acc[m], 0, 0, 0);
                 acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, w3, acc[m], 0, 0, 0);
             }
         }
+        barrier_only();  // every wave is done with stage b before group g + 2's copies
     }
     // lane (c, h): expert column c, token rows 8 (v / 4) + 4 h + v % 4 of each subtile
     if (eo < E) {
@@ -503,7 +525,7 @@ __global__ void __launch_bounds__(256) router_bf16x3_kernel(const float *__restr
                 if (t < T) part[((int64_t)sl * T + t) * E + eo] = acc[m][v];
             }
     }
-    ss += __shfl_xor(ss, 32, kWave);  // the two halves of each 16-wide step
+    ss += __shfl_xor(ss, 32, kWave);  // the two halves of each group's 64 columns
     if (tt == 0 && h == 0 && eo < E) wn[sl * E + eo] = ss;
 }
 
@@ -675,10 +697,10 @@ hipError_t launch_router_logits(const moe_layer_desc *d, const void *x, int32_t 
     if (router_split_ok(T, D, E, x_type)) {
         const dim3 g((unsigned)((T + kRtTok - 1) / kRtTok), (unsigned)((E + kRtExp - 1) / kRtExp), kRtSplit);
         auto go = [&](auto kern) { kern<<<g, 256, 0, s>>>(d->router_w, (const uint16_t *)x, T, D, E, ws.rt_part, ws.rt_wn); };
-        static_assert((1024 / (16 * kRtSplit)) % 4 == 0, "whole groups of 4 steps");
-        if (D == 1024) go(router_bf16x3_kernel<1024 / (16 * kRtSplit)>);
-        else if (D == 2048) go(router_bf16x3_kernel<2048 / (16 * kRtSplit)>);
-        else go(router_bf16x3_kernel<4096 / (16 * kRtSplit)>);
+        static_assert(1024 % (64 * kRtSplit) == 0, "whole groups of 64 columns per slice");
+        if (D == 1024) go(router_bf16x3_kernel<1024 / (64 * kRtSplit)>);
+        else if (D == 2048) go(router_bf16x3_kernel<2048 / (64 * kRtSplit)>);
+        else go(router_bf16x3_kernel<4096 / (64 * kRtSplit)>);
         return hipGetLastError();
     }
     if (router_rows_ok(T)) {

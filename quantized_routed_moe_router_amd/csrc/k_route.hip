@@ -685,9 +685,10 @@ __global__ void __launch_bounds__(256) router_refine_kernel(const float *__restr
 
 // one block per expert row for few tokens, 16 x 16 tiles for many
 bool router_rows_ok(int T) { return T <= 16; }
-// the matrix-core router: a wave per 16 x 16 tile from 128 rows on (the k
-// steps need D % 128 == 0); below that, for more rows than the one-block
-// router takes, four waves per tile (D % 512 == 0)
+// the fp64 matrix-core router: a wave per 16 x 16 tile from 128 rows on (the
+// k steps need D % 128 == 0; bf16 rows of the shapes router_split_ok takes
+// go to the two-pass router instead); below that, for more rows than the
+// one-block router takes, four waves per tile (D % 512 == 0)
 bool router_mfma_ok(int T, int D) { return T >= 128 && D % 128 == 0; }
 bool router_mfma4_ok(int T, int D) { return T > 16 && D % 512 == 0; }
 

@@ -206,8 +206,9 @@ def test_route_two_pass_bf16(T, E, k, D, bias):
     # reach the top k are computed again exactly.  Exact ties (four copies of
     # one enlarged router row, so they reach the top k often), a near tie (a
     # fifth copy with one weight changed in its last bit), ragged token and
-    # expert tiles, k = 1 and 8, a Zipf bias: indices and bucketing bit-exact
-    # against the fp64 oracle, weights within tolerance
+    # expert tiles, k = 1 and 8, a Zipf bias, a zero row (all logits equal):
+    # indices and bucketing bit-exact against the fp64 oracle, weights within
+    # tolerance
     import quantized_routed_moe_router_amd as moe
     L = synth.make_layer(120 + T, 0, D=D, E=E, k=k, F=256, Fs=0)
     rw = np.array(L.router_w, dtype=np.float32).reshape(E, D)
@@ -222,6 +223,7 @@ def test_route_two_pass_bf16(T, E, k, D, bias):
     if bias:
         L.router_bias = synth.zipf_bias(121 + T, E)
     x = synth.activations(122 + T, T, D)
+    x[5] = 0.0  # every logit equal (the bias alone): every expert is a candidate
     xb = synth.to_bf16_bits(x)
     idx_ref, w_ref, gap = oracle.route(L, x_bf16=xb)
     n_tied = int(np.sum(np.isin(idx_ref, [base, base + 1, base + 2, base + 3, E - 1])))

@@ -29,6 +29,13 @@ constexpr int kSgqRows = 16;       // weight rows of a block (the MFMA's columns
 constexpr int kSgqTileTok = 16;    // token rows of an MFMA tile
 constexpr int kSgqTiles = 2;       // token tiles per pass
 constexpr int kSgqGroup = 4;       // block pairs a wave loads before it multiplies
+constexpr int kSgqChunk = 64;      // block pairs of a row staged in LDS at a time
+constexpr int kSgqRowDw = kSgqChunk * 17 + 4;  // LDS dwords of a staged row (4 more: rows 4 banks apart)
+constexpr int kSgqRowU = kSgqRowDw / 4;        // 16-byte units of a staged row
+constexpr int kSgqUnits = kSgqRows * kSgqRowU;  // 16-byte units of the staged rows
+constexpr int kSgqDmaSlots = ((kSgqUnits + 63) / 64 + kSgqWaves - 1) / kSgqWaves;  // 64-unit copies a wave
+// 4-byte copies per thread of a full chunk
+constexpr int kSgqStage4 = (kSgqRows * kSgqChunk * 17 + 64 * kSgqWaves - 1) / (64 * kSgqWaves);
 struct SgqArgs {
     const uint8_t *w0, *w1;  // MODE 0: gate and up rows [Fs][K]; MODE 1: down rows [D][K]
     const uint32_t *aq;      // token records [T][K/64][32 dwords]
@@ -38,26 +45,68 @@ struct SgqArgs {
     int ld;                  // row length of out
 };
 
-MOE_DEV uint2 sgq_load2(const uint8_t *p) {
-    uint2 v;
-    __builtin_memcpy(&v, __builtin_assume_aligned(p, 4), 8);
-    return v;
-}
-
 // MODE 0: block b owns gate rows 8b..8b+7 (columns 0-7) and the same up rows
 // (columns 8-15) and writes hs = silu(g) * u; MODE 1: down rows 16b..16b+15,
-// written to ys.  Wave w takes the block pairs w, w + 8, ...; the partial
-// sums meet in LDS and are added in wave order.
+// written to ys.  The block's 16 weight rows are first copied into LDS, up to
+// kSgqChunk block pairs of each at a time, by 16-byte global-to-LDS copies
+// along the rows, so that the matrix operands come from LDS instead of from
+// many narrow global loads.  Wave w takes the block pairs w, w + 8, ... of a
+// chunk; the partial sums meet in LDS and are added in wave order.
 template <int MODE>
 __global__ void __launch_bounds__(64 * kSgqWaves) sgq_gemm_kernel(SgqArgs a) {
     __shared__ float red[kSgqWaves][kSgqTiles][4][64];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    __shared__ u32x4 wst4[kSgqRows * kSgqRowDw / 4];
+    uint32_t *const wst = (uint32_t *)wst4;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int j = lane & 15, g = lane >> 4;  // the lane's weight row (column) and k group
     const int64_t rowbytes = (int64_t)(a.K / 32) * kQ8Bytes;
-    const uint8_t *wrow;
-    if (MODE == 0) wrow = (j < 8 ? a.w0 : a.w1) + (int64_t)(8 * blockIdx.x + (j & 7)) * rowbytes;
-    else wrow = a.w0 + (int64_t)(kSgqRows * blockIdx.x + j) * rowbytes;
     const int np = a.K / 64;
+    auto row_ptr = [&](int r) -> const uint8_t * {
+        if (MODE == 0) return (r < 8 ? a.w0 : a.w1) + (int64_t)(8 * blockIdx.x + (r & 7)) * rowbytes;
+        return a.w0 + (int64_t)(kSgqRows * blockIdx.x + r) * rowbytes;
+    };
+    // block pairs c0.. of the 16 rows go to wst (row r at dword r * kSgqRowDw,
+    // 17 dwords a pair)
+    const bool vec = (np & 3) == 0;  // rows and chunk starts 16-byte aligned
+    // vec: the copies go straight to LDS (global_load_lds, 64 consecutive
+    // 16-byte units an instruction): LDS unit P = 273 r + u holds unit u of
+    // row r's chunk; a unit beyond the chunk (the pad, or a short chunk's
+    // tail) takes a copy of unit 0 and is never read.
+    auto stage_dma = [&](int c0) {
+        const int nu = min(kSgqChunk, np - c0) * 17 >> 2;
+        const uint32_t lds0 = lds_addr(wst4);
+#pragma unroll
+        for (int i = 0; i < kSgqDmaSlots; ++i) {
+            const int slot = i * kSgqWaves + wave;
+            if (slot * 64 < kSgqUnits) {  // uniform over the wave
+                const int P = slot * 64 + lane, r = min(P / kSgqRowU, kSgqRows - 1), u = P - r * kSgqRowU;
+                const uint8_t *src = row_ptr(r) + (int64_t)c0 * 68 + 16 * (u < nu ? u : 0);
+                const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds0 + 16u * (uint32_t)(slot * 64));
+                if (P < kSgqUnits) dma16_m0(src, m0);
+            }
+        }
+    };
+    // rows whose length is not a multiple of 16 bytes: dwords through
+    // registers, 8 a thread in flight at a time
+    auto stage_words = [&](int c0) {
+        const int rdw = min(kSgqChunk, np - c0) * 17;
+        for (int i0 = 0; i0 < kSgqStage4; i0 += 8) {
+            uint32_t v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int q = tid + (i0 + i) * 64 * kSgqWaves, r = q / rdw, u = q - r * rdw;
+                if (i0 + i < kSgqStage4 && r < kSgqRows) v[i] = load_u32(row_ptr(r) + (int64_t)c0 * 68 + 4 * u);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int q = tid + (i0 + i) * 64 * kSgqWaves, r = q / rdw, u = q - r * rdw;
+                if (i0 + i < kSgqStage4 && r < kSgqRows) wst[r * kSgqRowDw + u] = v[i];
+            }
+        }
+    };
+    const bool once = np <= kSgqChunk;  // every pass of tokens uses the one staged chunk
+    bool staged = false;
+    const uint32_t *const wrow = wst + j * kSgqRowDw;
     for (int t0 = 0; t0 < a.T; t0 += kSgqTiles * kSgqTileTok) {
         float tot[kSgqTiles][4];
 #pragma unroll
@@ -73,65 +122,84 @@ __global__ void __launch_bounds__(64 * kSgqWaves) sgq_gemm_kernel(SgqArgs a) {
             aok[i] = t < a.T;
             arow[i] = a.aq + (int64_t)(aok[i] ? t : 0) * np * kSgqPairDw + 4 * g;
         }
-        // groups of kSgqGroup pairs: every load of a group is issued before
-        // its products, so that a wave has that many pairs in flight
-        for (int p0 = wave; p0 < np; p0 += kSgqGroup * kSgqWaves) {
-            uint2 e[kSgqGroup], o[kSgqGroup];
-            uint32_t w0[kSgqGroup], w8[kSgqGroup];
-            u32x4 hv[kSgqGroup][kSgqTiles], lv[kSgqGroup][kSgqTiles];
+        for (int c0 = 0; c0 < np; c0 += kSgqChunk) {
+            const bool restage = !(once && staged);
+            const int cend = min(np, c0 + kSgqChunk);
+            if (restage && !vec) {
+                __syncthreads();  // the earlier chunk's reads of wst are done
+                stage_words(c0);
+                __syncthreads();
+            }
+            // groups of kSgqGroup pairs: the activation loads of a group are
+            // issued before its products, those of the first group also
+            // before the chunk's copies to LDS, so that both streams are in
+            // flight together (every wave runs the first group, even one
+            // with no pair in it, so that all of them reach the barriers)
+            for (int p0 = c0 + wave, first = 1;; p0 += kSgqGroup * kSgqWaves, first = 0) {
+                if (!first && p0 >= cend) break;  // uniform over the wave
+                u32x4 hv[kSgqGroup][kSgqTiles], lv[kSgqGroup][kSgqTiles];
 #pragma unroll
-            for (int u = 0; u < kSgqGroup; ++u) {
-                const int p = p0 + u * kSgqWaves;
-                const bool pok = p < np;
-                const uint8_t *wp = wrow + (int64_t)(pok ? p : 0) * 2 * kQ8Bytes;
-                e[u] = sgq_load2(wp + 4 + 8 * g);
-                o[u] = sgq_load2(wp + 36 + 8 * g);
-                w0[u] = load_u32(wp);
-                w8[u] = load_u32(wp + 32);
+                for (int u = 0; u < kSgqGroup; ++u) {
+                    const int p = p0 + u * kSgqWaves;
+                    const bool pok = p < cend;
 #pragma unroll
-                for (int i = 0; i < kSgqTiles; ++i) {
-                    hv[u][i] = lv[u][i] = u32x4{0u, 0u, 0u, 0u};
-                    if (aok[i] && pok) {
-                        hv[u][i] = *(const u32x4 *)(arow[i] + p * kSgqPairDw);
-                        lv[u][i] = *(const u32x4 *)(arow[i] + p * kSgqPairDw + 16);
+                    for (int i = 0; i < kSgqTiles; ++i) {
+                        hv[u][i] = lv[u][i] = u32x4{0u, 0u, 0u, 0u};
+                        if (aok[i] && pok) {
+                            hv[u][i] = *(const u32x4 *)(arow[i] + p * kSgqPairDw);
+                            lv[u][i] = *(const u32x4 *)(arow[i] + p * kSgqPairDw + 16);
+                        }
+                    }
+                }
+                if (restage && vec && first) {
+                    // after the group's activation loads, so that both are in
+                    // flight at once
+                    if (staged) __syncthreads();  // the earlier chunk's reads of wst are done
+                    stage_dma(c0);
+                    vmem_wait_le<0>();
+                    __syncthreads();
+                }
+#pragma unroll
+                for (int u = 0; u < kSgqGroup; ++u) {
+                    const int p = p0 + u * kSgqWaves;
+                    if (p >= cend) break;  // uniform over the wave
+                    const uint32_t *wp = wrow + 17 * (p - c0);
+                    const uint32_t w0 = wp[0], w8 = wp[8];
+                    uint2 ev = {wp[1 + 2 * g], wp[2 + 2 * g]};
+                    const uint2 ov = {wp[9 + 2 * g], wp[10 + 2 * g]};
+                    if (g == 3) ev.y = __builtin_amdgcn_alignbyte(w8, w0, 2);  // codes 0, 1, 30, 31
+                    const float d0 = half_bits_to_float(w0 & 0xFFFFu), d1 = half_bits_to_float(w8 >> 16);
+                    long be, bo;
+                    __builtin_memcpy(&be, &ev, 8);
+                    __builtin_memcpy(&bo, &ov, 8);
+#pragma unroll
+                    for (int i = 0; i < kSgqTiles; ++i) {
+                        long he, ho, le, lo;
+                        const uint2 hve = {hv[u][i][0], hv[u][i][1]}, hvo = {hv[u][i][2], hv[u][i][3]};
+                        const uint2 lve = {lv[u][i][0], lv[u][i][1]}, lvo = {lv[u][i][2], lv[u][i][3]};
+                        __builtin_memcpy(&he, &hve, 8);
+                        __builtin_memcpy(&ho, &hvo, 8);
+                        __builtin_memcpy(&le, &lve, 8);
+                        __builtin_memcpy(&lo, &lvo, 8);
+                        const sgq_v4i z = {0, 0, 0, 0};
+                        sgq_v4i ce = __builtin_amdgcn_mfma_i32_16x16x32_i8(he, be, z, 0, 0, 0);
+                        sgq_v4i co = __builtin_amdgcn_mfma_i32_16x16x32_i8(ho, bo, z, 0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            ce[r] <<= 8;
+                            co[r] <<= 8;
+                        }
+                        ce = __builtin_amdgcn_mfma_i32_16x16x32_i8(le, be, ce, 0, 0, 0);
+                        co = __builtin_amdgcn_mfma_i32_16x16x32_i8(lo, bo, co, 0, 0, 0);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            tot[i][r] = __builtin_fmaf(d0, (float)ce[r], tot[i][r]);
+                            tot[i][r] = __builtin_fmaf(d1, (float)co[r], tot[i][r]);
+                        }
                     }
                 }
             }
-#pragma unroll
-            for (int u = 0; u < kSgqGroup; ++u) {
-                if (p0 + u * kSgqWaves >= np) break;  // uniform over the wave
-                uint2 ev = e[u];
-                if (g == 3) ev.y = __builtin_amdgcn_alignbyte(w8[u], w0[u], 2);  // codes 0, 1, 30, 31
-                const float d0 = half_bits_to_float(w0[u] & 0xFFFFu), d1 = half_bits_to_float(w8[u] >> 16);
-                long be, bo;
-                __builtin_memcpy(&be, &ev, 8);
-                __builtin_memcpy(&bo, &o[u], 8);
-#pragma unroll
-                for (int i = 0; i < kSgqTiles; ++i) {
-                    long he, ho, le, lo;
-                    const uint2 hve = {hv[u][i][0], hv[u][i][1]}, hvo = {hv[u][i][2], hv[u][i][3]};
-                    const uint2 lve = {lv[u][i][0], lv[u][i][1]}, lvo = {lv[u][i][2], lv[u][i][3]};
-                    __builtin_memcpy(&he, &hve, 8);
-                    __builtin_memcpy(&ho, &hvo, 8);
-                    __builtin_memcpy(&le, &lve, 8);
-                    __builtin_memcpy(&lo, &lvo, 8);
-                    const sgq_v4i z = {0, 0, 0, 0};
-                    sgq_v4i ce = __builtin_amdgcn_mfma_i32_16x16x32_i8(he, be, z, 0, 0, 0);
-                    sgq_v4i co = __builtin_amdgcn_mfma_i32_16x16x32_i8(ho, bo, z, 0, 0, 0);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        ce[r] <<= 8;
-                        co[r] <<= 8;
-                    }
-                    ce = __builtin_amdgcn_mfma_i32_16x16x32_i8(le, be, ce, 0, 0, 0);
-                    co = __builtin_amdgcn_mfma_i32_16x16x32_i8(lo, bo, co, 0, 0, 0);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        tot[i][r] = __builtin_fmaf(d0, (float)ce[r], tot[i][r]);
-                        tot[i][r] = __builtin_fmaf(d1, (float)co[r], tot[i][r]);
-                    }
-                }
-            }
+            staged = true;
         }
         // output element of register r: token 4g + r of the tile, column j
 #pragma unroll

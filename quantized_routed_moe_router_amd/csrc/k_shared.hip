@@ -29,7 +29,7 @@ constexpr int kSgqRows = 16;       // weight rows of a block (the MFMA's columns
 constexpr int kSgqTileTok = 16;    // token rows of an MFMA tile
 constexpr int kSgqTiles = 2;       // token tiles per pass
 constexpr int kSgqGroup = 4;       // block pairs a wave loads before it multiplies
-constexpr int kSgqChunk = 64;      // block pairs of a row staged in LDS at a time
+constexpr int kSgqChunk = 64;      // block pairs of a staged row: reductions up to 4096 values
 constexpr int kSgqRowDw = kSgqChunk * 17 + 4;  // LDS dwords of a staged row (4 more: rows 4 banks apart)
 constexpr int kSgqRowU = kSgqRowDw / 4;        // 16-byte units of a staged row
 constexpr int kSgqUnits = kSgqRows * kSgqRowU;  // 16-byte units of the staged rows
@@ -65,37 +65,37 @@ __global__ void __launch_bounds__(64 * kSgqWaves) sgq_gemm_kernel(SgqArgs a) {
         if (MODE == 0) return (r < 8 ? a.w0 : a.w1) + (int64_t)(8 * blockIdx.x + (r & 7)) * rowbytes;
         return a.w0 + (int64_t)(kSgqRows * blockIdx.x + r) * rowbytes;
     };
-    // block pairs c0.. of the 16 rows go to wst (row r at dword r * kSgqRowDw,
-    // 17 dwords a pair)
+    // the 16 rows go to wst (row r at dword r * kSgqRowDw, 17 dwords a block
+    // pair); the launcher takes this kernel only for np <= kSgqChunk
     const bool vec = (np & 3) == 0;  // rows and chunk starts 16-byte aligned
     // vec: the copies go straight to LDS (global_load_lds, 64 consecutive
     // 16-byte units an instruction): LDS unit P = 273 r + u holds unit u of
     // row r's chunk; a unit beyond the chunk (the pad, or a short chunk's
     // tail) takes a copy of unit 0 and is never read.
-    auto stage_dma = [&](int c0) {
-        const int nu = min(kSgqChunk, np - c0) * 17 >> 2;
+    auto stage_dma = [&]() {
+        const int nu = np * 17 >> 2;
         const uint32_t lds0 = lds_addr(wst4);
 #pragma unroll
         for (int i = 0; i < kSgqDmaSlots; ++i) {
             const int slot = i * kSgqWaves + wave;
             if (slot * 64 < kSgqUnits) {  // uniform over the wave
                 const int P = slot * 64 + lane, r = min(P / kSgqRowU, kSgqRows - 1), u = P - r * kSgqRowU;
-                const uint8_t *src = row_ptr(r) + (int64_t)c0 * 68 + 16 * (u < nu ? u : 0);
+                const uint8_t *src = row_ptr(r) + 16 * (u < nu ? u : 0);
                 const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds0 + 16u * (uint32_t)(slot * 64));
                 if (P < kSgqUnits) dma16_m0(src, m0);
             }
         }
     };
-    // rows whose length is not a multiple of 16 bytes: dwords through
-    // registers, 8 a thread in flight at a time
-    auto stage_words = [&](int c0) {
-        const int rdw = min(kSgqChunk, np - c0) * 17;
+    // rows whose length is not a multiple of 16 bytes (64 or 128 values):
+    // dwords through registers, 8 a thread in flight at a time
+    auto stage_words = [&]() {
+        const int rdw = np * 17;
         for (int i0 = 0; i0 < kSgqStage4; i0 += 8) {
             uint32_t v[8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int q = tid + (i0 + i) * 64 * kSgqWaves, r = q / rdw, u = q - r * rdw;
-                if (i0 + i < kSgqStage4 && r < kSgqRows) v[i] = load_u32(row_ptr(r) + (int64_t)c0 * 68 + 4 * u);
+                if (i0 + i < kSgqStage4 && r < kSgqRows) v[i] = load_u32(row_ptr(r) + 4 * u);
             }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -104,8 +104,11 @@ __global__ void __launch_bounds__(64 * kSgqWaves) sgq_gemm_kernel(SgqArgs a) {
             }
         }
     };
-    const bool once = np <= kSgqChunk;  // every pass of tokens uses the one staged chunk
-    bool staged = false;
+    if (!vec) {
+        stage_words();
+        __syncthreads();
+    }
+    bool staged = !vec;  // every pass over the tokens uses the one staged copy
     const uint32_t *const wrow = wst + j * kSgqRowDw;
     for (int t0 = 0; t0 < a.T; t0 += kSgqTiles * kSgqTileTok) {
         float tot[kSgqTiles][4];
@@ -122,84 +125,74 @@ __global__ void __launch_bounds__(64 * kSgqWaves) sgq_gemm_kernel(SgqArgs a) {
             aok[i] = t < a.T;
             arow[i] = a.aq + (int64_t)(aok[i] ? t : 0) * np * kSgqPairDw + 4 * g;
         }
-        for (int c0 = 0; c0 < np; c0 += kSgqChunk) {
-            const bool restage = !(once && staged);
-            const int cend = min(np, c0 + kSgqChunk);
-            if (restage && !vec) {
-                __syncthreads();  // the earlier chunk's reads of wst are done
-                stage_words(c0);
+        // groups of kSgqGroup pairs: the activation loads of a group are
+        // issued before its products, those of the first group also
+        // before the weights' copies to LDS, so that both streams are in
+        // flight together (every wave runs the first group, even one
+        // with no pair in it, so that all of them reach the barriers)
+        for (int p0 = wave, first = 1;; p0 += kSgqGroup * kSgqWaves, first = 0) {
+            if (!first && p0 >= np) break;  // uniform over the wave
+            u32x4 hv[kSgqGroup][kSgqTiles], lv[kSgqGroup][kSgqTiles];
+#pragma unroll
+            for (int u = 0; u < kSgqGroup; ++u) {
+                const int p = p0 + u * kSgqWaves;
+                const bool pok = p < np;
+#pragma unroll
+                for (int i = 0; i < kSgqTiles; ++i) {
+                    hv[u][i] = lv[u][i] = u32x4{0u, 0u, 0u, 0u};
+                    if (aok[i] && pok) {
+                        hv[u][i] = *(const u32x4 *)(arow[i] + p * kSgqPairDw);
+                        lv[u][i] = *(const u32x4 *)(arow[i] + p * kSgqPairDw + 16);
+                    }
+                }
+            }
+            if (!staged && first) {
+                // after the group's activation loads, so that both are in
+                // flight at once (every wave passes here)
+                stage_dma();
+                vmem_wait_le<0>();
                 __syncthreads();
+                staged = true;
             }
-            // groups of kSgqGroup pairs: the activation loads of a group are
-            // issued before its products, those of the first group also
-            // before the chunk's copies to LDS, so that both streams are in
-            // flight together (every wave runs the first group, even one
-            // with no pair in it, so that all of them reach the barriers)
-            for (int p0 = c0 + wave, first = 1;; p0 += kSgqGroup * kSgqWaves, first = 0) {
-                if (!first && p0 >= cend) break;  // uniform over the wave
-                u32x4 hv[kSgqGroup][kSgqTiles], lv[kSgqGroup][kSgqTiles];
 #pragma unroll
-                for (int u = 0; u < kSgqGroup; ++u) {
-                    const int p = p0 + u * kSgqWaves;
-                    const bool pok = p < cend;
+            for (int u = 0; u < kSgqGroup; ++u) {
+                const int p = p0 + u * kSgqWaves;
+                if (p >= np) break;  // uniform over the wave
+                const uint32_t *wp = wrow + 17 * p;
+                const uint32_t w0 = wp[0], w8 = wp[8];
+                uint2 ev = {wp[1 + 2 * g], wp[2 + 2 * g]};
+                const uint2 ov = {wp[9 + 2 * g], wp[10 + 2 * g]};
+                if (g == 3) ev.y = __builtin_amdgcn_alignbyte(w8, w0, 2);  // codes 0, 1, 30, 31
+                const float d0 = half_bits_to_float(w0 & 0xFFFFu), d1 = half_bits_to_float(w8 >> 16);
+                long be, bo;
+                __builtin_memcpy(&be, &ev, 8);
+                __builtin_memcpy(&bo, &ov, 8);
 #pragma unroll
-                    for (int i = 0; i < kSgqTiles; ++i) {
-                        hv[u][i] = lv[u][i] = u32x4{0u, 0u, 0u, 0u};
-                        if (aok[i] && pok) {
-                            hv[u][i] = *(const u32x4 *)(arow[i] + p * kSgqPairDw);
-                            lv[u][i] = *(const u32x4 *)(arow[i] + p * kSgqPairDw + 16);
-                        }
+                for (int i = 0; i < kSgqTiles; ++i) {
+                    long he, ho, le, lo;
+                    const uint2 hve = {hv[u][i][0], hv[u][i][1]}, hvo = {hv[u][i][2], hv[u][i][3]};
+                    const uint2 lve = {lv[u][i][0], lv[u][i][1]}, lvo = {lv[u][i][2], lv[u][i][3]};
+                    __builtin_memcpy(&he, &hve, 8);
+                    __builtin_memcpy(&ho, &hvo, 8);
+                    __builtin_memcpy(&le, &lve, 8);
+                    __builtin_memcpy(&lo, &lvo, 8);
+                    const sgq_v4i z = {0, 0, 0, 0};
+                    sgq_v4i ce = __builtin_amdgcn_mfma_i32_16x16x32_i8(he, be, z, 0, 0, 0);
+                    sgq_v4i co = __builtin_amdgcn_mfma_i32_16x16x32_i8(ho, bo, z, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        ce[r] <<= 8;
+                        co[r] <<= 8;
                     }
-                }
-                if (restage && vec && first) {
-                    // after the group's activation loads, so that both are in
-                    // flight at once
-                    if (staged) __syncthreads();  // the earlier chunk's reads of wst are done
-                    stage_dma(c0);
-                    vmem_wait_le<0>();
-                    __syncthreads();
-                }
+                    ce = __builtin_amdgcn_mfma_i32_16x16x32_i8(le, be, ce, 0, 0, 0);
+                    co = __builtin_amdgcn_mfma_i32_16x16x32_i8(lo, bo, co, 0, 0, 0);
 #pragma unroll
-                for (int u = 0; u < kSgqGroup; ++u) {
-                    const int p = p0 + u * kSgqWaves;
-                    if (p >= cend) break;  // uniform over the wave
-                    const uint32_t *wp = wrow + 17 * (p - c0);
-                    const uint32_t w0 = wp[0], w8 = wp[8];
-                    uint2 ev = {wp[1 + 2 * g], wp[2 + 2 * g]};
-                    const uint2 ov = {wp[9 + 2 * g], wp[10 + 2 * g]};
-                    if (g == 3) ev.y = __builtin_amdgcn_alignbyte(w8, w0, 2);  // codes 0, 1, 30, 31
-                    const float d0 = half_bits_to_float(w0 & 0xFFFFu), d1 = half_bits_to_float(w8 >> 16);
-                    long be, bo;
-                    __builtin_memcpy(&be, &ev, 8);
-                    __builtin_memcpy(&bo, &ov, 8);
-#pragma unroll
-                    for (int i = 0; i < kSgqTiles; ++i) {
-                        long he, ho, le, lo;
-                        const uint2 hve = {hv[u][i][0], hv[u][i][1]}, hvo = {hv[u][i][2], hv[u][i][3]};
-                        const uint2 lve = {lv[u][i][0], lv[u][i][1]}, lvo = {lv[u][i][2], lv[u][i][3]};
-                        __builtin_memcpy(&he, &hve, 8);
-                        __builtin_memcpy(&ho, &hvo, 8);
-                        __builtin_memcpy(&le, &lve, 8);
-                        __builtin_memcpy(&lo, &lvo, 8);
-                        const sgq_v4i z = {0, 0, 0, 0};
-                        sgq_v4i ce = __builtin_amdgcn_mfma_i32_16x16x32_i8(he, be, z, 0, 0, 0);
-                        sgq_v4i co = __builtin_amdgcn_mfma_i32_16x16x32_i8(ho, bo, z, 0, 0, 0);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            ce[r] <<= 8;
-                            co[r] <<= 8;
-                        }
-                        ce = __builtin_amdgcn_mfma_i32_16x16x32_i8(le, be, ce, 0, 0, 0);
-                        co = __builtin_amdgcn_mfma_i32_16x16x32_i8(lo, bo, co, 0, 0, 0);
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            tot[i][r] = __builtin_fmaf(d0, (float)ce[r], tot[i][r]);
-                            tot[i][r] = __builtin_fmaf(d1, (float)co[r], tot[i][r]);
-                        }
+                    for (int r = 0; r < 4; ++r) {
+                        tot[i][r] = __builtin_fmaf(d0, (float)ce[r], tot[i][r]);
+                        tot[i][r] = __builtin_fmaf(d1, (float)co[r], tot[i][r]);
                     }
                 }
             }
-            staged = true;
         }
         // output element of register r: token 4g + r of the tile, column j
 #pragma unroll
@@ -239,7 +232,8 @@ __global__ void __launch_bounds__(64 * kSgqWaves) sgq_gemm_kernel(SgqArgs a) {
 }
 
 bool shared_q8_mfma_ok(const moe_layer_desc *d) {
-    return d->n_ff_shared > 0 && d->shared_type == MOE_Q8_0 && d->n_embd % 64 == 0 && d->n_ff_shared % 64 == 0;
+    return d->n_ff_shared > 0 && d->shared_type == MOE_Q8_0 && d->n_embd % 64 == 0 && d->n_ff_shared % 64 == 0 &&
+           d->n_embd <= 64 * kSgqChunk && d->n_ff_shared <= 64 * kSgqChunk;
 }
 
 // stage 3: the gate/up GEMM into hs, on x's records; stage 4: the down GEMM

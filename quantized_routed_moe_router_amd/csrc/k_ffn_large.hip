@@ -92,11 +92,24 @@ __global__ void __launch_bounds__(256) combine_kernel(FfnArgs a) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= (int64_t)a.T * a.D) return;
     const int t = (int)(i / a.D), d = (int)(i % a.D);
+    // every slot's row and weight first, then every slot's value, so that
+    // the loads are in flight together; the sum is taken in slot order
+    int64_t off[kMaxUsed];
+    float w[kMaxUsed], v[kMaxUsed];
+#pragma unroll
+    for (int s = 0; s < kMaxUsed; ++s)
+        if (s < a.k) {
+            const int p = t * a.k + s;
+            off[s] = (int64_t)a.pos[p] * a.D + d;
+            w[s] = a.topk_w[p];
+        }
+#pragma unroll
+    for (int s = 0; s < kMaxUsed; ++s)
+        if (s < a.k) v[s] = a.ypart[off[s]];
     float acc = a.Fs > 0 ? a.ys[i] : 0.f;
-    for (int s = 0; s < a.k; ++s) {
-        const int p = t * a.k + s;
-        acc = __builtin_fmaf(a.topk_w[p], a.ypart[(int64_t)a.pos[p] * a.D + d], acc);
-    }
+#pragma unroll
+    for (int s = 0; s < kMaxUsed; ++s)
+        if (s < a.k) acc = __builtin_fmaf(w[s], v[s], acc);
     if (a.flags & MOE_ACCUMULATE) acc += a.y[i];
     a.y[i] = acc;
 }
